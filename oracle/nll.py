@@ -1,0 +1,104 @@
+"""Weighted log-softmax NLL over the tree, and the same loss averaged over branches (fp64).
+
+Tree Training, Abstract: the loss averaged over all branches, each branch
+trained on its own, is the same number as a per-token weighted loss whose
+weight is the fraction of branches passing through the token.
+
+Readings (the pages are silent):
+  * a branch is an input sequence, counted with multiplicity, B = #sequences;
+  * a branch's loss is the SUM of its next-token NLLs, and the branch-averaged
+    loss is (1/B) * sum over branches -- the only reading under which the
+    identity is exact;
+  * every non-root row t is a target, predicted from its parent's logits row:
+    its token id x_t indexes the parent's vocabulary row, its weight is
+    w_t = n_pass(t)/B.
+"""
+import numpy as np
+
+
+def _lse(z):
+    m = z.max(axis=-1, keepdims=True)
+    return (m + np.log(np.exp(z - m).sum(axis=-1, keepdims=True)))[..., 0]
+
+
+def tree_loss(parent, token, weight, logits):
+    """Per-token weighted loss over the tree's rows.
+
+    parent/token: int arrays [N]; weight: [N] (w_t for target t); logits: [N,V].
+    Returns (loss, logp [N] with nan at roots, dZ [N,V])."""
+    z = np.asarray(logits, dtype=np.float64)
+    lse = _lse(z)
+    soft = np.exp(z - lse[:, None])
+    N = len(parent)
+    loss = 0.0
+    logp = np.full(N, np.nan)
+    dz = np.zeros_like(z)
+    for t in range(N):
+        r = int(parent[t])
+        if r < 0:
+            continue
+        x = int(token[t])
+        w = float(weight[t])
+        lp = z[r, x] - lse[r]
+        logp[t] = lp
+        loss += -w * lp
+        dz[r] += w * soft[r]
+        dz[r, x] -= w
+    return loss, logp, dz
+
+
+def branch_loss(nodes_of, token, logits):
+    """Loss averaged over branches: (1/B) * sum_s sum_{k>=1} -log softmax(z[node(s,k-1)])[x_{s,k}].
+
+    nodes_of: per input sequence, its row at each position.  Returns
+    (loss, per-copy logp list, dZ [N,V] accumulated over copies)."""
+    z = np.asarray(logits, dtype=np.float64)
+    lse = _lse(z)
+    soft = np.exp(z - lse[:, None])
+    B = len(nodes_of)
+    loss = 0.0
+    dz = np.zeros_like(z)
+    copies = []
+    for nodes in nodes_of:
+        lps = []
+        for k in range(1, len(nodes)):
+            r = nodes[k - 1]
+            x = int(token[nodes[k]])
+            lp = z[r, x] - lse[r]
+            lps.append((nodes[k], lp))
+            loss += -lp / B
+            dz[r] += soft[r] / B
+            dz[r, x] -= 1.0 / B
+        copies.append(lps)
+    return loss, copies, dz
+
+
+def lmhead(hidden, w_vocab, parent, token, weight):
+    """Fused lm-head: z = H W, tree loss, dZ, dH = dZ W^T, dW = H^T dZ (fp64)."""
+    H = np.asarray(hidden, dtype=np.float64)
+    W = np.asarray(w_vocab, dtype=np.float64)
+    z = H @ W
+    loss, logp, dz = tree_loss(parent, token, weight, z)
+    return loss, logp, dz, dz @ W.T, H.T @ dz
+
+
+def lmhead_rows(hidden_rows, w_vocab, targets):
+    """Row-local part of the fused lm-head for selected rows.
+
+    targets: per selected row, a list of (token id, weight).  Returns per row
+    (lse, [logp of each target], dZ row, dH row)."""
+    W = np.asarray(w_vocab, dtype=np.float64)
+    out = []
+    for h, tg in zip(hidden_rows, targets):
+        z = np.asarray(h, dtype=np.float64) @ W
+        m = z.max()
+        lse = m + np.log(np.exp(z - m).sum())
+        soft = np.exp(z - lse)
+        wsum = sum(w for _, w in tg)
+        dz = wsum * soft
+        lps = []
+        for x, w in tg:
+            lps.append(z[x] - lse)
+            dz[x] -= w
+        out.append((lse, lps, dz, dz @ W.T))
+    return out
