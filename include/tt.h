@@ -1,0 +1,249 @@
+/*
+ * tt.h -- C ABI of libtreeattn: prefix-tree attention and the branch-weighted
+ * loss on one AMD MI355X (gfx950).
+ *
+ * What it computes.  Rollout sequences that share prefixes form a tree; the
+ * tree is serialized in DFS order so that every unique token is one row and is
+ * computed once (Tree Training, arXiv 2511.00413, Abstract; AReaL-DTA, arXiv
+ * 2602.00482, summary page, What This Paper Is About).  Row i attends to row j
+ * iff j is i or an ancestor of i -- in DFS order exactly  j <= i < end[j] --
+ * with rotary position equal to the depth, which reproduces per-branch causal
+ * attention row for row (Tree Training, Abstract: per-branch log-probabilities
+ * must be matched exactly).  The loss is the per-token weighted NLL whose
+ * weight is the fraction of branches through the token, which equals the loss
+ * averaged over branches (Tree Training, Abstract).
+ *
+ * Conventions used by every call (the pages leave them open):
+ *   - a branch is an input sequence, counted with multiplicity; B = n_seqs;
+ *   - sibling order is ascending token id (lexicographic DFS; AReaL-DTA
+ *     summary, Key Contributions 3);
+ *   - RoPE: theta_k = base^(-2k/d), k < d/2, coordinate k paired with k + d/2
+ *     ("rotate half"), position = depth;
+ *   - softmax scale 1/sqrt(d) unless given; query head h uses key/value head
+ *     h / (h_q / h_kv); LSE is natural-log;
+ *   - every non-root row t is a loss target predicted from its parent's row.
+ *
+ * Ownership and errors.  Every function returns TT_OK (0) or a negative
+ * tt_status and never throws or aborts.  tt_last_error() returns text for the
+ * last failure on the calling thread.  All preconditions the host can check
+ * are checked before anything is launched; on failure nothing is launched and
+ * no output is touched.  The caller allocates every device buffer (outputs,
+ * plan, workspace) and passes the stream; the library never allocates device
+ * memory and never synchronises.  Launch errors are reported as TT_EDEVICE;
+ * faults during execution surface at the caller's next synchronisation.  The
+ * tree_* host functions (all but tree_plan_upload) make no HIP call and work
+ * with no GPU present.  A built tree is immutable: concurrent calls on
+ * different streams may share it.
+ *
+ * Layouts.  Row-major, contiguous, no padding.  Device pointers must be
+ * 16-byte aligned.  "dtype" tensors are float32 (TT_F32) or bfloat16 (TT_BF16).
+ */
+#ifndef TT_H
+#define TT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TT_OK = 0,
+  TT_EINVAL = -1,        /* bad argument (NULL, range, shape, alignment, layout) */
+  TT_ENOMEM = -2,        /* host allocation failed */
+  TT_EWORKSPACE = -3,    /* workspace or plan buffer too small */
+  TT_EUNSUPPORTED = -4,  /* valid but not implemented (head dim, dtype, block size) */
+  TT_EDEVICE = -5,       /* a HIP call or kernel launch failed */
+  TT_EOVERFLOW = -6      /* sizes exceed the library's index ranges */
+} tt_status;
+
+typedef enum { TT_F32 = 0, TT_BF16 = 1 } tt_dtype;
+
+/* hipStream_t, passed as an opaque pointer (NULL = the null stream). */
+typedef void* tt_stream;
+
+/* Flags of tree_attn_bwd. */
+#define TT_ACCUMULATE_DKDV 1u /* d_k, d_v are float32 and the call ADDS into them */
+
+typedef struct tt_tree tt_tree; /* opaque, host memory owned by the library */
+
+typedef struct {
+  int64_t n_nodes;      /* N: unique tokens = rows of the DFS order */
+  int64_t n_seqs;       /* B: input sequences (branches), with multiplicity */
+  int64_t n_roots;      /* rows with no parent (first tokens of the forest) */
+  int64_t n_leaves;     /* rows with no child */
+  int64_t max_depth;    /* -1 if N == 0 */
+  int64_t seq_tokens;   /* sum of |s| over the input */
+  int64_t leaf_tokens;  /* sum over leaves of (depth+1): tokens of distinct maximal sequences */
+  int64_t n_targets;    /* N - n_roots */
+  int64_t pairs;        /* visible (query, key) pairs per head = sum_i (depth_i + 1) */
+  int64_t dense_pairs;  /* causal pairs of the branches computed apart = sum_s |s|(|s|+1)/2 */
+  int64_t block_q;      /* schedule tile sizes */
+  int64_t block_k;
+  int64_t n_tiles;      /* non-empty (q-block, k-block) tiles */
+  int64_t n_full_tiles; /* tiles in which every pair is visible */
+} tt_tree_info;
+
+/* Caller-owned HOST arrays for tree_export; NULL members are skipped. */
+typedef struct {
+  int32_t* token;          /* [N] token id of each row */
+  int32_t* depth;          /* [N] */
+  int32_t* end;            /* [N] exclusive end of the row's subtree */
+  int32_t* parent;         /* [N] -1 at a root */
+  int32_t* n_pass;         /* [N] input sequences (with multiplicity) through the row */
+  float* weight;           /* [N] n_pass / B rounded once to float32 */
+  int32_t* seq_pos_to_dfs; /* [seq_tokens] row of each input token, input order */
+  int32_t* tgt_row_ptr;    /* [N+1] CSR: targets predicted from row r are its children */
+  int32_t* tgt_dfs;        /* [n_targets] child rows, ascending */
+  int32_t* tgt_token;      /* [n_targets] their token ids (vocabulary index) */
+  float* tgt_w;            /* [n_targets] their weights */
+} tt_tree_arrays;
+
+/*
+ * tree_build -- prefix tree of the input sequences in lexicographic DFS order.
+ * (Tree Training, Abstract: DFS serialization, each token once, branch-fraction
+ * weights; AReaL-DTA summary, Key Contributions 3 and Methodology: rollouts
+ * sorted into one prefix tree in lexicographic DFS order.)
+ *   tokens       host [seq_offsets[n_seqs]] int32, each >= 0
+ *   seq_offsets  host [n_seqs+1] int64, seq_offsets[0] == 0, non-decreasing
+ *                (empty sequences are allowed and count towards B)
+ *   n_seqs       0 <= n_seqs < 2^24 (so n_pass/B is exact to one rounding)
+ *   block_q/k    schedule tile sizes, 0 = 64; powers of two in [16, 256]
+ *   out          receives the tree; free with tree_free
+ * Errors: TT_EINVAL (NULL, offsets, negative token, block size),
+ * TT_EOVERFLOW (n_seqs >= 2^24 or more than 2^31-1 tokens), TT_ENOMEM.
+ */
+int tree_build(const int32_t* tokens, const int64_t* seq_offsets, int32_t n_seqs,
+               int32_t block_q, int32_t block_k, tt_tree** out);
+
+/* Frees a tree (NULL is a no-op). Do not free before a plan upload from it has completed. */
+void tree_free(tt_tree* tree);
+
+/* Sizes and statistics (AReaL-DTA summary, Main Findings 1: compression is
+ * seq_tokens / n_nodes; leaves-only compression is leaf_tokens / n_nodes). */
+int tree_info(const tt_tree* tree, tt_tree_info* out);
+
+/* Copies the DFS arrays into caller-owned host arrays (NULL members skipped). */
+int tree_export(const tt_tree* tree, const tt_tree_arrays* dst);
+
+/*
+ * Device plan: depth[], end[] and the tile schedule (per q-block list of
+ * non-empty k-blocks tagged FULL or PARTIAL; per k-block the contiguous range
+ * of query rows that see it; largest-first launch orders).
+ * tree_plan_bytes gives its size; tree_plan_upload copies it (hipMemcpyAsync on
+ * `stream`) into the caller's device buffer of at least that many bytes.
+ * Errors: TT_EINVAL, TT_EWORKSPACE (buffer too small), TT_EDEVICE.
+ */
+int tree_plan_bytes(const tt_tree* tree, size_t* bytes);
+int tree_plan_upload(const tt_tree* tree, void* dev_plan, size_t bytes, tt_stream stream);
+
+/* Copies the same plan image into caller-owned HOST memory (for inspection;
+ * int32 words: header, then the sections).  No HIP call. */
+int tree_plan_copy(const tt_tree* tree, void* host_dst, size_t bytes);
+
+/*
+ * Attention geometry and buffers.  Query rows are the DFS rows
+ * [q_off, q_off + n_q); key rows are [0, n_k).  Tree mode: q_off = 0,
+ * n_q = n_k = N.  Path/chunk mode (AReaL-DTA summary, Key Contributions 2 and
+ * Methodology: a long suffix split into fixed chunks run right to left against
+ * the cached prefix state): queries are one chunk, keys the prefix plus the
+ * chunk.  Requires 0 <= q_off, q_off % block_q == 0, q_off + n_q <= n_k <= N.
+ */
+typedef struct {
+  const tt_tree* tree;     /* host tree the plan was built from */
+  const void* plan;        /* device plan from tree_plan_upload */
+  int32_t q_off, n_q, n_k;
+  int32_t h_q, h_kv, d;    /* h_q % h_kv == 0; d = 128 (bf16) or d in {16..256, %16} (f32) */
+  tt_dtype dtype;
+  float scale;             /* 0 = 1/sqrt(d) */
+  float rope_base;         /* 0 = no rotation */
+  const void* q;           /* device [n_q, h_q, d] dtype */
+  const void* k;           /* device [n_k, h_kv, d] dtype */
+  const void* v;           /* device [n_k, h_kv, d] dtype */
+  void* o;                 /* device [n_q, h_q, d] dtype: output of fwd, input of bwd */
+  float* lse;              /* device [n_q, h_q] float32: output of fwd, input of bwd */
+  void* workspace;         /* device scratch, >= tree_attn_workspace_bytes */
+  size_t workspace_bytes;
+} tt_attn_args;
+
+/* Workspace size for tree_attn_fwd (for_bwd = 0) or tree_attn_bwd (for_bwd = 1). */
+int tree_attn_workspace_bytes(const tt_attn_args* args, int for_bwd, size_t* bytes);
+
+/*
+ * tree_attn_fwd -- O[i,h] = sum over visible j of softmax_j(scale q'_i.k'_j) v_j and
+ * LSE[i,h], where ' is the rotation at the row's depth (Tree Training,
+ * Abstract; AReaL-DTA summary, Key Contributions 1: shared prefix segments
+ * computed once).  Overwrites o and lse.
+ */
+int tree_attn_fwd(const tt_attn_args* args, tt_stream stream);
+
+/*
+ * tree_attn_bwd -- gradients of sum(dO * O) with respect to q, k, v, recomputing
+ * the probabilities from LSE.  A shared prefix row receives the sum of the
+ * gradients of all its descendants' queries (AReaL-DTA summary, Key
+ * Contributions 1 and Methodology: gradients from all descendant leaves
+ * accumulated into the shared prefix).
+ *   a.o, a.lse  the forward's outputs for the same arguments
+ *   d_o         device [n_q, h_q, d] dtype
+ *   d_q         device [n_q, h_q, d] dtype, overwritten
+ *   d_k, d_v    device [n_k, h_kv, d]: dtype and overwritten, or float32 and
+ *               added into with TT_ACCUMULATE_DKDV (chunked path mode: the
+ *               prefix keys collect every chunk's contribution)
+ */
+typedef struct {
+  tt_attn_args a;
+  const void* d_o;
+  void* d_q;
+  void* d_k;
+  void* d_v;
+  uint32_t flags;
+} tt_attn_bwd_args;
+
+int tree_attn_bwd(const tt_attn_bwd_args* args, tt_stream stream);
+
+/*
+ * Weighted tree NLL (Tree Training, Abstract: branch-averaged loss == per-token
+ * weighted loss).  For every row r with targets t (token x_t, weight w_t):
+ *   loss   += sum_t w_t (lse(z_r) - z_r[x_t])
+ *   logp_t  = z_r[x_t] - lse(z_r)
+ *   dZ_r    = (sum_t w_t) softmax(z_r) - sum_t w_t e_{x_t}
+ * Two modes, exactly one per call:
+ *   logits mode: z = logits [n_rows, vocab] (dtype logits_dtype); d_logits
+ *                (same dtype and shape, may alias logits) receives dZ.
+ *   fused mode:  z = hidden [n_rows, d_model] @ w_vocab [d_model, vocab], both
+ *                bf16; d_hidden [n_rows, d_model] bf16 receives dZ w_vocab^T and
+ *                d_w_vocab [d_model, vocab] (dtype dw_dtype) receives hidden^T dZ.
+ * Targets are a device CSR: tgt_row_ptr [n_rows+1], tgt_id [n_tgt] (0 <= id <
+ * vocab), tgt_w [n_tgt].  loss is a device float32 scalar (overwritten); logp
+ * [n_tgt] float32 or NULL; each gradient pointer may be NULL to skip it.
+ */
+typedef struct {
+  int32_t n_rows, d_model, vocab, n_tgt;
+  const void* hidden;
+  const void* w_vocab;
+  const void* logits;
+  tt_dtype logits_dtype;
+  const int32_t* tgt_row_ptr;
+  const int32_t* tgt_id;
+  const float* tgt_w;
+  float* loss;
+  float* logp;
+  void* d_hidden;
+  void* d_w_vocab;
+  tt_dtype dw_dtype;
+  void* d_logits;
+  void* workspace;
+  size_t workspace_bytes;
+} tt_nll_args;
+
+int tree_nll_workspace_bytes(const tt_nll_args* args, size_t* bytes);
+int tree_weighted_nll(const tt_nll_args* args, tt_stream stream);
+
+/* Text of the last error on this thread ("" if none). Valid until the next call. */
+const char* tt_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TT_H */

@@ -1,0 +1,397 @@
+// Generic tree-attention kernels: any head dim (multiple of 16, <= 256), fp32 or
+// bf16 storage, fp32 arithmetic.  They serve the fp32 configurations and every
+// shape the MFMA kernels do not take; they are also the rotation and
+// preprocessing kernels the MFMA path shares.
+//
+// Visibility: key row j is seen by query row i iff j <= i < end[j] (j is i or
+// an ancestor of i in DFS order); positions are depths, so each row's result
+// equals its per-branch causal-attention result (Tree Training, Abstract).
+#include "device.h"
+#include "kernels.h"
+
+using namespace ttd;
+
+namespace {
+
+// ---------------------------------------------------------------- RoPE (K1/K5)
+// y = R(depth * theta) x (or R^T x), theta_k = base^(-2k/d), pairs (k, k+d/2).
+// One thread per (row, k); the angle is formed and rotated in fp64.
+template <typename Tin, typename Tout, bool ACC>
+__global__ __launch_bounds__(256) void rope_kernel(const Tin* __restrict__ x, Tout* __restrict__ y,
+                                                   const int32_t* __restrict__ depth, int32_t row0,
+                                                   int32_t n_rows, int32_t heads, int32_t d, double base,
+                                                   double sign) {
+  const int half = d >> 1;
+  const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx >= int64_t(n_rows) * half) return;
+  const int64_t r = idx / half;
+  const int k = int(idx - r * half);
+  double c = 1.0, s = 0.0;
+  if (base != 0.0) {
+    const double theta = pow(base, -2.0 * double(k) / double(d));
+    sincos(double(depth[row0 + r]) * theta, &s, &c);
+    s *= sign;
+  }
+  for (int h = 0; h < heads; ++h) {
+    const int64_t b = (r * heads + h) * d;
+    const double x1 = Elem<Tin>::load(x, b + k), x2 = Elem<Tin>::load(x, b + k + half);
+    const float y1 = float(x1 * c - x2 * s), y2 = float(x2 * c + x1 * s);
+    if (ACC) {
+      Elem<Tout>::store(y, b + k, Elem<Tout>::load(y, b + k) + y1);
+      Elem<Tout>::store(y, b + k + half, Elem<Tout>::load(y, b + k + half) + y2);
+    } else {
+      Elem<Tout>::store(y, b + k, y1);
+      Elem<Tout>::store(y, b + k + half, y2);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- forward
+// One wave per (query row, query head).  Keys are visited tile by tile
+// through the q-block's list of non-empty k-blocks; lane = key.
+template <typename T, int DMAX>
+__global__ __launch_bounds__(256) void fwd_generic(const T* __restrict__ q, const T* __restrict__ k,
+                                                   const T* __restrict__ v, T* __restrict__ o,
+                                                   float* __restrict__ lse, PlanPtrs P, AttnGeom g) {
+  constexpr int NT = DMAX / kWave;
+  __shared__ float qs[4][DMAX];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t pair = int64_t(blockIdx.x) * 4 + wave;
+  const bool valid = pair < int64_t(g.n_q) * g.h_q;
+  const int il = valid ? int(pair / g.h_q) : 0;
+  const int h = valid ? int(pair % g.h_q) : 0;
+  const int i = g.q_off + il;
+  const int kvh = h / (g.h_q / g.h_kv);
+  const int d = g.d;
+  if (valid)
+    for (int c = lane; c < d; c += kWave) qs[wave][c] = Elem<T>::load(q, (int64_t(il) * g.h_q + h) * d + c);
+  __syncthreads();
+  if (!valid) return;
+  float m = -INFINITY, l = 0.f;
+  float acc[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) acc[t] = 0.f;
+  const int qb = i / P.bq;
+  for (int e = P.qb_ptr[qb]; e < P.qb_ptr[qb + 1]; ++e) {
+    const int kb = P.qb_tiles[e] & 0x3FFFFFFF;
+    for (int j0 = kb * P.bk; j0 < kb * P.bk + P.bk; j0 += kWave) {
+      const int j = j0 + lane;
+      const bool vis = j < kb * P.bk + P.bk && j < g.n_k && j <= i && i < P.end[j];
+      float s = -INFINITY;
+      if (vis) {
+        const T* kr = k + (int64_t(j) * g.h_kv + kvh) * d;
+        float a = 0.f;
+        for (int c = 0; c < d; ++c) a += qs[wave][c] * Elem<T>::load(kr, c);
+        s = a * g.scale;
+      }
+      const float mt = wave_max(s);
+      if (mt == -INFINITY) continue;
+      const float mn = fmaxf(m, mt);
+      const float alpha = expf(m - mn);
+      const float p = vis ? expf(s - mn) : 0.f;
+      l = l * alpha + wave_sum(p);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) acc[t] *= alpha;
+      for (int jj = 0; jj < kWave; ++jj) {
+        const float pj = __shfl(p, jj, kWave);
+        if (pj != 0.f) {
+          const T* vr = v + (int64_t(j0 + jj) * g.h_kv + kvh) * d;
+#pragma unroll
+          for (int t = 0; t < NT; ++t) {
+            const int c = lane + t * kWave;
+            if (c < d) acc[t] += pj * Elem<T>::load(vr, c);
+          }
+        }
+      }
+      m = mn;
+    }
+  }
+  const float inv = 1.f / l;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int c = lane + t * kWave;
+    if (c < d) Elem<T>::store(o, (int64_t(il) * g.h_q + h) * d + c, acc[t] * inv);
+  }
+  if (lane == 0) lse[int64_t(il) * g.h_q + h] = m + logf(l);
+}
+
+// ---------------------------------------------------------------- backward pre (K3)
+// D[i,h] = sum_c dO[i,h,c] * O[i,h,c]; one wave per (row, head).
+template <typename T>
+__global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ o, const T* __restrict__ d_o,
+                                                      float* __restrict__ D, int64_t rows, int d) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t r = int64_t(blockIdx.x) * 4 + wave;
+  if (r >= rows) return;
+  float a = 0.f;
+  for (int c = lane; c < d; c += kWave) a += Elem<T>::load(o, r * d + c) * Elem<T>::load(d_o, r * d + c);
+  a = wave_sum(a);
+  if (lane == 0) D[r] = a;
+}
+
+// ---------------------------------------------------------------- dQ
+// One wave per (query row, head); writes scale * sum_j dS_ij k'_j (rotated
+// frame, fp32) into dq_acc.
+template <typename T, int DMAX>
+__global__ __launch_bounds__(256) void dq_generic(const T* __restrict__ q, const T* __restrict__ k,
+                                                  const T* __restrict__ v, const T* __restrict__ d_o,
+                                                  const float* __restrict__ lse, const float* __restrict__ D,
+                                                  float* __restrict__ dq_acc, PlanPtrs P, AttnGeom g) {
+  constexpr int NT = DMAX / kWave;
+  __shared__ float qs[4][DMAX];
+  __shared__ float ds_[4][DMAX];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t pair = int64_t(blockIdx.x) * 4 + wave;
+  const bool valid = pair < int64_t(g.n_q) * g.h_q;
+  const int il = valid ? int(pair / g.h_q) : 0;
+  const int h = valid ? int(pair % g.h_q) : 0;
+  const int i = g.q_off + il;
+  const int kvh = h / (g.h_q / g.h_kv);
+  const int d = g.d;
+  const int64_t row = int64_t(il) * g.h_q + h;
+  if (valid)
+    for (int c = lane; c < d; c += kWave) {
+      qs[wave][c] = Elem<T>::load(q, row * d + c);
+      ds_[wave][c] = Elem<T>::load(d_o, row * d + c);
+    }
+  __syncthreads();
+  if (!valid) return;
+  const float Li = lse[row], Di = D[row];
+  float acc[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) acc[t] = 0.f;
+  const int qb = i / P.bq;
+  for (int e = P.qb_ptr[qb]; e < P.qb_ptr[qb + 1]; ++e) {
+    const int kb = P.qb_tiles[e] & 0x3FFFFFFF;
+    for (int j0 = kb * P.bk; j0 < kb * P.bk + P.bk; j0 += kWave) {
+      const int j = j0 + lane;
+      const bool vis = j < kb * P.bk + P.bk && j < g.n_k && j <= i && i < P.end[j];
+      float dsj = 0.f;
+      if (vis) {
+        const T* kr = k + (int64_t(j) * g.h_kv + kvh) * d;
+        const T* vr = v + (int64_t(j) * g.h_kv + kvh) * d;
+        float s = 0.f, dp = 0.f;
+        for (int c = 0; c < d; ++c) {
+          s += qs[wave][c] * Elem<T>::load(kr, c);
+          dp += ds_[wave][c] * Elem<T>::load(vr, c);
+        }
+        const float p = expf(s * g.scale - Li);
+        dsj = p * (dp - Di);
+      }
+      for (int jj = 0; jj < kWave; ++jj) {
+        const float x = __shfl(dsj, jj, kWave);
+        if (x != 0.f) {
+          const T* kr = k + (int64_t(j0 + jj) * g.h_kv + kvh) * d;
+#pragma unroll
+          for (int t = 0; t < NT; ++t) {
+            const int c = lane + t * kWave;
+            if (c < d) acc[t] += x * Elem<T>::load(kr, c);
+          }
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int c = lane + t * kWave;
+    if (c < d) dq_acc[row * d + c] = acc[t] * g.scale;
+  }
+}
+
+// ---------------------------------------------------------------- dK, dV
+// One wave per (key row, kv head).  Key j is seen by the query rows
+// [max(j, q_off), min(end[j], q_off + n_q)); lane = query.  dK is rotated
+// back (R^T at the key's depth) before it is stored.
+template <typename T, typename TG, bool ACC, int DMAX>
+__global__ __launch_bounds__(256) void dkdv_generic(const T* __restrict__ q, const T* __restrict__ k,
+                                                    const T* __restrict__ v, const T* __restrict__ d_o,
+                                                    const float* __restrict__ lse, const float* __restrict__ D,
+                                                    TG* __restrict__ d_k, TG* __restrict__ d_v, PlanPtrs P,
+                                                    AttnGeom g) {
+  constexpr int NT = DMAX / kWave;
+  __shared__ float ks[4][DMAX];
+  __shared__ float vs[4][DMAX];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t pair = int64_t(blockIdx.x) * 4 + wave;
+  const bool valid = pair < int64_t(g.n_k) * g.h_kv;
+  const int j = valid ? int(pair / g.h_kv) : 0;
+  const int kvh = valid ? int(pair % g.h_kv) : 0;
+  const int d = g.d;
+  const int64_t krow = int64_t(j) * g.h_kv + kvh;
+  if (valid)
+    for (int c = lane; c < d; c += kWave) {
+      ks[wave][c] = Elem<T>::load(k, krow * d + c);
+      vs[wave][c] = Elem<T>::load(v, krow * d + c);
+    }
+  __syncthreads();
+  float dk[NT], dv[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) dk[t] = dv[t] = 0.f;
+  const int G = g.h_q / g.h_kv;
+  const int lo = valid ? max(j, g.q_off) : 0;
+  const int hi = valid ? min(P.end[j], g.q_off + g.n_q) : 0;
+  for (int hh = 0; hh < G && valid; ++hh) {
+    const int h = kvh * G + hh;
+    for (int i0 = lo; i0 < hi; i0 += kWave) {
+      const int i = i0 + lane;
+      float p = 0.f, dsi = 0.f;
+      if (i < hi) {
+        const int64_t row = int64_t(i - g.q_off) * g.h_q + h;
+        const T* qr = q + row * d;
+        const T* dor = d_o + row * d;
+        float s = 0.f, dp = 0.f;
+        for (int c = 0; c < d; ++c) {
+          s += Elem<T>::load(qr, c) * ks[wave][c];
+          dp += Elem<T>::load(dor, c) * vs[wave][c];
+        }
+        p = expf(s * g.scale - lse[row]);
+        dsi = p * (dp - D[row]);
+      }
+      const int cnt = min(kWave, hi - i0);
+      for (int ii = 0; ii < cnt; ++ii) {
+        const float pi = __shfl(p, ii, kWave);
+        const float x = __shfl(dsi, ii, kWave);
+        const int64_t row = int64_t(i0 + ii - g.q_off) * g.h_q + h;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          const int c = lane + t * kWave;
+          if (c < d) {
+            dv[t] += pi * Elem<T>::load(d_o, row * d + c);
+            dk[t] += x * Elem<T>::load(q, row * d + c);
+          }
+        }
+      }
+    }
+  }
+  // rotate dK back: stage in LDS (reuse ks), then each lane reads its pair partner
+  __syncthreads();
+  if (valid)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int c = lane + t * kWave;
+      if (c < d) ks[wave][c] = dk[t] * g.scale;
+    }
+  __syncthreads();
+  if (!valid) return;
+  const int half = d >> 1;
+  double cs = 1.0, sn = 0.0;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int c = lane + t * kWave;
+    if (c >= d) continue;
+    const int kk = c < half ? c : c - half;
+    if (g.rope_base != 0.f) {
+      const double theta = pow(double(g.rope_base), -2.0 * double(kk) / double(d));
+      sincos(double(P.depth[j]) * theta, &sn, &cs);
+    }
+    // R^T: x'_k = x_k cos + x_{k+h} sin ; x'_{k+h} = x_{k+h} cos - x_k sin
+    float val;
+    if (c < half)
+      val = float(double(ks[wave][c]) * cs + double(ks[wave][c + half]) * sn);
+    else
+      val = float(double(ks[wave][c]) * cs - double(ks[wave][c - half]) * sn);
+    const int64_t off = krow * d + c;
+    if (ACC) {
+      Elem<TG>::store(d_k, off, Elem<TG>::load(d_k, off) + val);
+      Elem<TG>::store(d_v, off, Elem<TG>::load(d_v, off) + dv[t]);
+    } else {
+      Elem<TG>::store(d_k, off, val);
+      Elem<TG>::store(d_v, off, dv[t]);
+    }
+  }
+}
+
+inline unsigned blocks_for(int64_t n, int per) { return unsigned((n + per - 1) / per); }
+
+}  // namespace
+
+// ---------------------------------------------------------------- launchers
+int launch_rope(const void* x, void* y, tt_dtype tin, tt_dtype tout, bool acc, const int32_t* depth, int32_t row0,
+                int32_t n_rows, int32_t heads, int32_t d, float base, bool inverse, hipStream_t st) {
+  const int64_t n = int64_t(n_rows) * (d / 2);
+  if (n == 0) return 0;
+  const dim3 grid(blocks_for(n, 256)), block(256);
+  const double sg = inverse ? -1.0 : 1.0;
+  const double b = double(base);
+  if (tin == TT_F32 && tout == TT_F32 && !acc)
+    rope_kernel<float, float, false><<<grid, block, 0, st>>>((const float*)x, (float*)y, depth, row0, n_rows, heads, d, b, sg);
+  else if (tin == TT_F32 && tout == TT_F32 && acc)
+    rope_kernel<float, float, true><<<grid, block, 0, st>>>((const float*)x, (float*)y, depth, row0, n_rows, heads, d, b, sg);
+  else if (tin == TT_BF16 && tout == TT_BF16 && !acc)
+    rope_kernel<uint16_t, uint16_t, false><<<grid, block, 0, st>>>((const uint16_t*)x, (uint16_t*)y, depth, row0, n_rows, heads, d, b, sg);
+  else if (tin == TT_F32 && tout == TT_BF16 && !acc)
+    rope_kernel<float, uint16_t, false><<<grid, block, 0, st>>>((const float*)x, (uint16_t*)y, depth, row0, n_rows, heads, d, b, sg);
+  else
+    return -1;
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+#define TT_DMAX_DISPATCH(d, FN) \
+  ((d) <= 64 ? FN(64) : (d) <= 128 ? FN(128) : FN(256))
+
+int launch_fwd_generic(tt_dtype dt, const void* q, const void* k, const void* v, void* o, float* lse,
+                       const PlanPtrs& P, const AttnGeom& g, hipStream_t st) {
+  const int64_t pairs = int64_t(g.n_q) * g.h_q;
+  if (pairs == 0) return 0;
+  const dim3 grid(blocks_for(pairs, 4)), block(256);
+#define FWD(DM)                                                                                                 \
+  (dt == TT_F32 ? (fwd_generic<float, DM><<<grid, block, 0, st>>>((const float*)q, (const float*)k,             \
+                                                                   (const float*)v, (float*)o, lse, P, g), 0)   \
+                : (fwd_generic<uint16_t, DM><<<grid, block, 0, st>>>((const uint16_t*)q, (const uint16_t*)k,    \
+                                                                      (const uint16_t*)v, (uint16_t*)o, lse, P, g), 0))
+  TT_DMAX_DISPATCH(g.d, FWD);
+#undef FWD
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int launch_bwd_pre(tt_dtype dt, const void* o, const void* d_o, float* D, int64_t rows, int d, hipStream_t st) {
+  if (rows == 0) return 0;
+  const dim3 grid(blocks_for(rows, 4)), block(256);
+  if (dt == TT_F32)
+    bwd_pre_kernel<float><<<grid, block, 0, st>>>((const float*)o, (const float*)d_o, D, rows, d);
+  else
+    bwd_pre_kernel<uint16_t><<<grid, block, 0, st>>>((const uint16_t*)o, (const uint16_t*)d_o, D, rows, d);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int launch_dq_generic(tt_dtype dt, const void* q, const void* k, const void* v, const void* d_o, const float* lse,
+                      const float* D, float* dq_acc, const PlanPtrs& P, const AttnGeom& g, hipStream_t st) {
+  const int64_t pairs = int64_t(g.n_q) * g.h_q;
+  if (pairs == 0) return 0;
+  const dim3 grid(blocks_for(pairs, 4)), block(256);
+#define DQ(DM)                                                                                                   \
+  (dt == TT_F32 ? (dq_generic<float, DM><<<grid, block, 0, st>>>((const float*)q, (const float*)k,               \
+                                                                  (const float*)v, (const float*)d_o, lse, D,    \
+                                                                  dq_acc, P, g), 0)                              \
+                : (dq_generic<uint16_t, DM><<<grid, block, 0, st>>>((const uint16_t*)q, (const uint16_t*)k,      \
+                                                                     (const uint16_t*)v, (const uint16_t*)d_o,   \
+                                                                     lse, D, dq_acc, P, g), 0))
+  TT_DMAX_DISPATCH(g.d, DQ);
+#undef DQ
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int launch_dkdv_generic(tt_dtype dt, bool acc, const void* q, const void* k, const void* v, const void* d_o,
+                        const float* lse, const float* D, void* d_k, void* d_v, const PlanPtrs& P,
+                        const AttnGeom& g, hipStream_t st) {
+  const int64_t pairs = int64_t(g.n_k) * g.h_kv;
+  if (pairs == 0) return 0;
+  const dim3 grid(blocks_for(pairs, 4)), block(256);
+#define KV(DM)                                                                                                   \
+  (dt == TT_F32                                                                                                  \
+       ? (acc ? (dkdv_generic<float, float, true, DM><<<grid, block, 0, st>>>(                                   \
+                     (const float*)q, (const float*)k, (const float*)v, (const float*)d_o, lse, D, (float*)d_k,  \
+                     (float*)d_v, P, g), 0)                                                                      \
+              : (dkdv_generic<float, float, false, DM><<<grid, block, 0, st>>>(                                  \
+                     (const float*)q, (const float*)k, (const float*)v, (const float*)d_o, lse, D, (float*)d_k,  \
+                     (float*)d_v, P, g), 0))                                                                     \
+       : (acc ? (dkdv_generic<uint16_t, float, true, DM><<<grid, block, 0, st>>>(                                \
+                     (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)d_o, lse, D,   \
+                     (float*)d_k, (float*)d_v, P, g), 0)                                                         \
+              : (dkdv_generic<uint16_t, uint16_t, false, DM><<<grid, block, 0, st>>>(                            \
+                     (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)d_o, lse, D,   \
+                     (uint16_t*)d_k, (uint16_t*)d_v, P, g), 0)))
+  TT_DMAX_DISPATCH(g.d, KV);
+#undef KV
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}

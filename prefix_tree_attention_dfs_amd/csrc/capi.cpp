@@ -1,0 +1,320 @@
+// C ABI entry points that touch the device: plan upload, tree attention
+// forward/backward, weighted NLL.  Validation happens here, before any launch.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+#include <string>
+
+#include "internal.h"
+#include "kernels.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+size_t dsize(tt_dtype t) { return t == TT_F32 ? 4 : 2; }
+
+PlanPtrs plan_ptrs(const tt_tree* t, const void* dev_plan) {
+  const int32_t* base = static_cast<const int32_t*>(dev_plan);
+  const int32_t* h = t->plan.data();
+  PlanPtrs P;
+  P.depth = base + h[ttp::H_DEPTH];
+  P.end = base + h[ttp::H_END];
+  P.qb_ptr = base + h[ttp::H_QB_PTR];
+  P.qb_tiles = base + h[ttp::H_QB_TILES];
+  P.qb_order = base + h[ttp::H_QB_ORDER];
+  P.kb_qlo = base + h[ttp::H_KB_QLO];
+  P.kb_qhi = base + h[ttp::H_KB_QHI];
+  P.kb_minend = base + h[ttp::H_KB_MINEND];
+  P.kb_order = base + h[ttp::H_KB_ORDER];
+  P.N = t->N;
+  P.bq = t->bq;
+  P.bk = t->bk;
+  P.nqb = t->nqb;
+  P.nkb = t->nkb;
+  return P;
+}
+
+// Workspace carve-up, identical for the size query and the calls.
+struct AttnWs {
+  size_t q_rot = 0, k_rot = 0, D = 0, dq = 0, total = 0;
+  bool rope = false;
+};
+
+AttnWs attn_ws(const tt_attn_args* a, bool bwd) {
+  AttnWs w;
+  const size_t es = dsize(a->dtype);
+  w.rope = a->rope_base != 0.f;
+  size_t off = 0;
+  if (w.rope) {
+    w.q_rot = off;
+    off = align_up(off + size_t(a->n_q) * a->h_q * a->d * es);
+    w.k_rot = off;
+    off = align_up(off + size_t(a->n_k) * a->h_kv * a->d * es);
+  }
+  if (bwd) {
+    w.D = off;
+    off = align_up(off + size_t(a->n_q) * a->h_q * 4);
+    w.dq = off;
+    off = align_up(off + size_t(a->n_q) * a->h_q * a->d * 4);
+  }
+  w.total = off;
+  return w;
+}
+
+int check_attn(const tt_attn_args* a, const char* fn) {
+  using std::string;
+  if (!a) return tt::fail(TT_EINVAL, string(fn) + ": args is NULL");
+  if (!a->tree) return tt::fail(TT_EINVAL, string(fn) + ": tree is NULL");
+  if (!a->plan) return tt::fail(TT_EINVAL, string(fn) + ": plan is NULL");
+  if (a->dtype != TT_F32 && a->dtype != TT_BF16) return tt::fail(TT_EINVAL, string(fn) + ": bad dtype");
+  if (a->h_q <= 0 || a->h_kv <= 0 || a->h_q % a->h_kv != 0)
+    return tt::fail(TT_EINVAL, string(fn) + ": need h_q, h_kv > 0 and h_q % h_kv == 0");
+  if (a->d <= 0 || a->d % 2 != 0) return tt::fail(TT_EINVAL, string(fn) + ": d must be positive and even");
+  if (a->d % 16 != 0 || a->d > 256)
+    return tt::fail(TT_EUNSUPPORTED, string(fn) + ": head dim must be a multiple of 16 and <= 256");
+  const tt_tree* t = a->tree;
+  if (a->q_off < 0 || a->n_q < 0 || a->n_k < 0) return tt::fail(TT_EINVAL, string(fn) + ": negative q_off/n_q/n_k");
+  if (int64_t(a->q_off) + a->n_q > a->n_k || a->n_k > t->N)
+    return tt::fail(TT_EINVAL, string(fn) + ": need q_off + n_q <= n_k <= N");
+  if (a->q_off % t->bq != 0) return tt::fail(TT_EINVAL, string(fn) + ": q_off must be a multiple of block_q");
+  if (!(a->scale >= 0.f) || !std::isfinite(a->scale)) return tt::fail(TT_EINVAL, string(fn) + ": bad scale");
+  if (!(a->rope_base >= 0.f) || !std::isfinite(a->rope_base))
+    return tt::fail(TT_EINVAL, string(fn) + ": bad rope_base");
+  const int64_t qe = int64_t(a->n_q) * a->h_q * a->d, ke = int64_t(a->n_k) * a->h_kv * a->d;
+  if (qe * 4 > (int64_t(1) << 40) || ke * 4 > (int64_t(1) << 40))
+    return tt::fail(TT_EOVERFLOW, string(fn) + ": tensors too large");
+  if (a->n_q > 0 && (!a->q || !a->o || !a->lse))
+    return tt::fail(TT_EINVAL, string(fn) + ": q, o and lse are required");
+  if (a->n_k > 0 && (!a->k || !a->v)) return tt::fail(TT_EINVAL, string(fn) + ": k and v are required");
+  for (const void* p : {a->q, a->k, a->v, static_cast<const void*>(a->o), static_cast<const void*>(a->lse),
+                        static_cast<const void*>(a->workspace), a->plan})
+    if (p && !aligned16(p)) return tt::fail(TT_EINVAL, string(fn) + ": device pointers must be 16-byte aligned");
+  return TT_OK;
+}
+
+int check_ws(const tt_attn_args* a, bool bwd, const char* fn) {
+  const AttnWs w = attn_ws(a, bwd);
+  if (w.total > 0 && (!a->workspace || a->workspace_bytes < w.total))
+    return tt::fail(TT_EWORKSPACE, std::string(fn) + ": workspace too small (need " + std::to_string(w.total) +
+                                       " bytes)");
+  return TT_OK;
+}
+
+AttnGeom geom(const tt_attn_args* a) {
+  AttnGeom g;
+  g.q_off = a->q_off;
+  g.n_q = a->n_q;
+  g.n_k = a->n_k;
+  g.h_q = a->h_q;
+  g.h_kv = a->h_kv;
+  g.d = a->d;
+  g.scale = a->scale == 0.f ? float(1.0 / std::sqrt(double(a->d))) : a->scale;
+  g.rope_base = a->rope_base;
+  return g;
+}
+
+int dev_fail(const char* fn, const char* what) {
+  const hipError_t e = hipGetLastError();
+  return tt::fail(TT_EDEVICE, std::string(fn) + ": " + what + " failed: " + hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" int tree_plan_upload(const tt_tree* t, void* dev_plan, size_t bytes, tt_stream stream) {
+  tt::clear_error();
+  if (!t || !dev_plan) return tt::fail(TT_EINVAL, "tree_plan_upload: NULL argument");
+  if (!aligned16(dev_plan)) return tt::fail(TT_EINVAL, "tree_plan_upload: plan must be 16-byte aligned");
+  const size_t need = t->plan.size() * sizeof(int32_t);
+  if (bytes < need) return tt::fail(TT_EWORKSPACE, "tree_plan_upload: buffer smaller than tree_plan_bytes");
+  if (hipMemcpyAsync(dev_plan, t->plan.data(), need, hipMemcpyHostToDevice, (hipStream_t)stream) != hipSuccess)
+    return dev_fail("tree_plan_upload", "hipMemcpyAsync");
+  return TT_OK;
+}
+
+extern "C" int tree_attn_workspace_bytes(const tt_attn_args* a, int for_bwd, size_t* bytes) {
+  tt::clear_error();
+  if (!bytes) return tt::fail(TT_EINVAL, "tree_attn_workspace_bytes: bytes is NULL");
+  if (!a || !a->tree) return tt::fail(TT_EINVAL, "tree_attn_workspace_bytes: args/tree is NULL");
+  if (a->n_q < 0 || a->n_k < 0 || a->h_q <= 0 || a->h_kv <= 0 || a->d <= 0)
+    return tt::fail(TT_EINVAL, "tree_attn_workspace_bytes: bad geometry");
+  *bytes = attn_ws(a, for_bwd != 0).total;
+  return TT_OK;
+}
+
+extern "C" int tree_attn_fwd(const tt_attn_args* a, tt_stream stream) {
+  tt::clear_error();
+  int rc = check_attn(a, "tree_attn_fwd");
+  if (rc) return rc;
+  if ((rc = check_ws(a, false, "tree_attn_fwd"))) return rc;
+  if (a->n_q == 0) return TT_OK;
+  hipStream_t st = (hipStream_t)stream;
+  const PlanPtrs P = plan_ptrs(a->tree, a->plan);
+  const AttnGeom g = geom(a);
+  const AttnWs w = attn_ws(a, false);
+  char* ws = static_cast<char*>(a->workspace);
+  const void* q = a->q;
+  const void* k = a->k;
+  if (w.rope) {
+    if (launch_rope(a->q, ws + w.q_rot, a->dtype, a->dtype, false, P.depth, a->q_off, a->n_q, a->h_q, a->d,
+                    a->rope_base, false, st))
+      return dev_fail("tree_attn_fwd", "rope(q)");
+    if (launch_rope(a->k, ws + w.k_rot, a->dtype, a->dtype, false, P.depth, 0, a->n_k, a->h_kv, a->d, a->rope_base,
+                    false, st))
+      return dev_fail("tree_attn_fwd", "rope(k)");
+    q = ws + w.q_rot;
+    k = ws + w.k_rot;
+  }
+  const bool full_range = a->q_off == 0 && a->n_q == P.N;
+  if (a->dtype == TT_BF16 && mfma_attn_supported(g, P)) {
+    if (launch_fwd_mfma(q, k, a->v, a->o, a->lse, P, g, full_range, st))
+      return dev_fail("tree_attn_fwd", "attention kernel launch");
+  } else if (launch_fwd_generic(a->dtype, q, k, a->v, a->o, a->lse, P, g, st)) {
+    return dev_fail("tree_attn_fwd", "attention kernel launch");
+  }
+  return TT_OK;
+}
+
+extern "C" int tree_attn_bwd(const tt_attn_bwd_args* b, tt_stream stream) {
+  tt::clear_error();
+  if (!b) return tt::fail(TT_EINVAL, "tree_attn_bwd: args is NULL");
+  const tt_attn_args* a = &b->a;
+  int rc = check_attn(a, "tree_attn_bwd");
+  if (rc) return rc;
+  if (b->flags & ~TT_ACCUMULATE_DKDV) return tt::fail(TT_EINVAL, "tree_attn_bwd: unknown flags");
+  const bool acc = (b->flags & TT_ACCUMULATE_DKDV) != 0;
+  if (a->n_q > 0 && (!b->d_o || !b->d_q)) return tt::fail(TT_EINVAL, "tree_attn_bwd: d_o and d_q are required");
+  if (a->n_k > 0 && (!b->d_k || !b->d_v)) return tt::fail(TT_EINVAL, "tree_attn_bwd: d_k and d_v are required");
+  for (const void* p : {b->d_o, static_cast<const void*>(b->d_q), static_cast<const void*>(b->d_k),
+                        static_cast<const void*>(b->d_v)})
+    if (p && !aligned16(p)) return tt::fail(TT_EINVAL, "tree_attn_bwd: device pointers must be 16-byte aligned");
+  if ((rc = check_ws(a, true, "tree_attn_bwd"))) return rc;
+  if (a->n_k == 0) return TT_OK;
+  hipStream_t st = (hipStream_t)stream;
+  const PlanPtrs P = plan_ptrs(a->tree, a->plan);
+  const AttnGeom g = geom(a);
+  const AttnWs w = attn_ws(a, true);
+  char* ws = static_cast<char*>(a->workspace);
+  const void* q = a->q;
+  const void* k = a->k;
+  if (w.rope) {
+    if (a->n_q > 0 && launch_rope(a->q, ws + w.q_rot, a->dtype, a->dtype, false, P.depth, a->q_off, a->n_q, a->h_q,
+                                  a->d, a->rope_base, false, st))
+      return dev_fail("tree_attn_bwd", "rope(q)");
+    if (launch_rope(a->k, ws + w.k_rot, a->dtype, a->dtype, false, P.depth, 0, a->n_k, a->h_kv, a->d, a->rope_base,
+                    false, st))
+      return dev_fail("tree_attn_bwd", "rope(k)");
+    q = ws + w.q_rot;
+    k = ws + w.k_rot;
+  }
+  float* D = reinterpret_cast<float*>(ws + w.D);
+  float* dq = reinterpret_cast<float*>(ws + w.dq);
+  if (launch_bwd_pre(a->dtype, a->o, b->d_o, D, int64_t(a->n_q) * a->h_q, a->d, st))
+    return dev_fail("tree_attn_bwd", "preprocess");
+  const bool full_range = a->q_off == 0 && a->n_q == P.N;
+  if (a->dtype == TT_BF16 && mfma_attn_supported(g, P)) {
+    if (launch_bwd_mfma(q, k, a->v, b->d_o, a->lse, D, dq, b->d_k, b->d_v, acc, P, g, full_range, st))
+      return dev_fail("tree_attn_bwd", "attention kernel launch");
+  } else {
+    if (launch_dq_generic(a->dtype, q, k, a->v, b->d_o, a->lse, D, dq, P, g, st))
+      return dev_fail("tree_attn_bwd", "dq kernel launch");
+    if (launch_dkdv_generic(a->dtype, acc, q, k, a->v, b->d_o, a->lse, D, b->d_k, b->d_v, P, g, st))
+      return dev_fail("tree_attn_bwd", "dk/dv kernel launch");
+  }
+  // dQ: rotate back at the query rows' depths, convert to the output dtype
+  if (a->n_q > 0 && launch_rope(dq, b->d_q, TT_F32, a->dtype, false, P.depth, a->q_off, a->n_q, a->h_q, a->d,
+                                a->rope_base, true, st))
+    return dev_fail("tree_attn_bwd", "dq finalize");
+  return TT_OK;
+}
+
+// ---------------------------------------------------------------- weighted NLL
+namespace {
+
+struct NllWs {
+  size_t z = 0, row_loss = 0, total = 0;
+  bool fused = false;
+};
+
+NllWs nll_ws(const tt_nll_args* a) {
+  NllWs w;
+  w.fused = a->hidden != nullptr;
+  size_t off = 0;
+  if (w.fused) {
+    w.z = off;
+    off = align_up(off + size_t(a->n_rows) * size_t(a->vocab) * 2);
+  }
+  w.row_loss = off;
+  off = align_up(off + size_t(a->n_rows) * 4);
+  w.total = off;
+  return w;
+}
+
+}  // namespace
+
+extern "C" int tree_nll_workspace_bytes(const tt_nll_args* a, size_t* bytes) {
+  tt::clear_error();
+  if (!a || !bytes) return tt::fail(TT_EINVAL, "tree_nll_workspace_bytes: NULL argument");
+  if (a->n_rows < 0 || a->vocab <= 0) return tt::fail(TT_EINVAL, "tree_nll_workspace_bytes: bad sizes");
+  *bytes = nll_ws(a).total;
+  return TT_OK;
+}
+
+extern "C" int tree_weighted_nll(const tt_nll_args* a, tt_stream stream) {
+  tt::clear_error();
+  const char* fn = "tree_weighted_nll";
+  if (!a) return tt::fail(TT_EINVAL, "tree_weighted_nll: args is NULL");
+  const bool fused = a->hidden != nullptr || a->w_vocab != nullptr;
+  const bool logits = a->logits != nullptr;
+  if (fused == logits) return tt::fail(TT_EINVAL, "tree_weighted_nll: give exactly one of logits or hidden+w_vocab");
+  if (fused && (!a->hidden || !a->w_vocab))
+    return tt::fail(TT_EINVAL, "tree_weighted_nll: fused mode needs hidden and w_vocab");
+  if (a->n_rows < 0 || a->vocab <= 0 || a->n_tgt < 0) return tt::fail(TT_EINVAL, "tree_weighted_nll: bad sizes");
+  if (fused && a->d_model <= 0) return tt::fail(TT_EINVAL, "tree_weighted_nll: bad d_model");
+  if (a->vocab > (1 << 18)) return tt::fail(TT_EUNSUPPORTED, "tree_weighted_nll: vocab > 262144");
+  if (logits && a->logits_dtype != TT_F32 && a->logits_dtype != TT_BF16)
+    return tt::fail(TT_EINVAL, "tree_weighted_nll: bad logits dtype");
+  if (fused && a->d_w_vocab && a->dw_dtype != TT_F32 && a->dw_dtype != TT_BF16)
+    return tt::fail(TT_EINVAL, "tree_weighted_nll: bad dw dtype");
+  if (!a->loss || !a->tgt_row_ptr || (a->n_tgt > 0 && (!a->tgt_id || !a->tgt_w)))
+    return tt::fail(TT_EINVAL, "tree_weighted_nll: loss and the target CSR are required");
+  if (logits && a->d_hidden) return tt::fail(TT_EINVAL, "tree_weighted_nll: d_hidden needs fused mode");
+  if (logits && a->d_w_vocab) return tt::fail(TT_EINVAL, "tree_weighted_nll: d_w_vocab needs fused mode");
+  if (fused && a->d_logits) return tt::fail(TT_EINVAL, "tree_weighted_nll: d_logits needs logits mode");
+  for (const void* p : {a->hidden, a->w_vocab, a->logits, static_cast<const void*>(a->tgt_row_ptr),
+                        static_cast<const void*>(a->tgt_id), static_cast<const void*>(a->tgt_w),
+                        static_cast<const void*>(a->loss), static_cast<const void*>(a->logp),
+                        static_cast<const void*>(a->d_hidden), static_cast<const void*>(a->d_w_vocab),
+                        static_cast<const void*>(a->d_logits), static_cast<const void*>(a->workspace)})
+    if (p && !aligned16(p)) return tt::fail(TT_EINVAL, "tree_weighted_nll: device pointers must be 16-byte aligned");
+  const NllWs w = nll_ws(a);
+  if (!a->workspace || a->workspace_bytes < w.total)
+    return tt::fail(TT_EWORKSPACE, std::string(fn) + ": workspace too small (need " + std::to_string(w.total) +
+                                       " bytes)");
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = static_cast<char*>(a->workspace);
+  float* row_loss = reinterpret_cast<float*>(ws + w.row_loss);
+  if (logits) {
+    if (launch_nll_rows(a->logits_dtype, a->logits, a->d_logits, a->n_rows, a->vocab, a->vocab, a->tgt_row_ptr,
+                        a->tgt_id, a->tgt_w, a->n_tgt, a->logp, row_loss, st))
+      return dev_fail(fn, "nll kernel launch");
+  } else {
+    uint16_t* z = reinterpret_cast<uint16_t*>(ws + w.z);
+    const uint16_t* H = static_cast<const uint16_t*>(a->hidden);
+    const uint16_t* W = static_cast<const uint16_t*>(a->w_vocab);
+    if (a->n_rows > 0 && launch_gemm_nn(H, W, z, a->n_rows, a->vocab, a->d_model, st))
+      return dev_fail(fn, "lm-head gemm");
+    if (launch_nll_rows(TT_BF16, z, z, a->n_rows, a->vocab, a->vocab, a->tgt_row_ptr, a->tgt_id, a->tgt_w, a->n_tgt,
+                        a->logp, row_loss, st))
+      return dev_fail(fn, "nll kernel launch");
+    if (a->d_hidden && a->n_rows > 0 &&
+        launch_gemm_nt(z, W, static_cast<uint16_t*>(a->d_hidden), a->n_rows, a->d_model, a->vocab, st))
+      return dev_fail(fn, "d_hidden gemm");
+    if (a->d_w_vocab && launch_gemm_tn(H, z, a->d_w_vocab, a->dw_dtype == TT_F32, a->d_model, a->vocab, a->n_rows, st))
+      return dev_fail(fn, "d_w_vocab gemm");
+  }
+  if (launch_sum_loss(row_loss, a->n_rows, a->loss, st)) return dev_fail(fn, "loss reduction");
+  return TT_OK;
+}

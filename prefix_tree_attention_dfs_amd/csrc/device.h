@@ -1,0 +1,67 @@
+// Device-side helpers shared by the HIP kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tt.h"
+
+namespace ttd {
+
+constexpr int kWave = 64;
+
+// bf16 <-> f32 (bit-exact widening; RNE narrowing, finite values)
+__device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return uint16_t(u >> 16);
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  static __device__ __forceinline__ float load(const float* p, int64_t i) { return p[i]; }
+  static __device__ __forceinline__ void store(float* p, int64_t i, float v) { p[i] = v; }
+};
+template <> struct Elem<uint16_t> {
+  static __device__ __forceinline__ float load(const uint16_t* p, int64_t i) { return bf2f(p[i]); }
+  static __device__ __forceinline__ void store(uint16_t* p, int64_t i, float v) { p[i] = f2bf(v); }
+};
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+}  // namespace ttd
+
+// Pointers into the uploaded plan (device addresses), resolved on the host.
+struct PlanPtrs {
+  const int32_t* depth;
+  const int32_t* end;
+  const int32_t* qb_ptr;
+  const int32_t* qb_tiles;
+  const int32_t* qb_order;
+  const int32_t* kb_qlo;
+  const int32_t* kb_qhi;
+  const int32_t* kb_minend;
+  const int32_t* kb_order;
+  int32_t N, bq, bk, nqb, nkb;
+};
+
+// Geometry of one attention call after validation.
+struct AttnGeom {
+  int32_t q_off, n_q, n_k, h_q, h_kv, d;
+  float scale, rope_base;
+};

@@ -1,0 +1,41 @@
+// Internal host-side definitions shared by the library's translation units.
+#pragma once
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "tt.h"
+
+// Device plan image: int32 words.  Header, then sections each aligned to 64
+// words (256 bytes) so every section is a naturally aligned device array.
+namespace ttp {
+enum : int32_t {
+  kMagic = 0x31505454,  // "TTP1"
+  // header word indices
+  H_MAGIC = 0, H_N, H_BQ, H_BK, H_NQB, H_NKB, H_NTILES, H_BYTES,
+  H_DEPTH, H_END, H_QB_PTR, H_QB_TILES, H_QB_ORDER,
+  H_KB_QLO, H_KB_QHI, H_KB_MINEND, H_KB_ORDER,
+  H_WORDS = 64
+};
+constexpr int32_t kFullBit = int32_t(0x40000000);  // tile entry: kb | kFullBit if FULL
+}  // namespace ttp
+
+struct tt_tree {
+  int32_t N = 0, B = 0, n_roots = 0, n_leaves = 0, max_depth = -1;
+  int64_t seq_tokens = 0, leaf_tokens = 0, pairs = 0, dense_pairs = 0;
+  std::vector<int32_t> token, depth, end, parent, n_pass;
+  std::vector<float> weight;
+  std::vector<int32_t> seq_pos_to_dfs;
+  std::vector<int32_t> tgt_row_ptr, tgt_dfs;
+  // schedule
+  int32_t bq = 64, bk = 64, nqb = 0, nkb = 0;
+  int64_t n_tiles = 0, n_full = 0;
+  std::vector<int32_t> plan;  // the device plan image (host copy)
+};
+
+namespace tt {
+int fail(int code, const std::string& msg);  // records msg, returns code
+void clear_error();
+inline const int32_t* plan_section(const tt_tree* t, int hdr) { return t->plan.data() + t->plan[hdr]; }
+}  // namespace tt

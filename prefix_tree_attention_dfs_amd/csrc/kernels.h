@@ -1,0 +1,48 @@
+// Host-callable launchers of the library's kernels.  Each returns 0 on success
+// or -1 if the launch failed.  All take the caller's stream; none allocates.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "device.h"
+#include "tt.h"
+
+// RoPE (and its transpose) at the rows' depths; acc adds into an fp32 output.
+int launch_rope(const void* x, void* y, tt_dtype tin, tt_dtype tout, bool acc, const int32_t* depth, int32_t row0,
+                int32_t n_rows, int32_t heads, int32_t d, float base, bool inverse, hipStream_t st);
+
+// Generic (any d <= 256) path, fp32 or bf16 storage.
+int launch_fwd_generic(tt_dtype dt, const void* q, const void* k, const void* v, void* o, float* lse,
+                       const PlanPtrs& P, const AttnGeom& g, hipStream_t st);
+int launch_bwd_pre(tt_dtype dt, const void* o, const void* d_o, float* D, int64_t rows, int d, hipStream_t st);
+int launch_dq_generic(tt_dtype dt, const void* q, const void* k, const void* v, const void* d_o, const float* lse,
+                      const float* D, float* dq_acc, const PlanPtrs& P, const AttnGeom& g, hipStream_t st);
+int launch_dkdv_generic(tt_dtype dt, bool acc, const void* q, const void* k, const void* v, const void* d_o,
+                        const float* lse, const float* D, void* d_k, void* d_v, const PlanPtrs& P,
+                        const AttnGeom& g, hipStream_t st);
+
+// bf16 MFMA path, head dim 128 (returns -2 if the geometry is not covered).
+bool mfma_attn_supported(const AttnGeom& g, const PlanPtrs& P);
+int launch_fwd_mfma(const void* q, const void* k, const void* v, void* o, float* lse, const PlanPtrs& P,
+                    const AttnGeom& g, bool full_range, hipStream_t st);
+int launch_bwd_mfma(const void* q, const void* k, const void* v, const void* d_o, const float* lse, const float* D,
+                    float* dq_acc, void* d_k, void* d_v, bool acc, const PlanPtrs& P, const AttnGeom& g,
+                    bool full_range, hipStream_t st);
+
+// Weighted NLL.
+int launch_nll_rows(tt_dtype zt, const void* z, void* dz, int32_t n_rows, int32_t vocab, int64_t ldz,
+                    const int32_t* row_ptr, const int32_t* tgt_id, const float* tgt_w, int32_t n_tgt, float* logp,
+                    float* row_loss, hipStream_t st);
+int launch_sum_loss(const float* row_loss, int32_t n, float* loss, hipStream_t st);
+
+// bf16 GEMMs of the fused lm-head (row-major operands).
+//   Z  [M,N] = H [M,K] * W [K,N]
+//   dH [M,K] = dZ [M,N] * W^T
+//   dW [K,N] = H^T * dZ   (fp32 or bf16 out)
+int launch_gemm_nn(const uint16_t* A, const uint16_t* B, uint16_t* C, int64_t M, int64_t N, int64_t K,
+                   hipStream_t st);
+int launch_gemm_nt(const uint16_t* A, const uint16_t* B, uint16_t* C, int64_t M, int64_t N, int64_t K,
+                   hipStream_t st);
+int launch_gemm_tn(const uint16_t* A, const uint16_t* B, void* C, bool c_f32, int64_t M, int64_t N, int64_t K,
+                   hipStream_t st);

@@ -1,0 +1,155 @@
+// Weighted log-softmax NLL over the tree's logits rows (Tree Training, Abstract:
+// the branch-averaged loss equals the per-token loss weighted by the fraction
+// of branches through the token).  Row r predicts the tokens of its children:
+//   loss_r = sum_t w_t (lse_r - z_r[x_t]),  logp_t = z_r[x_t] - lse_r,
+//   dZ_r   = W_r softmax(z_r) - sum_t w_t e_{x_t},  W_r = sum_t w_t.
+// dZ may overwrite z (in place): target positions are kept intact until their
+// own value is written, so every dZ element is rounded exactly once.
+#include "device.h"
+#include "kernels.h"
+
+using namespace ttd;
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kMaxVocab = 1 << 18;  // LDS bitmap of target positions: 32 KB
+
+__device__ __forceinline__ void merge_ms(float& m, float& s, float m2, float s2) {
+  if (m2 == -INFINITY) return;
+  if (m == -INFINITY) {
+    m = m2;
+    s = s2;
+    return;
+  }
+  const float mn = fmaxf(m, m2);
+  s = s * __expf(m - mn) + s2 * __expf(m2 - mn);
+  m = mn;
+}
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void nll_rows_kernel(const T* z, T* dz, int32_t vocab,
+                                                            int64_t ldz, const int32_t* __restrict__ row_ptr,
+                                                            const int32_t* __restrict__ tgt_id,
+                                                            const float* __restrict__ tgt_w, int32_t n_tgt,
+                                                            float* __restrict__ logp, float* __restrict__ row_loss) {
+  __shared__ uint32_t bitmap[kMaxVocab / 32];
+  __shared__ float red_m[kThreads / kWave], red_s[kThreads / kWave];
+  __shared__ float red_a[kThreads / kWave], red_b[kThreads / kWave];
+  const int r = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const T* zr = z + int64_t(r) * ldz;
+  // pass 1: max and sum of exp (online, per thread, then merged)
+  float m = -INFINITY, s = 0.f;
+  for (int v = tid; v < vocab; v += kThreads) {
+    const float x = Elem<T>::load(zr, v);
+    if (x > m) {
+      s = s * __expf(m - x) + 1.f;
+      m = x;
+    } else {
+      s += __expf(x - m);
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const float m2 = __shfl_xor(m, o, kWave), s2 = __shfl_xor(s, o, kWave);
+    merge_ms(m, s, m2, s2);
+  }
+  if (lane == 0) {
+    red_m[wv] = m;
+    red_s[wv] = s;
+  }
+  const int words = (vocab + 31) / 32;
+  for (int w = tid; w < words; w += kThreads) bitmap[w] = 0u;
+  __syncthreads();
+  m = red_m[0];
+  s = red_s[0];
+  for (int w = 1; w < kThreads / kWave; ++w) merge_ms(m, s, red_m[w], red_s[w]);
+  const float lse = m + logf(s);
+  // pass 2: targets -> logp, loss, row weight; mark target positions
+  // targets outside [0, n_tgt) or ids outside [0, vocab) are ignored (logp = NaN)
+  const int t0 = min(max(row_ptr[r], 0), n_tgt), t1 = min(max(row_ptr[r + 1], t0), n_tgt);
+  float loss = 0.f, W = 0.f;
+  for (int t = t0 + tid; t < t1; t += kThreads) {
+    const int x = tgt_id[t];
+    if (x < 0 || x >= vocab) {
+      if (logp) logp[t] = NAN;
+      continue;
+    }
+    const float w = tgt_w[t];
+    const float lp = Elem<T>::load(zr, x) - lse;
+    if (logp) logp[t] = lp;
+    loss -= w * lp;
+    W += w;
+    atomicOr(&bitmap[x >> 5], 1u << (x & 31));
+  }
+  loss = wave_sum(loss);
+  W = wave_sum(W);
+  if (lane == 0) {
+    red_a[wv] = loss;
+    red_b[wv] = W;
+  }
+  __syncthreads();
+  loss = 0.f;
+  W = 0.f;
+  for (int w = 0; w < kThreads / kWave; ++w) {
+    loss += red_a[w];
+    W += red_b[w];
+  }
+  if (tid == 0) row_loss[r] = loss;
+  if (dz == nullptr) return;
+  T* dr = dz + int64_t(r) * ldz;
+  // pass 3a: every non-target position
+  for (int v = tid; v < vocab; v += kThreads) {
+    if (bitmap[v >> 5] & (1u << (v & 31))) continue;
+    Elem<T>::store(dr, v, W * __expf(Elem<T>::load(zr, v) - lse));
+  }
+  __syncthreads();
+  // pass 3b: each distinct target position, claimed by the first thread to clear its bit
+  for (int t = t0 + tid; t < t1; t += kThreads) {
+    const int x = tgt_id[t];
+    if (x < 0 || x >= vocab) continue;
+    const uint32_t bit = 1u << (x & 31);
+    if (!(atomicAnd(&bitmap[x >> 5], ~bit) & bit)) continue;
+    float ws = 0.f;
+    for (int u = t0; u < t1; ++u)
+      if (tgt_id[u] == x) ws += tgt_w[u];
+    Elem<T>::store(dr, x, W * __expf(Elem<T>::load(zr, x) - lse) - ws);
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void sum_loss_kernel(const float* __restrict__ row_loss, int32_t n,
+                                                            float* __restrict__ loss) {
+  __shared__ double red[kThreads / kWave];
+  double a = 0.0;
+  for (int i = threadIdx.x; i < n; i += kThreads) a += double(row_loss[i]);
+  a = wave_sum(a);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = a;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double t = 0.0;
+    for (int w = 0; w < kThreads / kWave; ++w) t += red[w];
+    *loss = float(t);
+  }
+}
+
+}  // namespace
+
+int launch_nll_rows(tt_dtype zt, const void* z, void* dz, int32_t n_rows, int32_t vocab, int64_t ldz,
+                    const int32_t* row_ptr, const int32_t* tgt_id, const float* tgt_w, int32_t n_tgt, float* logp,
+                    float* row_loss, hipStream_t st) {
+  if (vocab > kMaxVocab) return -1;
+  if (n_rows == 0) return 0;
+  if (zt == TT_F32)
+    nll_rows_kernel<float><<<n_rows, kThreads, 0, st>>>((const float*)z, (float*)dz, vocab, ldz, row_ptr, tgt_id,
+                                                        tgt_w, n_tgt, logp, row_loss);
+  else
+    nll_rows_kernel<uint16_t><<<n_rows, kThreads, 0, st>>>((const uint16_t*)z, (uint16_t*)dz, vocab, ldz, row_ptr,
+                                                           tgt_id, tgt_w, n_tgt, logp, row_loss);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int launch_sum_loss(const float* row_loss, int32_t n, float* loss, hipStream_t st) {
+  sum_loss_kernel<<<1, kThreads, 0, st>>>(row_loss, n, loss);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
