@@ -1,12 +1,246 @@
-// bf16 MFMA tree attention (head dim 128) -- placeholder until the kernels land.
+// bf16 MFMA tree attention forward, head dim 128 (gfx950).
+//
+// Tree Training (arXiv 2511.00413), Abstract: each unique token is computed
+// once and must get exactly its per-branch result; row i attends to row j iff
+// j <= i < end[j] (j is i or an ancestor of i in DFS order).
+//
+// One workgroup = one 64-row query block x one key/value head, i.e. the G
+// query heads that share that K/V (GQA).  It walks the block's list of
+// non-empty 64-key tiles (the plan's CSR); FULL tiles skip the mask.  K and V
+// tiles are staged global -> registers -> LDS, double buffered, one barrier
+// per tile.  Per wave: NT sub-tiles of 32 query rows of one head, Q held in
+// registers as B operands.
+//   S^T  = K Q^T        (A = K rows from LDS, B = Q)
+//   online softmax over keys (columns are lanes: row statistics are per lane)
+//   O^T += V^T P^T      (A = V^T via ds_read_tr16_b64, B = P^T straight from
+//                        the S^T accumulator registers)
 #include "device.h"
 #include "kernels.h"
+#include "mfma_common.h"
 
-bool mfma_attn_supported(const AttnGeom&, const PlanPtrs&) { return false; }
-int launch_fwd_mfma(const void*, const void*, const void*, void*, float*, const PlanPtrs&, const AttnGeom&, bool,
-                    hipStream_t) {
-  return -1;
+using namespace ttm;
+
+namespace {
+
+template <int G>
+struct FwdCfg {
+  static constexpr int NT = G >= 4 ? 2 : 1;             // 32-row query sub-tiles per wave
+  static constexpr int WAVES = (G * BQ) / (32 * NT);     // waves per workgroup
+  static constexpr int THREADS = WAVES * 64;
+  static constexpr int CH = (BK * D / 8) / THREADS;      // 16-byte chunks per thread per K (or V) tile
+  static constexpr int WPH = 2 / NT;                     // waves per head
+};
+
+struct __align__(16) FwdStage {
+  uint16_t K[BK * KSTR];
+  uint16_t V[BK * VSTR];
+  int32_t end[BK];
+};
+
+template <int G>
+__global__ __launch_bounds__(FwdCfg<G>::THREADS) void fwd_mfma_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    uint16_t* __restrict__ o, float* __restrict__ lse, PlanPtrs P, AttnGeom g, int full_range, int qb_first,
+    int n_qb) {
+  using C = FwdCfg<G>;
+  constexpr int NT = C::NT;
+  __shared__ FwdStage st[2];
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r = lane & 31, hh = lane >> 5;
+  const int kvh = blockIdx.x % g.h_kv;
+  const int idx = blockIdx.x / g.h_kv;
+  const int qb = full_range ? P.qb_order[idx] : (qb_first + n_qb - 1 - idx);
+  const int head = kvh * G + wave / C::WPH;
+  const int pos0 = (wave % C::WPH) * 32 * NT;
+  const int qrow0 = qb * BQ - g.q_off;  // q-buffer row of the block's first position
+  const float c2 = g.scale * 1.4426950408889634f;
+
+  // Q fragments (B operands): lane holds Q[row][dc*16 + 8hh .. +8]
+  bf16x8 qf[NT][8];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int row = qrow0 + pos0 + nt * 32 + r;
+#pragma unroll
+    for (int dc = 0; dc < 8; ++dc)
+      qf[nt][dc] = row < g.n_q ? ld16(q + (int64_t(row) * g.h_q + head) * D + dc * 16 + 8 * hh) : zero8();
+  }
+
+  f32x16 oacc[NT][4];
+  float m[NT], lpart[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    m[nt] = -INFINITY;
+    lpart[nt] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) oacc[nt][dt] = zero16();
+  }
+
+  // tile staging
+  bf16x8 kreg[C::CH], vreg[C::CH];
+  int32_t ereg = -1;
+  auto load_tile = [&](int kb) {
+#pragma unroll
+    for (int u = 0; u < C::CH; ++u) {
+      const int c = tid + u * C::THREADS;
+      const int key = c >> 4, dch = c & 15;
+      const int j = kb * BK + key;
+      const bool ok = j < g.n_k;
+      const int64_t off = (int64_t(j) * g.h_kv + kvh) * D + dch * 8;
+      kreg[u] = ok ? ld16(k + off) : zero8();
+      vreg[u] = ok ? ld16(v + off) : zero8();
+    }
+    if (tid < BK) {
+      const int j = kb * BK + tid;
+      ereg = j < g.n_k ? P.end[j] : -1;
+    }
+  };
+  auto store_tile = [&](FwdStage& s) {
+#pragma unroll
+    for (int u = 0; u < C::CH; ++u) {
+      const int c = tid + u * C::THREADS;
+      const int key = c >> 4, dch = c & 15;
+      *reinterpret_cast<bf16x8*>(&s.K[key * KSTR + dch * 8]) = kreg[u];
+      *reinterpret_cast<bf16x8*>(&s.V[key * VSTR + dch * 8]) = vreg[u];
+    }
+    if (tid < BK) s.end[tid] = ereg;
+  };
+
+  const int e0 = P.qb_ptr[qb], e1 = P.qb_ptr[qb + 1];
+  if (e0 < e1) {
+    load_tile(P.qb_tiles[e0] & kKbMask);
+    store_tile(st[0]);
+  }
+  __syncthreads();
+
+  for (int e = e0; e < e1; ++e) {
+    const int sidx = (e - e0) & 1;
+    const int ent = P.qb_tiles[e];
+    const int kb = ent & kKbMask;
+    const bool full = (ent & kFull) != 0;
+    if (e + 1 < e1) load_tile(P.qb_tiles[e + 1] & kKbMask);
+    const FwdStage& S = st[sidx];
+
+    // Each 32-key half of the tile in turn: S^T = K Q^T, mask, online
+    // softmax (rows = lanes), O^T += V^T P^T.
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      f32x16 sacc[NT];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) sacc[nt] = zero16();
+#pragma unroll
+      for (int dc = 0; dc < 8; ++dc) {
+        const bf16x8 a = lds_read16(&S.K[(kt * 32 + r) * KSTR + dc * 16 + 8 * hh]);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) sacc[nt] = mfma(a, qf[nt][dc], sacc[nt]);
+      }
+      if (!full) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const int qpos = qb * BQ + pos0 + nt * 32 + r;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int kl = kt * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
+            const bool vis = (kb * BK + kl <= qpos) && (qpos < S.end[kl]);
+            sacc[nt][i] = vis ? sacc[nt][i] : -INFINITY;
+          }
+        }
+      }
+      bf16x8 pf[2][NT];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[nt][i]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        const float mnew = fmaxf(m[nt], mx);
+        if (__any(mnew != m[nt])) {  // rescale only when some row's max grew
+          const float alpha = (mnew == m[nt]) ? 1.f : exp2_fast((m[nt] - mnew) * c2);
+          lpart[nt] *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) oacc[nt][dt][i] *= alpha;
+          m[nt] = mnew;
+        }
+        const float mexp = m[nt] == -INFINITY ? 0.f : m[nt] * c2;
+        float ls = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float p = exp2_fast(sacc[nt][i] * c2 - mexp);
+          sacc[nt][i] = p;
+          ls += p;
+        }
+        lpart[nt] += ls;
+#pragma unroll
+        for (int c = 0; c < 2; ++c) pf[c][nt] = c_to_b(sacc[nt], c);
+      }
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const bf16x8 a = tr_frag(S.V, VSTR, kt * 32 + 16 * c, dt * 32, lane);
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) oacc[nt][dt] = mfma(a, pf[c][nt], oacc[nt][dt]);
+        }
+    }
+
+    if (e + 1 < e1) store_tile(st[sidx ^ 1]);
+    __syncthreads();
+  }
+
+  // epilogue: O = O^T / l (lane = query row, registers = head-dim entries), LSE
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const float lt = lpart[nt] + __shfl_xor(lpart[nt], 32, 64);
+    const int row = qrow0 + pos0 + nt * 32 + r;
+    if (row >= g.n_q) continue;
+    const float inv = 1.f / lt;
+    uint16_t* orow = o + (int64_t(row) * g.h_q + head) * D;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        bf16x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = __bf16(oacc[nt][dt][4 * i4 + e] * inv);
+        *reinterpret_cast<bf16x4*>(orow + dt * 32 + 8 * i4 + 4 * hh) = w;
+      }
+    if (hh == 0) lse[int64_t(row) * g.h_q + head] = m[nt] * g.scale + logf(lt);
+  }
 }
+
+template <int G>
+int launch_fwd_g(const void* q, const void* k, const void* v, void* o, float* lse, const PlanPtrs& P,
+                 const AttnGeom& g, bool full_range, hipStream_t st) {
+  const int qb_first = g.q_off / BQ;
+  const int qb_end = (g.q_off + g.n_q + BQ - 1) / BQ;
+  const int n_qb = qb_end - qb_first;
+  if (n_qb <= 0) return 0;
+  const dim3 grid(unsigned(n_qb) * unsigned(g.h_kv)), block(FwdCfg<G>::THREADS);
+  fwd_mfma_kernel<G><<<grid, block, 0, st>>>((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
+                                             (uint16_t*)o, lse, P, g, full_range ? 1 : 0, qb_first, n_qb);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+}  // namespace
+
+bool mfma_attn_supported(const AttnGeom& g, const PlanPtrs& P) {
+  const int G = g.h_q / g.h_kv;
+  return g.d == D && P.bq == BQ && P.bk == BK && (G == 1 || G == 2 || G == 4);
+}
+
+int launch_fwd_mfma(const void* q, const void* k, const void* v, void* o, float* lse, const PlanPtrs& P,
+                    const AttnGeom& g, bool full_range, hipStream_t st) {
+  switch (g.h_q / g.h_kv) {
+    case 1: return launch_fwd_g<1>(q, k, v, o, lse, P, g, full_range, st);
+    case 2: return launch_fwd_g<2>(q, k, v, o, lse, P, g, full_range, st);
+    case 4: return launch_fwd_g<4>(q, k, v, o, lse, P, g, full_range, st);
+    default: return -1;
+  }
+}
+
+bool mfma_bwd_supported(const AttnGeom&, const PlanPtrs&) { return false; }
+
 int launch_bwd_mfma(const void*, const void*, const void*, const void*, const float*, const float*, float*, void*,
                     void*, bool, const PlanPtrs&, const AttnGeom&, bool, hipStream_t) {
   return -1;

@@ -214,7 +214,7 @@ extern "C" int tree_attn_bwd(const tt_attn_bwd_args* b, tt_stream stream) {
   if (launch_bwd_pre(a->dtype, a->o, b->d_o, D, int64_t(a->n_q) * a->h_q, a->d, st))
     return dev_fail("tree_attn_bwd", "preprocess");
   const bool full_range = a->q_off == 0 && a->n_q == P.N;
-  if (a->dtype == TT_BF16 && mfma_attn_supported(g, P)) {
+  if (a->dtype == TT_BF16 && mfma_bwd_supported(g, P)) {
     if (launch_bwd_mfma(q, k, a->v, b->d_o, a->lse, D, dq, b->d_k, b->d_v, acc, P, g, full_range, st))
       return dev_fail("tree_attn_bwd", "attention kernel launch");
   } else {

@@ -24,6 +24,7 @@ int launch_dkdv_generic(tt_dtype dt, bool acc, const void* q, const void* k, con
 
 // bf16 MFMA path, head dim 128 (returns -2 if the geometry is not covered).
 bool mfma_attn_supported(const AttnGeom& g, const PlanPtrs& P);
+bool mfma_bwd_supported(const AttnGeom& g, const PlanPtrs& P);
 int launch_fwd_mfma(const void* q, const void* k, const void* v, void* o, float* lse, const PlanPtrs& P,
                     const AttnGeom& g, bool full_range, hipStream_t st);
 int launch_bwd_mfma(const void* q, const void* k, const void* v, const void* d_o, const float* lse, const float* D,

@@ -1,0 +1,92 @@
+// Shared pieces of the bf16 MFMA attention kernels (gfx950, head dim 128).
+//
+// v_mfma_f32_32x32x16_bf16 operand layout (lane l, r = l % 32, h = l / 32):
+//   A (32 x 16):  lane holds A[r][8h .. 8h+7]
+//   B (16 x 32):  lane holds B[8h .. 8h+7][r]
+//   C (32 x 32):  lane holds C[8*(i/4) + 4h + i%4][r], i = 0..15
+// so the columns of a C tile are lanes and its rows are registers.  A C tile
+// S^T[key][query] therefore feeds the B operand of the next product with its
+// rows as the reduction index: register block 8c..8c+7 of lane-half h holds
+// rows 16c + 8*(s/4) + 4h + s%4 (s = 0..7).  The A operand that pairs with it
+// is read from a row-major LDS tile with ds_read_tr16_b64, which within each
+// group of 16 lanes returns out[i][e] = (lane 4e + i/4's 8 bytes)[i % 4]: when
+// lane r' of a group points at row key0 + r'/4, column col0 + 4*(r'%4), lane i
+// receives column col0 + i of rows key0 .. key0+3.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ttm {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+constexpr int D = 128;     // head dim
+constexpr int BQ = 64;     // query rows per plan block
+constexpr int BK = 64;     // key rows per plan block
+constexpr int KSTR = 136;  // LDS row stride (bf16) of tiles read with ds_read_b128
+constexpr int VSTR = 144;  // LDS row stride (bf16) of tiles read with ds_read_tr16_b64
+constexpr int32_t kFull = 0x40000000;
+constexpr int32_t kKbMask = 0x3FFFFFFF;
+
+__device__ __forceinline__ f32x16 mfma(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 zero8() {
+  bf16x8 z;
+#pragma unroll
+  for (int s = 0; s < 8; ++s) z[s] = __bf16(0.f);
+  return z;
+}
+
+__device__ __forceinline__ f32x16 zero16() {
+  f32x16 z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+  return z;
+}
+
+// 16 bytes from global memory (row guard done by the caller)
+__device__ __forceinline__ bf16x8 ld16(const uint16_t* p) { return *reinterpret_cast<const bf16x8*>(p); }
+
+__device__ __forceinline__ bf16x8 lds_read16(const uint16_t* p) { return *reinterpret_cast<const bf16x8*>(p); }
+
+// Transposed 8-byte LDS read (see header comment).
+__device__ __forceinline__ bf16x4 lds_tr4(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
+}
+
+// A operand (rows = 32 "m" columns of a row-major LDS tile, reduction over 16
+// tile rows) for the pairing described above: lane (r, h) gets tile column
+// col0 + r of tile rows row0 + 16c + {4h..4h+3, 8+4h..8+4h+3}.
+__device__ __forceinline__ bf16x8 tr_frag(const uint16_t* tile, int stride, int row0, int col0, int lane) {
+  const int g = lane >> 4, rr = lane & 15;
+  const int h = g >> 1, half = g & 1;
+  const uint16_t* p = tile + (row0 + 4 * h + (rr >> 2)) * stride + col0 + 16 * half + 4 * (rr & 3);
+  const bf16x4 lo = lds_tr4(p);
+  const bf16x4 hi = lds_tr4(p + 8 * stride);
+  bf16x8 a;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    a[e] = lo[e];
+    a[4 + e] = hi[e];
+  }
+  return a;
+}
+
+// Register block c (regs 8c..8c+7) of a C tile as a bf16 B operand.
+__device__ __forceinline__ bf16x8 c_to_b(const f32x16& x, int c) {
+  bf16x8 b;
+#pragma unroll
+  for (int s = 0; s < 8; ++s) b[s] = __bf16(x[8 * c + s]);
+  return b;
+}
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+}  // namespace ttm
