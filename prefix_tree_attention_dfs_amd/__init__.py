@@ -152,8 +152,11 @@ class Tree:
 
     def __del__(self):
         h = getattr(self, "handle", None)
-        if h is not None and h.value:
-            lib().tree_free(h)
+        if h is not None and h.value and _LIB is not None:
+            try:
+                _LIB.tree_free(h)
+            except Exception:  # interpreter shutdown
+                pass
             self.handle = None
 
     def export(self):

@@ -238,10 +238,3 @@ int launch_fwd_mfma(const void* q, const void* k, const void* v, void* o, float*
     default: return -1;
   }
 }
-
-bool mfma_bwd_supported(const AttnGeom&, const PlanPtrs&) { return false; }
-
-int launch_bwd_mfma(const void*, const void*, const void*, const void*, const float*, const float*, float*, void*,
-                    void*, bool, const PlanPtrs&, const AttnGeom&, bool, hipStream_t) {
-  return -1;
-}

@@ -1,0 +1,407 @@
+// bf16 MFMA tree attention backward, head dim 128 (gfx950).
+//
+// Gradients of sum(dO * O) with the probabilities recomputed from the
+// forward's LSE; a shared prefix key collects the gradient of every query in
+// its subtree (AReaL-DTA summary, Key Contributions 1 and Methodology:
+// shared segments are backpropagated once with the gradients of all
+// descendant leaves accumulated).
+//
+// Two kernels, neither uses atomics:
+//   dq_mfma_kernel   query-stationary (the forward's walk over the block's
+//                    non-empty key tiles):  S^T = K Q^T, P^T, dP^T = V dO^T,
+//                    dS^T = P^T (dP^T - D), dQ^T += K^T dS^T.
+//   dkdv_mfma_kernel key-stationary: one workgroup per 128 keys x kv head,
+//                    each wave owns 32 keys (K, V in registers) and walks the
+//                    contiguous range of query rows that see those keys, for
+//                    every query head of the group:  S = Q K^T, P, dP = dO V^T,
+//                    dS, dV^T += dO^T P, dK^T += Q^T dS.
+// Recomputing S and dP in both kernels costs 14 d MFMA flops per visible pair
+// instead of 10 d, in exchange for no fp32 atomic traffic on dQ.
+#include "device.h"
+#include "kernels.h"
+#include "mfma_common.h"
+
+using namespace ttm;
+using ttd::Elem;
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ------------------------------------------------------------------ dQ
+template <int G>
+struct DqCfg {
+  static constexpr int WAVES = 2 * G;  // each wave: 32 query rows of one head
+  static constexpr int THREADS = WAVES * 64;
+  static constexpr int CH = (BK * D / 8) / THREADS;
+};
+
+struct __align__(16) DqStage {
+  uint16_t K[BK * KSTR];
+  uint16_t V[BK * KSTR];
+  int32_t end[BK];
+};
+
+template <int G>
+__global__ __launch_bounds__(DqCfg<G>::THREADS) void dq_mfma_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const uint16_t* __restrict__ d_o, const float* __restrict__ lse, const float* __restrict__ Dv,
+    float* __restrict__ dq_acc, PlanPtrs P, AttnGeom g, int full_range, int qb_first, int n_qb) {
+  using C = DqCfg<G>;
+  __shared__ DqStage st[2];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r = lane & 31, hh = lane >> 5;
+  const int kvh = blockIdx.x % g.h_kv;
+  const int idx = blockIdx.x / g.h_kv;
+  const int qb = full_range ? P.qb_order[idx] : (qb_first + n_qb - 1 - idx);
+  const int head = kvh * G + (wave >> 1);
+  const int pos0 = (wave & 1) * 32;
+  const int row = qb * BQ - g.q_off + pos0 + r;  // q-buffer row of this lane's query
+  const bool rok = row < g.n_q;
+  const int qpos = qb * BQ + pos0 + r;
+  const float c2 = g.scale * kLog2e;
+
+  bf16x8 qf[8], of[8];
+#pragma unroll
+  for (int dc = 0; dc < 8; ++dc) {
+    const int64_t off = (int64_t(row) * g.h_q + head) * D + dc * 16 + 8 * hh;
+    qf[dc] = rok ? ld16(q + off) : zero8();
+    of[dc] = rok ? ld16(d_o + off) : zero8();
+  }
+  const float lse2 = rok ? lse[int64_t(row) * g.h_q + head] * kLog2e : 0.f;
+  const float Dq = rok ? Dv[int64_t(row) * g.h_q + head] : 0.f;
+
+  f32x16 acc[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) acc[dt] = zero16();
+
+  bf16x8 kreg[C::CH], vreg[C::CH];
+  int32_t ereg = -1;
+  auto load_tile = [&](int kb) {
+#pragma unroll
+    for (int u = 0; u < C::CH; ++u) {
+      const int c = tid + u * C::THREADS;
+      const int key = c >> 4, dch = c & 15;
+      const int j = kb * BK + key;
+      const bool ok = j < g.n_k;
+      const int64_t off = (int64_t(j) * g.h_kv + kvh) * D + dch * 8;
+      kreg[u] = ok ? ld16(k + off) : zero8();
+      vreg[u] = ok ? ld16(v + off) : zero8();
+    }
+    if (tid < BK) {
+      const int j = kb * BK + tid;
+      ereg = j < g.n_k ? P.end[j] : -1;
+    }
+  };
+  auto store_tile = [&](DqStage& s) {
+#pragma unroll
+    for (int u = 0; u < C::CH; ++u) {
+      const int c = tid + u * C::THREADS;
+      const int key = c >> 4, dch = c & 15;
+      *reinterpret_cast<bf16x8*>(&s.K[key * KSTR + dch * 8]) = kreg[u];
+      *reinterpret_cast<bf16x8*>(&s.V[key * KSTR + dch * 8]) = vreg[u];
+    }
+    if (tid < BK) s.end[tid] = ereg;
+  };
+
+  const int e0 = P.qb_ptr[qb], e1 = P.qb_ptr[qb + 1];
+  if (e0 < e1) {
+    load_tile(P.qb_tiles[e0] & kKbMask);
+    store_tile(st[0]);
+  }
+  __syncthreads();
+  for (int e = e0; e < e1; ++e) {
+    const int sidx = (e - e0) & 1;
+    const int ent = P.qb_tiles[e];
+    const int kb = ent & kKbMask;
+    const bool full = (ent & kFull) != 0;
+    if (e + 1 < e1) load_tile(P.qb_tiles[e + 1] & kKbMask);
+    const DqStage& S = st[sidx];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      f32x16 s = zero16(), dp = zero16();
+#pragma unroll
+      for (int dc = 0; dc < 8; ++dc) {
+        const bf16x8 a = lds_read16(&S.K[(kt * 32 + r) * KSTR + dc * 16 + 8 * hh]);
+        s = mfma(a, qf[dc], s);
+        const bf16x8 b = lds_read16(&S.V[(kt * 32 + r) * KSTR + dc * 16 + 8 * hh]);
+        dp = mfma(b, of[dc], dp);
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int kl = kt * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
+        const bool vis = full || ((kb * BK + kl <= qpos) && (qpos < S.end[kl]));
+        const float p = vis ? exp2_fast(s[i] * c2 - lse2) : 0.f;
+        s[i] = p * (dp[i] - Dq);
+      }
+      const bf16x8 d0 = c_to_b(s, 0), d1 = c_to_b(s, 1);
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        acc[dt] = mfma(tr_frag(S.K, KSTR, kt * 32, dt * 32, lane), d0, acc[dt]);
+        acc[dt] = mfma(tr_frag(S.K, KSTR, kt * 32 + 16, dt * 32, lane), d1, acc[dt]);
+      }
+    }
+    if (e + 1 < e1) store_tile(st[sidx ^ 1]);
+    __syncthreads();
+  }
+  if (!rok) return;
+  float* out = dq_acc + (int64_t(row) * g.h_q + head) * D;
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      f32x4 w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[e] = acc[dt][4 * i4 + e] * g.scale;
+      *reinterpret_cast<f32x4*>(out + dt * 32 + 8 * i4 + 4 * hh) = w;
+    }
+}
+
+// ------------------------------------------------------------------ dK, dV
+constexpr int KV_WAVES = 4;
+constexpr int KV_THREADS = KV_WAVES * 64;
+constexpr int KV_KEYS = 32 * KV_WAVES;            // keys per workgroup
+constexpr int QT = 64;                             // query rows per staged tile
+constexpr int QCH = (QT * D / 8) / KV_THREADS;     // 16-byte chunks per thread per Q (or dO) tile
+
+struct __align__(16) KvStage {
+  uint16_t Q[QT * KSTR];
+  uint16_t O[QT * KSTR];  // dO
+  float lse2[QT];
+  float Dv[QT];
+};
+
+template <int G, bool ACC, typename TG>
+__global__ __launch_bounds__(KV_THREADS) void dkdv_mfma_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const uint16_t* __restrict__ d_o, const float* __restrict__ lse, const float* __restrict__ Dv,
+    TG* __restrict__ d_k, TG* __restrict__ d_v, PlanPtrs P, AttnGeom g) {
+  __shared__ KvStage st[2];
+  __shared__ int32_t red[2][KV_WAVES];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r = lane & 31, hh = lane >> 5;
+  const int kvh = blockIdx.x % g.h_kv;
+  const int kb2 = blockIdx.x / g.h_kv;
+  const int kbase = kb2 * KV_KEYS;
+  const int j = kbase + wave * 32 + r;  // this lane's key (lane column of S, dP, dK^T, dV^T)
+  const bool jok = j < g.n_k;
+  const float c2 = g.scale * kLog2e;
+
+  bf16x8 kf[8], vf[8];
+#pragma unroll
+  for (int dc = 0; dc < 8; ++dc) {
+    const int64_t off = (int64_t(j) * g.h_kv + kvh) * D + dc * 16 + 8 * hh;
+    kf[dc] = jok ? ld16(k + off) : zero8();
+    vf[dc] = jok ? ld16(v + off) : zero8();
+  }
+  const int endj = jok ? P.end[j] : -1;
+
+  // query rows seen by this workgroup's keys: [kbase, max end) within the call's query range
+  int mx = jok ? endj : 0, mn = jok ? endj : 0x7FFFFFFF;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    mx = max(mx, __shfl_xor(mx, o, 64));
+    mn = min(mn, __shfl_xor(mn, o, 64));
+  }
+  if (lane == 0) {
+    red[0][wave] = mx;
+    red[1][wave] = mn;
+  }
+  __syncthreads();
+  int hi = 0;
+#pragma unroll
+  for (int w = 0; w < KV_WAVES; ++w) hi = max(hi, red[0][w]);
+  const int wave_min_end = red[1][wave];
+  const int lo = max(kbase, g.q_off);
+  hi = min(hi, g.q_off + g.n_q);
+  const int wave_kmax = kbase + wave * 32 + 31;
+
+  f32x16 dk[4], dv[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) {
+    dk[dt] = zero16();
+    dv[dt] = zero16();
+  }
+
+  const int qt_first = lo / QT;  // query tiles are aligned to 64 tree rows
+  const int n_qt = hi > lo ? (hi - 1) / QT - qt_first + 1 : 0;
+  const int n_steps = n_qt * G;
+
+  bf16x8 qreg[QCH], oreg[QCH];
+  float lreg = 0.f, dreg = 0.f;
+  auto load_tile = [&](int step) {
+    const int qt = qt_first + step / G, head = kvh * G + step % G;
+#pragma unroll
+    for (int u = 0; u < QCH; ++u) {
+      const int c = tid + u * KV_THREADS;
+      const int rr = c >> 4, dch = c & 15;
+      const int row = qt * QT + rr - g.q_off;  // q-buffer row
+      const bool ok = row >= 0 && row < g.n_q;
+      const int64_t off = (int64_t(row) * g.h_q + head) * D + dch * 8;
+      qreg[u] = ok ? ld16(q + off) : zero8();
+      oreg[u] = ok ? ld16(d_o + off) : zero8();
+    }
+    if (tid < QT) {
+      const int row = qt * QT + tid - g.q_off;
+      const bool ok = row >= 0 && row < g.n_q;
+      lreg = ok ? lse[int64_t(row) * g.h_q + head] * kLog2e : 0.f;
+      dreg = ok ? Dv[int64_t(row) * g.h_q + head] : 0.f;
+    }
+  };
+  auto store_tile = [&](KvStage& s) {
+#pragma unroll
+    for (int u = 0; u < QCH; ++u) {
+      const int c = tid + u * KV_THREADS;
+      const int rr = c >> 4, dch = c & 15;
+      *reinterpret_cast<bf16x8*>(&s.Q[rr * KSTR + dch * 8]) = qreg[u];
+      *reinterpret_cast<bf16x8*>(&s.O[rr * KSTR + dch * 8]) = oreg[u];
+    }
+    if (tid < QT) {
+      s.lse2[tid] = lreg;
+      s.Dv[tid] = dreg;
+    }
+  };
+
+  if (n_steps > 0) {
+    load_tile(0);
+    store_tile(st[0]);
+  }
+  __syncthreads();
+  for (int step = 0; step < n_steps; ++step) {
+    const int sidx = step & 1;
+    const int qt = qt_first + step / G;
+    if (step + 1 < n_steps) load_tile(step + 1);
+    const KvStage& S = st[sidx];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      const int q0 = qt * QT + mt * 32;  // tree row of the sub-tile's first query
+      // every (query, key) pair of this wave's 32 x 32 block visible and in range?
+      const bool full = wave_kmax <= q0 && wave_min_end > q0 + 31 && q0 >= lo && q0 + 31 < hi;
+      f32x16 s = zero16(), dp = zero16();
+#pragma unroll
+      for (int dc = 0; dc < 8; ++dc) {
+        const bf16x8 a = lds_read16(&S.Q[(mt * 32 + r) * KSTR + dc * 16 + 8 * hh]);
+        s = mfma(a, kf[dc], s);
+        const bf16x8 b = lds_read16(&S.O[(mt * 32 + r) * KSTR + dc * 16 + 8 * hh]);
+        dp = mfma(b, vf[dc], dp);
+      }
+      f32x16 ds;
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int ql = mt * 32 + 8 * i4 + 4 * hh;
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&S.lse2[ql]);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&S.Dv[ql]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 4 * i4 + e;
+          const int qq = qt * QT + ql + e;
+          const bool vis = full || (j <= qq && qq < endj && qq >= lo && qq < hi);
+          const float p = vis ? exp2_fast(s[i] * c2 - l4[e]) : 0.f;
+          s[i] = p;
+          ds[i] = p * (dp[i] - d4[e]);
+        }
+      }
+      const bf16x8 p0 = c_to_b(s, 0), p1 = c_to_b(s, 1);
+      const bf16x8 s0 = c_to_b(ds, 0), s1 = c_to_b(ds, 1);
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        dv[dt] = mfma(tr_frag(S.O, KSTR, mt * 32, dt * 32, lane), p0, dv[dt]);
+        dv[dt] = mfma(tr_frag(S.O, KSTR, mt * 32 + 16, dt * 32, lane), p1, dv[dt]);
+        dk[dt] = mfma(tr_frag(S.Q, KSTR, mt * 32, dt * 32, lane), s0, dk[dt]);
+        dk[dt] = mfma(tr_frag(S.Q, KSTR, mt * 32 + 16, dt * 32, lane), s1, dk[dt]);
+      }
+    }
+    if (step + 1 < n_steps) store_tile(st[sidx ^ 1]);
+    __syncthreads();
+  }
+  if (!jok) return;
+
+  // dK = R^T (scale * dK') at the key's depth; coordinates (c, c+64) are the
+  // same register of blocks dt and dt+2.
+  const int depth = P.depth[j];
+  const int64_t base = (int64_t(j) * g.h_kv + kvh) * D;
+#pragma unroll
+  for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      float lo4[4], hi4[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int c = dt * 32 + 8 * i4 + 4 * hh + e;
+        const double x1 = double(dk[dt][4 * i4 + e]) * g.scale, x2 = double(dk[dt + 2][4 * i4 + e]) * g.scale;
+        double cs = 1.0, sn = 0.0;
+        if (g.rope_base != 0.f) {
+          const double theta = pow(double(g.rope_base), -2.0 * double(c) / double(D));
+          sincos(double(depth) * theta, &sn, &cs);
+        }
+        lo4[e] = float(x1 * cs + x2 * sn);
+        hi4[e] = float(x2 * cs - x1 * sn);
+      }
+      const int c0 = dt * 32 + 8 * i4 + 4 * hh;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (ACC) {
+          d_k[base + c0 + e] += lo4[e];
+          d_k[base + c0 + 64 + e] += hi4[e];
+        } else {
+          Elem<TG>::store(d_k, base + c0 + e, lo4[e]);
+          Elem<TG>::store(d_k, base + c0 + 64 + e, hi4[e]);
+        }
+      }
+    }
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int c = dt * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
+      if (ACC)
+        d_v[base + c] += dv[dt][i];
+      else
+        Elem<TG>::store(d_v, base + c, dv[dt][i]);
+    }
+}
+
+template <int G>
+int launch_bwd_g(const void* q, const void* k, const void* v, const void* d_o, const float* lse, const float* D_,
+                 float* dq_acc, void* d_k, void* d_v, bool acc, const PlanPtrs& P, const AttnGeom& g,
+                 bool full_range, hipStream_t st) {
+  const int qb_first = g.q_off / BQ;
+  const int qb_end = (g.q_off + g.n_q + BQ - 1) / BQ;
+  const int n_qb = qb_end - qb_first;
+  if (n_qb > 0) {
+    dq_mfma_kernel<G><<<dim3(unsigned(n_qb) * unsigned(g.h_kv)), dim3(DqCfg<G>::THREADS), 0, st>>>(
+        (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)d_o, lse, D_, dq_acc, P, g,
+        full_range ? 1 : 0, qb_first, n_qb);
+    if (hipGetLastError() != hipSuccess) return -1;
+  }
+  const int nkb2 = (g.n_k + KV_KEYS - 1) / KV_KEYS;
+  if (nkb2 > 0) {
+    const dim3 grid(unsigned(nkb2) * unsigned(g.h_kv)), block(KV_THREADS);
+    if (acc)
+      dkdv_mfma_kernel<G, true, float><<<grid, block, 0, st>>>((const uint16_t*)q, (const uint16_t*)k,
+                                                                (const uint16_t*)v, (const uint16_t*)d_o, lse, D_,
+                                                                (float*)d_k, (float*)d_v, P, g);
+    else
+      dkdv_mfma_kernel<G, false, uint16_t><<<grid, block, 0, st>>>((const uint16_t*)q, (const uint16_t*)k,
+                                                                    (const uint16_t*)v, (const uint16_t*)d_o, lse,
+                                                                    D_, (uint16_t*)d_k, (uint16_t*)d_v, P, g);
+    if (hipGetLastError() != hipSuccess) return -1;
+  }
+  return 0;
+}
+
+}  // namespace
+
+bool mfma_bwd_supported(const AttnGeom& g, const PlanPtrs& P) {
+  const int G = g.h_q / g.h_kv;
+  return g.d == D && P.bq == BQ && P.bk == BK && (G == 1 || G == 2 || G == 4);
+}
+
+int launch_bwd_mfma(const void* q, const void* k, const void* v, const void* d_o, const float* lse, const float* D_,
+                    float* dq_acc, void* d_k, void* d_v, bool acc, const PlanPtrs& P, const AttnGeom& g,
+                    bool full_range, hipStream_t st) {
+  switch (g.h_q / g.h_kv) {
+    case 1: return launch_bwd_g<1>(q, k, v, d_o, lse, D_, dq_acc, d_k, d_v, acc, P, g, full_range, st);
+    case 2: return launch_bwd_g<2>(q, k, v, d_o, lse, D_, dq_acc, d_k, d_v, acc, P, g, full_range, st);
+    case 4: return launch_bwd_g<4>(q, k, v, d_o, lse, D_, dq_acc, d_k, d_v, acc, P, g, full_range, st);
+    default: return -1;
+  }
+}

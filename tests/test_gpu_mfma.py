@@ -103,3 +103,96 @@ def test_mfma_forward_agentic_8b_shape_sampled():
     Or, Lr = OA.forward_rows(o, None, None, None, rows, get=_lazy_rows(qb, kb, vb))
     ri = torch.as_tensor(rows, device=O.device)
     assert rel_err(O[ri], Or) < TOL and rel_err(L[ri], Lr) < TOL
+
+
+# ------------------------------------------------------------------ backward
+def _bwd_case(name, hq, hkv, std, seed):
+    case = TREES[name]()
+    tree = tt.Tree(case.seqs)
+    o = dfs_arrays(case.seqs)
+    plan = tree.upload_plan()
+    (q, qn), (k, kn), (v, vn), (do, don) = inputs(torch.bfloat16, seed, tree.N, tree.N, hq, hkv, 128, std)
+    print(f"{name}: N={tree.N} hq={hq} hkv={hkv} std={std}", flush=True)
+    O, L = tt.tree_attn_fwd(tree, plan, q, k, v)
+    dq, dk, dv = tt.tree_attn_bwd(tree, plan, q, k, v, O, L, do)
+    dQr, dKr, dVr = OA.backward(o, qn, kn, vn, don, which="leaves")
+    return (dq, dk, dv), (dQr, dKr, dVr)
+
+
+@pytest.mark.parametrize("name", list(TREES))
+@pytest.mark.parametrize("heads", [(8, 2), (4, 2), (2, 2)])
+def test_mfma_backward(name, heads):
+    got, ref = _bwd_case(name, heads[0], heads[1], 128 ** -0.5, 41)
+    for n, g_, r_ in zip(("dq", "dk", "dv"), got, ref):
+        assert rel_err(g_, r_) < TOL, (n, rel_err(g_, r_))
+
+
+@pytest.mark.parametrize("name", ["beam_small", "forest"])
+def test_mfma_backward_peaky(name):
+    got, ref = _bwd_case(name, 4, 1, 1.0, 42)
+    for n, g_, r_ in zip(("dq", "dk", "dv"), got, ref):
+        assert rel_err(g_, r_) < TOL, (n, rel_err(g_, r_))
+
+
+def test_mfma_backward_chunks_accumulate():
+    """Right-to-left chunks of a suffix against a cached prefix, dK/dV added
+    into fp32 buffers across chunks == oracle backward with dO = 0 on the prefix."""
+    L, prefix, chunk = 1000, 448, 192
+    seqs = ts.long_chain(6, length=L).seqs
+    tree = tt.Tree(seqs)
+    o = dfs_arrays(seqs)
+    plan = tree.upload_plan()
+    (q, qn), (k, kn), (v, vn), (do, don) = inputs(torch.bfloat16, 9, L, L, 8, 2, 128, 128 ** -0.5)
+    don[:prefix] = 0.0
+    dQr, dKr, dVr = OA.backward(o, qn, kn, vn, don)
+    dk = torch.zeros(L, 2, 128, dtype=torch.float32, device="cuda")
+    dv = torch.zeros_like(dk)
+    for s in reversed(range(prefix, L, chunk)):
+        e = min(L, s + chunk)
+        Oc, Lc = tt.tree_attn_fwd(tree, plan, q[s:e], k[:e], v[:e], q_off=s)
+        dqc, _, _ = tt.tree_attn_bwd(tree, plan, q[s:e], k[:e], v[:e], Oc, Lc, do[s:e], q_off=s,
+                                     d_k=dk[:e], d_v=dv[:e], accumulate=True)
+        assert rel_err(dqc, dQr[s:e]) < TOL
+    assert rel_err(dk, dKr) < TOL and rel_err(dv, dVr) < TOL
+
+
+def test_mfma_backward_agentic_8b_shape_sampled():
+    """8B-shape agentic tree at full size: dQ on sampled rows; dK/dV on keys
+    with small subtrees; over all keys, sum_j dV_j = sum over the group's
+    query heads of sum_i dO_i, and sum_j R(depth_j) dK_j = 0 (rows of dS sum
+    to zero)."""
+    case = ts.agentic_beam_tree(0)
+    tree = tt.Tree(case.seqs)
+    o = dfs_arrays(case.seqs)
+    N = tree.N
+    rng = ts.rng_for(2000)
+    qb = ts.normal_bf16(rng, (N, 32, 128), 128 ** -0.5)
+    kb = ts.normal_bf16(rng, (N, 8, 128), 128 ** -0.5)
+    vb = ts.normal_bf16(rng, (N, 8, 128), 128 ** -0.5)
+    ob = ts.normal_bf16(rng, (N, 32, 128), 1.0)
+    dev = lambda b: torch.from_numpy(b.view(np.int16)).cuda().view(torch.bfloat16)  # noqa: E731
+    plan = tree.upload_plan()
+    q, k, v, do = dev(qb), dev(kb), dev(vb), dev(ob)
+    O, L = tt.tree_attn_fwd(tree, plan, q, k, v)
+    dq, dk, dv = tt.tree_attn_bwd(tree, plan, q, k, v, O, L, do)
+
+    def get(name, idx):
+        return ts.bf16_bits_to_f64({"q": qb, "k": kb, "v": vb, "do": ob}[name][idx])
+
+    rows = np.unique(np.concatenate([np.linspace(0, N - 1, 12).astype(int), [0, N - 1]]))
+    ref = OA.dq_rows(o, None, None, None, None, rows, get=get)
+    assert rel_err(dq[torch.as_tensor(rows, device="cuda")], ref) < TOL
+    # keys whose subtree holds at most 40 rows (deep in a leaf segment)
+    small = np.nonzero(o["end"] - np.arange(N) <= 40)[0]
+    keys = small[np.linspace(0, len(small) - 1, 6).astype(int)]
+    rk, rv = OA.dkdv_keys(o, None, None, None, None, keys, get=get)
+    ki = torch.as_tensor(keys, device="cuda")
+    assert rel_err(dk[ki], rk) < TOL and rel_err(dv[ki], rv) < TOL
+    # identities over all keys
+    sdv = dv.float().sum(0).cpu().double().numpy()
+    sdo = do.float().reshape(N, 8, 4, 128).sum((0, 2)).cpu().double().numpy()
+    assert rel_err(torch.from_numpy(sdv), sdo) < TOL
+    from oracle.rope import rotate
+    dkr = rotate(dk.float().cpu().double().numpy(), o["depth"], 10000.0)
+    tot = np.abs(dkr.sum(0)).max()
+    assert tot < 2e-2 * np.abs(dkr).sum(0).max(), tot
