@@ -1,0 +1,326 @@
+#!/usr/bin/env python3
+"""Benchmark of the prefix-tree attention hot path on one MI355X.
+
+Headline workload (one "step"): forward + backward tree attention over the
+8B-class agentic tree (32 query heads, 8 kv heads, head dim 128, bf16,
+RoPE at depth): beam of depth 10 from a 4096-token root, branch 2, 16 kept,
+segments U[512, 2048], random leaves dropped until <= 67.2k unique tokens.
+Inputs are resident in HBM before the timed region; the host trie build and
+plan upload happen once, outside it, and are reported separately.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+
+Prints ONE JSON line.  value = unique tree tokens per second of the
+forward+backward step; useful TFLOP/s counts visible (query, key) pairs only:
+forward 4 d Hq P, backward 10 d Hq P (P = sum over rows of depth + 1).
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+METRIC = "tree attn fwd+bwd unique tokens/s + useful TFLOP/s (% bf16 MFMA peak), 8B shape"
+
+# HBM traffic of the roofline kernel from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE
+# runs (scaled by the same counters' reading for a plain copy of known size),
+# valid only for the kernel source it was measured on.
+MEASURED_TRAFFIC = None  # {"kernel": ..., "source_sha1": ..., "bytes_per_launch": ...}
+
+
+def _source_sha(path):
+    with open(path, "rb") as f:
+        return hashlib.sha1(f.read()).hexdigest()
+
+
+def _bf16(t):
+    import torch
+    return t.to(torch.bfloat16)
+
+
+def _make_inputs(N, hq, hkv, d, seed, device="cuda"):
+    import torch
+    g = torch.Generator(device=device).manual_seed(seed)
+    s = d ** -0.5
+    q = _bf16(torch.randn(N, hq, d, device=device, generator=g) * s)
+    k = _bf16(torch.randn(N, hkv, d, device=device, generator=g) * s)
+    v = _bf16(torch.randn(N, hkv, d, device=device, generator=g) * s)
+    do = _bf16(torch.randn(N, hq, d, device=device, generator=g))
+    return q, k, v, do
+
+
+class Step:
+    """Preallocated fwd+bwd over one tree (or one chunk of a path)."""
+
+    def __init__(self, tt, tree, plan, q, k, v, do, q_off=0, accumulate=False, d_k=None, d_v=None):
+        import torch
+        self.tt, self.tree, self.plan = tt, tree, plan
+        self.q, self.k, self.v, self.do, self.q_off = q, k, v, do, q_off
+        self.o = torch.empty_like(q)
+        self.lse = torch.empty(q.shape[0], q.shape[1], dtype=torch.float32, device=q.device)
+        self.dq = torch.empty_like(q)
+        self.accumulate = accumulate
+        self.dk = d_k if d_k is not None else torch.empty_like(k)
+        self.dv = d_v if d_v is not None else torch.empty_like(v)
+        nb = max(tt.attn_workspace_bytes(tree, plan, q, k, v, True, q_off=q_off),
+                 tt.attn_workspace_bytes(tree, plan, q, k, v, False, q_off=q_off))
+        self.ws = torch.empty(max(nb, 256), dtype=torch.uint8, device=q.device)
+
+    def fwd(self):
+        self.tt.tree_attn_fwd(self.tree, self.plan, self.q, self.k, self.v, q_off=self.q_off, o=self.o,
+                              lse=self.lse, workspace=self.ws)
+
+    def bwd(self):
+        self.tt.tree_attn_bwd(self.tree, self.plan, self.q, self.k, self.v, self.o, self.lse, self.do,
+                              q_off=self.q_off, d_q=self.dq, d_k=self.dk, d_v=self.dv,
+                              accumulate=self.accumulate, workspace=self.ws)
+
+
+def _time(fn, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def secondary(tt, ts, steps):
+    """Shorter measurements of the other configurations (not the headline)."""
+    import torch
+    out = {}
+    d = 128
+    # 1.7B-class forward on the RL forest (16 q heads, 8 kv heads)
+    case = ts.rl_forest_accepted(0)
+    tree = tt.Tree(case.seqs)
+    plan = tree.upload_plan()
+    q, k, v, do = _make_inputs(tree.N, 16, 8, d, 11)
+    st = Step(tt, tree, plan, q, k, v, do)
+    ms = _time(st.fwd, steps, 2)
+    fl = 4 * d * 16 * tree.info["pairs"]
+    out["rl_forest_1p7b_fwd"] = dict(N=tree.N, seed=case.seed, compression=round(case.seq_tokens / tree.N, 3),
+                                     ms=round(ms, 4), tokens_per_s=round(tree.N / ms * 1e3),
+                                     useful_tflops=round(fl / ms / 1e9, 1),
+                                     pct_bf16_peak=round(fl / ms / 1e9 / PEAK_BF16_TFLOPS * 100, 2))
+    del st, q, k, v, do
+    # path mode: 49,152-token chain, 16k suffix in 2048-token chunks right to left against a 32k prefix
+    case = ts.long_chain(0)
+    tree = tt.Tree(case.seqs)
+    plan = tree.upload_plan()
+    L, prefix, chunk = 49152, 32768, 2048
+    q, k, v, do = _make_inputs(L, 32, 8, d, 12)
+    dk = torch.zeros(L, 8, d, dtype=torch.float32, device="cuda")
+    dv = torch.zeros_like(dk)
+    steps_c = []
+    for s in reversed(range(prefix, L, chunk)):
+        e = min(L, s + chunk)
+        steps_c.append(Step(tt, tree, plan, q[s:e], k[:e], v[:e], do[s:e], q_off=s, accumulate=True,
+                            d_k=dk[:e], d_v=dv[:e]))
+
+    def path_step():
+        for sc in steps_c:
+            sc.fwd()
+            sc.bwd()
+
+    ms = _time(path_step, max(2, steps // 2), 1)
+    P = sum(chunk * (s + 1) + chunk * (chunk - 1) // 2 for s in range(prefix, L, chunk))
+    fl = 14 * d * 32 * P
+    out["chain_path_mode_8b"] = dict(chunks=len(steps_c), chunk=chunk, prefix=prefix, pairs_per_head=P,
+                                     ms=round(ms, 3), ms_per_chunk=round(ms / len(steps_c), 3),
+                                     useful_tflops=round(fl / ms / 1e9, 1),
+                                     pct_bf16_peak=round(fl / ms / 1e9 / PEAK_BF16_TFLOPS * 100, 2))
+    del steps_c, q, k, v, do, dk, dv
+    torch.cuda.empty_cache()
+    return out
+
+
+def per_branch_dense(tt, ts, tree, case, q, k, v, do, steps):
+    """The same kernels run on every input sequence as its own chain (no prefix sharing)."""
+    import torch
+    arr = tree.export()
+    offs = [0]
+    for s in case.seqs:
+        offs.append(offs[-1] + len(s))
+    steps_b = []
+    for b, s in enumerate(case.seqs):
+        rows = torch.as_tensor(arr["seq_pos_to_dfs"][offs[b]:offs[b + 1]].astype("int64"), device="cuda")
+        bt = tt.Tree([s])
+        bp = bt.upload_plan()
+        steps_b.append((bt, Step(tt, bt, bp, q[rows].contiguous(), k[rows].contiguous(), v[rows].contiguous(),
+                                 do[rows].contiguous())))
+
+    def run():
+        for _, sb in steps_b:
+            sb.fwd()
+            sb.bwd()
+
+    ms = _time(run, max(2, steps // 2), 1)
+    branch_tokens = sum(len(s) for s in case.seqs)
+    del steps_b
+    torch.cuda.empty_cache()
+    return dict(branches=len(case.seqs), branch_tokens=branch_tokens, ms=round(ms, 3),
+                branch_tokens_per_s=round(branch_tokens / ms * 1e3))
+
+
+def cpu_baseline(ts, case, seed, budget_s):
+    """The fp64 oracle on sampled rows of the same tree: per-row forward and dQ
+    (each row from the branch ending at it), rows drawn uniformly at random."""
+    import numpy as np
+    from oracle import attention as OA
+    from oracle.tree import dfs_arrays
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    o = dfs_arrays(case.seqs)
+    N = o["N"]
+    rng = ts.rng_for(seed + 77)
+
+    def rowbits(shape_h, std, rows):
+        # the same distribution as the GPU inputs, drawn per sampled row set
+        return ts.bf16_bits_to_f64(ts.normal_bf16(rng, (len(rows),) + shape_h, std))
+
+    done = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < budget_s:
+        i = int(rng.integers(0, N))
+        br = OA.ancestors(o, i)
+        qv = rowbits((32, 128), 128 ** -0.5, br)
+        kv = rowbits((8, 128), 128 ** -0.5, br)
+        vv = rowbits((8, 128), 128 ** -0.5, br)
+        dov = rowbits((32, 128), 1.0, br)
+        idx = {int(r): n for n, r in enumerate(br)}
+
+        def get(name, ix, qv=qv, kv=kv, vv=vv, dov=dov, idx=idx):
+            src = {"q": qv, "k": kv, "v": vv, "do": dov}[name]
+            return src[[idx[int(x)] for x in ix]]
+
+        OA.forward_rows(o, None, None, None, [i], get=get)
+        OA.dq_rows(o, None, None, None, None, [i], get=get)
+        done += 1
+    el = time.perf_counter() - t0
+    return {"value": round(done / el, 3), "unit": "unique tokens/s (forward + dQ only)", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{done} rows drawn uniformly from the {N}-row agentic tree; per row the oracle's per-branch "
+                      f"forward and dQ over all 32 heads (forward_rows + dq_rows, fp64 numpy) in {el:.1f} s; "
+                      "dK/dV are not included (the oracle's per-key form costs the key's whole subtree), so this "
+                      "overstates the oracle's full forward+backward rate"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 (the multi-GPU dispatcher "
+                                   "is design-only)"}), flush=True)
+        sys.exit(2)
+
+    import torch
+    import prefix_tree_attention_dfs_amd as tt
+    import treesynth as ts
+
+    torch.cuda.set_device(0)
+    t0 = time.perf_counter()
+    case = ts.agentic_beam_tree(args.seed)
+    gen_s = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    tree = tt.Tree(case.seqs)
+    build_ms = (time.perf_counter() - t0) * 1e3
+    plan = tree.upload_plan()
+    info = tree.info
+    N, hq, hkv, d = tree.N, 32, 8, 128
+    P = info["pairs"]
+    q, k, v, do = _make_inputs(N, hq, hkv, d, args.seed + 1)
+    st = Step(tt, tree, plan, q, k, v, do)
+
+    def step():
+        st.fwd()
+        st.bwd()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    tt.timing_enable(True)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    tt.timing_enable(False)
+    ms = e0.elapsed_time(e1) / args.steps
+    kt = tt.timing_collect()
+
+    useful = 14 * d * hq * P
+    value = N / (ms * 1e-3)
+    tflops = useful / (ms * 1e-3) / 1e12
+    # roofline of the dominant kernel (largest share of the step's device time)
+    algo = {"attn_fwd_mfma": 4 * d * hq * P, "attn_bwd_dkdv_mfma": 8 * d * hq * P,
+            "attn_bwd_dq_mfma": 6 * d * hq * P}
+    dom = max(kt, key=lambda n: kt[n][1])
+    launches, tot, mx = kt[dom]
+    avg_ms = tot / launches
+    achieved = algo.get(dom, 0) / (avg_ms * 1e-3) / 1e12
+    src = os.path.join(ROOT, "prefix_tree_attention_dfs_amd", "csrc",
+                       "attn_mfma.hip" if dom == "attn_fwd_mfma" else "attn_mfma_bwd.hip")
+    traffic = None
+    if MEASURED_TRAFFIC and MEASURED_TRAFFIC.get("kernel") == dom and \
+            MEASURED_TRAFFIC.get("source_sha1") == _source_sha(src):
+        traffic = MEASURED_TRAFFIC["bytes_per_launch"]
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                "avg_launch_ms": round(avg_ms, 4),
+                "algorithmic_flops_per_launch": algo.get(dom, 0)}
+    kernels = {n: {"launches": c, "avg_ms": round(t / c, 4), "max_ms": round(m, 4),
+                   "share": round(t / sum(x[1] for x in kt.values()), 4)} for n, (c, t, m) in kt.items()}
+
+    result = {
+        "metric": METRIC, "value": round(value, 1), "unit": "unique tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "8B-class agentic tree fwd+bwd (Hq 32, Hkv 8, d 128, RoPE at depth)",
+                   "unique_tokens": N, "seq_tokens": info["seq_tokens"], "leaves": info["n_leaves"],
+                   "max_depth": info["max_depth"], "pairs_per_head": P, "seed": args.seed,
+                   "tiles_64x64": info["n_tiles"], "full_tiles": info["n_full_tiles"]},
+        "useful_tflops": round(tflops, 1), "pct_bf16_peak": round(tflops / PEAK_BF16_TFLOPS * 100, 2),
+        "roofline": roofline, "kernels": kernels,
+        "tree_build_ms": round(build_ms, 2), "tree_gen_s": round(gen_s, 2),
+    }
+    dense = per_branch_dense(tt, ts, tree, case, q, k, v, do, args.steps)
+    dense["tree_speedup"] = round(dense["ms"] / ms, 3)
+    result["per_branch_dense"] = dense
+    del st
+    torch.cuda.empty_cache()
+    if not args.no_secondary:
+        result["secondary"] = secondary(tt, ts, args.steps)
+    if not args.no_cpu_baseline:
+        cb = cpu_baseline(ts, case, args.seed, args.cpu_seconds)
+        cb["gpu_over_cpu"] = round(value / cb["value"], 1)
+        result["cpu_baseline"] = cb
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

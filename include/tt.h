@@ -240,6 +240,24 @@ typedef struct {
 int tree_nll_workspace_bytes(const tt_nll_args* args, size_t* bytes);
 int tree_weighted_nll(const tt_nll_args* args, tt_stream stream);
 
+/*
+ * Kernel timing (diagnostics).  While enabled on the calling thread, every
+ * kernel this library launches from that thread is bracketed by two HIP
+ * events recorded on the launch stream.  tt_timing_collect waits for the
+ * recorded events, returns per kernel name the launch count, total and
+ * maximum duration, and clears the record.  Events are created on first use
+ * and reused; no device memory is allocated.
+ */
+typedef struct {
+  char name[48];
+  int64_t launches;
+  double total_ms;
+  double max_ms;
+} tt_kernel_time;
+
+int tt_timing_enable(int on);
+int tt_timing_collect(tt_kernel_time* out, int capacity, int* count);
+
 /* Text of the last error on this thread ("" if none). Valid until the next call. */
 const char* tt_last_error(void);
 

@@ -24,7 +24,7 @@ TT_ACCUMULATE_DKDV = 1
 EXPORTED = ("tree_build", "tree_free", "tree_info", "tree_export", "tree_plan_bytes", "tree_plan_upload",
             "tree_plan_copy",
             "tree_attn_workspace_bytes", "tree_attn_fwd", "tree_attn_bwd", "tree_nll_workspace_bytes",
-            "tree_weighted_nll", "tt_last_error")
+            "tree_weighted_nll", "tt_last_error", "tt_timing_enable", "tt_timing_collect")
 
 
 class TTError(RuntimeError):
@@ -65,6 +65,11 @@ class AttnBwdArgs(ctypes.Structure):
                 ("d_k", ctypes.c_void_p), ("d_v", ctypes.c_void_p), ("flags", ctypes.c_uint32)]
 
 
+class KernelTime(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 48), ("launches", ctypes.c_int64), ("total_ms", ctypes.c_double),
+                ("max_ms", ctypes.c_double)]
+
+
 class NllArgs(ctypes.Structure):
     _fields_ = [("n_rows", ctypes.c_int32), ("d_model", ctypes.c_int32), ("vocab", ctypes.c_int32),
                 ("n_tgt", ctypes.c_int32),
@@ -97,6 +102,10 @@ def _setup(lib):
     lib.tree_nll_workspace_bytes.argtypes = [ctypes.POINTER(NllArgs), ctypes.POINTER(ctypes.c_size_t)]
     lib.tree_weighted_nll.argtypes = [ctypes.POINTER(NllArgs), ctypes.c_void_p]
     lib.tt_last_error.restype = ctypes.c_char_p
+    lib.tt_timing_enable.argtypes = [ctypes.c_int]
+    lib.tt_timing_enable.restype = ctypes.c_int
+    lib.tt_timing_collect.argtypes = [ctypes.POINTER(KernelTime), ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
+    lib.tt_timing_collect.restype = ctypes.c_int
     for _n in ("tree_info", "tree_export", "tree_plan_bytes", "tree_plan_upload", "tree_plan_copy", "tree_attn_workspace_bytes",
                "tree_attn_fwd", "tree_attn_bwd", "tree_nll_workspace_bytes", "tree_weighted_nll"):
         getattr(lib, _n).restype = ctypes.c_int
@@ -126,6 +135,21 @@ def last_error():
 
 def _ptr(a, ctype):
     return a.ctypes.data_as(ctypes.POINTER(ctype)) if a is not None else None
+
+
+# ------------------------------------------------------------------ kernel timing
+def timing_enable(on=True):
+    """Bracket every kernel the library launches (this thread) with HIP events."""
+    _check(lib().tt_timing_enable(1 if on else 0))
+
+
+def timing_collect():
+    """{kernel name: (launches, total_ms, max_ms)} since the last collect; waits for the events."""
+    buf = (KernelTime * 64)()
+    n = ctypes.c_int()
+    _check(lib().tt_timing_collect(buf, 64, ctypes.byref(n)))
+    return {buf[i].name.decode(): (int(buf[i].launches), float(buf[i].total_ms), float(buf[i].max_ms))
+            for i in range(min(n.value, 64))}
 
 
 # ------------------------------------------------------------------ tree

@@ -360,32 +360,33 @@ __global__ __launch_bounds__(KV_THREADS) void dkdv_mfma_kernel(
 }
 
 template <int G>
-int launch_bwd_g(const void* q, const void* k, const void* v, const void* d_o, const float* lse, const float* D_,
-                 float* dq_acc, void* d_k, void* d_v, bool acc, const PlanPtrs& P, const AttnGeom& g,
-                 bool full_range, hipStream_t st) {
+int launch_dq_g(const void* q, const void* k, const void* v, const void* d_o, const float* lse, const float* D_,
+                float* dq_acc, const PlanPtrs& P, const AttnGeom& g, bool full_range, hipStream_t st) {
   const int qb_first = g.q_off / BQ;
   const int qb_end = (g.q_off + g.n_q + BQ - 1) / BQ;
   const int n_qb = qb_end - qb_first;
-  if (n_qb > 0) {
-    dq_mfma_kernel<G><<<dim3(unsigned(n_qb) * unsigned(g.h_kv)), dim3(DqCfg<G>::THREADS), 0, st>>>(
-        (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)d_o, lse, D_, dq_acc, P, g,
-        full_range ? 1 : 0, qb_first, n_qb);
-    if (hipGetLastError() != hipSuccess) return -1;
-  }
+  if (n_qb <= 0) return 0;
+  dq_mfma_kernel<G><<<dim3(unsigned(n_qb) * unsigned(g.h_kv)), dim3(DqCfg<G>::THREADS), 0, st>>>(
+      (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)d_o, lse, D_, dq_acc, P, g,
+      full_range ? 1 : 0, qb_first, n_qb);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+template <int G>
+int launch_dkdv_g(const void* q, const void* k, const void* v, const void* d_o, const float* lse, const float* D_,
+                  void* d_k, void* d_v, bool acc, const PlanPtrs& P, const AttnGeom& g, hipStream_t st) {
   const int nkb2 = (g.n_k + KV_KEYS - 1) / KV_KEYS;
-  if (nkb2 > 0) {
-    const dim3 grid(unsigned(nkb2) * unsigned(g.h_kv)), block(KV_THREADS);
-    if (acc)
-      dkdv_mfma_kernel<G, true, float><<<grid, block, 0, st>>>((const uint16_t*)q, (const uint16_t*)k,
-                                                                (const uint16_t*)v, (const uint16_t*)d_o, lse, D_,
-                                                                (float*)d_k, (float*)d_v, P, g);
-    else
-      dkdv_mfma_kernel<G, false, uint16_t><<<grid, block, 0, st>>>((const uint16_t*)q, (const uint16_t*)k,
-                                                                    (const uint16_t*)v, (const uint16_t*)d_o, lse,
-                                                                    D_, (uint16_t*)d_k, (uint16_t*)d_v, P, g);
-    if (hipGetLastError() != hipSuccess) return -1;
-  }
-  return 0;
+  if (nkb2 <= 0) return 0;
+  const dim3 grid(unsigned(nkb2) * unsigned(g.h_kv)), block(KV_THREADS);
+  if (acc)
+    dkdv_mfma_kernel<G, true, float><<<grid, block, 0, st>>>((const uint16_t*)q, (const uint16_t*)k,
+                                                              (const uint16_t*)v, (const uint16_t*)d_o, lse, D_,
+                                                              (float*)d_k, (float*)d_v, P, g);
+  else
+    dkdv_mfma_kernel<G, false, uint16_t><<<grid, block, 0, st>>>((const uint16_t*)q, (const uint16_t*)k,
+                                                                  (const uint16_t*)v, (const uint16_t*)d_o, lse, D_,
+                                                                  (uint16_t*)d_k, (uint16_t*)d_v, P, g);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 }  // namespace
@@ -395,13 +396,22 @@ bool mfma_bwd_supported(const AttnGeom& g, const PlanPtrs& P) {
   return g.d == D && P.bq == BQ && P.bk == BK && (G == 1 || G == 2 || G == 4);
 }
 
-int launch_bwd_mfma(const void* q, const void* k, const void* v, const void* d_o, const float* lse, const float* D_,
-                    float* dq_acc, void* d_k, void* d_v, bool acc, const PlanPtrs& P, const AttnGeom& g,
-                    bool full_range, hipStream_t st) {
+int launch_dq_mfma(const void* q, const void* k, const void* v, const void* d_o, const float* lse, const float* D_,
+                   float* dq_acc, const PlanPtrs& P, const AttnGeom& g, bool full_range, hipStream_t st) {
   switch (g.h_q / g.h_kv) {
-    case 1: return launch_bwd_g<1>(q, k, v, d_o, lse, D_, dq_acc, d_k, d_v, acc, P, g, full_range, st);
-    case 2: return launch_bwd_g<2>(q, k, v, d_o, lse, D_, dq_acc, d_k, d_v, acc, P, g, full_range, st);
-    case 4: return launch_bwd_g<4>(q, k, v, d_o, lse, D_, dq_acc, d_k, d_v, acc, P, g, full_range, st);
+    case 1: return launch_dq_g<1>(q, k, v, d_o, lse, D_, dq_acc, P, g, full_range, st);
+    case 2: return launch_dq_g<2>(q, k, v, d_o, lse, D_, dq_acc, P, g, full_range, st);
+    case 4: return launch_dq_g<4>(q, k, v, d_o, lse, D_, dq_acc, P, g, full_range, st);
+    default: return -1;
+  }
+}
+
+int launch_dkdv_mfma(const void* q, const void* k, const void* v, const void* d_o, const float* lse, const float* D_,
+                     void* d_k, void* d_v, bool acc, const PlanPtrs& P, const AttnGeom& g, hipStream_t st) {
+  switch (g.h_q / g.h_kv) {
+    case 1: return launch_dkdv_g<1>(q, k, v, d_o, lse, D_, d_k, d_v, acc, P, g, st);
+    case 2: return launch_dkdv_g<2>(q, k, v, d_o, lse, D_, d_k, d_v, acc, P, g, st);
+    case 4: return launch_dkdv_g<4>(q, k, v, d_o, lse, D_, d_k, d_v, acc, P, g, st);
     default: return -1;
   }
 }

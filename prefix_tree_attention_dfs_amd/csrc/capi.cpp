@@ -3,8 +3,10 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <algorithm>
 #include <cstring>
 #include <string>
+#include <vector>
 
 #include "internal.h"
 #include "kernels.h"
@@ -121,7 +123,85 @@ int dev_fail(const char* fn, const char* what) {
   return tt::fail(TT_EDEVICE, std::string(fn) + ": " + what + " failed: " + hipGetErrorString(e));
 }
 
+// ---- optional per-launch timing (tt_timing_enable)
+struct TimedLaunch {
+  const char* name;
+  hipEvent_t a, b;
+};
+thread_local bool g_timing = false;
+thread_local std::vector<TimedLaunch> g_launches;
+thread_local std::vector<hipEvent_t> g_pool;
+
+hipEvent_t take_event() {
+  if (!g_pool.empty()) {
+    hipEvent_t e = g_pool.back();
+    g_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Brackets one kernel launch with events on its stream when timing is on.
+class KTimer {
+ public:
+  KTimer(const char* name, hipStream_t st) : name_(name), st_(st) {
+    if (!g_timing) return;
+    a_ = take_event();
+    b_ = take_event();
+    if (a_ && b_) (void)hipEventRecord(a_, st_);
+  }
+  ~KTimer() {
+    if (!g_timing || !a_ || !b_) return;
+    (void)hipEventRecord(b_, st_);
+    g_launches.push_back({name_, a_, b_});
+  }
+
+ private:
+  const char* name_;
+  hipStream_t st_;
+  hipEvent_t a_ = nullptr, b_ = nullptr;
+};
+
 }  // namespace
+
+extern "C" int tt_timing_enable(int on) {
+  tt::clear_error();
+  g_timing = on != 0;
+  return TT_OK;
+}
+
+extern "C" int tt_timing_collect(tt_kernel_time* out, int capacity, int* count) {
+  tt::clear_error();
+  if (!count || (capacity > 0 && !out)) return tt::fail(TT_EINVAL, "tt_timing_collect: NULL argument");
+  std::vector<tt_kernel_time> agg;
+  int rc = TT_OK;
+  for (const TimedLaunch& t : g_launches) {
+    float ms = 0.f;
+    if (hipEventSynchronize(t.b) != hipSuccess || hipEventElapsedTime(&ms, t.a, t.b) != hipSuccess) {
+      rc = TT_EDEVICE;
+      ms = 0.f;
+    }
+    size_t k = 0;
+    while (k < agg.size() && std::strncmp(agg[k].name, t.name, sizeof(agg[k].name)) != 0) ++k;
+    if (k == agg.size()) {
+      tt_kernel_time z{};
+      std::strncpy(z.name, t.name, sizeof(z.name) - 1);
+      agg.push_back(z);
+    }
+    agg[k].launches += 1;
+    agg[k].total_ms += ms;
+    agg[k].max_ms = std::max(agg[k].max_ms, double(ms));
+    g_pool.push_back(t.a);
+    g_pool.push_back(t.b);
+  }
+  g_launches.clear();
+  *count = int(agg.size());
+  for (int i = 0; i < capacity && i < int(agg.size()); ++i) out[i] = agg[size_t(i)];
+  if (rc != TT_OK) return tt::fail(rc, "tt_timing_collect: event query failed");
+  return TT_OK;
+}
 
 extern "C" int tree_plan_upload(const tt_tree* t, void* dev_plan, size_t bytes, tt_stream stream) {
   tt::clear_error();
@@ -146,9 +226,10 @@ extern "C" int tree_attn_workspace_bytes(const tt_attn_args* a, int for_bwd, siz
 
 extern "C" int tree_attn_fwd(const tt_attn_args* a, tt_stream stream) {
   tt::clear_error();
-  int rc = check_attn(a, "tree_attn_fwd");
+  const char* fn = "tree_attn_fwd";
+  int rc = check_attn(a, fn);
   if (rc) return rc;
-  if ((rc = check_ws(a, false, "tree_attn_fwd"))) return rc;
+  if ((rc = check_ws(a, false, fn))) return rc;
   if (a->n_q == 0) return TT_OK;
   hipStream_t st = (hipStream_t)stream;
   const PlanPtrs P = plan_ptrs(a->tree, a->plan);
@@ -158,30 +239,38 @@ extern "C" int tree_attn_fwd(const tt_attn_args* a, tt_stream stream) {
   const void* q = a->q;
   const void* k = a->k;
   if (w.rope) {
-    if (launch_rope(a->q, ws + w.q_rot, a->dtype, a->dtype, false, P.depth, a->q_off, a->n_q, a->h_q, a->d,
-                    a->rope_base, false, st))
-      return dev_fail("tree_attn_fwd", "rope(q)");
-    if (launch_rope(a->k, ws + w.k_rot, a->dtype, a->dtype, false, P.depth, 0, a->n_k, a->h_kv, a->d, a->rope_base,
-                    false, st))
-      return dev_fail("tree_attn_fwd", "rope(k)");
+    {
+      KTimer t("rope_q", st);
+      if (launch_rope(a->q, ws + w.q_rot, a->dtype, a->dtype, false, P.depth, a->q_off, a->n_q, a->h_q, a->d,
+                      a->rope_base, false, st))
+        return dev_fail(fn, "rope(q)");
+    }
+    {
+      KTimer t("rope_k", st);
+      if (launch_rope(a->k, ws + w.k_rot, a->dtype, a->dtype, false, P.depth, 0, a->n_k, a->h_kv, a->d,
+                      a->rope_base, false, st))
+        return dev_fail(fn, "rope(k)");
+    }
     q = ws + w.q_rot;
     k = ws + w.k_rot;
   }
   const bool full_range = a->q_off == 0 && a->n_q == P.N;
   if (a->dtype == TT_BF16 && mfma_attn_supported(g, P)) {
-    if (launch_fwd_mfma(q, k, a->v, a->o, a->lse, P, g, full_range, st))
-      return dev_fail("tree_attn_fwd", "attention kernel launch");
-  } else if (launch_fwd_generic(a->dtype, q, k, a->v, a->o, a->lse, P, g, st)) {
-    return dev_fail("tree_attn_fwd", "attention kernel launch");
+    KTimer t("attn_fwd_mfma", st);
+    if (launch_fwd_mfma(q, k, a->v, a->o, a->lse, P, g, full_range, st)) return dev_fail(fn, "attention kernel");
+  } else {
+    KTimer t("attn_fwd_generic", st);
+    if (launch_fwd_generic(a->dtype, q, k, a->v, a->o, a->lse, P, g, st)) return dev_fail(fn, "attention kernel");
   }
   return TT_OK;
 }
 
 extern "C" int tree_attn_bwd(const tt_attn_bwd_args* b, tt_stream stream) {
   tt::clear_error();
+  const char* fn = "tree_attn_bwd";
   if (!b) return tt::fail(TT_EINVAL, "tree_attn_bwd: args is NULL");
   const tt_attn_args* a = &b->a;
-  int rc = check_attn(a, "tree_attn_bwd");
+  int rc = check_attn(a, fn);
   if (rc) return rc;
   if (b->flags & ~TT_ACCUMULATE_DKDV) return tt::fail(TT_EINVAL, "tree_attn_bwd: unknown flags");
   const bool acc = (b->flags & TT_ACCUMULATE_DKDV) != 0;
@@ -190,7 +279,7 @@ extern "C" int tree_attn_bwd(const tt_attn_bwd_args* b, tt_stream stream) {
   for (const void* p : {b->d_o, static_cast<const void*>(b->d_q), static_cast<const void*>(b->d_k),
                         static_cast<const void*>(b->d_v)})
     if (p && !aligned16(p)) return tt::fail(TT_EINVAL, "tree_attn_bwd: device pointers must be 16-byte aligned");
-  if ((rc = check_ws(a, true, "tree_attn_bwd"))) return rc;
+  if ((rc = check_ws(a, true, fn))) return rc;
   if (a->n_k == 0) return TT_OK;
   hipStream_t st = (hipStream_t)stream;
   const PlanPtrs P = plan_ptrs(a->tree, a->plan);
@@ -200,33 +289,57 @@ extern "C" int tree_attn_bwd(const tt_attn_bwd_args* b, tt_stream stream) {
   const void* q = a->q;
   const void* k = a->k;
   if (w.rope) {
-    if (a->n_q > 0 && launch_rope(a->q, ws + w.q_rot, a->dtype, a->dtype, false, P.depth, a->q_off, a->n_q, a->h_q,
-                                  a->d, a->rope_base, false, st))
-      return dev_fail("tree_attn_bwd", "rope(q)");
-    if (launch_rope(a->k, ws + w.k_rot, a->dtype, a->dtype, false, P.depth, 0, a->n_k, a->h_kv, a->d, a->rope_base,
-                    false, st))
-      return dev_fail("tree_attn_bwd", "rope(k)");
+    if (a->n_q > 0) {
+      KTimer t("rope_q", st);
+      if (launch_rope(a->q, ws + w.q_rot, a->dtype, a->dtype, false, P.depth, a->q_off, a->n_q, a->h_q, a->d,
+                      a->rope_base, false, st))
+        return dev_fail(fn, "rope(q)");
+    }
+    {
+      KTimer t("rope_k", st);
+      if (launch_rope(a->k, ws + w.k_rot, a->dtype, a->dtype, false, P.depth, 0, a->n_k, a->h_kv, a->d,
+                      a->rope_base, false, st))
+        return dev_fail(fn, "rope(k)");
+    }
     q = ws + w.q_rot;
     k = ws + w.k_rot;
   }
   float* D = reinterpret_cast<float*>(ws + w.D);
   float* dq = reinterpret_cast<float*>(ws + w.dq);
-  if (launch_bwd_pre(a->dtype, a->o, b->d_o, D, int64_t(a->n_q) * a->h_q, a->d, st))
-    return dev_fail("tree_attn_bwd", "preprocess");
+  {
+    KTimer t("attn_bwd_pre", st);
+    if (launch_bwd_pre(a->dtype, a->o, b->d_o, D, int64_t(a->n_q) * a->h_q, a->d, st))
+      return dev_fail(fn, "preprocess");
+  }
   const bool full_range = a->q_off == 0 && a->n_q == P.N;
   if (a->dtype == TT_BF16 && mfma_bwd_supported(g, P)) {
-    if (launch_bwd_mfma(q, k, a->v, b->d_o, a->lse, D, dq, b->d_k, b->d_v, acc, P, g, full_range, st))
-      return dev_fail("tree_attn_bwd", "attention kernel launch");
+    {
+      KTimer t("attn_bwd_dq_mfma", st);
+      if (launch_dq_mfma(q, k, a->v, b->d_o, a->lse, D, dq, P, g, full_range, st)) return dev_fail(fn, "dq kernel");
+    }
+    {
+      KTimer t("attn_bwd_dkdv_mfma", st);
+      if (launch_dkdv_mfma(q, k, a->v, b->d_o, a->lse, D, b->d_k, b->d_v, acc, P, g, st))
+        return dev_fail(fn, "dk/dv kernel");
+    }
   } else {
-    if (launch_dq_generic(a->dtype, q, k, a->v, b->d_o, a->lse, D, dq, P, g, st))
-      return dev_fail("tree_attn_bwd", "dq kernel launch");
-    if (launch_dkdv_generic(a->dtype, acc, q, k, a->v, b->d_o, a->lse, D, b->d_k, b->d_v, P, g, st))
-      return dev_fail("tree_attn_bwd", "dk/dv kernel launch");
+    {
+      KTimer t("attn_bwd_dq_generic", st);
+      if (launch_dq_generic(a->dtype, q, k, a->v, b->d_o, a->lse, D, dq, P, g, st)) return dev_fail(fn, "dq kernel");
+    }
+    {
+      KTimer t("attn_bwd_dkdv_generic", st);
+      if (launch_dkdv_generic(a->dtype, acc, q, k, a->v, b->d_o, a->lse, D, b->d_k, b->d_v, P, g, st))
+        return dev_fail(fn, "dk/dv kernel");
+    }
   }
   // dQ: rotate back at the query rows' depths, convert to the output dtype
-  if (a->n_q > 0 && launch_rope(dq, b->d_q, TT_F32, a->dtype, false, P.depth, a->q_off, a->n_q, a->h_q, a->d,
-                                a->rope_base, true, st))
-    return dev_fail("tree_attn_bwd", "dq finalize");
+  if (a->n_q > 0) {
+    KTimer t("dq_finalize", st);
+    if (launch_rope(dq, b->d_q, TT_F32, a->dtype, false, P.depth, a->q_off, a->n_q, a->h_q, a->d, a->rope_base, true,
+                    st))
+      return dev_fail(fn, "dq finalize");
+  }
   return TT_OK;
 }
 
@@ -297,6 +410,7 @@ extern "C" int tree_weighted_nll(const tt_nll_args* a, tt_stream stream) {
   char* ws = static_cast<char*>(a->workspace);
   float* row_loss = reinterpret_cast<float*>(ws + w.row_loss);
   if (logits) {
+    KTimer t("nll_rows", st);
     if (launch_nll_rows(a->logits_dtype, a->logits, a->d_logits, a->n_rows, a->vocab, a->vocab, a->tgt_row_ptr,
                         a->tgt_id, a->tgt_w, a->n_tgt, a->logp, row_loss, st))
       return dev_fail(fn, "nll kernel launch");
@@ -304,17 +418,31 @@ extern "C" int tree_weighted_nll(const tt_nll_args* a, tt_stream stream) {
     uint16_t* z = reinterpret_cast<uint16_t*>(ws + w.z);
     const uint16_t* H = static_cast<const uint16_t*>(a->hidden);
     const uint16_t* W = static_cast<const uint16_t*>(a->w_vocab);
-    if (a->n_rows > 0 && launch_gemm_nn(H, W, z, a->n_rows, a->vocab, a->d_model, st))
-      return dev_fail(fn, "lm-head gemm");
-    if (launch_nll_rows(TT_BF16, z, z, a->n_rows, a->vocab, a->vocab, a->tgt_row_ptr, a->tgt_id, a->tgt_w, a->n_tgt,
-                        a->logp, row_loss, st))
-      return dev_fail(fn, "nll kernel launch");
-    if (a->d_hidden && a->n_rows > 0 &&
-        launch_gemm_nt(z, W, static_cast<uint16_t*>(a->d_hidden), a->n_rows, a->d_model, a->vocab, st))
-      return dev_fail(fn, "d_hidden gemm");
-    if (a->d_w_vocab && launch_gemm_tn(H, z, a->d_w_vocab, a->dw_dtype == TT_F32, a->d_model, a->vocab, a->n_rows, st))
-      return dev_fail(fn, "d_w_vocab gemm");
+    {
+      KTimer t("lmhead_z_gemm", st);
+      if (a->n_rows > 0 && launch_gemm_nn(H, W, z, a->n_rows, a->vocab, a->d_model, st))
+        return dev_fail(fn, "lm-head gemm");
+    }
+    {
+      KTimer t("nll_rows", st);
+      if (launch_nll_rows(TT_BF16, z, z, a->n_rows, a->vocab, a->vocab, a->tgt_row_ptr, a->tgt_id, a->tgt_w,
+                          a->n_tgt, a->logp, row_loss, st))
+        return dev_fail(fn, "nll kernel launch");
+    }
+    if (a->d_hidden && a->n_rows > 0) {
+      KTimer t("lmhead_dh_gemm", st);
+      if (launch_gemm_nt(z, W, static_cast<uint16_t*>(a->d_hidden), a->n_rows, a->d_model, a->vocab, st))
+        return dev_fail(fn, "d_hidden gemm");
+    }
+    if (a->d_w_vocab) {
+      KTimer t("lmhead_dw_gemm", st);
+      if (launch_gemm_tn(H, z, a->d_w_vocab, a->dw_dtype == TT_F32, a->d_model, a->vocab, a->n_rows, st))
+        return dev_fail(fn, "d_w_vocab gemm");
+    }
   }
-  if (launch_sum_loss(row_loss, a->n_rows, a->loss, st)) return dev_fail(fn, "loss reduction");
+  {
+    KTimer t("nll_sum", st);
+    if (launch_sum_loss(row_loss, a->n_rows, a->loss, st)) return dev_fail(fn, "loss reduction");
+  }
   return TT_OK;
 }

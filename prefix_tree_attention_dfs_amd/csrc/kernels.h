@@ -27,9 +27,10 @@ bool mfma_attn_supported(const AttnGeom& g, const PlanPtrs& P);
 bool mfma_bwd_supported(const AttnGeom& g, const PlanPtrs& P);
 int launch_fwd_mfma(const void* q, const void* k, const void* v, void* o, float* lse, const PlanPtrs& P,
                     const AttnGeom& g, bool full_range, hipStream_t st);
-int launch_bwd_mfma(const void* q, const void* k, const void* v, const void* d_o, const float* lse, const float* D,
-                    float* dq_acc, void* d_k, void* d_v, bool acc, const PlanPtrs& P, const AttnGeom& g,
-                    bool full_range, hipStream_t st);
+int launch_dq_mfma(const void* q, const void* k, const void* v, const void* d_o, const float* lse, const float* D,
+                   float* dq_acc, const PlanPtrs& P, const AttnGeom& g, bool full_range, hipStream_t st);
+int launch_dkdv_mfma(const void* q, const void* k, const void* v, const void* d_o, const float* lse, const float* D,
+                     void* d_k, void* d_v, bool acc, const PlanPtrs& P, const AttnGeom& g, hipStream_t st);
 
 // Weighted NLL.
 int launch_nll_rows(tt_dtype zt, const void* z, void* dz, int32_t n_rows, int32_t vocab, int64_t ldz,
