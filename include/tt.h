@@ -212,8 +212,11 @@ int tree_attn_bwd(const tt_attn_bwd_args* args, tt_stream stream);
  *   logits mode: z = logits [n_rows, vocab] (dtype logits_dtype); d_logits
  *                (same dtype and shape, may alias logits) receives dZ.
  *   fused mode:  z = hidden [n_rows, d_model] @ w_vocab [d_model, vocab], both
- *                bf16; d_hidden [n_rows, d_model] bf16 receives dZ w_vocab^T and
- *                d_w_vocab [d_model, vocab] (dtype dw_dtype) receives hidden^T dZ.
+ *                bf16, d_model and vocab multiples of 8; z and dZ live in the
+ *                workspace as bf16; d_hidden [n_rows, d_model] bf16 receives
+ *                dZ w_vocab^T and d_w_vocab [d_model, vocab] (dtype dw_dtype)
+ *                receives hidden^T dZ.
+ * vocab <= 262144 (TT_EUNSUPPORTED beyond).
  * Targets are a device CSR: tgt_row_ptr [n_rows+1], tgt_id [n_tgt] (0 <= id <
  * vocab), tgt_w [n_tgt].  loss is a device float32 scalar (overwritten); logp
  * [n_tgt] float32 or NULL; each gradient pointer may be NULL to skip it.

@@ -54,6 +54,7 @@ __global__ __launch_bounds__(FwdCfg<G>::THREADS) void fwd_mfma_kernel(
   const int pos0 = (wave % C::WPH) * 32 * NT;
   const int qrow0 = qb * BQ - g.q_off;  // q-buffer row of the block's first position
   const float c2 = g.scale * 1.4426950408889634f;
+  const float tau = 8.f / c2;  // 8 in log2 units, in raw score units
 
   // Q fragments (B operands): lane holds Q[row][dc*16 + 8hh .. +8]
   bf16x8 qf[NT][8];
@@ -85,13 +86,15 @@ __global__ __launch_bounds__(FwdCfg<G>::THREADS) void fwd_mfma_kernel(
       const int key = c >> 4, dch = c & 15;
       const int j = kb * BK + key;
       const bool ok = j < g.n_k;
-      const int64_t off = (int64_t(j) * g.h_kv + kvh) * D + dch * 8;
-      kreg[u] = ok ? ld16(k + off) : zero8();
-      vreg[u] = ok ? ld16(v + off) : zero8();
+      const int64_t off = (int64_t(ok ? j : g.n_k - 1) * g.h_kv + kvh) * D + dch * 8;
+      const bf16x8 kx = ld16(k + off), vx = ld16(v + off);
+      kreg[u] = ok ? kx : zero8();
+      vreg[u] = ok ? vx : zero8();
     }
     if (tid < BK) {
       const int j = kb * BK + tid;
-      ereg = j < g.n_k ? P.end[j] : -1;
+      const int ej = P.end[min(j, g.n_k - 1)];
+      ereg = j < g.n_k ? ej : -1;
     }
   };
   auto store_tile = [&](FwdStage& s) {
@@ -140,7 +143,7 @@ __global__ __launch_bounds__(FwdCfg<G>::THREADS) void fwd_mfma_kernel(
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int kl = kt * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
-            const bool vis = (kb * BK + kl <= qpos) && (qpos < S.end[kl]);
+            const bool vis = (kb * BK + kl <= qpos) & (qpos < S.end[kl]);
             sacc[nt][i] = vis ? sacc[nt][i] : -INFINITY;
           }
         }
@@ -152,8 +155,12 @@ __global__ __launch_bounds__(FwdCfg<G>::THREADS) void fwd_mfma_kernel(
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[nt][i]);
         mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const float mnew = fmaxf(m[nt], mx);
-        if (__any(mnew != m[nt])) {  // rescale only when some row's max grew
+        // The running max moves only when a row's tile max exceeds it by more
+        // than tau (2^8 in probability); until then p may reach 2^8, which the
+        // fp32 sums and the bf16 P operand carry without loss of relative precision.
+        const bool grow = mx > m[nt] + tau;
+        if (__any(grow)) {
+          const float mnew = grow ? mx : m[nt];
           const float alpha = (mnew == m[nt]) ? 1.f : exp2_fast((m[nt] - mnew) * c2);
           lpart[nt] *= alpha;
 #pragma unroll
@@ -205,7 +212,7 @@ __global__ __launch_bounds__(FwdCfg<G>::THREADS) void fwd_mfma_kernel(
         for (int e = 0; e < 4; ++e) w[e] = __bf16(oacc[nt][dt][4 * i4 + e] * inv);
         *reinterpret_cast<bf16x4*>(orow + dt * 32 + 8 * i4 + 4 * hh) = w;
       }
-    if (hh == 0) lse[int64_t(row) * g.h_q + head] = m[nt] * g.scale + logf(lt);
+    if (hh == 0) lse[int64_t(row) * g.h_q + head] = m[nt] * g.scale + logf(lt);  // ln sum exp(scale (s - m)) + scale m
   }
 }
 

@@ -37,8 +37,8 @@ struct DqCfg {
 };
 
 struct __align__(16) DqStage {
-  uint16_t K[BK * KSTR];
-  uint16_t V[BK * KSTR];
+  uint16_t K[BK * D];     // swizzled: row reads (S^T) and transposed reads (dQ^T)
+  uint16_t V[BK * KSTR];  // padded: row reads only (dP^T)
   int32_t end[BK];
 };
 
@@ -83,13 +83,15 @@ __global__ __launch_bounds__(DqCfg<G>::THREADS) void dq_mfma_kernel(
       const int key = c >> 4, dch = c & 15;
       const int j = kb * BK + key;
       const bool ok = j < g.n_k;
-      const int64_t off = (int64_t(j) * g.h_kv + kvh) * D + dch * 8;
-      kreg[u] = ok ? ld16(k + off) : zero8();
-      vreg[u] = ok ? ld16(v + off) : zero8();
+      const int64_t off = (int64_t(ok ? j : g.n_k - 1) * g.h_kv + kvh) * D + dch * 8;
+      const bf16x8 kx = ld16(k + off), vx = ld16(v + off);
+      kreg[u] = ok ? kx : zero8();
+      vreg[u] = ok ? vx : zero8();
     }
     if (tid < BK) {
       const int j = kb * BK + tid;
-      ereg = j < g.n_k ? P.end[j] : -1;
+      const int ej = P.end[min(j, g.n_k - 1)];
+      ereg = j < g.n_k ? ej : -1;
     }
   };
   auto store_tile = [&](DqStage& s) {
@@ -97,7 +99,7 @@ __global__ __launch_bounds__(DqCfg<G>::THREADS) void dq_mfma_kernel(
     for (int u = 0; u < C::CH; ++u) {
       const int c = tid + u * C::THREADS;
       const int key = c >> 4, dch = c & 15;
-      *reinterpret_cast<bf16x8*>(&s.K[key * KSTR + dch * 8]) = kreg[u];
+      *reinterpret_cast<bf16x8*>(&s.K[soff(key, dch * 8)]) = kreg[u];
       *reinterpret_cast<bf16x8*>(&s.V[key * KSTR + dch * 8]) = vreg[u];
     }
     if (tid < BK) s.end[tid] = ereg;
@@ -121,23 +123,28 @@ __global__ __launch_bounds__(DqCfg<G>::THREADS) void dq_mfma_kernel(
       f32x16 s = zero16(), dp = zero16();
 #pragma unroll
       for (int dc = 0; dc < 8; ++dc) {
-        const bf16x8 a = lds_read16(&S.K[(kt * 32 + r) * KSTR + dc * 16 + 8 * hh]);
+        const bf16x8 a = lds_read16(&S.K[soff(kt * 32 + r, dc * 16 + 8 * hh)]);
         s = mfma(a, qf[dc], s);
         const bf16x8 b = lds_read16(&S.V[(kt * 32 + r) * KSTR + dc * 16 + 8 * hh]);
         dp = mfma(b, of[dc], dp);
       }
+      if (full) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int kl = kt * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
-        const bool vis = full || ((kb * BK + kl <= qpos) && (qpos < S.end[kl]));
-        const float p = vis ? exp2_fast(s[i] * c2 - lse2) : 0.f;
-        s[i] = p * (dp[i] - Dq);
+        for (int i = 0; i < 16; ++i) s[i] = exp2_fast(s[i] * c2 - lse2) * (dp[i] - Dq);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int kl = kt * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
+          const bool vis = (kb * BK + kl <= qpos) & (qpos < S.end[kl]);
+          const float p = exp2_fast(s[i] * c2 - lse2);
+          s[i] = vis ? p * (dp[i] - Dq) : 0.f;
+        }
       }
       const bf16x8 d0 = c_to_b(s, 0), d1 = c_to_b(s, 1);
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
-        acc[dt] = mfma(tr_frag(S.K, KSTR, kt * 32, dt * 32, lane), d0, acc[dt]);
-        acc[dt] = mfma(tr_frag(S.K, KSTR, kt * 32 + 16, dt * 32, lane), d1, acc[dt]);
+        acc[dt] = mfma(tr_frag_swz(S.K, kt * 32, dt * 32, lane), d0, acc[dt]);
+        acc[dt] = mfma(tr_frag_swz(S.K, kt * 32 + 16, dt * 32, lane), d1, acc[dt]);
       }
     }
     if (e + 1 < e1) store_tile(st[sidx ^ 1]);
@@ -164,8 +171,8 @@ constexpr int QT = 64;                             // query rows per staged tile
 constexpr int QCH = (QT * D / 8) / KV_THREADS;     // 16-byte chunks per thread per Q (or dO) tile
 
 struct __align__(16) KvStage {
-  uint16_t Q[QT * KSTR];
-  uint16_t O[QT * KSTR];  // dO
+  uint16_t Q[QT * D];  // swizzled (row reads for S, transposed reads for dK^T)
+  uint16_t O[QT * D];  // dO, swizzled (row reads for dP, transposed reads for dV^T)
   float lse2[QT];
   float Dv[QT];
 };
@@ -235,15 +242,18 @@ __global__ __launch_bounds__(KV_THREADS) void dkdv_mfma_kernel(
       const int rr = c >> 4, dch = c & 15;
       const int row = qt * QT + rr - g.q_off;  // q-buffer row
       const bool ok = row >= 0 && row < g.n_q;
-      const int64_t off = (int64_t(row) * g.h_q + head) * D + dch * 8;
-      qreg[u] = ok ? ld16(q + off) : zero8();
-      oreg[u] = ok ? ld16(d_o + off) : zero8();
+      const int64_t off = (int64_t(min(max(row, 0), g.n_q - 1)) * g.h_q + head) * D + dch * 8;
+      const bf16x8 qx = ld16(q + off), ox = ld16(d_o + off);
+      qreg[u] = ok ? qx : zero8();
+      oreg[u] = ok ? ox : zero8();
     }
     if (tid < QT) {
       const int row = qt * QT + tid - g.q_off;
       const bool ok = row >= 0 && row < g.n_q;
-      lreg = ok ? lse[int64_t(row) * g.h_q + head] * kLog2e : 0.f;
-      dreg = ok ? Dv[int64_t(row) * g.h_q + head] : 0.f;
+      const int64_t o1 = int64_t(min(max(row, 0), g.n_q - 1)) * g.h_q + head;
+      const float lx = lse[o1] * kLog2e, dx = Dv[o1];
+      lreg = ok ? lx : 0.f;
+      dreg = ok ? dx : 0.f;
     }
   };
   auto store_tile = [&](KvStage& s) {
@@ -251,8 +261,8 @@ __global__ __launch_bounds__(KV_THREADS) void dkdv_mfma_kernel(
     for (int u = 0; u < QCH; ++u) {
       const int c = tid + u * KV_THREADS;
       const int rr = c >> 4, dch = c & 15;
-      *reinterpret_cast<bf16x8*>(&s.Q[rr * KSTR + dch * 8]) = qreg[u];
-      *reinterpret_cast<bf16x8*>(&s.O[rr * KSTR + dch * 8]) = oreg[u];
+      *reinterpret_cast<bf16x8*>(&s.Q[soff(rr, dch * 8)]) = qreg[u];
+      *reinterpret_cast<bf16x8*>(&s.O[soff(rr, dch * 8)]) = oreg[u];
     }
     if (tid < QT) {
       s.lse2[tid] = lreg;
@@ -278,9 +288,9 @@ __global__ __launch_bounds__(KV_THREADS) void dkdv_mfma_kernel(
       f32x16 s = zero16(), dp = zero16();
 #pragma unroll
       for (int dc = 0; dc < 8; ++dc) {
-        const bf16x8 a = lds_read16(&S.Q[(mt * 32 + r) * KSTR + dc * 16 + 8 * hh]);
+        const bf16x8 a = lds_read16(&S.Q[soff(mt * 32 + r, dc * 16 + 8 * hh)]);
         s = mfma(a, kf[dc], s);
-        const bf16x8 b = lds_read16(&S.O[(mt * 32 + r) * KSTR + dc * 16 + 8 * hh]);
+        const bf16x8 b = lds_read16(&S.O[soff(mt * 32 + r, dc * 16 + 8 * hh)]);
         dp = mfma(b, vf[dc], dp);
       }
       f32x16 ds;
@@ -289,24 +299,34 @@ __global__ __launch_bounds__(KV_THREADS) void dkdv_mfma_kernel(
         const int ql = mt * 32 + 8 * i4 + 4 * hh;
         const f32x4 l4 = *reinterpret_cast<const f32x4*>(&S.lse2[ql]);
         const f32x4 d4 = *reinterpret_cast<const f32x4*>(&S.Dv[ql]);
+        if (full) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = 4 * i4 + e;
-          const int qq = qt * QT + ql + e;
-          const bool vis = full || (j <= qq && qq < endj && qq >= lo && qq < hi);
-          const float p = vis ? exp2_fast(s[i] * c2 - l4[e]) : 0.f;
-          s[i] = p;
-          ds[i] = p * (dp[i] - d4[e]);
+          for (int e = 0; e < 4; ++e) {
+            const int i = 4 * i4 + e;
+            const float p = exp2_fast(s[i] * c2 - l4[e]);
+            s[i] = p;
+            ds[i] = p * (dp[i] - d4[e]);
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int i = 4 * i4 + e;
+            const int qq = qt * QT + ql + e;
+            const bool vis = (j <= qq) & (qq < endj) & (qq >= lo) & (qq < hi);
+            const float p = vis ? exp2_fast(s[i] * c2 - l4[e]) : 0.f;
+            s[i] = p;
+            ds[i] = p * (dp[i] - d4[e]);
+          }
         }
       }
       const bf16x8 p0 = c_to_b(s, 0), p1 = c_to_b(s, 1);
       const bf16x8 s0 = c_to_b(ds, 0), s1 = c_to_b(ds, 1);
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
-        dv[dt] = mfma(tr_frag(S.O, KSTR, mt * 32, dt * 32, lane), p0, dv[dt]);
-        dv[dt] = mfma(tr_frag(S.O, KSTR, mt * 32 + 16, dt * 32, lane), p1, dv[dt]);
-        dk[dt] = mfma(tr_frag(S.Q, KSTR, mt * 32, dt * 32, lane), s0, dk[dt]);
-        dk[dt] = mfma(tr_frag(S.Q, KSTR, mt * 32 + 16, dt * 32, lane), s1, dk[dt]);
+        dv[dt] = mfma(tr_frag_swz(S.O, mt * 32, dt * 32, lane), p0, dv[dt]);
+        dv[dt] = mfma(tr_frag_swz(S.O, mt * 32 + 16, dt * 32, lane), p1, dv[dt]);
+        dk[dt] = mfma(tr_frag_swz(S.Q, mt * 32, dt * 32, lane), s0, dk[dt]);
+        dk[dt] = mfma(tr_frag_swz(S.Q, mt * 32 + 16, dt * 32, lane), s1, dk[dt]);
       }
     }
     if (step + 1 < n_steps) store_tile(st[sidx ^ 1]);

@@ -387,6 +387,8 @@ extern "C" int tree_weighted_nll(const tt_nll_args* a, tt_stream stream) {
   if (a->n_rows < 0 || a->vocab <= 0 || a->n_tgt < 0) return tt::fail(TT_EINVAL, "tree_weighted_nll: bad sizes");
   if (fused && a->d_model <= 0) return tt::fail(TT_EINVAL, "tree_weighted_nll: bad d_model");
   if (a->vocab > (1 << 18)) return tt::fail(TT_EUNSUPPORTED, "tree_weighted_nll: vocab > 262144");
+  if (fused && (a->vocab % 8 != 0 || a->d_model % 8 != 0))
+    return tt::fail(TT_EUNSUPPORTED, "tree_weighted_nll: fused mode needs vocab and d_model multiples of 8");
   if (logits && a->logits_dtype != TT_F32 && a->logits_dtype != TT_BF16)
     return tt::fail(TT_EINVAL, "tree_weighted_nll: bad logits dtype");
   if (fused && a->d_w_vocab && a->dw_dtype != TT_F32 && a->dw_dtype != TT_BF16)

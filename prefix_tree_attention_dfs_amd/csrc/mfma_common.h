@@ -79,6 +79,35 @@ __device__ __forceinline__ bf16x8 tr_frag(const uint16_t* tile, int stride, int 
   return a;
 }
 
+// Swizzled 128-column tiles (256-byte rows, no padding): 16-byte chunk c of
+// row k lives at chunk c ^ swz(k).  swz is a bijection on 0..15 whose bits 1-2
+// follow k % 4, so that
+//   * a 16-byte row read by 16 consecutive rows hits 16 distinct chunks, and
+//   * a transposed read (4 consecutive rows x 2 adjacent chunks per 16-lane
+//     group) hits 8 distinct chunks,
+// i.e. both access patterns of the backward kernels are free of bank conflicts.
+__device__ __forceinline__ int swz(int k) { return ((k & 3) << 1) | ((k >> 2) & 1) | (k & 8); }
+__device__ __forceinline__ int soff(int row, int col) {
+  return row * D + ((((col >> 3) ^ swz(row))) << 3) + (col & 7);
+}
+
+// tr_frag on a swizzled tile
+__device__ __forceinline__ bf16x8 tr_frag_swz(const uint16_t* tile, int row0, int col0, int lane) {
+  const int g = lane >> 4, rr = lane & 15;
+  const int h = g >> 1, half = g & 1;
+  const int row = row0 + 4 * h + (rr >> 2);
+  const int col = col0 + 16 * half + 4 * (rr & 3);
+  const bf16x4 lo = lds_tr4(tile + soff(row, col));
+  const bf16x4 hi = lds_tr4(tile + soff(row + 8, col));
+  bf16x8 a;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    a[e] = lo[e];
+    a[4 + e] = hi[e];
+  }
+  return a;
+}
+
 // Register block c (regs 8c..8c+7) of a C tile as a bf16 B operand.
 __device__ __forceinline__ bf16x8 c_to_b(const f32x16& x, int c) {
   bf16x8 b;

@@ -241,4 +241,6 @@ def test_nll_argument_errors():
     assert nll(d_hidden=FAKE) == tt.TT_EINVAL                             # needs fused mode
     assert nll(loss=FAKE + 4) == tt.TT_EINVAL                             # misaligned
     assert nll(workspace_bytes=8) == tt.TT_EWORKSPACE
-    assert nll(logits=0, hidden=FAKE, w_vocab=FAKE, d_model=8, d_logits=FAKE) == tt.TT_EINVAL
+    assert nll(logits=0, hidden=FAKE, w_vocab=FAKE, d_model=8, vocab=104, d_logits=FAKE) == tt.TT_EINVAL
+    assert nll(logits=0, hidden=FAKE, w_vocab=FAKE, d_model=8, vocab=100) == tt.TT_EUNSUPPORTED  # vocab % 8
+    assert nll(logits=0, hidden=FAKE, w_vocab=FAKE, d_model=12, vocab=104) == tt.TT_EUNSUPPORTED  # d_model % 8
