@@ -31,7 +31,8 @@ METRIC = "tree attn fwd+bwd unique tokens/s + useful TFLOP/s (% bf16 MFMA peak),
 # HBM traffic of the roofline kernel from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE
 # runs (scaled by the same counters' reading for a plain copy of known size),
 # valid only for the kernel source it was measured on.
-MEASURED_TRAFFIC = None  # {"kernel": ..., "source_sha1": ..., "bytes_per_launch": ...}
+MEASURED_TRAFFIC = {"kernel": "attn_bwd_dkdv_mfma", "source_sha1": "19947779c6d6342a6c45304610f5ed6ebb118605",
+                    "bytes_per_launch": 35007894732}
 
 
 def _source_sha(path):
@@ -143,7 +144,57 @@ def secondary(tt, ts, steps):
                                      pct_bf16_peak=round(fl / ms / 1e9 / PEAK_BF16_TFLOPS * 100, 2))
     del steps_c, q, k, v, do, dk, dv
     torch.cuda.empty_cache()
+    out["lmhead_weighted_nll"] = lmhead_bench(tt, ts, steps)
     return out
+
+
+def lmhead_bench(tt, ts, steps):
+    """Fused lm-head + weighted NLL: 16384 tree tokens x 4096 -> 151936 vocabulary,
+    32-leaf tree (compression about 5.5); loss, dH and dW (fp32)."""
+    import numpy as np
+    import torch
+    case = ts.lmhead_tree(0)
+    tree = tt.Tree(case.seqs)
+    a = tree.export()
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()  # noqa: E731
+    rp, tid, tw = dev(a["tgt_row_ptr"]), dev(a["tgt_token"]), dev(a["tgt_w"])
+    N, dm, V = tree.N, 4096, 151936
+    g = torch.Generator(device="cuda").manual_seed(21)
+    H = _bf16(torch.randn(N, dm, device="cuda", generator=g))
+    W = _bf16(torch.randn(dm, V, device="cuda", generator=g) * 0.02)
+    ws = None
+    out = tt.tree_weighted_nll(rp, tid, tw, hidden=H, w_vocab=W)
+    dh, dw = out["d_hidden"], out["d_w_vocab"]
+
+    def call():
+        nonlocal ws
+        o = tt.tree_weighted_nll(rp, tid, tw, hidden=H, w_vocab=W, workspace=ws)
+        return o
+
+    # keep one workspace alive across calls
+    import ctypes  # noqa: F401
+    nb = tt.NllArgs(n_rows=N, d_model=dm, vocab=V, n_tgt=int(tid.numel()), hidden=1, w_vocab=1)
+    n = ctypes.c_size_t()
+    tt.lib().tree_nll_workspace_bytes(ctypes.byref(nb), ctypes.byref(n))
+    ws = torch.empty(n.value, dtype=torch.uint8, device="cuda")
+    del dh, dw, out
+    call()
+    torch.cuda.synchronize()
+    tt.timing_enable(True)
+    ms = _time(call, max(2, steps // 3), 0)
+    tt.timing_enable(False)
+    kt = tt.timing_collect()
+    fl = 6 * N * dm * V
+    red = kt.get("nll_rows", (1, 0.0, 0.0))
+    red_ms = red[1] / max(1, red[0])
+    zbytes = 2 * N * V * 2  # read Z once, write dZ once (bf16)
+    res = dict(rows=N, d_model=dm, vocab=V, compression=round(case.seq_tokens / N, 3), ms=round(ms, 3),
+               useful_tflops=round(fl / ms / 1e9, 1), pct_bf16_peak=round(fl / ms / 1e9 / PEAK_BF16_TFLOPS * 100, 2),
+               nll_reduce_ms=round(red_ms, 3), nll_reduce_gbs=round(zbytes / red_ms / 1e6, 1),
+               kernels={k_: {"launches": c, "avg_ms": round(t / c, 3)} for k_, (c, t, _) in kt.items()})
+    del H, W, ws
+    torch.cuda.empty_cache()
+    return res
 
 
 def per_branch_dense(tt, ts, tree, case, q, k, v, do, steps):
@@ -229,7 +280,19 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-dense", action="store_true", help="skip the per-branch dense comparison")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy 5 times (counter calibration)")
     args = ap.parse_args()
+    if args.copy_calibration:
+        import torch
+        x = torch.ones(1 << 29, dtype=torch.int16, device="cuda")
+        y = torch.empty_like(x)
+        for _ in range(5):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": x.numel() * 2, "launches": 5}), flush=True)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 (the multi-GPU dispatcher "
                                    "is design-only)"}), flush=True)
@@ -308,9 +371,10 @@ def main():
         "roofline": roofline, "kernels": kernels,
         "tree_build_ms": round(build_ms, 2), "tree_gen_s": round(gen_s, 2),
     }
-    dense = per_branch_dense(tt, ts, tree, case, q, k, v, do, args.steps)
-    dense["tree_speedup"] = round(dense["ms"] / ms, 3)
-    result["per_branch_dense"] = dense
+    if not args.no_dense:
+        dense = per_branch_dense(tt, ts, tree, case, q, k, v, do, args.steps)
+        dense["tree_speedup"] = round(dense["ms"] / ms, 3)
+        result["per_branch_dense"] = dense
     del st
     torch.cuda.empty_cache()
     if not args.no_secondary:
