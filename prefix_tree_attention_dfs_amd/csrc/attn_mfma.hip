@@ -24,7 +24,7 @@ namespace {
 
 template <int G>
 struct FwdCfg {
-  static constexpr int NT = G >= 4 ? 2 : 1;             // 32-row query sub-tiles per wave
+  static constexpr int NT = 1;                          // 32-row query sub-tiles per wave
   static constexpr int WAVES = (G * BQ) / (32 * NT);     // waves per workgroup
   static constexpr int THREADS = WAVES * 64;
   static constexpr int CH = (BK * D / 8) / THREADS;      // 16-byte chunks per thread per K (or V) tile
@@ -123,19 +123,24 @@ __global__ __launch_bounds__(FwdCfg<G>::THREADS) void fwd_mfma_kernel(
     if (e + 1 < e1) load_tile(P.qb_tiles[e + 1] & kKbMask);
     const FwdStage& S = st[sidx];
 
-    // Each 32-key half of the tile in turn: S^T = K Q^T, mask, online
-    // softmax (rows = lanes), O^T += V^T P^T.
+    // S^T = K Q^T for both 32-key halves first, then for each half: mask,
+    // online softmax (rows = lanes), O^T += V^T P^T -- the second half's
+    // products run on the matrix pipe while the first half's softmax runs.
+    f32x16 sv[2][NT];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
-      f32x16 sacc[NT];
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) sacc[nt] = zero16();
+      for (int nt = 0; nt < NT; ++nt) sv[kt][nt] = zero16();
 #pragma unroll
       for (int dc = 0; dc < 8; ++dc) {
         const bf16x8 a = lds_read16(&S.K[(kt * 32 + r) * KSTR + dc * 16 + 8 * hh]);
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) sacc[nt] = mfma(a, qf[nt][dc], sacc[nt]);
+        for (int nt = 0; nt < NT; ++nt) sv[kt][nt] = mfma(a, qf[nt][dc], sv[kt][nt]);
       }
+    }
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      f32x16(&sacc)[NT] = sv[kt];
       if (!full) {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {

@@ -164,11 +164,17 @@ __global__ __launch_bounds__(DqCfg<G>::THREADS) void dq_mfma_kernel(
 }
 
 // ------------------------------------------------------------------ dK, dV
-constexpr int KV_WAVES = 4;
+// One workgroup per 128 keys x kv head, 8 waves (two per SIMD).  K and V of
+// the 128 keys stay in LDS for the whole kernel; query tiles of 64 rows (Q,
+// dO, LSE, D of one head) stream through a double-buffered stage.  Wave w
+// owns keys 32*(w%4) .. +32 and the query half w/4 of every staged tile; the
+// two waves that share keys add their partial dK, dV through LDS at the end.
+constexpr int KV_WAVES = 8;
 constexpr int KV_THREADS = KV_WAVES * 64;
-constexpr int KV_KEYS = 32 * KV_WAVES;            // keys per workgroup
+constexpr int KV_KEYS = 128;                       // keys per workgroup
 constexpr int QT = 64;                             // query rows per staged tile
 constexpr int QCH = (QT * D / 8) / KV_THREADS;     // 16-byte chunks per thread per Q (or dO) tile
+constexpr int KCH = (KV_KEYS * D / 8) / KV_THREADS;
 
 struct __align__(16) KvStage {
   uint16_t Q[QT * D];  // swizzled (row reads for S, transposed reads for dK^T)
@@ -177,27 +183,45 @@ struct __align__(16) KvStage {
   float Dv[QT];
 };
 
+struct __align__(16) KvLds {
+  union {
+    struct {
+      uint16_t K[KV_KEYS * KSTR];  // padded: row reads only
+      uint16_t V[KV_KEYS * KSTR];
+      KvStage st[2];
+    } run;
+    float part[4][8][16][64];  // epilogue: partial dK^T, dV^T of the upper query halves
+  };
+  int32_t red[2][KV_WAVES];
+};
+
 template <int G, bool ACC, typename TG>
-__global__ __launch_bounds__(KV_THREADS) void dkdv_mfma_kernel(
+__global__ __launch_bounds__(KV_THREADS, 2) void dkdv_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ d_o, const float* __restrict__ lse, const float* __restrict__ Dv,
     TG* __restrict__ d_k, TG* __restrict__ d_v, PlanPtrs P, AttnGeom g) {
-  __shared__ KvStage st[2];
-  __shared__ int32_t red[2][KV_WAVES];
+  __shared__ KvLds L;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r = lane & 31, hh = lane >> 5;
+  const int ks = wave & 3;  // key sub-tile
+  const int mt = wave >> 2; // query half of each staged tile
   const int kvh = blockIdx.x % g.h_kv;
   const int kb2 = blockIdx.x / g.h_kv;
   const int kbase = kb2 * KV_KEYS;
-  const int j = kbase + wave * 32 + r;  // this lane's key (lane column of S, dP, dK^T, dV^T)
+  const int j = kbase + ks * 32 + r;  // this lane's key (lane column of S, dP, dK^T, dV^T)
   const bool jok = j < g.n_k;
   const float c2 = g.scale * kLog2e;
 
-  bf16x8 kf[8], vf[8];
+  // K, V of the workgroup's keys -> LDS (rows past n_k are zero)
 #pragma unroll
-  for (int dc = 0; dc < 8; ++dc) {
-    const int64_t off = (int64_t(j) * g.h_kv + kvh) * D + dc * 16 + 8 * hh;
-    kf[dc] = jok ? ld16(k + off) : zero8();
-    vf[dc] = jok ? ld16(v + off) : zero8();
+  for (int u = 0; u < KCH; ++u) {
+    const int c = tid + u * KV_THREADS;
+    const int key = c >> 4, dch = c & 15;
+    const int jj = kbase + key;
+    const bool ok = jj < g.n_k;
+    const int64_t off = (int64_t(ok ? jj : g.n_k - 1) * g.h_kv + kvh) * D + dch * 8;
+    const bf16x8 kx = ld16(k + off), vx = ld16(v + off);
+    *reinterpret_cast<bf16x8*>(&L.run.K[key * KSTR + dch * 8]) = ok ? kx : zero8();
+    *reinterpret_cast<bf16x8*>(&L.run.V[key * KSTR + dch * 8]) = ok ? vx : zero8();
   }
   const int endj = jok ? P.end[j] : -1;
 
@@ -209,17 +233,17 @@ __global__ __launch_bounds__(KV_THREADS) void dkdv_mfma_kernel(
     mn = min(mn, __shfl_xor(mn, o, 64));
   }
   if (lane == 0) {
-    red[0][wave] = mx;
-    red[1][wave] = mn;
+    L.red[0][wave] = mx;
+    L.red[1][wave] = mn;
   }
   __syncthreads();
   int hi = 0;
 #pragma unroll
-  for (int w = 0; w < KV_WAVES; ++w) hi = max(hi, red[0][w]);
-  const int wave_min_end = red[1][wave];
+  for (int w = 0; w < 4; ++w) hi = max(hi, L.red[0][w]);
+  const int wave_min_end = L.red[1][ks];
   const int lo = max(kbase, g.q_off);
   hi = min(hi, g.q_off + g.n_q);
-  const int wave_kmax = kbase + wave * 32 + 31;
+  const int wave_kmax = kbase + ks * 32 + 31;
 
   f32x16 dk[4], dv[4];
 #pragma unroll
@@ -272,67 +296,83 @@ __global__ __launch_bounds__(KV_THREADS) void dkdv_mfma_kernel(
 
   if (n_steps > 0) {
     load_tile(0);
-    store_tile(st[0]);
+    store_tile(L.run.st[0]);
   }
   __syncthreads();
+  const uint16_t* Kt = L.run.K + (ks * 32 + r) * KSTR + 8 * hh;
+  const uint16_t* Vt = L.run.V + (ks * 32 + r) * KSTR + 8 * hh;
   for (int step = 0; step < n_steps; ++step) {
     const int sidx = step & 1;
     const int qt = qt_first + step / G;
     if (step + 1 < n_steps) load_tile(step + 1);
-    const KvStage& S = st[sidx];
+    const KvStage& S = L.run.st[sidx];
+    const int q0 = qt * QT + mt * 32;  // tree row of this wave's first query
+    // every (query, key) pair of this wave's 32 x 32 block visible and in range?
+    const bool full = wave_kmax <= q0 && wave_min_end > q0 + 31 && q0 >= lo && q0 + 31 < hi;
+    f32x16 s = zero16(), dp = zero16();
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      const int q0 = qt * QT + mt * 32;  // tree row of the sub-tile's first query
-      // every (query, key) pair of this wave's 32 x 32 block visible and in range?
-      const bool full = wave_kmax <= q0 && wave_min_end > q0 + 31 && q0 >= lo && q0 + 31 < hi;
-      f32x16 s = zero16(), dp = zero16();
+    for (int dc = 0; dc < 8; ++dc) {
+      s = mfma(lds_read16(&S.Q[soff(mt * 32 + r, dc * 16 + 8 * hh)]), lds_read16(Kt + dc * 16), s);
+      dp = mfma(lds_read16(&S.O[soff(mt * 32 + r, dc * 16 + 8 * hh)]), lds_read16(Vt + dc * 16), dp);
+    }
+    f32x16 ds;
 #pragma unroll
-      for (int dc = 0; dc < 8; ++dc) {
-        const bf16x8 a = lds_read16(&S.Q[soff(mt * 32 + r, dc * 16 + 8 * hh)]);
-        s = mfma(a, kf[dc], s);
-        const bf16x8 b = lds_read16(&S.O[soff(mt * 32 + r, dc * 16 + 8 * hh)]);
-        dp = mfma(b, vf[dc], dp);
-      }
-      f32x16 ds;
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const int ql = mt * 32 + 8 * i4 + 4 * hh;
+      const f32x4 l4 = *reinterpret_cast<const f32x4*>(&S.lse2[ql]);
+      const f32x4 d4 = *reinterpret_cast<const f32x4*>(&S.Dv[ql]);
+      if (full) {
 #pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const int ql = mt * 32 + 8 * i4 + 4 * hh;
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&S.lse2[ql]);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&S.Dv[ql]);
-        if (full) {
+        for (int e = 0; e < 4; ++e) {
+          const int i = 4 * i4 + e;
+          const float p = exp2_fast(s[i] * c2 - l4[e]);
+          s[i] = p;
+          ds[i] = p * (dp[i] - d4[e]);
+        }
+      } else {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int i = 4 * i4 + e;
-            const float p = exp2_fast(s[i] * c2 - l4[e]);
-            s[i] = p;
-            ds[i] = p * (dp[i] - d4[e]);
-          }
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int i = 4 * i4 + e;
-            const int qq = qt * QT + ql + e;
-            const bool vis = (j <= qq) & (qq < endj) & (qq >= lo) & (qq < hi);
-            const float p = vis ? exp2_fast(s[i] * c2 - l4[e]) : 0.f;
-            s[i] = p;
-            ds[i] = p * (dp[i] - d4[e]);
-          }
+        for (int e = 0; e < 4; ++e) {
+          const int i = 4 * i4 + e;
+          const int qq = qt * QT + ql + e;
+          const bool vis = (j <= qq) & (qq < endj) & (qq >= lo) & (qq < hi);
+          const float p = vis ? exp2_fast(s[i] * c2 - l4[e]) : 0.f;
+          s[i] = p;
+          ds[i] = p * (dp[i] - d4[e]);
         }
       }
-      const bf16x8 p0 = c_to_b(s, 0), p1 = c_to_b(s, 1);
-      const bf16x8 s0 = c_to_b(ds, 0), s1 = c_to_b(ds, 1);
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        dv[dt] = mfma(tr_frag_swz(S.O, mt * 32, dt * 32, lane), p0, dv[dt]);
-        dv[dt] = mfma(tr_frag_swz(S.O, mt * 32 + 16, dt * 32, lane), p1, dv[dt]);
-        dk[dt] = mfma(tr_frag_swz(S.Q, mt * 32, dt * 32, lane), s0, dk[dt]);
-        dk[dt] = mfma(tr_frag_swz(S.Q, mt * 32 + 16, dt * 32, lane), s1, dk[dt]);
-      }
     }
-    if (step + 1 < n_steps) store_tile(st[sidx ^ 1]);
+    const bf16x8 p0 = c_to_b(s, 0), p1 = c_to_b(s, 1);
+    const bf16x8 s0 = c_to_b(ds, 0), s1 = c_to_b(ds, 1);
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      dv[dt] = mfma(tr_frag_swz(S.O, mt * 32, dt * 32, lane), p0, dv[dt]);
+      dv[dt] = mfma(tr_frag_swz(S.O, mt * 32 + 16, dt * 32, lane), p1, dv[dt]);
+      dk[dt] = mfma(tr_frag_swz(S.Q, mt * 32, dt * 32, lane), s0, dk[dt]);
+      dk[dt] = mfma(tr_frag_swz(S.Q, mt * 32 + 16, dt * 32, lane), s1, dk[dt]);
+    }
+    if (step + 1 < n_steps) store_tile(L.run.st[sidx ^ 1]);
     __syncthreads();
   }
-  if (!jok) return;
+
+  // sum the two query halves: the upper half's waves hand their partials over LDS
+  if (mt == 1) {
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        L.part[ks][dt][i][lane] = dk[dt][i];
+        L.part[ks][4 + dt][i][lane] = dv[dt][i];
+      }
+  }
+  __syncthreads();
+  if (mt == 1 || !jok) return;
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      dk[dt][i] += L.part[ks][dt][i][lane];
+      dv[dt][i] += L.part[ks][4 + dt][i][lane];
+    }
 
   // dK = R^T (scale * dK') at the key's depth; coordinates (c, c+64) are the
   // same register of blocks dt and dt+2.
