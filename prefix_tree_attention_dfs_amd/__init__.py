@@ -15,7 +15,8 @@ import os
 import numpy as np
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libtreeattn.so")
+# TT_LIB_PATH selects another build of the same library (e.g. an instrumented one)
+LIB_PATH = os.environ.get("TT_LIB_PATH") or os.path.join(_PKG, "libtreeattn.so")
 
 TT_OK, TT_EINVAL, TT_ENOMEM, TT_EWORKSPACE, TT_EUNSUPPORTED, TT_EDEVICE, TT_EOVERFLOW = 0, -1, -2, -3, -4, -5, -6
 TT_F32, TT_BF16 = 0, 1

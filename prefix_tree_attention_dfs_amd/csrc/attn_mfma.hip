@@ -76,26 +76,27 @@ __global__ __launch_bounds__(FwdCfg<G>::THREADS) void fwd_mfma_kernel(
     for (int dt = 0; dt < 4; ++dt) oacc[nt][dt] = zero16();
   }
 
-  // tile staging
+  // tile staging: buffer loads, zero past n_k keys (end = 0 there: invisible)
+  const uint32_t kv_bytes = uint32_t(g.n_k) * uint32_t(g.h_kv) * D * 2;
+  const rsrc_t rk = make_rsrc(k, kv_bytes), rv = make_rsrc(v, kv_bytes);
+  const rsrc_t re = make_rsrc(P.end, uint32_t(g.n_k) * 4);
+  const uint32_t tile_bytes = uint32_t(BK) * g.h_kv * D * 2;  // one 64-key tile of K (or V)
+  uint32_t voff[C::CH];
+#pragma unroll
+  for (int u = 0; u < C::CH; ++u) {
+    const int c = tid + u * C::THREADS;
+    voff[u] = (uint32_t((c >> 4) * g.h_kv + kvh) * D + (c & 15) * 8) * 2;
+  }
   bf16x8 kreg[C::CH], vreg[C::CH];
-  int32_t ereg = -1;
+  int32_t ereg = 0;
   auto load_tile = [&](int kb) {
+    const uint32_t so = uint32_t(kb) * tile_bytes;
 #pragma unroll
     for (int u = 0; u < C::CH; ++u) {
-      const int c = tid + u * C::THREADS;
-      const int key = c >> 4, dch = c & 15;
-      const int j = kb * BK + key;
-      const bool ok = j < g.n_k;
-      const int64_t off = (int64_t(ok ? j : g.n_k - 1) * g.h_kv + kvh) * D + dch * 8;
-      const bf16x8 kx = ld16(k + off), vx = ld16(v + off);
-      kreg[u] = ok ? kx : zero8();
-      vreg[u] = ok ? vx : zero8();
+      kreg[u] = bload16(rk, voff[u], so);
+      vreg[u] = bload16(rv, voff[u], so);
     }
-    if (tid < BK) {
-      const int j = kb * BK + tid;
-      const int ej = P.end[min(j, g.n_k - 1)];
-      ereg = j < g.n_k ? ej : -1;
-    }
+    if (tid < BK) ereg = bloadi(re, uint32_t(tid) * 4, uint32_t(kb) * BK * 4);
   };
   auto store_tile = [&](FwdStage& s) {
 #pragma unroll
@@ -238,7 +239,10 @@ int launch_fwd_g(const void* q, const void* k, const void* v, void* o, float* ls
 
 bool mfma_attn_supported(const AttnGeom& g, const PlanPtrs& P) {
   const int G = g.h_q / g.h_kv;
-  return g.d == D && P.bq == BQ && P.bk == BK && (G == 1 || G == 2 || G == 4);
+  // buffer loads address Q/dO and K/V with 32-bit byte offsets
+  const bool small = int64_t(g.n_q) * g.h_q * D * 2 < (int64_t(1) << 31) &&
+                     int64_t(g.n_k) * g.h_kv * D * 2 < (int64_t(1) << 31);
+  return g.d == D && P.bq == BQ && P.bk == BK && (G == 1 || G == 2 || G == 4) && small;
 }
 
 int launch_fwd_mfma(const void* q, const void* k, const void* v, void* o, float* lse, const PlanPtrs& P,

@@ -74,25 +74,27 @@ __global__ __launch_bounds__(DqCfg<G>::THREADS) void dq_mfma_kernel(
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) acc[dt] = zero16();
 
+  // tile staging: buffer loads, zero past n_k keys (end = 0 there: invisible)
+  const uint32_t kv_bytes = uint32_t(g.n_k) * uint32_t(g.h_kv) * D * 2;
+  const rsrc_t rk = make_rsrc(k, kv_bytes), rv = make_rsrc(v, kv_bytes);
+  const rsrc_t re = make_rsrc(P.end, uint32_t(g.n_k) * 4);
+  const uint32_t tile_bytes = uint32_t(BK) * g.h_kv * D * 2;
+  uint32_t voff[C::CH];
+#pragma unroll
+  for (int u = 0; u < C::CH; ++u) {
+    const int c = tid + u * C::THREADS;
+    voff[u] = (uint32_t((c >> 4) * g.h_kv + kvh) * D + (c & 15) * 8) * 2;
+  }
   bf16x8 kreg[C::CH], vreg[C::CH];
-  int32_t ereg = -1;
+  int32_t ereg = 0;
   auto load_tile = [&](int kb) {
+    const uint32_t so = uint32_t(kb) * tile_bytes;
 #pragma unroll
     for (int u = 0; u < C::CH; ++u) {
-      const int c = tid + u * C::THREADS;
-      const int key = c >> 4, dch = c & 15;
-      const int j = kb * BK + key;
-      const bool ok = j < g.n_k;
-      const int64_t off = (int64_t(ok ? j : g.n_k - 1) * g.h_kv + kvh) * D + dch * 8;
-      const bf16x8 kx = ld16(k + off), vx = ld16(v + off);
-      kreg[u] = ok ? kx : zero8();
-      vreg[u] = ok ? vx : zero8();
+      kreg[u] = bload16(rk, voff[u], so);
+      vreg[u] = bload16(rv, voff[u], so);
     }
-    if (tid < BK) {
-      const int j = kb * BK + tid;
-      const int ej = P.end[min(j, g.n_k - 1)];
-      ereg = j < g.n_k ? ej : -1;
-    }
+    if (tid < BK) ereg = bloadi(re, uint32_t(tid) * 4, uint32_t(kb) * BK * 4);
   };
   auto store_tile = [&](DqStage& s) {
 #pragma unroll
@@ -258,26 +260,28 @@ __global__ __launch_bounds__(KV_THREADS, 2) void dkdv_mfma_kernel(
 
   bf16x8 qreg[QCH], oreg[QCH];
   float lreg = 0.f, dreg = 0.f;
+  // buffer loads: query rows past n_q read zeros (tiles start at or after
+  // q_off, which is a multiple of 64, so rows are never below the buffer)
+  const uint32_t q_bytes = uint32_t(g.n_q) * uint32_t(g.h_q) * D * 2;
+  const rsrc_t rq = make_rsrc(q, q_bytes), ro = make_rsrc(d_o, q_bytes);
+  const rsrc_t rl = make_rsrc(lse, uint32_t(g.n_q) * g.h_q * 4), rd = make_rsrc(Dv, uint32_t(g.n_q) * g.h_q * 4);
+  uint32_t voff[QCH];
+#pragma unroll
+  for (int u = 0; u < QCH; ++u) {
+    const int c = tid + u * KV_THREADS;
+    voff[u] = (uint32_t(c >> 4) * g.h_q * D + (c & 15) * 8) * 2;
+  }
   auto load_tile = [&](int step) {
     const int qt = qt_first + step / G, head = kvh * G + step % G;
+    const uint32_t rowh = uint32_t(qt * QT - g.q_off) * g.h_q + head;  // (row, head) of the tile's first row
 #pragma unroll
     for (int u = 0; u < QCH; ++u) {
-      const int c = tid + u * KV_THREADS;
-      const int rr = c >> 4, dch = c & 15;
-      const int row = qt * QT + rr - g.q_off;  // q-buffer row
-      const bool ok = row >= 0 && row < g.n_q;
-      const int64_t off = (int64_t(min(max(row, 0), g.n_q - 1)) * g.h_q + head) * D + dch * 8;
-      const bf16x8 qx = ld16(q + off), ox = ld16(d_o + off);
-      qreg[u] = ok ? qx : zero8();
-      oreg[u] = ok ? ox : zero8();
+      qreg[u] = bload16(rq, voff[u], rowh * D * 2);
+      oreg[u] = bload16(ro, voff[u], rowh * D * 2);
     }
     if (tid < QT) {
-      const int row = qt * QT + tid - g.q_off;
-      const bool ok = row >= 0 && row < g.n_q;
-      const int64_t o1 = int64_t(min(max(row, 0), g.n_q - 1)) * g.h_q + head;
-      const float lx = lse[o1] * kLog2e, dx = Dv[o1];
-      lreg = ok ? lx : 0.f;
-      dreg = ok ? dx : 0.f;
+      lreg = bloadf(rl, uint32_t(tid) * g.h_q * 4, rowh * 4) * kLog2e;
+      dreg = bloadf(rd, uint32_t(tid) * g.h_q * 4, rowh * 4);
     }
   };
   auto store_tile = [&](KvStage& s) {
@@ -453,7 +457,10 @@ int launch_dkdv_g(const void* q, const void* k, const void* v, const void* d_o, 
 
 bool mfma_bwd_supported(const AttnGeom& g, const PlanPtrs& P) {
   const int G = g.h_q / g.h_kv;
-  return g.d == D && P.bq == BQ && P.bk == BK && (G == 1 || G == 2 || G == 4);
+  // buffer loads address Q/dO and K/V with 32-bit byte offsets
+  const bool small = int64_t(g.n_q) * g.h_q * D * 2 < (int64_t(1) << 31) &&
+                     int64_t(g.n_k) * g.h_kv * D * 2 < (int64_t(1) << 31);
+  return g.d == D && P.bq == BQ && P.bk == BK && (G == 1 || G == 2 || G == 4) && small;
 }
 
 int launch_dq_mfma(const void* q, const void* k, const void* v, const void* d_o, const float* lse, const float* D_,

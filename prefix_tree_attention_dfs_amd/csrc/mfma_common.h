@@ -54,6 +54,24 @@ __device__ __forceinline__ f32x16 zero16() {
 // 16 bytes from global memory (row guard done by the caller)
 __device__ __forceinline__ bf16x8 ld16(const uint16_t* p) { return *reinterpret_cast<const bf16x8*>(p); }
 
+// Raw buffer loads: the hardware compares (voffset + soffset) with the
+// buffer's byte size and returns zeros past the end, so tile rows beyond a
+// tensor need no clamp and no select.  Offsets are bytes; tensors used this
+// way are below 2 GiB (checked on the host).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, int(bytes), 0x00020000);
+}
+__device__ __forceinline__ bf16x8 bload16(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+__device__ __forceinline__ float bloadf(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+}
+__device__ __forceinline__ int32_t bloadi(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return int32_t(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+}
+
 __device__ __forceinline__ bf16x8 lds_read16(const uint16_t* p) { return *reinterpret_cast<const bf16x8*>(p); }
 
 // Transposed 8-byte LDS read (see header comment).
