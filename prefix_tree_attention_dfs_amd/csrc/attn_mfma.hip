@@ -29,6 +29,7 @@ struct FwdCfg {
   static constexpr int THREADS = WAVES * 64;
   static constexpr int CH = (BK * D / 8) / THREADS;      // 16-byte chunks per thread per K (or V) tile
   static constexpr int WPH = 2 / NT;                     // waves per head
+  static constexpr int MINB = WAVES >= 8 ? 1 : 8 / WAVES;  // workgroups per CU for two waves per SIMD
 };
 
 struct __align__(16) FwdStage {
@@ -38,7 +39,7 @@ struct __align__(16) FwdStage {
 };
 
 template <int G>
-__global__ __launch_bounds__(FwdCfg<G>::THREADS) void fwd_mfma_kernel(
+__global__ __launch_bounds__(FwdCfg<G>::THREADS, FwdCfg<G>::MINB) void fwd_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     uint16_t* __restrict__ o, float* __restrict__ lse, PlanPtrs P, AttnGeom g, int full_range, int qb_first,
     int n_qb) {
@@ -114,6 +115,7 @@ __global__ __launch_bounds__(FwdCfg<G>::THREADS) void fwd_mfma_kernel(
     load_tile(P.qb_tiles[e0] & kKbMask);
     store_tile(st[0]);
   }
+  wait_vmem();
   __syncthreads();
 
   for (int e = e0; e < e1; ++e) {

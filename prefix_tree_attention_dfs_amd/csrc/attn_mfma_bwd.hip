@@ -112,6 +112,7 @@ __global__ __launch_bounds__(DqCfg<G>::THREADS) void dq_mfma_kernel(
     load_tile(P.qb_tiles[e0] & kKbMask);
     store_tile(st[0]);
   }
+  wait_vmem();
   __syncthreads();
   for (int e = e0; e < e1; ++e) {
     const int sidx = (e - e0) & 1;
@@ -280,7 +281,7 @@ __global__ __launch_bounds__(KV_THREADS, 2) void dkdv_mfma_kernel(
       oreg[u] = bload16(ro, voff[u], rowh * D * 2);
     }
     if (tid < QT) {
-      lreg = bloadf(rl, uint32_t(tid) * g.h_q * 4, rowh * 4) * kLog2e;
+      lreg = bloadf(rl, uint32_t(tid) * g.h_q * 4, rowh * 4);
       dreg = bloadf(rd, uint32_t(tid) * g.h_q * 4, rowh * 4);
     }
   };
@@ -293,7 +294,7 @@ __global__ __launch_bounds__(KV_THREADS, 2) void dkdv_mfma_kernel(
       *reinterpret_cast<bf16x8*>(&s.O[soff(rr, dch * 8)]) = oreg[u];
     }
     if (tid < QT) {
-      s.lse2[tid] = lreg;
+      s.lse2[tid] = lreg * kLog2e;  // scaled here, not at the load: no wait in the loop head
       s.Dv[tid] = dreg;
     }
   };
@@ -302,6 +303,7 @@ __global__ __launch_bounds__(KV_THREADS, 2) void dkdv_mfma_kernel(
     load_tile(0);
     store_tile(L.run.st[0]);
   }
+  wait_vmem();
   __syncthreads();
   const uint16_t* Kt = L.run.K + (ks * 32 + r) * KSTR + 8 * hh;
   const uint16_t* Vt = L.run.V + (ks * 32 + r) * KSTR + 8 * hh;

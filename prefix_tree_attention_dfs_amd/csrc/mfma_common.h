@@ -29,7 +29,7 @@ constexpr int D = 128;     // head dim
 constexpr int BQ = 64;     // query rows per plan block
 constexpr int BK = 64;     // key rows per plan block
 constexpr int KSTR = 136;  // LDS row stride (bf16) of tiles read with ds_read_b128
-constexpr int VSTR = 144;  // LDS row stride (bf16) of tiles read with ds_read_tr16_b64
+constexpr int VSTR = 160;  // LDS row stride (bf16) of tiles read with ds_read_tr16_b64
 constexpr int32_t kFull = 0x40000000;
 constexpr int32_t kKbMask = 0x3FFFFFFF;
 
@@ -72,6 +72,13 @@ __device__ __forceinline__ int32_t bloadi(rsrc_t r, uint32_t voff, uint32_t soff
   return int32_t(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
 }
 
+// Wait until every vector-memory load issued so far has returned
+// (s_waitcnt vmcnt(0); expcnt and lgkmcnt left at their maxima).  Placed
+// after a kernel's prologue, it tells the compiler's wait insertion that the
+// registers loaded there are ready, so the main loop's first use of them does
+// not wait for the tile prefetch issued just before it.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 __device__ __forceinline__ bf16x8 lds_read16(const uint16_t* p) { return *reinterpret_cast<const bf16x8*>(p); }
 
 // Transposed 8-byte LDS read (see header comment).
@@ -97,14 +104,25 @@ __device__ __forceinline__ bf16x8 tr_frag(const uint16_t* tile, int stride, int 
   return a;
 }
 
+// LDS on gfx950: 64 banks of 4 bytes.  A 16-byte read is served 16 lanes per
+// cycle and an 8-byte read (plain or transposed) 32 lanes per cycle, so a read
+// is free of bank conflicts when each such group of lanes covers distinct banks.
+//
+// Padded tiles: a row stride of 272 bytes (KSTR) puts 16 consecutive rows of a
+// 16-byte column read on distinct banks; 320 bytes (VSTR) puts the 4 rows x
+// 64 bytes of a 32-lane transposed read on distinct banks.
+//
 // Swizzled 128-column tiles (256-byte rows, no padding): 16-byte chunk c of
-// row k lives at chunk c ^ swz(k).  swz is a bijection on 0..15 whose bits 1-2
-// follow k % 4, so that
-//   * a 16-byte row read by 16 consecutive rows hits 16 distinct chunks, and
-//   * a transposed read (4 consecutive rows x 2 adjacent chunks per 16-lane
-//     group) hits 8 distinct chunks,
-// i.e. both access patterns of the backward kernels are free of bank conflicts.
-__device__ __forceinline__ int swz(int k) { return ((k & 3) << 1) | ((k >> 2) & 1) | (k & 8); }
+// row k lives at chunk c ^ swz(k), swz(k) = the two low 2-bit fields of k
+// swapped.  Every row spans all 64 banks once, so a chunk's banks are set by
+// its position alone, and
+//   * a 16-byte row read by 16 consecutive (16-aligned) rows hits 16 distinct
+//     positions, swz being a bijection on them, and
+//   * a transposed read, 4 consecutive (4-aligned) rows x 4 adjacent chunks
+//     per 32 lanes, hits 16 distinct positions: bits 2-3 of the position
+//     follow k % 4 and bits 0-1 the chunk,
+// i.e. both access patterns of the backward kernels are free of conflicts.
+__device__ __forceinline__ int swz(int k) { return ((k & 3) << 2) | ((k >> 2) & 3); }
 __device__ __forceinline__ int soff(int row, int col) {
   return row * D + ((((col >> 3) ^ swz(row))) << 3) + (col & 7);
 }
