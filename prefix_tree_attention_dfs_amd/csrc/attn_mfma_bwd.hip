@@ -182,8 +182,8 @@ constexpr int KCH = (KV_KEYS * D / 8) / KV_THREADS;
 struct __align__(16) KvStage {
   uint16_t Q[QT * D];  // swizzled (row reads for S, transposed reads for dK^T)
   uint16_t O[QT * D];  // dO, swizzled (row reads for dP, transposed reads for dV^T)
-  float lse2[QT];
-  float Dv[QT];
+  float s0[QT];  // -LSE / scale: start value of the S accumulator, so that P = exp2(c2 S)
+  float d0[QT];  // -D: start value of the dP accumulator, so that dS = P dP
 };
 
 struct __align__(16) KvLds {
@@ -213,6 +213,7 @@ __global__ __launch_bounds__(KV_THREADS, 2) void dkdv_mfma_kernel(
   const int j = kbase + ks * 32 + r;  // this lane's key (lane column of S, dP, dK^T, dV^T)
   const bool jok = j < g.n_k;
   const float c2 = g.scale * kLog2e;
+  const float inv_scale = 1.f / g.scale;
 
   // K, V of the workgroup's keys -> LDS (rows past n_k are zero)
 #pragma unroll
@@ -294,8 +295,8 @@ __global__ __launch_bounds__(KV_THREADS, 2) void dkdv_mfma_kernel(
       *reinterpret_cast<bf16x8*>(&s.O[soff(rr, dch * 8)]) = oreg[u];
     }
     if (tid < QT) {
-      s.lse2[tid] = lreg * kLog2e;  // scaled here, not at the load: no wait in the loop head
-      s.Dv[tid] = dreg;
+      s.s0[tid] = -lreg * inv_scale;  // scaled here, not at the load: no wait in the loop head
+      s.d0[tid] = -dreg;
     }
   };
 
@@ -314,8 +315,22 @@ __global__ __launch_bounds__(KV_THREADS, 2) void dkdv_mfma_kernel(
     const KvStage& S = L.run.st[sidx];
     const int q0 = qt * QT + mt * 32;  // tree row of this wave's first query
     // every (query, key) pair of this wave's 32 x 32 block visible and in range?
-    const bool full = wave_kmax <= q0 && wave_min_end > q0 + 31 && q0 >= lo && q0 + 31 < hi;
-    f32x16 s = zero16(), dp = zero16();
+    const bool full =
+        __builtin_amdgcn_readfirstlane(wave_kmax <= q0 && wave_min_end > q0 + 31 && q0 >= lo && q0 + 31 < hi);
+    // S starts at -LSE/scale and dP at -D (both per query = per register), so
+    // that the products below give c2 S - LSE log2(e) and dP - D directly
+    f32x16 s, dp;
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const int ql = mt * 32 + 8 * i4 + 4 * hh;
+      const f32x4 l4 = *reinterpret_cast<const f32x4*>(&S.s0[ql]);
+      const f32x4 d4 = *reinterpret_cast<const f32x4*>(&S.d0[ql]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        s[4 * i4 + e] = l4[e];
+        dp[4 * i4 + e] = d4[e];
+      }
+    }
 #pragma unroll
     for (int dc = 0; dc < 8; ++dc) {
       s = mfma(lds_read16(&S.Q[soff(mt * 32 + r, dc * 16 + 8 * hh)]), lds_read16(Kt + dc * 16), s);
@@ -325,15 +340,13 @@ __global__ __launch_bounds__(KV_THREADS, 2) void dkdv_mfma_kernel(
 #pragma unroll
     for (int i4 = 0; i4 < 4; ++i4) {
       const int ql = mt * 32 + 8 * i4 + 4 * hh;
-      const f32x4 l4 = *reinterpret_cast<const f32x4*>(&S.lse2[ql]);
-      const f32x4 d4 = *reinterpret_cast<const f32x4*>(&S.Dv[ql]);
       if (full) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int i = 4 * i4 + e;
-          const float p = exp2_fast(s[i] * c2 - l4[e]);
+          const float p = exp2_fast(s[i] * c2);
           s[i] = p;
-          ds[i] = p * (dp[i] - d4[e]);
+          ds[i] = p * dp[i];
         }
       } else {
 #pragma unroll
@@ -341,9 +354,9 @@ __global__ __launch_bounds__(KV_THREADS, 2) void dkdv_mfma_kernel(
           const int i = 4 * i4 + e;
           const int qq = qt * QT + ql + e;
           const bool vis = (j <= qq) & (qq < endj) & (qq >= lo) & (qq < hi);
-          const float p = vis ? exp2_fast(s[i] * c2 - l4[e]) : 0.f;
+          const float p = vis ? exp2_fast(s[i] * c2) : 0.f;
           s[i] = p;
-          ds[i] = p * (dp[i] - d4[e]);
+          ds[i] = p * dp[i];
         }
       }
     }
