@@ -244,6 +244,94 @@ int tree_nll_workspace_bytes(const tt_nll_args* args, size_t* bytes);
 int tree_weighted_nll(const tt_nll_args* args, tt_stream stream);
 
 /*
+ * Path mode: one attention layer over the tree, walked depth-first with a
+ * stack that holds only the current root-to-node path (AReaL-DTA, arXiv
+ * 2602.00482, summary page, Methodology in Plain English: forward only the new
+ * segment on entering a branch against the cached ancestors, backpropagate a
+ * segment when it is left for good, live state proportional to the longest
+ * path; Key Contributions 2: long suffixes backpropagated in fixed-length
+ * chunks, right to left).
+ *
+ * A segment is a maximal run of DFS rows in which every row but the last has
+ * exactly one child; the segments form a tree.  Entering a segment pushes its
+ * Q, K (rotated at their depths) and V onto the stack at positions = depths
+ * and runs its forward in chunks against stack positions [0, end of chunk).
+ * Leaving it (after all descendants) runs its backward chunk by chunk from the
+ * right, adding dK, dV into float32 stack accumulators, then writes the
+ * segment's dK, dV rows out and clears their stack slots.  Each call starts at
+ * the 64-aligned position at or below its first query; the ancestor rows below
+ * the chunk are recomputed with a zero upstream gradient ("pad rows", counted
+ * in tt_path_info), so results equal tree mode (tree_attn_fwd/bwd) up to the
+ * order of floating-point sums.
+ *
+ * tree_path_build
+ *   tree    built tree; must outlive the path object
+ *   chunk   queries per call, a positive multiple of 64 (Key Contributions 2
+ *           gives 2048 as the default and 4096 as the faster setting)
+ *   order   child visiting order: 0 = DFS (ascending token id), 1 = largest
+ *           subtree first (the pages name a greedy ordering heuristic without
+ *           defining it; this is one reading, offered for comparison)
+ *   out     receives the path object; free with tree_path_free
+ * Errors: TT_EINVAL (NULL, chunk, order), TT_ENOMEM.  Host only.
+ */
+typedef struct tt_path tt_path;
+
+typedef struct {
+  int32_t n_segments;
+  int32_t max_path;      /* longest root-to-leaf path in rows (max depth + 1): the stack size */
+  int32_t chunk, order;
+  int64_t fwd_calls;     /* attention calls of one forward traversal */
+  int64_t bwd_calls;     /* attention calls of one backward traversal */
+  int64_t pad_rows;      /* ancestor query rows recomputed per traversal (64-alignment of calls) */
+  int64_t query_rows;    /* rows the calls compute in total: N + pad_rows */
+} tt_path_info;
+
+int tree_path_build(const tt_tree* tree, int32_t chunk, int32_t order, tt_path** out);
+void tree_path_free(tt_path* path);
+int tree_path_info(const tt_path* path, tt_path_info* out);
+
+/* Copies the segment table and the walk into caller-owned HOST arrays (NULL
+ * members skipped): row0, len, depth0, parent (-1 at a root) [n_segments];
+ * events [2 n_segments], e >= 0 entering segment e, e < 0 leaving -1 - e. */
+int tree_path_segments(const tt_path* path, int32_t* row0, int32_t* len, int32_t* depth0, int32_t* parent,
+                       int32_t* events);
+
+/*
+ * tree_attn_path -- forward (d_o == NULL) or forward then backward of one
+ * layer, walked as above.  In the combined call each segment's backward runs
+ * when the walk leaves it, as in the pages' push-pop execution.
+ *   path          from tree_path_build
+ *   h_q, h_kv, d, dtype, scale, rope_base   as in tt_attn_args
+ *   q, k, v       [N,h_q,d], [N,h_kv,d], [N,h_kv,d] tree rows (DFS order)
+ *   o, lse        [N,h_q,d], [N,h_q] outputs, written for every row
+ *   d_o           [N,h_q,d] upstream gradient, or NULL for forward only
+ *   d_q, d_k, d_v [N,h_q,d], [N,h_kv,d], [N,h_kv,d] outputs in dtype,
+ *                 overwritten (ignored when d_o is NULL)
+ *   workspace     tree_path_workspace_bytes bytes, 256-byte aligned: the
+ *                 stack (Q, K, V, O, LSE and, with d_o, float32 dK, dV) of
+ *                 max_path positions plus per-call buffers of chunk + 64 rows
+ *                 and the chain plan; proportional to the longest path, not N
+ * Errors: TT_EINVAL, TT_EUNSUPPORTED, TT_EWORKSPACE, TT_EOVERFLOW, TT_EDEVICE.
+ */
+typedef struct {
+  const tt_path* path;
+  int32_t h_q, h_kv, d;
+  tt_dtype dtype;
+  float scale;
+  float rope_base;
+  const void *q, *k, *v;
+  void* o;
+  float* lse;
+  const void* d_o;
+  void *d_q, *d_k, *d_v;
+  void* workspace;
+  size_t workspace_bytes;
+} tt_path_args;
+
+int tree_path_workspace_bytes(const tt_path_args* args, size_t* bytes);
+int tree_attn_path(const tt_path_args* args, tt_stream stream);
+
+/*
  * Kernel timing (diagnostics).  While enabled on the calling thread, every
  * kernel this library launches from that thread is bracketed by two HIP
  * events recorded on the launch stream.  tt_timing_collect waits for the

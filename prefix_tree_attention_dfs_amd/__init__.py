@@ -25,7 +25,9 @@ TT_ACCUMULATE_DKDV = 1
 EXPORTED = ("tree_build", "tree_free", "tree_info", "tree_export", "tree_plan_bytes", "tree_plan_upload",
             "tree_plan_copy",
             "tree_attn_workspace_bytes", "tree_attn_fwd", "tree_attn_bwd", "tree_nll_workspace_bytes",
-            "tree_weighted_nll", "tt_last_error", "tt_timing_enable", "tt_timing_collect")
+            "tree_weighted_nll", "tt_last_error", "tt_timing_enable", "tt_timing_collect",
+            "tree_path_build", "tree_path_free", "tree_path_info", "tree_path_segments", "tree_path_workspace_bytes",
+            "tree_attn_path")
 
 
 class TTError(RuntimeError):
@@ -86,6 +88,21 @@ class NllArgs(ctypes.Structure):
 _LIB = None
 
 
+class PathInfo(ctypes.Structure):
+    _fields_ = [("n_segments", ctypes.c_int32), ("max_path", ctypes.c_int32), ("chunk", ctypes.c_int32),
+                ("order", ctypes.c_int32), ("fwd_calls", ctypes.c_int64), ("bwd_calls", ctypes.c_int64),
+                ("pad_rows", ctypes.c_int64), ("query_rows", ctypes.c_int64)]
+
+
+class PathArgs(ctypes.Structure):
+    _fields_ = [("path", ctypes.c_void_p), ("h_q", ctypes.c_int32), ("h_kv", ctypes.c_int32), ("d", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("scale", ctypes.c_float), ("rope_base", ctypes.c_float),
+                ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("o", ctypes.c_void_p),
+                ("lse", ctypes.c_void_p), ("d_o", ctypes.c_void_p), ("d_q", ctypes.c_void_p),
+                ("d_k", ctypes.c_void_p), ("d_v", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
+                ("workspace_bytes", ctypes.c_size_t)]
+
+
 def _setup(lib):
     lib.tree_build.argtypes = [_i32p, _i64p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                 ctypes.POINTER(ctypes.c_void_p)]
@@ -102,6 +119,13 @@ def _setup(lib):
     lib.tree_attn_bwd.argtypes = [ctypes.POINTER(AttnBwdArgs), ctypes.c_void_p]
     lib.tree_nll_workspace_bytes.argtypes = [ctypes.POINTER(NllArgs), ctypes.POINTER(ctypes.c_size_t)]
     lib.tree_weighted_nll.argtypes = [ctypes.POINTER(NllArgs), ctypes.c_void_p]
+    lib.tree_path_build.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(ctypes.c_void_p)]
+    lib.tree_path_free.argtypes = [ctypes.c_void_p]
+    lib.tree_path_free.restype = None
+    lib.tree_path_info.argtypes = [ctypes.c_void_p, ctypes.POINTER(PathInfo)]
+    lib.tree_path_segments.argtypes = [ctypes.c_void_p] + [_i32p] * 5
+    lib.tree_path_workspace_bytes.argtypes = [ctypes.POINTER(PathArgs), ctypes.POINTER(ctypes.c_size_t)]
+    lib.tree_attn_path.argtypes = [ctypes.POINTER(PathArgs), ctypes.c_void_p]
     lib.tt_last_error.restype = ctypes.c_char_p
     lib.tt_timing_enable.argtypes = [ctypes.c_int]
     lib.tt_timing_enable.restype = ctypes.c_int
@@ -314,6 +338,74 @@ def tree_attn_bwd(tree, plan, q, k, v, o, lse, d_o, q_off=0, scale=0.0, rope_bas
                     flags=TT_ACCUMULATE_DKDV if accumulate else 0)
     _check(lib().tree_attn_bwd(ctypes.byref(b), _stream()))
     return d_q, d_k, d_v
+
+
+# ------------------------------------------------------------------ path mode
+class Path:
+    """Depth-first walk plan over a tree's segments; see tree_path_build in include/tt.h."""
+
+    def __init__(self, tree, chunk=2048, order=0):
+        self.tree = tree  # the walk reads the tree: keep it alive
+        self.handle = ctypes.c_void_p()
+        _check(lib().tree_path_build(tree.handle, int(chunk), int(order), ctypes.byref(self.handle)))
+        inf = PathInfo()
+        _check(lib().tree_path_info(self.handle, ctypes.byref(inf)))
+        self.info = {n: int(getattr(inf, n)) for n, _ in PathInfo._fields_}
+
+    def segments(self):
+        """Segment table (row0, len, depth0, parent) and the walk's events, as host arrays."""
+        S = self.info["n_segments"]
+        out = {k: np.zeros(S, dtype=np.int32) for k in ("row0", "len", "depth0", "parent")}
+        out["events"] = np.zeros(2 * S, dtype=np.int32)
+        _check(lib().tree_path_segments(self.handle, *(_ptr(out[k], ctypes.c_int32) for k in
+                                                      ("row0", "len", "depth0", "parent", "events"))))
+        return out
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h is not None and h.value and _LIB is not None:
+            try:
+                _LIB.tree_path_free(h)
+            except Exception:  # interpreter shutdown
+                pass
+            self.handle = None
+
+
+def _path_args(path, q, k, v, d_o, scale, rope_base):
+    _, h_q, d = q.shape
+    h_kv = k.shape[1]
+    return PathArgs(path=path.handle, h_q=h_q, h_kv=h_kv, d=d, dtype=_dt(q), scale=scale, rope_base=rope_base,
+                    q=_p(q), k=_p(k), v=_p(v), d_o=_p(d_o))
+
+
+def path_workspace_bytes(path, q, k, v, backward, scale=0.0, rope_base=10000.0):
+    a = _path_args(path, q, k, v, q if backward else None, scale, rope_base)
+    n = ctypes.c_size_t()
+    _check(lib().tree_path_workspace_bytes(ctypes.byref(a), ctypes.byref(n)))
+    return n.value
+
+
+def tree_attn_path(path, q, k, v, d_o=None, scale=0.0, rope_base=10000.0, o=None, lse=None, d_q=None, d_k=None,
+                   d_v=None, workspace=None):
+    """Path-mode walk of one layer: (o, lse), or (o, lse, d_q, d_k, d_v) when d_o is given."""
+    import torch
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty(q.shape[0], q.shape[1], dtype=torch.float32, device=q.device)
+    if d_o is not None:
+        d_q = torch.empty_like(q) if d_q is None else d_q
+        d_k = torch.empty_like(k) if d_k is None else d_k
+        d_v = torch.empty_like(v) if d_v is None else d_v
+    a = _path_args(path, q, k, v, d_o, scale, rope_base)
+    a.o, a.lse, a.d_q, a.d_k, a.d_v = _p(o), _p(lse), _p(d_q), _p(d_k), _p(d_v)
+    n = ctypes.c_size_t()
+    _check(lib().tree_path_workspace_bytes(ctypes.byref(a), ctypes.byref(n)))
+    ws = _workspace(n.value, q.device, workspace)
+    a.workspace = ctypes.c_void_p(ws.data_ptr())
+    a.workspace_bytes = ws.numel()
+    _check(lib().tree_attn_path(ctypes.byref(a), _stream()))
+    return (o, lse) if d_o is None else (o, lse, d_q, d_k, d_v)
 
 
 # ------------------------------------------------------------------ weighted NLL

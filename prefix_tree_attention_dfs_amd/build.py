@@ -20,8 +20,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libtreeattn.so")
 
-HOST_SOURCES = ["tree_host.cpp"]
-HIP_SOURCES = ["capi.cpp", "attn_generic.hip", "attn_mfma.hip", "attn_mfma_bwd.hip", "nll.hip", "gemm.hip"]
+HOST_SOURCES = ["tree_host.cpp", "path_host.cpp"]
+HIP_SOURCES = ["capi.cpp", "path.cpp", "attn_generic.hip", "attn_mfma.hip", "attn_mfma_bwd.hip", "nll.hip", "gemm.hip"]
 
 ARCH = "gfx950"
 

@@ -6,6 +6,8 @@
 // Visibility: key row j is seen by query row i iff j <= i < end[j] (j is i or
 // an ancestor of i in DFS order); positions are depths, so each row's result
 // equals its per-branch causal-attention result (Tree Training, Abstract).
+#include <algorithm>
+
 #include "device.h"
 #include "kernels.h"
 
@@ -393,5 +395,21 @@ int launch_dkdv_generic(tt_dtype dt, bool acc, const void* q, const void* k, con
                      (uint16_t*)d_k, (uint16_t*)d_v, P, g), 0)))
   TT_DMAX_DISPATCH(g.d, KV);
 #undef KV
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+// ---------------------------------------------------------------- fill
+// Zeroes a device buffer (bytes a multiple of 4) with plain vector stores, so
+// that code a caller may capture into a graph records no memset node.
+__global__ __launch_bounds__(256) void fill_zero_kernel(uint32_t* __restrict__ p, int64_t n) {
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += int64_t(gridDim.x) * blockDim.x)
+    p[i] = 0u;
+}
+
+int launch_fill_zero(void* p, size_t bytes, hipStream_t st) {
+  const int64_t n = int64_t(bytes / 4);
+  if (n == 0) return 0;
+  const int64_t blocks = std::min<int64_t>((n + 255) / 256, 4096);
+  fill_zero_kernel<<<dim3(unsigned(blocks)), dim3(256), 0, st>>>(static_cast<uint32_t*>(p), n);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }

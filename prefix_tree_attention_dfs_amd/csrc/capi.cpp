@@ -8,8 +8,13 @@
 #include <string>
 #include <vector>
 
+#include "attn_core.h"
 #include "internal.h"
 #include "kernels.h"
+
+using ttc::dev_fail;
+using ttc::KTimer;
+using ttc::plan_ptrs;
 
 namespace {
 
@@ -17,27 +22,6 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 size_t dsize(tt_dtype t) { return t == TT_F32 ? 4 : 2; }
-
-PlanPtrs plan_ptrs(const tt_tree* t, const void* dev_plan) {
-  const int32_t* base = static_cast<const int32_t*>(dev_plan);
-  const int32_t* h = t->plan.data();
-  PlanPtrs P;
-  P.depth = base + h[ttp::H_DEPTH];
-  P.end = base + h[ttp::H_END];
-  P.qb_ptr = base + h[ttp::H_QB_PTR];
-  P.qb_tiles = base + h[ttp::H_QB_TILES];
-  P.qb_order = base + h[ttp::H_QB_ORDER];
-  P.kb_qlo = base + h[ttp::H_KB_QLO];
-  P.kb_qhi = base + h[ttp::H_KB_QHI];
-  P.kb_minend = base + h[ttp::H_KB_MINEND];
-  P.kb_order = base + h[ttp::H_KB_ORDER];
-  P.N = t->N;
-  P.bq = t->bq;
-  P.bk = t->bk;
-  P.nqb = t->nqb;
-  P.nkb = t->nkb;
-  return P;
-}
 
 // Workspace carve-up, identical for the size query and the calls.
 struct AttnWs {
@@ -118,57 +102,59 @@ AttnGeom geom(const tt_attn_args* a) {
   return g;
 }
 
-int dev_fail(const char* fn, const char* what) {
-  const hipError_t e = hipGetLastError();
-  return tt::fail(TT_EDEVICE, std::string(fn) + ": " + what + " failed: " + hipGetErrorString(e));
-}
-
-// ---- optional per-launch timing (tt_timing_enable)
-struct TimedLaunch {
-  const char* name;
-  hipEvent_t a, b;
-};
-thread_local bool g_timing = false;
-thread_local std::vector<TimedLaunch> g_launches;
-thread_local std::vector<hipEvent_t> g_pool;
-
-hipEvent_t take_event() {
-  if (!g_pool.empty()) {
-    hipEvent_t e = g_pool.back();
-    g_pool.pop_back();
-    return e;
-  }
-  hipEvent_t e = nullptr;
-  if (hipEventCreate(&e) != hipSuccess) return nullptr;
-  return e;
-}
-
-// Brackets one kernel launch with events on its stream when timing is on.
-class KTimer {
- public:
-  KTimer(const char* name, hipStream_t st) : name_(name), st_(st) {
-    if (!g_timing) return;
-    a_ = take_event();
-    b_ = take_event();
-    if (a_ && b_) (void)hipEventRecord(a_, st_);
-  }
-  ~KTimer() {
-    if (!g_timing || !a_ || !b_) return;
-    (void)hipEventRecord(b_, st_);
-    g_launches.push_back({name_, a_, b_});
-  }
-
- private:
-  const char* name_;
-  hipStream_t st_;
-  hipEvent_t a_ = nullptr, b_ = nullptr;
-};
 
 }  // namespace
 
+namespace ttc {
+
+int attn_fwd_core(tt_dtype dt, const PlanPtrs& P, const AttnGeom& g, const void* q, const void* k, const void* v,
+                  void* o, float* lse, bool full_range, hipStream_t st) {
+  const char* fn = "attention forward";
+  if (dt == TT_BF16 && mfma_attn_supported(g, P)) {
+    KTimer t("attn_fwd_mfma", st);
+    if (launch_fwd_mfma(q, k, v, o, lse, P, g, full_range, st)) return dev_fail(fn, "attention kernel");
+  } else {
+    KTimer t("attn_fwd_generic", st);
+    if (launch_fwd_generic(dt, q, k, v, o, lse, P, g, st)) return dev_fail(fn, "attention kernel");
+  }
+  return TT_OK;
+}
+
+int attn_bwd_core(tt_dtype dt, const PlanPtrs& P, const AttnGeom& g, const void* q, const void* k, const void* v,
+                  const void* o, const void* d_o, const float* lse, float* D, float* dq, void* d_k, void* d_v,
+                  bool acc, bool full_range, hipStream_t st) {
+  const char* fn = "attention backward";
+  {
+    KTimer t("attn_bwd_pre", st);
+    if (launch_bwd_pre(dt, o, d_o, D, int64_t(g.n_q) * g.h_q, g.d, st)) return dev_fail(fn, "preprocess");
+  }
+  if (dt == TT_BF16 && mfma_bwd_supported(g, P)) {
+    {
+      KTimer t("attn_bwd_dq_mfma", st);
+      if (launch_dq_mfma(q, k, v, d_o, lse, D, dq, P, g, full_range, st)) return dev_fail(fn, "dq kernel");
+    }
+    {
+      KTimer t("attn_bwd_dkdv_mfma", st);
+      if (launch_dkdv_mfma(q, k, v, d_o, lse, D, d_k, d_v, acc, P, g, st)) return dev_fail(fn, "dk/dv kernel");
+    }
+  } else {
+    {
+      KTimer t("attn_bwd_dq_generic", st);
+      if (launch_dq_generic(dt, q, k, v, d_o, lse, D, dq, P, g, st)) return dev_fail(fn, "dq kernel");
+    }
+    {
+      KTimer t("attn_bwd_dkdv_generic", st);
+      if (launch_dkdv_generic(dt, acc, q, k, v, d_o, lse, D, d_k, d_v, P, g, st)) return dev_fail(fn, "dk/dv kernel");
+    }
+  }
+  return TT_OK;
+}
+
+}  // namespace ttc
+
 extern "C" int tt_timing_enable(int on) {
   tt::clear_error();
-  g_timing = on != 0;
+  ttc::g_timing = on != 0;
   return TT_OK;
 }
 
@@ -177,7 +163,7 @@ extern "C" int tt_timing_collect(tt_kernel_time* out, int capacity, int* count) 
   if (!count || (capacity > 0 && !out)) return tt::fail(TT_EINVAL, "tt_timing_collect: NULL argument");
   std::vector<tt_kernel_time> agg;
   int rc = TT_OK;
-  for (const TimedLaunch& t : g_launches) {
+  for (const ttc::TimedLaunch& t : ttc::g_launches) {
     float ms = 0.f;
     if (hipEventSynchronize(t.b) != hipSuccess || hipEventElapsedTime(&ms, t.a, t.b) != hipSuccess) {
       rc = TT_EDEVICE;
@@ -193,10 +179,10 @@ extern "C" int tt_timing_collect(tt_kernel_time* out, int capacity, int* count) 
     agg[k].launches += 1;
     agg[k].total_ms += ms;
     agg[k].max_ms = std::max(agg[k].max_ms, double(ms));
-    g_pool.push_back(t.a);
-    g_pool.push_back(t.b);
+    ttc::g_pool.push_back(t.a);
+    ttc::g_pool.push_back(t.b);
   }
-  g_launches.clear();
+  ttc::g_launches.clear();
   *count = int(agg.size());
   for (int i = 0; i < capacity && i < int(agg.size()); ++i) out[i] = agg[size_t(i)];
   if (rc != TT_OK) return tt::fail(rc, "tt_timing_collect: event query failed");
@@ -255,14 +241,7 @@ extern "C" int tree_attn_fwd(const tt_attn_args* a, tt_stream stream) {
     k = ws + w.k_rot;
   }
   const bool full_range = a->q_off == 0 && a->n_q == P.N;
-  if (a->dtype == TT_BF16 && mfma_attn_supported(g, P)) {
-    KTimer t("attn_fwd_mfma", st);
-    if (launch_fwd_mfma(q, k, a->v, a->o, a->lse, P, g, full_range, st)) return dev_fail(fn, "attention kernel");
-  } else {
-    KTimer t("attn_fwd_generic", st);
-    if (launch_fwd_generic(a->dtype, q, k, a->v, a->o, a->lse, P, g, st)) return dev_fail(fn, "attention kernel");
-  }
-  return TT_OK;
+  return ttc::attn_fwd_core(a->dtype, P, g, q, k, a->v, a->o, a->lse, full_range, st);
 }
 
 extern "C" int tree_attn_bwd(const tt_attn_bwd_args* b, tt_stream stream) {
@@ -306,33 +285,10 @@ extern "C" int tree_attn_bwd(const tt_attn_bwd_args* b, tt_stream stream) {
   }
   float* D = reinterpret_cast<float*>(ws + w.D);
   float* dq = reinterpret_cast<float*>(ws + w.dq);
-  {
-    KTimer t("attn_bwd_pre", st);
-    if (launch_bwd_pre(a->dtype, a->o, b->d_o, D, int64_t(a->n_q) * a->h_q, a->d, st))
-      return dev_fail(fn, "preprocess");
-  }
   const bool full_range = a->q_off == 0 && a->n_q == P.N;
-  if (a->dtype == TT_BF16 && mfma_bwd_supported(g, P)) {
-    {
-      KTimer t("attn_bwd_dq_mfma", st);
-      if (launch_dq_mfma(q, k, a->v, b->d_o, a->lse, D, dq, P, g, full_range, st)) return dev_fail(fn, "dq kernel");
-    }
-    {
-      KTimer t("attn_bwd_dkdv_mfma", st);
-      if (launch_dkdv_mfma(q, k, a->v, b->d_o, a->lse, D, b->d_k, b->d_v, acc, P, g, st))
-        return dev_fail(fn, "dk/dv kernel");
-    }
-  } else {
-    {
-      KTimer t("attn_bwd_dq_generic", st);
-      if (launch_dq_generic(a->dtype, q, k, a->v, b->d_o, a->lse, D, dq, P, g, st)) return dev_fail(fn, "dq kernel");
-    }
-    {
-      KTimer t("attn_bwd_dkdv_generic", st);
-      if (launch_dkdv_generic(a->dtype, acc, q, k, a->v, b->d_o, a->lse, D, b->d_k, b->d_v, P, g, st))
-        return dev_fail(fn, "dk/dv kernel");
-    }
-  }
+  if ((rc = ttc::attn_bwd_core(a->dtype, P, g, q, k, a->v, a->o, b->d_o, a->lse, D, dq, b->d_k, b->d_v, acc,
+                               full_range, st)))
+    return rc;
   // dQ: rotate back at the query rows' depths, convert to the output dtype
   if (a->n_q > 0) {
     KTimer t("dq_finalize", st);

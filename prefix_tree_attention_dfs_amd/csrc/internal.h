@@ -39,3 +39,20 @@ int fail(int code, const std::string& msg);  // records msg, returns code
 void clear_error();
 inline const int32_t* plan_section(const tt_tree* t, int hdr) { return t->plan.data() + t->plan[hdr]; }
 }  // namespace tt
+
+// Path-mode traversal plan (tree_path_build).  Segments are maximal chains of
+// DFS rows; events list the walk: e >= 0 enters segment e, e < 0 leaves
+// segment -1 - e.  `chain` is a one-sequence tree of max_path rows whose plan
+// serves every attention call of the walk (stack position = depth).
+struct tt_path {
+  struct Seg {
+    int32_t row0, len, depth0, parent;
+  };
+  const tt_tree* tree = nullptr;
+  tt_tree* chain = nullptr;
+  int32_t chunk = 2048, order = 0, max_path = 0;
+  std::vector<Seg> segs;
+  std::vector<int32_t> events;
+  int64_t fwd_calls = 0, bwd_calls = 0, pad_rows = 0;
+  ~tt_path();
+};

@@ -32,6 +32,9 @@ int launch_dq_mfma(const void* q, const void* k, const void* v, const void* d_o,
 int launch_dkdv_mfma(const void* q, const void* k, const void* v, const void* d_o, const float* lse, const float* D,
                      void* d_k, void* d_v, bool acc, const PlanPtrs& P, const AttnGeom& g, hipStream_t st);
 
+// Zeroes `bytes` (a multiple of 4) at p.
+int launch_fill_zero(void* p, size_t bytes, hipStream_t st);
+
 // Weighted NLL.
 int launch_nll_rows(tt_dtype zt, const void* z, void* dz, int32_t n_rows, int32_t vocab, int64_t ldz,
                     const int32_t* row_ptr, const int32_t* tgt_id, const float* tgt_w, int32_t n_tgt, float* logp,

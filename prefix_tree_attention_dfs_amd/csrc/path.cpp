@@ -1,0 +1,232 @@
+// Path mode (tree_attn_path): one attention layer walked depth-first over the
+// tree's segments with a stack of the current path (AReaL-DTA, arXiv
+// 2602.00482, summary page, Methodology in Plain English; Key Contributions 2
+// for the right-to-left chunks).  The stack keeps Q and K already rotated at
+// their positions (= depths), so every call runs the attention cores without
+// RoPE; gradients are rotated back as they leave the stack.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <string>
+#include <utility>
+#include <vector>
+
+#include "attn_core.h"
+#include "internal.h"
+#include "kernels.h"
+
+using ttc::dev_fail;
+using ttc::KTimer;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+size_t dsize(tt_dtype t) { return t == TT_F32 ? 4 : 2; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Workspace carve-up, identical for the size query and the call.
+struct PathWs {
+  size_t plan = 0, qp = 0, kp = 0, vp = 0, op = 0, lsep = 0;  // stack of max_path positions
+  size_t dka = 0, dva = 0;                                   // float32 dK, dV accumulators (backward)
+  size_t doc = 0, D = 0, dq = 0;                             // per-call buffers, chunk + 64 rows
+  size_t total = 0;
+};
+
+PathWs path_ws(const tt_path_args* a, bool bwd) {
+  const tt_path* p = a->path;
+  const size_t L = size_t(p->max_path), C = size_t(p->chunk) + 64, es = dsize(a->dtype);
+  const size_t hq = size_t(a->h_q), hk = size_t(a->h_kv), d = size_t(a->d);
+  PathWs w;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  };
+  w.plan = take(p->chain ? p->chain->plan.size() * sizeof(int32_t) : 0);
+  w.qp = take(L * hq * d * es);
+  w.kp = take(L * hk * d * es);
+  w.vp = take(L * hk * d * es);
+  w.op = take(L * hq * d * es);
+  w.lsep = take(L * hq * 4);
+  if (bwd) {
+    w.dka = take(L * hk * d * 4);
+    w.dva = take(L * hk * d * 4);
+    w.doc = take(C * hq * d * es);
+    w.D = take(C * hq * 4);
+    w.dq = take(C * hq * d * 4);
+  }
+  w.total = off;
+  return w;
+}
+
+int check_path(const tt_path_args* a, const char* fn) {
+  using std::string;
+  if (!a) return tt::fail(TT_EINVAL, string(fn) + ": args is NULL");
+  if (!a->path) return tt::fail(TT_EINVAL, string(fn) + ": path is NULL");
+  if (a->dtype != TT_F32 && a->dtype != TT_BF16) return tt::fail(TT_EINVAL, string(fn) + ": bad dtype");
+  if (a->h_q <= 0 || a->h_kv <= 0 || a->h_q % a->h_kv != 0)
+    return tt::fail(TT_EINVAL, string(fn) + ": need h_q, h_kv > 0 and h_q % h_kv == 0");
+  if (a->d <= 0 || a->d % 2 != 0) return tt::fail(TT_EINVAL, string(fn) + ": d must be positive and even");
+  if (a->d % 16 != 0 || a->d > 256)
+    return tt::fail(TT_EUNSUPPORTED, string(fn) + ": head dim must be a multiple of 16 and <= 256");
+  if (!(a->scale >= 0.f) || !std::isfinite(a->scale)) return tt::fail(TT_EINVAL, string(fn) + ": bad scale");
+  if (!(a->rope_base >= 0.f) || !std::isfinite(a->rope_base))
+    return tt::fail(TT_EINVAL, string(fn) + ": bad rope_base");
+  const int64_t N = a->path->tree->N;
+  if (N * a->h_q * a->d * 4 > (int64_t(1) << 40)) return tt::fail(TT_EOVERFLOW, string(fn) + ": tensors too large");
+  if (N > 0 && (!a->q || !a->k || !a->v || !a->o || !a->lse))
+    return tt::fail(TT_EINVAL, string(fn) + ": q, k, v, o and lse are required");
+  if (N > 0 && a->d_o && (!a->d_q || !a->d_k || !a->d_v))
+    return tt::fail(TT_EINVAL, string(fn) + ": d_q, d_k and d_v are required with d_o");
+  for (const void* p : {a->q, a->k, a->v, static_cast<const void*>(a->o), static_cast<const void*>(a->lse), a->d_o,
+                        static_cast<const void*>(a->d_q), static_cast<const void*>(a->d_k),
+                        static_cast<const void*>(a->d_v)})
+    if (p && !aligned16(p)) return tt::fail(TT_EINVAL, string(fn) + ": device pointers must be 16-byte aligned");
+  if (a->workspace && (reinterpret_cast<uintptr_t>(a->workspace) & (kAlign - 1)) != 0)
+    return tt::fail(TT_EINVAL, string(fn) + ": workspace must be 256-byte aligned");
+  return TT_OK;
+}
+
+// Chunks of stack positions [p0, p1) (boundaries at multiples of chunk).
+std::vector<std::pair<int32_t, int32_t>> chunks(int32_t p0, int32_t p1, int32_t chunk) {
+  std::vector<std::pair<int32_t, int32_t>> v;
+  for (int32_t c0 = p0; c0 < p1;) {
+    const int32_t c1 = std::min(p1, (c0 / chunk + 1) * chunk);
+    v.push_back({c0, c1});
+    c0 = c1;
+  }
+  return v;
+}
+
+}  // namespace
+
+extern "C" int tree_path_workspace_bytes(const tt_path_args* a, size_t* bytes) {
+  tt::clear_error();
+  if (!bytes) return tt::fail(TT_EINVAL, "tree_path_workspace_bytes: bytes is NULL");
+  if (!a || !a->path) return tt::fail(TT_EINVAL, "tree_path_workspace_bytes: args/path is NULL");
+  if (a->h_q <= 0 || a->h_kv <= 0 || a->d <= 0 || (a->dtype != TT_F32 && a->dtype != TT_BF16))
+    return tt::fail(TT_EINVAL, "tree_path_workspace_bytes: bad geometry");
+  *bytes = path_ws(a, a->d_o != nullptr).total;
+  return TT_OK;
+}
+
+extern "C" int tree_attn_path(const tt_path_args* a, tt_stream stream) {
+  tt::clear_error();
+  const char* fn = "tree_attn_path";
+  int rc = check_path(a, fn);
+  if (rc) return rc;
+  const tt_path* p = a->path;
+  const bool bwd = a->d_o != nullptr;
+  const PathWs w = path_ws(a, bwd);
+  if (w.total > 0 && (!a->workspace || a->workspace_bytes < w.total))
+    return tt::fail(TT_EWORKSPACE, std::string(fn) + ": workspace too small (need " + std::to_string(w.total) +
+                                       " bytes)");
+  if (p->tree->N == 0) return TT_OK;
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = static_cast<char*>(a->workspace);
+  const tt_dtype dt = a->dtype;
+  const size_t es = dsize(dt), hq = size_t(a->h_q), hk = size_t(a->h_kv), d = size_t(a->d);
+  const size_t qrow = hq * d * es, krow = hk * d * es;  // bytes per row
+  const float rb = a->rope_base;
+
+  if (hipMemcpyAsync(ws + w.plan, p->chain->plan.data(), p->chain->plan.size() * sizeof(int32_t),
+                     hipMemcpyHostToDevice, st) != hipSuccess)
+    return dev_fail(fn, "plan upload");
+  const PlanPtrs P = ttc::plan_ptrs(p->chain, ws + w.plan);
+  const int32_t* pos = P.depth;  // chain depth = stack position
+  AttnGeom g;
+  g.h_q = a->h_q;
+  g.h_kv = a->h_kv;
+  g.d = a->d;
+  g.scale = a->scale == 0.f ? float(1.0 / std::sqrt(double(a->d))) : a->scale;
+  g.rope_base = 0.f;  // the stack holds rotated rows
+
+  char *Qp = ws + w.qp, *Kp = ws + w.kp, *Vp = ws + w.vp, *Op = ws + w.op;
+  float* LSEp = reinterpret_cast<float*>(ws + w.lsep);
+  float* dKa = reinterpret_cast<float*>(ws + w.dka);
+  float* dVa = reinterpret_cast<float*>(ws + w.dva);
+  char* dOc = ws + w.doc;
+  float* D = reinterpret_cast<float*>(ws + w.D);
+  float* dq = reinterpret_cast<float*>(ws + w.dq);
+  const char* q = static_cast<const char*>(a->q);
+  const char* k = static_cast<const char*>(a->k);
+  const char* v = static_cast<const char*>(a->v);
+  char* o = static_cast<char*>(a->o);
+  const char* d_o = static_cast<const char*>(a->d_o);
+  char* d_q = static_cast<char*>(a->d_q);
+  char* d_k = static_cast<char*>(a->d_k);
+  char* d_v = static_cast<char*>(a->d_v);
+
+  if (bwd) {
+    KTimer t("path_clear", st);
+    if (launch_fill_zero(dKa, size_t(p->max_path) * hk * d * 4, st) ||
+        launch_fill_zero(dVa, size_t(p->max_path) * hk * d * 4, st))
+      return dev_fail(fn, "clear");
+  }
+  for (const int32_t e : p->events) {
+    if (e >= 0) {
+      // enter: push the segment's rows, then its forward against the stack
+      const tt_path::Seg& s = p->segs[size_t(e)];
+      const size_t r0 = size_t(s.row0), n = size_t(s.len), d0 = size_t(s.depth0);
+      {
+        KTimer t("path_push", st);
+        if (launch_rope(q + r0 * qrow, Qp + d0 * qrow, dt, dt, false, pos, s.depth0, s.len, a->h_q, a->d, rb, false,
+                        st) ||
+            launch_rope(k + r0 * krow, Kp + d0 * krow, dt, dt, false, pos, s.depth0, s.len, a->h_kv, a->d, rb, false,
+                        st) ||
+            hipMemcpyAsync(Vp + d0 * krow, v + r0 * krow, n * krow, hipMemcpyDeviceToDevice, st) != hipSuccess)
+          return dev_fail(fn, "push");
+      }
+      for (const auto& c : chunks(s.depth0, s.depth0 + s.len, p->chunk)) {
+        const int32_t qo = c.first & ~63;
+        g.q_off = qo;
+        g.n_q = c.second - qo;
+        g.n_k = c.second;
+        if ((rc = ttc::attn_fwd_core(dt, P, g, Qp + size_t(qo) * qrow, Kp, Vp, Op + size_t(qo) * qrow,
+                                     LSEp + size_t(qo) * hq, false, st)))
+          return rc;
+      }
+      KTimer t("path_out", st);
+      if (hipMemcpyAsync(o + r0 * qrow, Op + d0 * qrow, n * qrow, hipMemcpyDeviceToDevice, st) != hipSuccess ||
+          hipMemcpyAsync(a->lse + r0 * hq, LSEp + d0 * hq, n * hq * 4, hipMemcpyDeviceToDevice, st) != hipSuccess)
+        return dev_fail(fn, "forward outputs");
+    } else if (bwd) {
+      // leave: the segment's backward, chunks right to left, then pop its dK, dV
+      const tt_path::Seg& s = p->segs[size_t(-1 - e)];
+      const size_t r0 = size_t(s.row0), n = size_t(s.len), d0 = size_t(s.depth0);
+      const auto cs = chunks(s.depth0, s.depth0 + s.len, p->chunk);
+      for (auto it = cs.rbegin(); it != cs.rend(); ++it) {
+        const int32_t c0 = it->first, c1 = it->second, qo = c0 & ~63;
+        const size_t pad = size_t(c0 - qo), nc = size_t(c1 - c0), row = r0 + size_t(c0) - d0;
+        {
+          KTimer t("path_dout", st);
+          if (launch_fill_zero(dOc, pad * qrow, st) ||
+              hipMemcpyAsync(dOc + pad * qrow, d_o + row * qrow, nc * qrow, hipMemcpyDeviceToDevice, st) !=
+                  hipSuccess)
+            return dev_fail(fn, "upstream gradient");
+        }
+        g.q_off = qo;
+        g.n_q = c1 - qo;
+        g.n_k = c1;
+        if ((rc = ttc::attn_bwd_core(dt, P, g, Qp + size_t(qo) * qrow, Kp, Vp, Op + size_t(qo) * qrow, dOc,
+                                     LSEp + size_t(qo) * hq, D, dq, dKa, dVa, true, false, st)))
+          return rc;
+        KTimer t("dq_finalize", st);
+        if (launch_rope(dq + pad * hq * d, d_q + row * qrow, TT_F32, dt, false, pos, c0, c1 - c0, a->h_q, a->d, rb,
+                        true, st))
+          return dev_fail(fn, "dq finalize");
+      }
+      KTimer t("path_pop", st);
+      if (launch_rope(dKa + d0 * hk * d, d_k + r0 * krow, TT_F32, dt, false, pos, s.depth0, s.len, a->h_kv, a->d, rb,
+                      true, st) ||
+          launch_rope(dVa + d0 * hk * d, d_v + r0 * krow, TT_F32, dt, false, pos, s.depth0, s.len, a->h_kv, a->d, 0.f,
+                      false, st) ||
+          launch_fill_zero(dKa + d0 * hk * d, n * hk * d * 4, st) ||
+          launch_fill_zero(dVa + d0 * hk * d, n * hk * d * 4, st))
+        return dev_fail(fn, "pop");
+    }
+  }
+  return TT_OK;
+}

@@ -1,0 +1,88 @@
+"""GPU parity of path mode (tree_attn_path) against the fp64 oracle and tree mode.
+
+Path mode walks the tree depth-first with a stack of the current path and
+must give the tree-mode results: O and LSE of every row, and dQ, dK, dV equal
+to the per-branch gradients summed over copies.  bf16 (MFMA path, d = 128)
+within 2e-2 of the oracle like the tree-mode kernels; fp32 (generic path,
+d = 64) within 1e-4.  Chunks of 64 and 128 rows make calls start off 64-row
+boundaries (pad rows) and split segments; both child orders are covered.
+"""
+import numpy as np
+import pytest
+import torch
+
+import prefix_tree_attention_dfs_amd as tt
+import treesynth as ts
+from oracle import attention as OA
+from oracle.tree import dfs_arrays
+from tests.gpu_util import inputs, rel_err
+
+pytestmark = pytest.mark.gpu
+
+TREES = {
+    "beam_small": lambda: ts.agentic_beam_tree(5, root_len=300, turns=4, width=4, seg_len=(40, 160), n_max=10**9),
+    "random": lambda: ts.random_small_tree(7, n_seqs=10, max_len=400, vocab=3),
+    "forest": lambda: ts.rl_forest(3, n_trees=3, prompt=100, rollouts=4, turns=3, turn_len=(30, 90)),
+    "chain": lambda: ts.long_chain(2, length=777),
+}
+
+
+def _run(name, dtype, d, hq, hkv, chunk, order, seed, backward=True):
+    case = TREES[name]()
+    tree = tt.Tree(case.seqs)
+    o = dfs_arrays(case.seqs)
+    path = tt.Path(tree, chunk, order)
+    (q, qn), (k, kn), (v, vn), (do, don) = inputs(dtype, seed, tree.N, tree.N, hq, hkv, d, d ** -0.5)
+    print(f"{name}: N={tree.N} dtype={dtype} hq={hq} hkv={hkv} chunk={chunk} order={order} "
+          f"segments={path.info['n_segments']} pad_rows={path.info['pad_rows']}", flush=True)
+    out = tt.tree_attn_path(path, q, k, v, d_o=do if backward else None)
+    return tree, o, (q, k, v, do), (qn, kn, vn, don), out
+
+
+@pytest.mark.parametrize("name", list(TREES))
+@pytest.mark.parametrize("chunk,order", [(64, 0), (128, 1)])
+def test_path_bf16_vs_oracle_and_tree_mode(name, chunk, order):
+    tree, o, (q, k, v, do), (qn, kn, vn, don), (O, L, dq, dk, dv) = _run(name, torch.bfloat16, 128, 8, 2, chunk,
+                                                                         order, 51)
+    Or, Lr, _ = OA.forward(o, qn, kn, vn, which="leaves")
+    dQr, dKr, dVr = OA.backward(o, qn, kn, vn, don, which="leaves")
+    for n, g_, r_ in (("o", O, Or), ("lse", L, Lr), ("dq", dq, dQr), ("dk", dk, dKr), ("dv", dv, dVr)):
+        assert rel_err(g_, r_) < 2e-2, (n, rel_err(g_, r_))
+    # tree mode on the same inputs (same kernels, other summation order)
+    plan = tree.upload_plan()
+    Ot, Lt = tt.tree_attn_fwd(tree, plan, q, k, v)
+    dqt, dkt, dvt = tt.tree_attn_bwd(tree, plan, q, k, v, Ot, Lt, do)
+    for n, g_, t_ in (("o", O, Ot), ("lse", L, Lt), ("dq", dq, dqt), ("dk", dk, dkt), ("dv", dv, dvt)):
+        r = t_.double().cpu().numpy()
+        assert rel_err(g_, r) < 1e-2, (n, rel_err(g_, r))
+
+
+@pytest.mark.parametrize("name", ["beam_small", "random"])
+def test_path_f32_vs_oracle(name):
+    _, o, _, (qn, kn, vn, don), (O, L, dq, dk, dv) = _run(name, torch.float32, 64, 4, 2, 64, 0, 52)
+    Or, Lr, _ = OA.forward(o, qn, kn, vn, which="leaves")
+    dQr, dKr, dVr = OA.backward(o, qn, kn, vn, don, which="leaves")
+    for n, g_, r_ in (("o", O, Or), ("lse", L, Lr), ("dq", dq, dQr), ("dk", dk, dKr), ("dv", dv, dVr)):
+        assert rel_err(g_, r_) < 1e-4, (n, rel_err(g_, r_))
+
+
+def test_path_forward_only_and_orders_agree():
+    """Forward-only walk gives the combined walk's O and LSE; the child order
+    changes no result (every call is deterministic per row)."""
+    _, _, (q, k, v, do), _, (O0, L0) = _run("forest", torch.bfloat16, 128, 4, 1, 128, 0, 53, backward=False)
+    tree = tt.Tree(TREES["forest"]().seqs)
+    O1, L1, dq1, dk1, dv1 = tt.tree_attn_path(tt.Path(tree, 128, 1), q, k, v, d_o=do)
+    O2, L2, dq2, dk2, dv2 = tt.tree_attn_path(tt.Path(tree, 128, 0), q, k, v, d_o=do)
+    assert torch.equal(O0, O1) and torch.equal(L0, L1) and torch.equal(O1, O2) and torch.equal(L1, L2)
+    assert torch.equal(dq1, dq2)
+    for a, b in ((dk1, dk2), (dv1, dv2)):
+        assert rel_err(a, b.double().cpu().numpy()) < 1e-2
+
+
+def test_path_chain_equals_chunked_chain():
+    """A single chain in path mode: one segment, ceil(L / chunk) calls, right to left."""
+    tree, o, _, (qn, kn, vn, don), (O, L, dq, dk, dv) = _run("chain", torch.bfloat16, 128, 4, 2, 192, 0, 54)
+    Or, Lr, _ = OA.forward(o, qn, kn, vn)
+    dQr, dKr, dVr = OA.backward(o, qn, kn, vn, don)
+    for n, g_, r_ in (("o", O, Or), ("lse", L, Lr), ("dq", dq, dQr), ("dk", dk, dKr), ("dv", dv, dVr)):
+        assert rel_err(g_, r_) < 2e-2, (n, rel_err(g_, r_))

@@ -1,0 +1,151 @@
+"""Host side of path mode (tree_path_build), CPU only.
+
+The walk plan is checked against the tree's own parent/child structure taken
+from the oracle's DFS arrays:
+* segments partition the rows in DFS order, each is a chain (every row but
+  the last has exactly one child, which is the next row), and no two adjacent
+  segments could be merged (maximality);
+* a segment's parent is the segment holding its first row's parent;
+* the events are a depth-first walk: each segment entered once, left once,
+  children entered while their parent is on the stack, stack depth in rows
+  never above max_path = max depth + 1;
+* order 0 visits children by ascending first row, order 1 by descending
+  subtree size (ties by first row);
+* call and pad-row counts follow the chunk rule (boundaries at multiples of
+  the chunk, each call starting at the 64-aligned row at or below its first).
+"""
+import numpy as np
+import pytest
+
+import prefix_tree_attention_dfs_amd as tt
+import treesynth as ts
+from oracle.tree import dfs_arrays
+
+
+def _expected_segments(o):
+    N = o["N"]
+    nchild = np.bincount(o["parent"][o["parent"] >= 0], minlength=N) if N else np.zeros(0, np.int64)
+    starts = [i for i in range(N) if not (i > 0 and o["parent"][i] == i - 1 and nchild[i - 1] == 1)]
+    return starts, nchild
+
+
+def _check(seqs, chunk, order):
+    t = tt.Tree(seqs)
+    o = dfs_arrays(seqs)
+    p = tt.Path(t, chunk, order)
+    s = p.segments()
+    inf = p.info
+    N = o["N"]
+    S = inf["n_segments"]
+    starts, nchild = _expected_segments(o)
+    assert S == len(starts)
+    np.testing.assert_array_equal(s["row0"], starts)
+    ends = list(starts[1:]) + [N]
+    np.testing.assert_array_equal(s["len"], np.diff(starts + [N]) if N else [])
+    seg_of = np.zeros(N, dtype=np.int64)
+    for k, (a, b) in enumerate(zip(starts, ends)):
+        seg_of[a:b] = k
+        for r in range(a + 1, b):  # a chain: r's parent is r-1, whose only child is r
+            assert o["parent"][r] == r - 1 and nchild[r - 1] == 1
+        assert s["depth0"][k] == o["depth"][a]
+        np.testing.assert_array_equal(o["depth"][a:b], o["depth"][a] + np.arange(b - a))
+        par = o["parent"][a]
+        assert s["parent"][k] == (-1 if par < 0 else seg_of[par])
+        if par >= 0:
+            assert par == ends[s["parent"][k]] - 1  # attaches at its parent segment's last row
+    assert inf["max_path"] == (o["max_depth"] + 1 if N else 0)
+    # the walk
+    ev = s["events"]
+    assert len(ev) == 2 * S
+    entered, left, stack, rows_on_stack = set(), set(), [], 0
+    kids_seen = {}
+    for e in ev:
+        if e >= 0:
+            assert e not in entered
+            par = s["parent"][e]
+            assert (par < 0 and not stack) or (stack and stack[-1] == par)
+            kids_seen.setdefault(par, []).append(e)
+            entered.add(e)
+            stack.append(e)
+            rows_on_stack += s["len"][e]
+            assert rows_on_stack == s["depth0"][e] + s["len"][e] <= inf["max_path"]
+        else:
+            k = -1 - e
+            assert stack and stack[-1] == k and k not in left
+            left.add(k)
+            stack.pop()
+            rows_on_stack -= s["len"][k]
+    assert not stack and len(entered) == len(left) == S
+    size = lambda k: o["end"][s["row0"][k]] - s["row0"][k]  # noqa: E731
+    for par, kids in kids_seen.items():
+        want = sorted(kids, key=lambda k: s["row0"][k])
+        if order == 1:
+            want = sorted(want, key=lambda k: -size(k))  # stable: ties stay in row order
+        assert kids == want
+    # chunk accounting
+    calls = pad = 0
+    for k in range(S):
+        c0, c1 = s["depth0"][k], s["depth0"][k] + s["len"][k]
+        while c0 < c1:
+            calls += 1
+            pad += c0 % 64
+            c0 = min(c1, (c0 // chunk + 1) * chunk)
+    assert inf["fwd_calls"] == inf["bwd_calls"] == calls
+    assert inf["pad_rows"] == pad and inf["query_rows"] == N + pad
+    return p
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_path_plan_random(case):
+    rng = np.random.default_rng(100 + case)
+    seqs = ts.trees.random_small_tree(seed=100 + case, n_seqs=int(rng.integers(1, 12)), max_len=90, vocab=5,
+                                      p_dup=0.2, p_prefix=0.3).seqs
+    for chunk in (64, 128):
+        for order in (0, 1):
+            _check(seqs, chunk, order)
+
+
+def test_path_plan_workloads_and_edges():
+    _check(ts.trees.tiny_tree().seqs, 64, 0)
+    _check(ts.trees.tiny_tree().seqs, 2048, 1)
+    _check([list(range(300))], 128, 0)       # one chain: one segment, ceil chunks
+    _check([[1], [2], [3]], 64, 0)           # three one-row roots
+    _check([[5, 6], [5, 6], [5]], 64, 1)     # duplicates and a contained prefix
+    _check([], 64, 0)                        # empty tree
+    _check([[]], 64, 0)                      # one empty sequence
+
+
+def test_path_plan_c2_shape():
+    """The 8B-shape agentic tree: the walk's stack never exceeds the longest path."""
+    tree = ts.trees.agentic_beam_tree(seed=0)
+    p = _check(tree.seqs, 2048, 0)
+    assert p.info["max_path"] == max(len(s) for s in tree.seqs)
+
+
+def test_path_build_errors():
+    lib = tt.lib()
+    t = tt.Tree([[1, 2, 3]])
+    import ctypes
+    h = ctypes.c_void_p()
+    for chunk, order in ((0, 0), (100, 0), (-64, 0), (64, 2), (64, -1)):
+        assert lib.tree_path_build(t.handle, chunk, order, ctypes.byref(h)) == tt.TT_EINVAL
+        assert tt.last_error()
+    assert lib.tree_path_build(None, 64, 0, ctypes.byref(h)) == tt.TT_EINVAL
+    assert lib.tree_path_build(t.handle, 64, 0, None) == tt.TT_EINVAL
+    assert lib.tree_path_info(None, None) == tt.TT_EINVAL
+    assert lib.tree_path_segments(None, None, None, None, None, None) == tt.TT_EINVAL
+    p = tt.Path(t, 64, 0)
+    args = tt.PathArgs(path=p.handle, h_q=2, h_kv=1, d=128, dtype=tt.TT_BF16)
+    n = ctypes.c_size_t()
+    assert lib.tree_path_workspace_bytes(ctypes.byref(args), ctypes.byref(n)) == tt.TT_OK and n.value > 0
+    # the device entry point validates before touching the device
+    bad = [dict(h_q=3, h_kv=2), dict(d=100), dict(d=0), dict(dtype=7), dict(scale=-1.0),
+           dict(rope_base=float("inf"))]
+    for kw in bad:
+        a = tt.PathArgs(path=p.handle, h_q=2, h_kv=1, d=128, dtype=tt.TT_BF16)
+        for key, val in kw.items():
+            setattr(a, key, val)
+        assert lib.tree_attn_path(ctypes.byref(a), None) < 0, kw
+    a = tt.PathArgs(path=p.handle, h_q=2, h_kv=1, d=128, dtype=tt.TT_BF16)  # q, k, v, o, lse missing
+    assert lib.tree_attn_path(ctypes.byref(a), None) == tt.TT_EINVAL
+    assert lib.tree_attn_path(None, None) == tt.TT_EINVAL
