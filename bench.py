@@ -148,6 +148,46 @@ def secondary(tt, ts, steps):
     return out
 
 
+def path_mode_bench(tt, tree, plan, q, k, v, do, steps, tree_ms):
+    """Path mode on the headline tree: depth-first walk with a stack of the
+    current path, each segment's forward on entry and backward (right-to-left
+    chunks) on exit.  The pages' chunk sizes 2048 and 4096 and both child
+    orders; time against tree mode, recompute (pad rows) and workspace."""
+    import torch
+    d, hq = q.shape[2], q.shape[1]
+    P = tree.info["pairs"]
+    useful = 14 * d * hq * P
+    o, lse = torch.empty_like(q), torch.empty(q.shape[0], hq, dtype=torch.float32, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    out = {"tree_mode_ms": round(tree_ms, 3),
+           "tree_mode_workspace_bytes": tt.attn_workspace_bytes(tree, plan, q, k, v, True)}
+    for chunk, order in ((2048, 0), (4096, 0), (2048, 1)):
+        path = tt.Path(tree, chunk, order)
+        nbytes = tt.path_workspace_bytes(path, q, k, v, True)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+
+        def walk():
+            tt.tree_attn_path(path, q, k, v, d_o=do, o=o, lse=lse, d_q=dq, d_k=dk, d_v=dv, workspace=ws)
+
+        n = max(2, steps // 2)
+        ms = _time(walk, n, 1)
+        tt.timing_enable(True)
+        walk()
+        torch.cuda.synchronize()
+        tt.timing_enable(False)
+        kt = tt.timing_collect()
+        inf = path.info
+        out[f"chunk{chunk}_{'dfs' if order == 0 else 'largest_first'}"] = dict(
+            ms=round(ms, 3), vs_tree_mode=round(ms / tree_ms, 3), kernel_ms=round(sum(x[1] for x in kt.values()), 3),
+            launches=int(sum(x[0] for x in kt.values())), segments=inf["n_segments"], calls=inf["fwd_calls"],
+            max_path=inf["max_path"], pad_rows=inf["pad_rows"], pad_pairs_per_head=inf["pad_pairs"],
+            recompute_pct=round(100.0 * inf["pad_pairs"] / P, 3),
+            useful_tflops=round(useful / ms / 1e9, 1),
+            pct_bf16_peak=round(useful / ms / 1e9 / PEAK_BF16_TFLOPS * 100, 2), workspace_bytes=nbytes)
+        del ws, path
+    return out
+
+
 def lmhead_bench(tt, ts, steps):
     """Fused lm-head + weighted NLL: 16384 tree tokens x 4096 -> 151936 vocabulary,
     32-leaf tree (compression about 5.5); loss, dH and dW (fp32)."""
@@ -281,6 +321,7 @@ def main():
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-dense", action="store_true", help="skip the per-branch dense comparison")
+    ap.add_argument("--no-path", action="store_true", help="skip the path-mode walk of the headline tree")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (counter calibration)")
     args = ap.parse_args()
@@ -375,6 +416,8 @@ def main():
         dense = per_branch_dense(tt, ts, tree, case, q, k, v, do, args.steps)
         dense["tree_speedup"] = round(dense["ms"] / ms, 3)
         result["per_branch_dense"] = dense
+    if not args.no_path:
+        result["path_mode"] = path_mode_bench(tt, tree, plan, q, k, v, do, args.steps, ms)
     del st
     torch.cuda.empty_cache()
     if not args.no_secondary:

@@ -128,6 +128,26 @@ int tree_info(const tt_tree* tree, tt_tree_info* out);
 int tree_export(const tt_tree* tree, const tt_tree_arrays* dst);
 
 /*
+ * tree_target_weights -- loss weights of the targets for RL post-training:
+ * per-sequence scalars (e.g. advantages) and per-token loss masks (e.g. 0 on
+ * prompt tokens).  (AReaL-DTA, arXiv 2602.00482, summary page, Main Findings
+ * and Why This Matters: the trees come from RL rollouts trained with GRPO.)
+ * Token k >= 1 of sequence s is predicted from position k-1 and enters the
+ * branch-averaged loss with factor a_s * mask[s,k] / B, so the tree weight of
+ * target row t is  w_t = (1/B) * sum of a_s over the sequences s through t
+ * whose token at depth(t) is unmasked  -- summed in double over sequences in
+ * input order, divided once, rounded once to float32.  Weights may be
+ * negative.  With seq_scale == NULL (all 1) and token_mask == NULL (all kept)
+ * this is n_pass / B, bit for bit tree_export's tgt_w.
+ *   seq_scale   host [n_seqs] float32 (finite), or NULL
+ *   token_mask  host [seq_tokens] uint8 in input order (nonzero = in the
+ *               loss), or NULL; entries at k = 0 of a sequence are ignored
+ *   tgt_w       host [n_targets] float32 output, in tree_export's tgt_dfs order
+ * Errors: TT_EINVAL (NULL tree or output, non-finite scale).  Host only.
+ */
+int tree_target_weights(const tt_tree* tree, const float* seq_scale, const uint8_t* token_mask, float* tgt_w);
+
+/*
  * Device plan: depth[], end[] and the tile schedule (per q-block list of
  * non-empty k-blocks tagged FULL or PARTIAL; per k-block the contiguous range
  * of query rows that see it; largest-first launch orders).
@@ -284,6 +304,7 @@ typedef struct {
   int64_t bwd_calls;     /* attention calls of one backward traversal */
   int64_t pad_rows;      /* ancestor query rows recomputed per traversal (64-alignment of calls) */
   int64_t query_rows;    /* rows the calls compute in total: N + pad_rows */
+  int64_t pad_pairs;     /* visible (query, key) pairs per head of the pad rows: recompute cost */
 } tt_path_info;
 
 int tree_path_build(const tt_tree* tree, int32_t chunk, int32_t order, tt_path** out);

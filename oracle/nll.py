@@ -102,3 +102,48 @@ def lmhead_rows(hidden_rows, w_vocab, targets):
             dz[x] -= w
         out.append((lse, lps, dz, dz @ W.T))
     return out
+
+
+def rl_weights(seq_pos_to_dfs, seq_lens, N, seq_scale=None, token_mask=None):
+    """Per-row target weights for per-sequence scalars and per-token masks (fp64).
+
+    AReaL-DTA (arXiv 2602.00482), summary page, Main Findings and Why This
+    Matters: the method is used for RL post-training (GRPO), where each rollout
+    carries its own scalar (its advantage) and prompt tokens carry no loss.
+    Reading: token k >= 1 of sequence s, predicted from position k-1, enters
+    the branch loss with factor a_s * mask[s,k]; the tree weight of row t is
+    w_t = (1/B) * sum over sequences s through t with mask[s, depth t] = 1 of
+    a_s.  Sums run over sequences in input order.  Returns w [N] (0 at roots)."""
+    B = len(seq_lens)
+    w = np.zeros(N, dtype=np.float64)
+    off = 0
+    for s, L in enumerate(seq_lens):
+        a = 1.0 if seq_scale is None else float(seq_scale[s])
+        for k in range(1, L):
+            if token_mask is None or token_mask[off + k]:
+                w[seq_pos_to_dfs[off + k]] += a
+        off += L
+    return w / B if B else w
+
+
+def branch_loss_rl(nodes_of, token, logits, seq_scale=None, token_mask=None):
+    """(1/B) * sum_s a_s * sum_{k>=1, mask[s,k]} -log softmax(z[node(s,k-1)])[x_{s,k}] and its dZ (fp64)."""
+    z = np.asarray(logits, dtype=np.float64)
+    lse = _lse(z)
+    soft = np.exp(z - lse[:, None])
+    B = len(nodes_of)
+    loss = 0.0
+    dz = np.zeros_like(z)
+    off = 0
+    for s, nodes in enumerate(nodes_of):
+        a = 1.0 if seq_scale is None else float(seq_scale[s])
+        for k in range(1, len(nodes)):
+            if token_mask is not None and not token_mask[off + k]:
+                continue
+            r = nodes[k - 1]
+            x = int(token[nodes[k]])
+            loss += -a * (z[r, x] - lse[r]) / B
+            dz[r] += a * soft[r] / B
+            dz[r, x] -= a / B
+        off += len(nodes)
+    return loss, dz

@@ -26,7 +26,7 @@ EXPORTED = ("tree_build", "tree_free", "tree_info", "tree_export", "tree_plan_by
             "tree_plan_copy",
             "tree_attn_workspace_bytes", "tree_attn_fwd", "tree_attn_bwd", "tree_nll_workspace_bytes",
             "tree_weighted_nll", "tt_last_error", "tt_timing_enable", "tt_timing_collect",
-            "tree_path_build", "tree_path_free", "tree_path_info", "tree_path_segments", "tree_path_workspace_bytes",
+            "tree_target_weights", "tree_path_build", "tree_path_free", "tree_path_info", "tree_path_segments", "tree_path_workspace_bytes",
             "tree_attn_path")
 
 
@@ -91,7 +91,7 @@ _LIB = None
 class PathInfo(ctypes.Structure):
     _fields_ = [("n_segments", ctypes.c_int32), ("max_path", ctypes.c_int32), ("chunk", ctypes.c_int32),
                 ("order", ctypes.c_int32), ("fwd_calls", ctypes.c_int64), ("bwd_calls", ctypes.c_int64),
-                ("pad_rows", ctypes.c_int64), ("query_rows", ctypes.c_int64)]
+                ("pad_rows", ctypes.c_int64), ("query_rows", ctypes.c_int64), ("pad_pairs", ctypes.c_int64)]
 
 
 class PathArgs(ctypes.Structure):
@@ -119,6 +119,8 @@ def _setup(lib):
     lib.tree_attn_bwd.argtypes = [ctypes.POINTER(AttnBwdArgs), ctypes.c_void_p]
     lib.tree_nll_workspace_bytes.argtypes = [ctypes.POINTER(NllArgs), ctypes.POINTER(ctypes.c_size_t)]
     lib.tree_weighted_nll.argtypes = [ctypes.POINTER(NllArgs), ctypes.c_void_p]
+    lib.tree_target_weights.argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_float),
+                                        ctypes.POINTER(ctypes.c_uint8), ctypes.POINTER(ctypes.c_float)]
     lib.tree_path_build.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(ctypes.c_void_p)]
     lib.tree_path_free.argtypes = [ctypes.c_void_p]
     lib.tree_path_free.restype = None
@@ -220,6 +222,20 @@ class Tree:
         arr = TreeArrays(**{k: _ptr(v, ctypes.c_float if v.dtype == np.float32 else ctypes.c_int32)
                             for k, v in out.items()})
         _check(lib().tree_export(self.handle, ctypes.byref(arr)))
+        return out
+
+    def target_weights(self, seq_scale=None, token_mask=None):
+        """Target weights [n_targets] (tgt_dfs order) for per-sequence scalars and per-token masks."""
+        out = np.zeros(self.info["n_targets"], dtype=np.float32)
+        sc = None if seq_scale is None else np.ascontiguousarray(seq_scale, dtype=np.float32)
+        mk = None if token_mask is None else np.ascontiguousarray(token_mask, dtype=np.uint8)
+        if sc is not None and sc.shape != (self.info["n_seqs"],):
+            raise ValueError("seq_scale must have one entry per sequence")
+        if mk is not None and mk.shape != (self.info["seq_tokens"],):
+            raise ValueError("token_mask must have one entry per input token")
+        _check(lib().tree_target_weights(self.handle, None if sc is None else _ptr(sc, ctypes.c_float),
+                                         None if mk is None else _ptr(mk, ctypes.c_uint8),
+                                         _ptr(out, ctypes.c_float)))
         return out
 
     def plan_bytes(self):

@@ -27,6 +27,7 @@ struct tt_tree {
   std::vector<int32_t> token, depth, end, parent, n_pass;
   std::vector<float> weight;
   std::vector<int32_t> seq_pos_to_dfs;
+  std::vector<int64_t> seq_off;  // [B+1] input sequence offsets
   std::vector<int32_t> tgt_row_ptr, tgt_dfs;
   // schedule
   int32_t bq = 64, bk = 64, nqb = 0, nkb = 0;
@@ -53,6 +54,6 @@ struct tt_path {
   int32_t chunk = 2048, order = 0, max_path = 0;
   std::vector<Seg> segs;
   std::vector<int32_t> events;
-  int64_t fwd_calls = 0, bwd_calls = 0, pad_rows = 0;
+  int64_t fwd_calls = 0, bwd_calls = 0, pad_rows = 0, pad_pairs = 0;
   ~tt_path();
 };

@@ -94,7 +94,9 @@ extern "C" int tree_path_build(const tt_tree* t, int32_t chunk, int32_t order, t
     for (const auto& sg : p->segs)
       for_chunks(sg.depth0, sg.depth0 + sg.len, chunk, [&](int32_t c0, int32_t) {
         ++p->fwd_calls;
-        p->pad_rows += c0 % 64;
+        const int64_t qo = c0 & ~63;
+        p->pad_rows += c0 - qo;
+        p->pad_pairs += (int64_t(c0) * (c0 + 1) - qo * (qo + 1)) / 2;  // sum over rows r in [qo, c0) of r + 1
       });
     p->bwd_calls = p->fwd_calls;
     // the chain of the longest path: its plan serves every call
@@ -129,6 +131,7 @@ extern "C" int tree_path_info(const tt_path* p, tt_path_info* out) {
   out->bwd_calls = p->bwd_calls;
   out->pad_rows = p->pad_rows;
   out->query_rows = int64_t(p->tree->N) + p->pad_rows;
+  out->pad_pairs = p->pad_pairs;
   return TT_OK;
 }
 

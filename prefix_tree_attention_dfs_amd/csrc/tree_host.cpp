@@ -7,6 +7,7 @@
 // AReaL-DTA (arXiv 2602.00482) summary, Key Contributions 3: rollouts are
 // sorted into one prefix tree in lexicographic DFS order.
 #include <algorithm>
+#include <cmath>
 #include <cstring>
 #include <limits>
 #include <new>
@@ -169,6 +170,7 @@ int build(const int32_t* tokens, const int64_t* offs, int32_t B, tt_tree* t) {
   const int64_t total = offs[B];
   t->B = B;
   t->seq_tokens = total;
+  t->seq_off.assign(offs, offs + B + 1);
   // 1. trie insertion, nodes numbered in insertion order
   ChildMap map(static_cast<size_t>(total));
   std::vector<int32_t> ntok, npar, nterm;
@@ -373,6 +375,25 @@ extern "C" int tree_export(const tt_tree* t, const tt_tree_arrays* d) {
     if (d->tgt_token) d->tgt_token[i] = t->token[size_t(t->tgt_dfs[i])];
     if (d->tgt_w) d->tgt_w[i] = t->weight[size_t(t->tgt_dfs[i])];
   }
+  return TT_OK;
+}
+
+extern "C" int tree_target_weights(const tt_tree* t, const float* seq_scale, const uint8_t* token_mask,
+                                   float* tgt_w) {
+  tt::clear_error();
+  if (!t || !tgt_w) return tt::fail(TT_EINVAL, "tree_target_weights: NULL argument");
+  if (seq_scale)
+    for (int32_t s = 0; s < t->B; ++s)
+      if (!std::isfinite(seq_scale[s])) return tt::fail(TT_EINVAL, "tree_target_weights: seq_scale must be finite");
+  // sums in double over sequences in input order, one division, one rounding to float
+  std::vector<double> acc(size_t(t->N), 0.0);
+  for (int32_t s = 0; s < t->B; ++s) {
+    const double a = seq_scale ? double(seq_scale[s]) : 1.0;
+    for (int64_t k = t->seq_off[size_t(s)] + 1; k < t->seq_off[size_t(s) + 1]; ++k)
+      if (!token_mask || token_mask[k]) acc[size_t(t->seq_pos_to_dfs[size_t(k)])] += a;
+  }
+  const double B = double(t->B);
+  for (size_t i = 0; i < t->tgt_dfs.size(); ++i) tgt_w[i] = float(acc[size_t(t->tgt_dfs[i])] / B);
   return TT_OK;
 }
 

@@ -5,7 +5,7 @@ import torch
 
 import prefix_tree_attention_dfs_amd as tt
 import treesynth as ts
-from oracle.nll import tree_loss, branch_loss
+from oracle.nll import tree_loss, branch_loss, branch_loss_rl
 from oracle.tree import dfs_arrays
 from tests.gpu_util import rel_err, f32_input, bf16_input
 
@@ -63,3 +63,27 @@ def test_in_place_and_duplicates_fp32():
     out = tt.tree_weighted_nll(rp, ids, w, logits=zc, d_logits=zc)
     assert abs(out["loss"].item() - loss) / abs(loss) < 1e-5
     assert rel_err(zc, want) < 1e-5
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_rl_weights_logits_mode(dtype):
+    """Per-sequence advantages (either sign) and prompt masks through tree_target_weights
+    and the NLL kernel equal the scaled, masked per-branch loss of the oracle."""
+    case = ts.rl_forest(5, n_trees=2, prompt=40, rollouts=4, turns=2, turn_len=(10, 30), vocab=512)
+    tree = tt.Tree(case.seqs)
+    o = dfs_arrays(case.seqs)
+    a = tree.export()
+    rng = np.random.default_rng(11)
+    adv = rng.standard_normal(len(case.seqs)).astype(np.float32)
+    mask = np.concatenate([(np.arange(len(s)) >= 40).astype(np.uint8) for s in case.seqs])  # prompt masked
+    tw = torch.from_numpy(tree.target_weights(adv, mask)).cuda()
+    rp = torch.from_numpy(a["tgt_row_ptr"]).cuda()
+    tid = torch.from_numpy(a["tgt_token"]).cuda()
+    V = 512
+    z, zn = (f32_input if dtype == torch.float32 else bf16_input)(ts.rng_for(12), (tree.N, V))
+    print(f"N={tree.N} targets={len(a['tgt_dfs'])} dtype={dtype}", flush=True)
+    out = tt.tree_weighted_nll(rp, tid, tw, logits=z)
+    lb, dzb = branch_loss_rl(o["nodes_of"], o["token"], zn, adv, mask)
+    tol = 1e-5 if dtype == torch.float32 else 2e-2
+    assert abs(out["loss"].item() - lb) / abs(lb) < tol, (out["loss"].item(), lb)
+    assert rel_err(out["d_logits"], dzb) < tol

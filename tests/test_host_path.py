@@ -83,15 +83,17 @@ def _check(seqs, chunk, order):
             want = sorted(want, key=lambda k: -size(k))  # stable: ties stay in row order
         assert kids == want
     # chunk accounting
-    calls = pad = 0
+    calls = pad = pad_pairs = 0
     for k in range(S):
         c0, c1 = s["depth0"][k], s["depth0"][k] + s["len"][k]
         while c0 < c1:
             calls += 1
             pad += c0 % 64
+            pad_pairs += sum(r + 1 for r in range(c0 - c0 % 64, c0))  # a pad row at position r sees r + 1 keys
             c0 = min(c1, (c0 // chunk + 1) * chunk)
     assert inf["fwd_calls"] == inf["bwd_calls"] == calls
     assert inf["pad_rows"] == pad and inf["query_rows"] == N + pad
+    assert inf["pad_pairs"] == pad_pairs
     return p
 
 
