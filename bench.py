@@ -265,6 +265,38 @@ def per_branch_dense(tt, ts, tree, case, q, k, v, do, steps):
                 branch_tokens_per_s=round(branch_tokens / ms * 1e3))
 
 
+def compression_study(tt, ts, steps):
+    """Where the tree stops paying off: 8 branches of 8192 tokens sharing a
+    prefix of p tokens, p from 7168 down to 0 (compression to exactly 1).
+    Tree mode (one fwd+bwd over the tree) against the same kernels per branch
+    (AReaL-DTA summary, Main Findings: gains shrink as sharing falls)."""
+    import types
+    import torch
+    B, L, hq, hkv, d = 8, 8192, 32, 8, 128
+    points = []
+    for p in (7168, 6144, 4096, 2048, 1024, 512, 0):
+        prefix = list(range(p))
+        seqs = [prefix + [200000 + b * L + j for j in range(L - p)] for b in range(B)]
+        tree = tt.Tree(seqs)
+        plan = tree.upload_plan()
+        q, k, v, do = _make_inputs(tree.N, hq, hkv, d, 21)
+        st = Step(tt, tree, plan, q, k, v, do)
+
+        def step():
+            st.fwd()
+            st.bwd()
+
+        ms = _time(step, max(2, steps // 2), 1)
+        dense = per_branch_dense(tt, ts, tree, types.SimpleNamespace(seqs=seqs), q, k, v, do, steps)
+        inf = tree.info
+        points.append(dict(shared_prefix=p, compression=round(B * L / tree.N, 3), unique_tokens=tree.N,
+                           tree_ms=round(ms, 3), dense_ms=dense["ms"], tree_speedup=round(dense["ms"] / ms, 3),
+                           pair_ratio=round(inf["dense_pairs"] / inf["pairs"], 3)))
+        del st, q, k, v, do, tree, plan
+        torch.cuda.empty_cache()
+    return points
+
+
 def cpu_baseline(ts, case, seed, budget_s):
     """The fp64 oracle on sampled rows of the same tree: per-row forward and dQ
     (each row from the branch ending at it), rows drawn uniformly at random."""
@@ -322,6 +354,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-dense", action="store_true", help="skip the per-branch dense comparison")
     ap.add_argument("--no-path", action="store_true", help="skip the path-mode walk of the headline tree")
+    ap.add_argument("--study", action="store_true",
+                    help="only run the compression sweep (tree vs per-branch dense) and print it")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (counter calibration)")
     args = ap.parse_args()
@@ -344,6 +378,11 @@ def main():
     import treesynth as ts
 
     torch.cuda.set_device(0)
+    if args.study:
+        print(json.dumps({"study": "compression_sweep", "workload": "8 branches x 8192 tokens, shared prefix p, "
+                          "Hq 32, Hkv 8, d 128, bf16 fwd+bwd", "points": compression_study(tt, ts, args.steps)}),
+              flush=True)
+        return
     t0 = time.perf_counter()
     case = ts.agentic_beam_tree(args.seed)
     gen_s = time.perf_counter() - t0
