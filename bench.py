@@ -31,8 +31,8 @@ METRIC = "tree attn fwd+bwd unique tokens/s + useful TFLOP/s (% bf16 MFMA peak),
 # HBM traffic of the roofline kernel from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE
 # runs (scaled by the same counters' reading for a plain copy of known size),
 # valid only for the kernel source it was measured on.
-MEASURED_TRAFFIC = {"kernel": "attn_bwd_dkdv_mfma", "source_sha1": "19947779c6d6342a6c45304610f5ed6ebb118605",
-                    "bytes_per_launch": 35007894732}
+MEASURED_TRAFFIC = {"kernel": "attn_bwd_dkdv_mfma", "source_sha1": "a745c45817eee58f6ead75f415b9649a8542e8c2",
+                    "bytes_per_launch": 57706502425}
 
 
 def _source_sha(path):

@@ -274,7 +274,10 @@ __global__ __launch_bounds__(KV_THREADS, 2) void dkdv_mfma_kernel(
     voff[u] = (uint32_t(c >> 4) * g.h_q * D + (c & 15) * 8) * 2;
   }
   auto load_tile = [&](int step) {
-    const int qt = qt_first + step / G, head = kvh * G + step % G;
+    // query tiles from the top down: workgroups over a shared prefix have the
+    // same upper end, so they walk the same tiles together and share them in L2
+    const int rev = n_steps - 1 - step;
+    const int qt = qt_first + rev / G, head = kvh * G + rev % G;
     const uint32_t rowh = uint32_t(qt * QT - g.q_off) * g.h_q + head;  // (row, head) of the tile's first row
 #pragma unroll
     for (int u = 0; u < QCH; ++u) {
@@ -310,7 +313,7 @@ __global__ __launch_bounds__(KV_THREADS, 2) void dkdv_mfma_kernel(
   const uint16_t* Vt = L.run.V + (ks * 32 + r) * KSTR + 8 * hh;
   for (int step = 0; step < n_steps; ++step) {
     const int sidx = step & 1;
-    const int qt = qt_first + step / G;
+    const int qt = qt_first + (n_steps - 1 - step) / G;
     if (step + 1 < n_steps) load_tile(step + 1);
     const KvStage& S = L.run.st[sidx];
     const int q0 = qt * QT + mt * 32;  // tree row of this wave's first query
