@@ -31,13 +31,16 @@ METRIC = "tree attn fwd+bwd unique tokens/s + useful TFLOP/s (% bf16 MFMA peak),
 # HBM traffic of the roofline kernel from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE
 # runs (scaled by the same counters' reading for a plain copy of known size),
 # valid only for the kernel source it was measured on.
-MEASURED_TRAFFIC = {"kernel": "attn_bwd_dkdv_mfma", "source_sha1": "a745c45817eee58f6ead75f415b9649a8542e8c2",
-                    "bytes_per_launch": 57706502425}
+MEASURED_TRAFFIC = {"kernel": "attn_bwd_dkdv_mfma", "source_sha1": "0e879ba0d2a314e7e50efac3bc784e7c20772e5f",
+                    "bytes_per_launch": 20831060180}
 
 
 def _source_sha(path):
-    with open(path, "rb") as f:
-        return hashlib.sha1(f.read()).hexdigest()
+    """sha1 of a kernel source's code: // comments and blank lines removed, so
+    that a comment edit does not invalidate a traffic measurement."""
+    with open(path, encoding="utf-8") as f:
+        lines = [ln.split("//", 1)[0].rstrip() for ln in f]
+    return hashlib.sha1("\n".join(ln for ln in lines if ln).encode()).hexdigest()
 
 
 def _bf16(t):

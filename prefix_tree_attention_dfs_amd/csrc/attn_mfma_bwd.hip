@@ -11,10 +11,12 @@
 //                    non-empty key tiles):  S^T = K Q^T, P^T, dP^T = V dO^T,
 //                    dS^T = P^T (dP^T - D), dQ^T += K^T dS^T.
 //   dkdv_mfma_kernel key-stationary: one workgroup per 128 keys x kv head,
-//                    each wave owns 32 keys (K, V in registers) and walks the
-//                    contiguous range of query rows that see those keys, for
-//                    every query head of the group:  S = Q K^T, P, dP = dO V^T,
-//                    dS, dV^T += dO^T P, dK^T += Q^T dS.
+//                    K and V of those keys loaded once into LDS; 8 waves =
+//                    4 key slices of 32 x 2 query halves.  It streams 64-row
+//                    Q / dO tiles of every query head of the group over the
+//                    contiguous range of query rows that see its keys, top
+//                    down:  S = Q K^T, P, dP = dO V^T, dS, dV^T += dO^T P,
+//                    dK^T += Q^T dS.
 // Recomputing S and dP in both kernels costs 14 d MFMA flops per visible pair
 // instead of 10 d, in exchange for no fp32 atomic traffic on dQ.
 #include "device.h"
