@@ -23,13 +23,19 @@ namespace {
 
 constexpr int GBM = 256, GBN = 256, GBK = 64;
 constexpr int GTHREADS = 256;
-constexpr int KROW = GBK + 8;    // stride (elements) of tiles whose rows run along k
-constexpr int XROW = GBN + 16;   // stride (elements) of tiles whose rows run along m or n
+// LDS row strides (elements), chosen for gfx950's 64 banks: 16-byte reads are
+// served 16 lanes per cycle, 8-byte and transposed reads 32 lanes per cycle.
+constexpr int KROW = GBK + 8;    // rows along k, read 16 bytes per lane (144-byte rows)
+constexpr int KROW8 = GBK + 4;   // rows along k, read 8 bytes per lane (136 bytes: 32 rows on distinct banks)
+constexpr int XROW = GBN + 32;   // rows along m or n, read transposed (576 bytes: 4 rows x 64 bytes on distinct banks)
 
 template <bool A_T, bool B_T>
 struct GemmLds {
-  // A tile: [GBM][KROW] (m rows, k contiguous) or [GBK][XROW] (k rows, m contiguous)
-  static constexpr int A_ELEMS = A_T ? GBK * XROW : GBM * KROW;
+  static constexpr bool PERM = A_T || !B_T;  // some operand is read transposed: permuted reduction order
+  static constexpr int A_STRIDE = A_T ? XROW : (PERM ? KROW8 : KROW);
+  static constexpr int B_STRIDE = B_T ? KROW : XROW;
+  // A tile: [GBM][A_STRIDE] (m rows, k contiguous) or [GBK][XROW] (k rows, m contiguous)
+  static constexpr int A_ELEMS = A_T ? GBK * XROW : GBM * A_STRIDE;
   static constexpr int B_ELEMS = B_T ? GBN * KROW : GBK * XROW;
 };
 
@@ -62,7 +68,18 @@ __device__ __forceinline__ void store_tile(uint16_t* s, int tid, const bf16x8 (&
     const int c = tid + u * GTHREADS;
     const int row = KROWS ? (c >> 3) : (c >> 5);
     const int col = KROWS ? ((c & 7) << 3) : ((c & 31) << 3);
-    *reinterpret_cast<bf16x8*>(s + row * STRIDE + col) = reg[u];
+    if constexpr (STRIDE % 8 == 0) {
+      *reinterpret_cast<bf16x8*>(s + row * STRIDE + col) = reg[u];
+    } else {  // rows only 8-byte aligned: two 8-byte stores
+      bf16x4 lo, hi;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        lo[e] = reg[u][e];
+        hi[e] = reg[u][4 + e];
+      }
+      *reinterpret_cast<bf16x4*>(s + row * STRIDE + col) = lo;
+      *reinterpret_cast<bf16x4*>(s + row * STRIDE + col + 4) = hi;
+    }
   }
 }
 
@@ -102,7 +119,7 @@ __global__ __launch_bounds__(GTHREADS) void gemm_kernel(const uint16_t* __restri
     if (A_T)
       store_tile<false, XROW>(sa, tid, ra);
     else
-      store_tile<true, KROW>(sa, tid, ra);
+      store_tile<true, L::A_STRIDE>(sa, tid, ra);
     if (B_T)
       store_tile<true, KROW>(sb, tid, rb);
     else
@@ -122,7 +139,7 @@ __global__ __launch_bounds__(GTHREADS) void gemm_kernel(const uint16_t* __restri
   }
   __syncthreads();
   // reduction order: natural (8h + s) unless some operand is read transposed
-  constexpr bool PERM = A_T || !B_T;
+  constexpr bool PERM = L::PERM;
   for (int kt = 0; kt < nk; ++kt) {
     const int s = kt & 1;
     if (kt + 1 < nk) gload(int64_t(kt + 1) * GBK);
@@ -137,7 +154,7 @@ __global__ __launch_bounds__(GTHREADS) void gemm_kernel(const uint16_t* __restri
         if (A_T) {
           af[i] = tr_frag(a_s, XROW, ks * 16, mrow, lane);
         } else if (PERM) {
-          const uint16_t* p = a_s + (mrow + r) * KROW + ks * 16 + 4 * hh;
+          const uint16_t* p = a_s + (mrow + r) * L::A_STRIDE + ks * 16 + 4 * hh;
           const bf16x4 lo = *reinterpret_cast<const bf16x4*>(p);
           const bf16x4 hi = *reinterpret_cast<const bf16x4*>(p + 8);
 #pragma unroll
@@ -146,7 +163,7 @@ __global__ __launch_bounds__(GTHREADS) void gemm_kernel(const uint16_t* __restri
             af[i][4 + e] = hi[e];
           }
         } else {
-          af[i] = lds_read16(a_s + (mrow + r) * KROW + ks * 16 + 8 * hh);
+          af[i] = lds_read16(a_s + (mrow + r) * L::A_STRIDE + ks * 16 + 8 * hh);
         }
       }
 #pragma unroll
