@@ -86,3 +86,48 @@ def test_path_chain_equals_chunked_chain():
     dQr, dKr, dVr = OA.backward(o, qn, kn, vn, don)
     for n, g_, r_ in (("o", O, Or), ("lse", L, Lr), ("dq", dq, dQr), ("dk", dk, dKr), ("dv", dv, dVr)):
         assert rel_err(g_, r_) < 2e-2, (n, rel_err(g_, r_))
+
+
+def _gpu_rel(a, b):
+    """max |a - b| / max |b| over whole tensors, computed on the GPU in fp32."""
+    a, b = a.float(), b.float()
+    return ((a - b).abs().max() / b.abs().max().clamp_min(1e-30)).item()
+
+
+def test_path_agentic_8b_shape_vs_tree_mode_and_sampled_oracle():
+    """The 8B-shape agentic tree at full size, walked at the bench's chunk
+    (2048): every output equals tree mode's; sampled rows and keys equal the
+    oracle's per-branch values."""
+    case = ts.agentic_beam_tree(0)
+    tree = tt.Tree(case.seqs)
+    o = dfs_arrays(case.seqs)
+    N = tree.N
+    rng = ts.rng_for(2100)
+    qb = ts.normal_bf16(rng, (N, 32, 128), 128 ** -0.5)
+    kb = ts.normal_bf16(rng, (N, 8, 128), 128 ** -0.5)
+    vb = ts.normal_bf16(rng, (N, 8, 128), 128 ** -0.5)
+    ob = ts.normal_bf16(rng, (N, 32, 128), 1.0)
+    dev = lambda b: torch.from_numpy(b.view(np.int16)).cuda().view(torch.bfloat16)  # noqa: E731
+    q, k, v, do = dev(qb), dev(kb), dev(vb), dev(ob)
+    path = tt.Path(tree, 2048, 0)
+    print(f"N={N} segments={path.info['n_segments']} calls={path.info['fwd_calls']}", flush=True)
+    O, L, dq, dk, dv = tt.tree_attn_path(path, q, k, v, d_o=do)
+    plan = tree.upload_plan()
+    Ot, Lt = tt.tree_attn_fwd(tree, plan, q, k, v)
+    dqt, dkt, dvt = tt.tree_attn_bwd(tree, plan, q, k, v, Ot, Lt, do)
+    for n, a, b in (("o", O, Ot), ("lse", L, Lt), ("dq", dq, dqt), ("dk", dk, dkt), ("dv", dv, dvt)):
+        assert _gpu_rel(a, b) < 1e-2, (n, _gpu_rel(a, b))
+
+    def get(name, idx):
+        return ts.bf16_bits_to_f64({"q": qb, "k": kb, "v": vb, "do": ob}[name][idx])
+
+    rows = np.unique(np.concatenate([np.linspace(0, N - 1, 10).astype(int), [0, N - 1]]))
+    ri = torch.as_tensor(rows, device="cuda")
+    Or, Lr = OA.forward_rows(o, None, None, None, rows, get=get)
+    assert rel_err(O[ri], Or) < 2e-2 and rel_err(L[ri], Lr) < 2e-2
+    assert rel_err(dq[ri], OA.dq_rows(o, None, None, None, None, rows, get=get)) < 2e-2
+    small = np.nonzero(o["end"] - np.arange(N) <= 40)[0]
+    keys = small[np.linspace(0, len(small) - 1, 5).astype(int)]
+    rk, rv = OA.dkdv_keys(o, None, None, None, None, keys, get=get)
+    ki = torch.as_tensor(keys, device="cuda")
+    assert rel_err(dk[ki], rk) < 2e-2 and rel_err(dv[ki], rv) < 2e-2
