@@ -357,6 +357,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-dense", action="store_true", help="skip the per-branch dense comparison")
     ap.add_argument("--no-path", action="store_true", help="skip the path-mode walk of the headline tree")
+    ap.add_argument("--lmhead-only", action="store_true",
+                    help="only run the lm-head measurement and print it (for profiling its kernels)")
     ap.add_argument("--study", action="store_true",
                     help="only run the compression sweep (tree vs per-branch dense) and print it")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -381,6 +383,9 @@ def main():
     import treesynth as ts
 
     torch.cuda.set_device(0)
+    if args.lmhead_only:
+        print(json.dumps({"lmhead_weighted_nll": lmhead_bench(tt, ts, args.steps)}), flush=True)
+        return
     if args.study:
         print(json.dumps({"study": "compression_sweep", "workload": "8 branches x 8192 tokens, shared prefix p, "
                           "Hq 32, Hkv 8, d 128, bf16 fwd+bwd", "points": compression_study(tt, ts, args.steps)}),

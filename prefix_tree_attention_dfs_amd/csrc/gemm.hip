@@ -6,8 +6,10 @@
 //   dH = dZ W^T        (NT: A = dZ [M][K'], B stored [N][K'] = W)
 //   dW = H^T dZ        (TN: A stored [K][M] = H, B = dZ [K][N])
 //
-// Block tile 256 x 256, k-step 64, 4 waves of 128 x 128 (4 x 4 tiles of
-// v_mfma_f32_32x32x16_bf16), double-buffered LDS.  Operands whose reduction
+// Block tile 256 x 256, k-step 64, 8 waves of 128 x 64 (4 x 2 tiles of
+// v_mfma_f32_32x32x16_bf16, 128 accumulator registers), so that two waves
+// share each SIMD and one issues products while the other waits on loads,
+// the barrier or the epilogue; double-buffered LDS.  Operands whose reduction
 // index is contiguous in memory are read with ds_read_b128 (or two b64 reads
 // matching the permuted reduction order below); operands stored with the
 // reduction index strided are read with ds_read_tr16_b64, which returns rows
@@ -22,7 +24,8 @@ using namespace ttm;
 namespace {
 
 constexpr int GBM = 256, GBN = 256, GBK = 64;
-constexpr int GTHREADS = 256;
+constexpr int GTHREADS = 512;  // 8 waves: 2 (m) x 4 (n), each 128 x 64
+constexpr int WTN = 2;         // 32-column tiles per wave
 // LDS row strides (elements), chosen for gfx950's 64 banks: 16-byte reads are
 // served 16 lanes per cycle, 8-byte and transposed reads 32 lanes per cycle.
 constexpr int KROW = GBK + 8;    // rows along k, read 16 bytes per lane (144-byte rows)
@@ -45,10 +48,10 @@ struct GemmLds {
 // chunk is either wholly inside or wholly outside the matrix.
 template <bool KROWS>  // true: tile rows are the matrix rows (k contiguous, 64 wide)
 __device__ __forceinline__ void load_tile(const uint16_t* __restrict__ X, int64_t ld, int64_t r0, int64_t c0,
-                                          int64_t nrows, int64_t ncols, int tid, bf16x8 (&reg)[8]) {
+                                          int64_t nrows, int64_t ncols, int tid, bf16x8 (&reg)[4]) {
   // KROWS: tile = 256 rows x 64 cols (8 chunks per row); else 64 rows x 256 cols (32 chunks per row)
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
+  for (int u = 0; u < 4; ++u) {
     const int c = tid + u * GTHREADS;
     const int row = KROWS ? (c >> 3) : (c >> 5);
     const int col = KROWS ? ((c & 7) << 3) : ((c & 31) << 3);
@@ -62,9 +65,9 @@ __device__ __forceinline__ void load_tile(const uint16_t* __restrict__ X, int64_
 }
 
 template <bool KROWS, int STRIDE>
-__device__ __forceinline__ void store_tile(uint16_t* s, int tid, const bf16x8 (&reg)[8]) {
+__device__ __forceinline__ void store_tile(uint16_t* s, int tid, const bf16x8 (&reg)[4]) {
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
+  for (int u = 0; u < 4; ++u) {
     const int c = tid + u * GTHREADS;
     const int row = KROWS ? (c >> 3) : (c >> 5);
     const int col = KROWS ? ((c & 7) << 3) : ((c & 31) << 3);
@@ -92,7 +95,7 @@ __global__ __launch_bounds__(GTHREADS) void gemm_kernel(const uint16_t* __restri
   extern __shared__ __align__(16) uint16_t smem[];
   constexpr int STAGE = L::A_ELEMS + L::B_ELEMS;  // stage s: A at s*STAGE, B right after
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r = lane & 31, hh = lane >> 5;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 2, wn = wave & 3;
   // block -> tile; consecutive blocks share a B column panel
   const int tm = blockIdx.x % ((M + GBM - 1) / GBM);
   const int tn = blockIdx.x / ((M + GBM - 1) / GBM);
@@ -102,7 +105,7 @@ __global__ __launch_bounds__(GTHREADS) void gemm_kernel(const uint16_t* __restri
   const int64_t lda = A_T ? M : K;  // A stored [M][K] or [K][M]
   const int64_t ldb = B_T ? K : N;  // B stored [K][N] or [N][K]
 
-  bf16x8 ra[8], rb[8];
+  bf16x8 ra[4], rb[4];
   auto gload = [&](int64_t k0) {
     if (A_T)
       load_tile<false>(A, lda, k0, m0, K, M, tid, ra);
@@ -126,11 +129,11 @@ __global__ __launch_bounds__(GTHREADS) void gemm_kernel(const uint16_t* __restri
       store_tile<false, XROW>(sb, tid, rb);
   };
 
-  f32x16 acc[4][4];
+  f32x16 acc[4][WTN];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = zero16();
+    for (int j = 0; j < WTN; ++j) acc[i][j] = zero16();
 
   const int nk = int((K + GBK - 1) / GBK);
   if (nk > 0) {
@@ -147,7 +150,7 @@ __global__ __launch_bounds__(GTHREADS) void gemm_kernel(const uint16_t* __restri
     const uint16_t* b_s = a_s + L::A_ELEMS;
 #pragma unroll
     for (int ks = 0; ks < GBK / 16; ++ks) {
-      bf16x8 af[4], bfr[4];
+      bf16x8 af[4], bfr[WTN];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int mrow = wm * 128 + i * 32;
@@ -167,8 +170,8 @@ __global__ __launch_bounds__(GTHREADS) void gemm_kernel(const uint16_t* __restri
         }
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int ncol = wn * 128 + j * 32;
+      for (int j = 0; j < WTN; ++j) {
+        const int ncol = wn * 64 + j * 32;
         if (B_T)
           bfr[j] = lds_read16(b_s + (ncol + r) * KROW + ks * 16 + 8 * hh);
         else
@@ -177,7 +180,7 @@ __global__ __launch_bounds__(GTHREADS) void gemm_kernel(const uint16_t* __restri
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma(af[i], bfr[j], acc[i][j]);
+        for (int j = 0; j < WTN; ++j) acc[i][j] = mfma(af[i], bfr[j], acc[i][j]);
     }
     if (kt + 1 < nk) sstore(s ^ 1);
     __syncthreads();
@@ -187,8 +190,8 @@ __global__ __launch_bounds__(GTHREADS) void gemm_kernel(const uint16_t* __restri
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t n = n0 + wn * 128 + j * 32 + r;
+    for (int j = 0; j < WTN; ++j) {
+      const int64_t n = n0 + wn * 64 + j * 32 + r;
       if (n >= N) continue;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
