@@ -6,10 +6,10 @@
 //   dH = dZ W^T        (NT: A = dZ [M][K'], B stored [N][K'] = W)
 //   dW = H^T dZ        (TN: A stored [K][M] = H, B = dZ [K][N])
 //
-// Block tile 256 x 256, k-step 64, 8 waves of 128 x 64 (4 x 2 tiles of
-// v_mfma_f32_32x32x16_bf16, 128 accumulator registers), so that two waves
-// share each SIMD and one issues products while the other waits on loads,
-// the barrier or the epilogue; double-buffered LDS.  Operands whose reduction
+// Block tile 256 x 256, k-step 64, 16 waves of 64 x 64 (2 x 2 tiles of
+// v_mfma_f32_32x32x16_bf16, 64 accumulator registers, at most 128 VGPRs), so
+// that four waves share each SIMD and some issue products while others wait
+// on loads, the barrier or the epilogue; double-buffered LDS.  Operands whose reduction
 // index is contiguous in memory are read with ds_read_b128 (or two b64 reads
 // matching the permuted reduction order below); operands stored with the
 // reduction index strided are read with ds_read_tr16_b64, which returns rows
@@ -24,8 +24,9 @@ using namespace ttm;
 namespace {
 
 constexpr int GBM = 256, GBN = 256, GBK = 64;
-constexpr int GTHREADS = 512;  // 8 waves: 2 (m) x 4 (n), each 128 x 64
-constexpr int WTN = 2;         // 32-column tiles per wave
+constexpr int GTHREADS = 1024;  // 16 waves: 4 (m) x 4 (n), each 64 x 64
+constexpr int WTN = 2;          // 32-column tiles per wave
+constexpr int WTM = 2;          // 32-row tiles per wave
 // LDS row strides (elements), chosen for gfx950's 64 banks: 16-byte reads are
 // served 16 lanes per cycle, 8-byte and transposed reads 32 lanes per cycle.
 constexpr int KROW = GBK + 8;    // rows along k, read 16 bytes per lane (144-byte rows)
@@ -48,10 +49,10 @@ struct GemmLds {
 // chunk is either wholly inside or wholly outside the matrix.
 template <bool KROWS>  // true: tile rows are the matrix rows (k contiguous, 64 wide)
 __device__ __forceinline__ void load_tile(const uint16_t* __restrict__ X, int64_t ld, int64_t r0, int64_t c0,
-                                          int64_t nrows, int64_t ncols, int tid, bf16x8 (&reg)[4]) {
+                                          int64_t nrows, int64_t ncols, int tid, bf16x8 (&reg)[2]) {
   // KROWS: tile = 256 rows x 64 cols (8 chunks per row); else 64 rows x 256 cols (32 chunks per row)
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
+  for (int u = 0; u < 2; ++u) {
     const int c = tid + u * GTHREADS;
     const int row = KROWS ? (c >> 3) : (c >> 5);
     const int col = KROWS ? ((c & 7) << 3) : ((c & 31) << 3);
@@ -65,9 +66,9 @@ __device__ __forceinline__ void load_tile(const uint16_t* __restrict__ X, int64_
 }
 
 template <bool KROWS, int STRIDE>
-__device__ __forceinline__ void store_tile(uint16_t* s, int tid, const bf16x8 (&reg)[4]) {
+__device__ __forceinline__ void store_tile(uint16_t* s, int tid, const bf16x8 (&reg)[2]) {
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
+  for (int u = 0; u < 2; ++u) {
     const int c = tid + u * GTHREADS;
     const int row = KROWS ? (c >> 3) : (c >> 5);
     const int col = KROWS ? ((c & 7) << 3) : ((c & 31) << 3);
@@ -95,7 +96,7 @@ __global__ __launch_bounds__(GTHREADS) void gemm_kernel(const uint16_t* __restri
   extern __shared__ __align__(16) uint16_t smem[];
   constexpr int STAGE = L::A_ELEMS + L::B_ELEMS;  // stage s: A at s*STAGE, B right after
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r = lane & 31, hh = lane >> 5;
-  const int wm = wave >> 2, wn = wave & 3;
+  const int wm = wave >> 2, wn = wave & 3;  // 4 x 4
   // block -> tile; consecutive blocks share a B column panel
   const int tm = blockIdx.x % ((M + GBM - 1) / GBM);
   const int tn = blockIdx.x / ((M + GBM - 1) / GBM);
@@ -105,7 +106,7 @@ __global__ __launch_bounds__(GTHREADS) void gemm_kernel(const uint16_t* __restri
   const int64_t lda = A_T ? M : K;  // A stored [M][K] or [K][M]
   const int64_t ldb = B_T ? K : N;  // B stored [K][N] or [N][K]
 
-  bf16x8 ra[4], rb[4];
+  bf16x8 ra[2], rb[2];
   auto gload = [&](int64_t k0) {
     if (A_T)
       load_tile<false>(A, lda, k0, m0, K, M, tid, ra);
@@ -129,9 +130,9 @@ __global__ __launch_bounds__(GTHREADS) void gemm_kernel(const uint16_t* __restri
       store_tile<false, XROW>(sb, tid, rb);
   };
 
-  f32x16 acc[4][WTN];
+  f32x16 acc[WTM][WTN];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < WTM; ++i)
 #pragma unroll
     for (int j = 0; j < WTN; ++j) acc[i][j] = zero16();
 
@@ -150,10 +151,10 @@ __global__ __launch_bounds__(GTHREADS) void gemm_kernel(const uint16_t* __restri
     const uint16_t* b_s = a_s + L::A_ELEMS;
 #pragma unroll
     for (int ks = 0; ks < GBK / 16; ++ks) {
-      bf16x8 af[4], bfr[WTN];
+      bf16x8 af[WTM], bfr[WTN];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int mrow = wm * 128 + i * 32;
+      for (int i = 0; i < WTM; ++i) {
+        const int mrow = wm * 64 + i * 32;
         if (A_T) {
           af[i] = tr_frag(a_s, XROW, ks * 16, mrow, lane);
         } else if (PERM) {
@@ -178,7 +179,7 @@ __global__ __launch_bounds__(GTHREADS) void gemm_kernel(const uint16_t* __restri
           bfr[j] = tr_frag(b_s, XROW, ks * 16, ncol, lane);
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < WTM; ++i)
 #pragma unroll
         for (int j = 0; j < WTN; ++j) acc[i][j] = mfma(af[i], bfr[j], acc[i][j]);
     }
@@ -188,14 +189,14 @@ __global__ __launch_bounds__(GTHREADS) void gemm_kernel(const uint16_t* __restri
 
   // epilogue: lane holds C[m = 8*(e/4) + 4hh + e%4][n = r] of each 32 x 32 tile
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < WTM; ++i)
 #pragma unroll
     for (int j = 0; j < WTN; ++j) {
       const int64_t n = n0 + wn * 64 + j * 32 + r;
       if (n >= N) continue;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int64_t m = m0 + wm * 128 + i * 32 + 8 * (e >> 2) + 4 * hh + (e & 3);
+        const int64_t m = m0 + wm * 64 + i * 32 + 8 * (e >> 2) + 4 * hh + (e & 3);
         if (m >= M) continue;
         if (OUT == 0)
           static_cast<uint16_t*>(Cv)[m * N + n] = ttd::f2bf(acc[i][j][e]);
