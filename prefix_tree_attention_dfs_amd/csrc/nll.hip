@@ -118,6 +118,124 @@ __global__ __launch_bounds__(kThreads) void nll_rows_kernel(const T* z, T* dz, i
   }
 }
 
+// bf16 rows that fit in registers (vocab <= 8 * kRegThreads * kRegChunks,
+// vocab and ldz multiples of 8): 1024 threads hold the whole row as 16-byte
+// chunks, so Z is read once and dZ written once, both 16 bytes per lane.
+// Same arithmetic as nll_rows_kernel (max, sum of exp, targets, one rounding
+// per dZ element, targets written last from their original logits).
+constexpr int kRegThreads = 1024;
+constexpr int kRegChunks = 19;  // 8 * 1024 * 19 = 155,648 logits per row
+typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+
+__global__ __launch_bounds__(kRegThreads) void nll_rows_reg_kernel(const uint16_t* z, uint16_t* dz, int32_t vocab,
+                                                                   int64_t ldz, const int32_t* __restrict__ row_ptr,
+                                                                   const int32_t* __restrict__ tgt_id,
+                                                                   const float* __restrict__ tgt_w, int32_t n_tgt,
+                                                                   float* __restrict__ logp,
+                                                                   float* __restrict__ row_loss) {
+  __shared__ uint32_t bitmap[kMaxVocab / 32];
+  __shared__ float red_a[kRegThreads / kWave], red_b[kRegThreads / kWave];
+  const int r = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const uint16_t* zr = z + int64_t(r) * ldz;
+  const int nchunk = vocab >> 3;
+  u16x8 x[kRegChunks];
+#pragma unroll
+  for (int c = 0; c < kRegChunks; ++c) {
+    const int ch = c * kRegThreads + tid;
+    if (ch < nchunk) x[c] = *reinterpret_cast<const u16x8*>(zr + 8 * int64_t(ch));
+  }
+  const int words = (vocab + 31) / 32;
+  for (int w = tid; w < words; w += kRegThreads) bitmap[w] = 0u;
+  // pass 1: row max, then sum of exp
+  float m = -INFINITY;
+#pragma unroll
+  for (int c = 0; c < kRegChunks; ++c)
+    if (c * kRegThreads + tid < nchunk)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) m = fmaxf(m, bf2f(x[c][e]));
+  m = wave_max(m);
+  if (lane == 0) red_a[wv] = m;
+  __syncthreads();
+  m = red_a[0];
+  for (int w = 1; w < kRegThreads / kWave; ++w) m = fmaxf(m, red_a[w]);
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < kRegChunks; ++c)
+    if (c * kRegThreads + tid < nchunk)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s += __expf(bf2f(x[c][e]) - m);
+  s = wave_sum(s);
+  __syncthreads();  // red_a reused
+  if (lane == 0) red_b[wv] = s;
+  __syncthreads();
+  s = 0.f;
+  for (int w = 0; w < kRegThreads / kWave; ++w) s += red_b[w];
+  const float lse = m + logf(s);
+  // pass 2: targets -> logp, loss, row weight; mark target positions
+  const int t0 = min(max(row_ptr[r], 0), n_tgt), t1 = min(max(row_ptr[r + 1], t0), n_tgt);
+  float loss = 0.f, W = 0.f;
+  for (int t = t0 + tid; t < t1; t += kRegThreads) {
+    const int xi = tgt_id[t];
+    if (xi < 0 || xi >= vocab) {
+      if (logp) logp[t] = NAN;
+      continue;
+    }
+    const float w = tgt_w[t];
+    const float lp = bf2f(zr[xi]) - lse;
+    if (logp) logp[t] = lp;
+    loss -= w * lp;
+    W += w;
+    atomicOr(&bitmap[xi >> 5], 1u << (xi & 31));
+  }
+  loss = wave_sum(loss);
+  W = wave_sum(W);
+  __syncthreads();  // red_b read above
+  if (lane == 0) {
+    red_a[wv] = loss;
+    red_b[wv] = W;
+  }
+  __syncthreads();
+  loss = 0.f;
+  W = 0.f;
+  for (int w = 0; w < kRegThreads / kWave; ++w) {
+    loss += red_a[w];
+    W += red_b[w];
+  }
+  if (tid == 0) row_loss[r] = loss;
+  if (dz == nullptr) return;
+  uint16_t* dr = dz + int64_t(r) * ldz;
+  // pass 3a: every non-target position, 16 bytes at a time where a chunk holds no target
+#pragma unroll
+  for (int c = 0; c < kRegChunks; ++c) {
+    const int ch = c * kRegThreads + tid;
+    if (ch >= nchunk) continue;
+    const uint32_t bits = (bitmap[ch >> 2] >> ((ch & 3) * 8)) & 0xFFu;  // the chunk's 8 target bits
+    u16x8 y;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) y[e] = f2bf(W * __expf(bf2f(x[c][e]) - lse));
+    if (bits == 0u) {
+      *reinterpret_cast<u16x8*>(dr + 8 * int64_t(ch)) = y;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (!(bits & (1u << e))) dr[8 * int64_t(ch) + e] = y[e];
+    }
+  }
+  __syncthreads();
+  // pass 3b: each distinct target position, claimed by the first thread to clear its bit
+  for (int t = t0 + tid; t < t1; t += kRegThreads) {
+    const int xi = tgt_id[t];
+    if (xi < 0 || xi >= vocab) continue;
+    const uint32_t bit = 1u << (xi & 31);
+    if (!(atomicAnd(&bitmap[xi >> 5], ~bit) & bit)) continue;
+    float ws = 0.f;
+    for (int u = t0; u < t1; ++u)
+      if (tgt_id[u] == xi) ws += tgt_w[u];
+    dr[xi] = f2bf(W * __expf(bf2f(zr[xi]) - lse) - ws);
+  }
+}
+
 __global__ __launch_bounds__(kThreads) void sum_loss_kernel(const float* __restrict__ row_loss, int32_t n,
                                                             float* __restrict__ loss) {
   __shared__ double red[kThreads / kWave];
@@ -143,6 +261,10 @@ int launch_nll_rows(tt_dtype zt, const void* z, void* dz, int32_t n_rows, int32_
   if (zt == TT_F32)
     nll_rows_kernel<float><<<n_rows, kThreads, 0, st>>>((const float*)z, (float*)dz, vocab, ldz, row_ptr, tgt_id,
                                                         tgt_w, n_tgt, logp, row_loss);
+  else if (vocab % 8 == 0 && ldz % 8 == 0 && vocab <= 8 * kRegThreads * kRegChunks &&
+           (reinterpret_cast<uintptr_t>(z) & 15) == 0 && (reinterpret_cast<uintptr_t>(dz) & 15) == 0)
+    nll_rows_reg_kernel<<<n_rows, kRegThreads, 0, st>>>((const uint16_t*)z, (uint16_t*)dz, vocab, ldz, row_ptr,
+                                                        tgt_id, tgt_w, n_tgt, logp, row_loss);
   else
     nll_rows_kernel<uint16_t><<<n_rows, kThreads, 0, st>>>((const uint16_t*)z, (uint16_t*)dz, vocab, ldz, row_ptr,
                                                            tgt_id, tgt_w, n_tgt, logp, row_loss);
