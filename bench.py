@@ -319,9 +319,15 @@ def cpu_baseline(ts, case, seed, budget_s):
         # the same distribution as the GPU inputs, drawn per sampled row set
         return ts.bf16_bits_to_f64(ts.normal_bf16(rng, (len(rows),) + shape_h, std))
 
-    done = 0
-    t0 = time.perf_counter()
-    while time.perf_counter() - t0 < budget_s:
+    def run(budget):
+        done = 0
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < budget:
+            one_row()
+            done += 1
+        return done, time.perf_counter() - t0
+
+    def one_row():
         i = int(rng.integers(0, N))
         br = OA.ancestors(o, i)
         qv = rowbits((32, 128), 128 ** -0.5, br)
@@ -336,10 +342,18 @@ def cpu_baseline(ts, case, seed, budget_s):
 
         OA.forward_rows(o, None, None, None, [i], get=get)
         OA.dq_rows(o, None, None, None, None, [i], get=get)
-        done += 1
-    el = time.perf_counter() - t0
+
+    done, el = run(budget_s)
+    one = None
+    try:  # the same sample on one BLAS thread
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            d1, e1 = run(budget_s / 3)
+        one = round(d1 / e1, 3)
+    except Exception:  # pragma: no cover
+        pass
     return {"value": round(done / el, 3), "unit": "unique tokens/s (forward + dQ only)", "cores": threads,
-            "kind": "oracle",
+            "value_1core": one, "kind": "oracle",
             "sample": f"{done} rows drawn uniformly from the {N}-row agentic tree; per row the oracle's per-branch "
                       f"forward and dQ over all 32 heads (forward_rows + dq_rows, fp64 numpy) in {el:.1f} s; "
                       "dK/dV are not included (the oracle's per-key form costs the key's whole subtree), so this "
@@ -454,7 +468,9 @@ def main():
         "config": {"workload": "8B-class agentic tree fwd+bwd (Hq 32, Hkv 8, d 128, RoPE at depth)",
                    "unique_tokens": N, "seq_tokens": info["seq_tokens"], "leaves": info["n_leaves"],
                    "max_depth": info["max_depth"], "pairs_per_head": P, "seed": args.seed,
-                   "tiles_64x64": info["n_tiles"], "full_tiles": info["n_full_tiles"]},
+                   "tiles_64x64": info["n_tiles"], "full_tiles": info["n_full_tiles"],
+                   "generator": dict(name="agentic_beam_tree", rng="numpy PCG64", seed=case.seed, **case.params),
+                   "tensors": "torch CUDA generator seeded seed+1: q, k, v ~ N(0,1)/sqrt(128), dO ~ N(0,1), bf16"},
         "useful_tflops": round(tflops, 1), "pct_bf16_peak": round(tflops / PEAK_BF16_TFLOPS * 100, 2),
         "roofline": roofline, "kernels": kernels,
         "tree_build_ms": round(build_ms, 2), "tree_gen_s": round(gen_s, 2),
