@@ -54,7 +54,7 @@ __global__ __launch_bounds__(DqCfg<G>::THREADS) void dq_mfma_kernel(
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r = lane & 31, hh = lane >> 5;
   const int kvh = blockIdx.x % g.h_kv;
   const int idx = blockIdx.x / g.h_kv;
-  const int qb = full_range ? P.qb_order[idx] : (qb_first + n_qb - 1 - idx);
+  const int qb = full_range ? ld_uniform(P.qb_order, idx) : (qb_first + n_qb - 1 - idx);
   const int head = kvh * G + (wave >> 1);
   const int pos0 = (wave & 1) * 32;
   const int row = qb * BQ - g.q_off + pos0 + r;  // q-buffer row of this lane's query
@@ -109,19 +109,24 @@ __global__ __launch_bounds__(DqCfg<G>::THREADS) void dq_mfma_kernel(
     if (tid < BK) s.end[tid] = ereg;
   };
 
-  const int e0 = P.qb_ptr[qb], e1 = P.qb_ptr[qb + 1];
+  // tile-list entries two ahead, as in the forward
+  const int e0 = ld_uniform(P.qb_ptr, qb), e1 = ld_uniform(P.qb_ptr, qb + 1);
+  int cur = e0 < e1 ? ld_uniform(P.qb_tiles, e0) : 0;
+  int nxt = e0 + 1 < e1 ? ld_uniform(P.qb_tiles, e0 + 1) : 0;
   if (e0 < e1) {
-    load_tile(P.qb_tiles[e0] & kKbMask);
+    load_tile(cur & kKbMask);
     store_tile(st[0]);
   }
   wait_vmem();
   __syncthreads();
   for (int e = e0; e < e1; ++e) {
     const int sidx = (e - e0) & 1;
-    const int ent = P.qb_tiles[e];
+    const int ent = cur;
     const int kb = ent & kKbMask;
     const bool full = (ent & kFull) != 0;
-    if (e + 1 < e1) load_tile(P.qb_tiles[e + 1] & kKbMask);
+    cur = nxt;
+    if (e + 2 < e1) nxt = ld_uniform(P.qb_tiles, e + 2);
+    if (e + 1 < e1) load_tile(cur & kKbMask);
     const DqStage& S = st[sidx];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {

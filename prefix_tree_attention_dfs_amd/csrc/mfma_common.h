@@ -72,6 +72,15 @@ __device__ __forceinline__ int32_t bloadi(rsrc_t r, uint32_t voff, uint32_t soff
   return int32_t(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
 }
 
+// One int32 of the plan (read-only for the kernel's whole life) at a
+// workgroup-uniform index, loaded through the scalar unit: the value lands in
+// an SGPR, so the loop head needs no vector-memory wait, and buffer loads
+// whose soffset derives from it need no per-lane loop.
+__device__ __forceinline__ int32_t ld_uniform(const int32_t* p, int i) {
+  typedef __attribute__((address_space(4))) const int32_t const_i32;
+  return ((const_i32*)p)[i];
+}
+
 // Wait until every vector-memory load issued so far has returned
 // (s_waitcnt vmcnt(0); expcnt and lgkmcnt left at their maxima).  Placed
 // after a kernel's prologue, it tells the compiler's wait insertion that the
