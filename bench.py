@@ -31,8 +31,8 @@ METRIC = "tree attn fwd+bwd unique tokens/s + useful TFLOP/s (% bf16 MFMA peak),
 # HBM traffic of the roofline kernel from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE
 # runs (scaled by the same counters' reading for a plain copy of known size),
 # valid only for the kernel source it was measured on.
-MEASURED_TRAFFIC = {"kernel": "attn_bwd_dkdv_mfma", "source_sha1": "0e879ba0d2a314e7e50efac3bc784e7c20772e5f",
-                    "bytes_per_launch": 20831060180}
+MEASURED_TRAFFIC = {"kernel": "attn_bwd_dkdv_mfma", "source_sha1": "21467e3ba6669752a6cc735c1f25e9c1502dd660",
+                    "bytes_per_launch": 20994253437}
 
 
 def _source_sha(path):
