@@ -370,6 +370,18 @@ typedef struct {
 int tt_timing_enable(int on);
 int tt_timing_collect(tt_kernel_time* out, int capacity, int* count);
 
+/*
+ * Matrix-core throughput probe (measurement).  Launches n_blocks workgroups
+ * of 512 threads on `stream`; every wave issues iters * 32 dense
+ * 32x32x16 bf16 MFMAs on register operands.  `out` is a caller-owned device
+ * buffer of n_blocks * 512 floats (overwritten with per-thread sums); *flops
+ * receives the launch's FLOP count, so flops / elapsed time is the sustained
+ * bf16 MFMA rate, clock throttling included.  n_blocks in [1, 65536], iters
+ * in [1, 2^20]; TT_EINVAL otherwise (nothing launched), TT_EDEVICE if the
+ * launch fails.
+ */
+int tt_probe_mfma(int32_t n_blocks, int32_t iters, float* out, tt_stream stream, double* flops);
+
 /* Text of the last error on this thread ("" if none). Valid until the next call. */
 const char* tt_last_error(void);
 

@@ -27,7 +27,7 @@ EXPORTED = ("tree_build", "tree_free", "tree_info", "tree_export", "tree_plan_by
             "tree_attn_workspace_bytes", "tree_attn_fwd", "tree_attn_bwd", "tree_nll_workspace_bytes",
             "tree_weighted_nll", "tt_last_error", "tt_timing_enable", "tt_timing_collect",
             "tree_target_weights", "tree_path_build", "tree_path_free", "tree_path_info", "tree_path_segments", "tree_path_workspace_bytes",
-            "tree_attn_path")
+            "tree_attn_path", "tt_probe_mfma")
 
 
 class TTError(RuntimeError):
@@ -133,6 +133,9 @@ def _setup(lib):
     lib.tt_timing_enable.restype = ctypes.c_int
     lib.tt_timing_collect.argtypes = [ctypes.POINTER(KernelTime), ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
     lib.tt_timing_collect.restype = ctypes.c_int
+    lib.tt_probe_mfma.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                                  ctypes.POINTER(ctypes.c_double)]
+    lib.tt_probe_mfma.restype = ctypes.c_int
     for _n in ("tree_info", "tree_export", "tree_plan_bytes", "tree_plan_upload", "tree_plan_copy", "tree_attn_workspace_bytes",
                "tree_attn_fwd", "tree_attn_bwd", "tree_nll_workspace_bytes", "tree_weighted_nll"):
         getattr(lib, _n).restype = ctypes.c_int
@@ -177,6 +180,26 @@ def timing_collect():
     _check(lib().tt_timing_collect(buf, 64, ctypes.byref(n)))
     return {buf[i].name.decode(): (int(buf[i].launches), float(buf[i].total_ms), float(buf[i].max_ms))
             for i in range(min(n.value, 64))}
+
+
+def probe_mfma(n_blocks=1024, iters=2000, reps=3):
+    """Sustained dense bf16 MFMA rate (TFLOP/s) of tt_probe_mfma on the current
+    stream: one warm-up launch, then the best of `reps` timed launches."""
+    import torch
+    out = torch.empty(n_blocks * 512, dtype=torch.float32, device="cuda")
+    fl = ctypes.c_double()
+    best = None
+    for r in range(reps + 1):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        _check(lib().tt_probe_mfma(n_blocks, iters, ctypes.c_void_p(out.data_ptr()), _stream(), ctypes.byref(fl)))
+        e1.record()
+        e1.synchronize()
+        if r:
+            ms = e0.elapsed_time(e1)
+            best = ms if best is None else min(best, ms)
+    return fl.value / (best * 1e-3) / 1e12
 
 
 # ------------------------------------------------------------------ tree

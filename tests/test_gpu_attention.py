@@ -123,3 +123,11 @@ def test_empty_and_single():
     dq, dk, dv = tt.tree_attn_bwd(tree, plan, q, k, v, O, L, do)
     assert float(dq.abs().max()) < 1e-5 and float(dk.abs().max()) < 1e-5
     np.testing.assert_allclose(dv.cpu().numpy()[0], don[0].sum(0, keepdims=True), rtol=1e-6)
+
+
+def test_probe_mfma_rate_plausible():
+    """The sustained bf16 MFMA rate lies between a quarter of the published
+    2.5 PFLOP/s peak and the peak itself (it cannot exceed the hardware)."""
+    rate = tt.probe_mfma(n_blocks=512, iters=500, reps=2)
+    print(f"sustained bf16 MFMA: {rate:.1f} TFLOP/s", flush=True)
+    assert 625.0 < rate < 2520.0, rate

@@ -105,6 +105,29 @@ def test_mfma_forward_agentic_8b_shape_sampled():
     assert rel_err(O[ri], Or) < TOL and rel_err(L[ri], Lr) < TOL
 
 
+def test_mfma_forward_rl_forest_1p7b_sampled():
+    """The 1.7B-shape RL forest at full size (16 query heads, 8 kv heads),
+    forward only as timed: sampled rows against the oracle's per-row branch
+    computation."""
+    case = ts.rl_forest_accepted(0)
+    tree = tt.Tree(case.seqs)
+    o = dfs_arrays(case.seqs)
+    N = tree.N
+    rng = ts.rng_for(1100)
+    qb = ts.normal_bf16(rng, (N, 16, 128), 128 ** -0.5)
+    kb = ts.normal_bf16(rng, (N, 8, 128), 128 ** -0.5)
+    vb = ts.normal_bf16(rng, (N, 8, 128), 128 ** -0.5)
+    dev = lambda b: torch.from_numpy(b.view(np.int16)).cuda().view(torch.bfloat16)  # noqa: E731
+    plan = tree.upload_plan()
+    print(f"rl forest seed {case.seed}: N={N}", flush=True)
+    O, L = tt.tree_attn_fwd(tree, plan, dev(qb), dev(kb), dev(vb))
+    rows = np.unique(np.concatenate([np.linspace(0, N - 1, 24).astype(int), [0, 63, 64, N - 1],
+                                     ts.rng_for(6).integers(0, N, 8)]))
+    Or, Lr = OA.forward_rows(o, None, None, None, rows, get=_lazy_rows(qb, kb, vb))
+    ri = torch.as_tensor(rows, device=O.device)
+    assert rel_err(O[ri], Or) < TOL and rel_err(L[ri], Lr) < TOL
+
+
 # ------------------------------------------------------------------ backward
 def _bwd_case(name, hq, hkv, std, seed):
     case = TREES[name]()
@@ -194,5 +217,66 @@ def test_mfma_backward_agentic_8b_shape_sampled():
     assert rel_err(torch.from_numpy(sdv), sdo) < TOL
     from oracle.rope import rotate
     dkr = rotate(dk.float().cpu().double().numpy(), o["depth"], 10000.0)
+    tot = np.abs(dkr.sum(0)).max()
+    assert tot < 2e-2 * np.abs(dkr).sum(0).max(), tot
+
+
+def test_mfma_chain_suffix_chunks_8b_full():
+    """The 8B-shape path configuration at full size, launched as timed: a
+    49,152-token chain whose last 16,384 queries run in 2048-row chunks right
+    to left against all earlier keys, dK/dV added into fp32 buffers.  The
+    chunks partition the queries, so the result equals one call over the whole
+    suffix; sampled suffix rows (O, LSE, dQ) and the last keys (dK, dV) equal
+    the oracle's; over all keys sum_j dV_j is the sum of the suffix dO over the
+    group's query heads and sum_j R(depth_j) dK_j = 0."""
+    L, prefix, chunk = 49152, 32768, 2048
+    case = ts.long_chain(0)
+    tree = tt.Tree(case.seqs)
+    o = dfs_arrays(case.seqs)
+    rng = ts.rng_for(2200)
+    qb = ts.normal_bf16(rng, (L, 32, 128), 128 ** -0.5)
+    kb = ts.normal_bf16(rng, (L, 8, 128), 128 ** -0.5)
+    vb = ts.normal_bf16(rng, (L, 8, 128), 128 ** -0.5)
+    ob = ts.normal_bf16(rng, (L, 32, 128), 1.0)
+    ob[:prefix] = 0  # bf16 +0: no upstream gradient on the cached prefix
+    dev = lambda b: torch.from_numpy(b.view(np.int16)).cuda().view(torch.bfloat16)  # noqa: E731
+    q, k, v, do = dev(qb), dev(kb), dev(vb), dev(ob)
+    plan = tree.upload_plan()
+    dk = torch.zeros(L, 8, 128, dtype=torch.float32, device="cuda")
+    dv = torch.zeros_like(dk)
+    O = torch.empty(L - prefix, 32, 128, dtype=torch.bfloat16, device="cuda")
+    Ls = torch.empty(L - prefix, 32, dtype=torch.float32, device="cuda")
+    dq = torch.empty_like(O)
+    for s in reversed(range(prefix, L, chunk)):
+        e = min(L, s + chunk)
+        print(f"chunk [{s}, {e})", flush=True)
+        Oc, Lc = tt.tree_attn_fwd(tree, plan, q[s:e], k[:e], v[:e], q_off=s)
+        dqc, _, _ = tt.tree_attn_bwd(tree, plan, q[s:e], k[:e], v[:e], Oc, Lc, do[s:e], q_off=s,
+                                     d_k=dk[:e], d_v=dv[:e], accumulate=True)
+        O[s - prefix:e - prefix], Ls[s - prefix:e - prefix], dq[s - prefix:e - prefix] = Oc, Lc, dqc
+    print("one call over the suffix", flush=True)
+    Ou, Lu = tt.tree_attn_fwd(tree, plan, q[prefix:], k, v, q_off=prefix)
+    dqu, dku, dvu = tt.tree_attn_bwd(tree, plan, q[prefix:], k, v, Ou, Lu, do[prefix:], q_off=prefix)
+    for n, a, b in (("o", O, Ou), ("lse", Ls, Lu), ("dq", dq, dqu), ("dk", dk, dku), ("dv", dv, dvu)):
+        r = ((a.float() - b.float()).abs().max() / b.float().abs().max()).item()
+        assert r < 1e-2, (n, r)
+
+    def get(name, idx):
+        return ts.bf16_bits_to_f64({"q": qb, "k": kb, "v": vb, "do": ob}[name][idx])
+
+    rows = np.array([prefix, prefix + chunk - 1, prefix + chunk, L - chunk - 1, L - chunk, L - 1])
+    Or, Lr = OA.forward_rows(o, None, None, None, rows, get=get)
+    ri = torch.as_tensor(rows - prefix, device="cuda")
+    assert rel_err(O[ri], Or) < TOL and rel_err(Ls[ri], Lr) < TOL
+    assert rel_err(dq[ri], OA.dq_rows(o, None, None, None, None, rows, get=get)) < TOL
+    keys = np.array([L - 5, L - 2, L - 1])
+    rk, rv = OA.dkdv_keys(o, None, None, None, None, keys, get=get, q_lo=prefix)
+    ki = torch.as_tensor(keys, device="cuda")
+    assert rel_err(dk[ki], rk) < TOL and rel_err(dv[ki], rv) < TOL
+    sdv = dv.sum(0).cpu().double().numpy()
+    sdo = do[prefix:].float().reshape(L - prefix, 8, 4, 128).sum((0, 2)).cpu().double().numpy()
+    assert rel_err(torch.from_numpy(sdv), sdo) < TOL
+    from oracle.rope import rotate
+    dkr = rotate(dk.cpu().double().numpy(), o["depth"], 10000.0)
     tot = np.abs(dkr.sum(0)).max()
     assert tot < 2e-2 * np.abs(dkr).sum(0).max(), tot

@@ -244,3 +244,17 @@ def test_nll_argument_errors():
     assert nll(logits=0, hidden=FAKE, w_vocab=FAKE, d_model=8, vocab=104, d_logits=FAKE) == tt.TT_EINVAL
     assert nll(logits=0, hidden=FAKE, w_vocab=FAKE, d_model=8, vocab=100) == tt.TT_EUNSUPPORTED  # vocab % 8
     assert nll(logits=0, hidden=FAKE, w_vocab=FAKE, d_model=12, vocab=104) == tt.TT_EUNSUPPORTED  # d_model % 8
+
+
+def test_probe_mfma_validates_before_launch():
+    """The matrix-core probe rejects bad sizes and NULL pointers on the host."""
+    lib = tt.lib()
+    fl = ctypes.c_double()
+    dummy = ctypes.c_void_p(16)  # never dereferenced: validation fails first
+    assert lib.tt_probe_mfma(0, 10, dummy, None, ctypes.byref(fl)) == tt.TT_EINVAL
+    assert lib.tt_probe_mfma(65537, 10, dummy, None, ctypes.byref(fl)) == tt.TT_EINVAL
+    assert lib.tt_probe_mfma(4, 0, dummy, None, ctypes.byref(fl)) == tt.TT_EINVAL
+    assert lib.tt_probe_mfma(4, (1 << 20) + 1, dummy, None, ctypes.byref(fl)) == tt.TT_EINVAL
+    assert lib.tt_probe_mfma(4, 10, None, None, ctypes.byref(fl)) == tt.TT_EINVAL
+    assert lib.tt_probe_mfma(4, 10, dummy, None, None) == tt.TT_EINVAL
+    assert b"tt_probe_mfma" in lib.tt_last_error()
