@@ -154,6 +154,14 @@ int tree_target_weights(const tt_tree* tree, const float* seq_scale, const uint8
  * tree_plan_bytes gives its size; tree_plan_upload copies it (hipMemcpyAsync on
  * `stream`) into the caller's device buffer of at least that many bytes.
  * Errors: TT_EINVAL, TT_EWORKSPACE (buffer too small), TT_EDEVICE.
+ * The image's header carries its row count and an identity word (a hash of
+ * the image, which holds structure only, not token ids).  Every kernel that
+ * reads the plan first compares them with the tree of the call and returns
+ * without writing anything when they differ: a plan uploaded for another
+ * tree leaves the call's outputs unchanged instead of being read out of
+ * bounds.  That mismatch is not reported (detecting it would need a device
+ * synchronisation); passing the plan of the call's own tree is the caller's
+ * contract.
  */
 int tree_plan_bytes(const tt_tree* tree, size_t* bytes);
 int tree_plan_upload(const tt_tree* tree, void* dev_plan, size_t bytes, tt_stream stream);

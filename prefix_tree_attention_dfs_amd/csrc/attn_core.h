@@ -31,6 +31,8 @@ inline PlanPtrs plan_ptrs(const tt_tree* t, const void* dev_plan) {
   P.bk = t->bk;
   P.nqb = t->nqb;
   P.nkb = t->nkb;
+  P.hdr = base;
+  P.id = h[ttp::H_ID];
   return P;
 }
 

@@ -19,10 +19,11 @@ namespace {
 // y = R(depth * theta) x (or R^T x), theta_k = base^(-2k/d), pairs (k, k+d/2).
 // One thread per (row, k); the angle is formed and rotated in fp64.
 template <typename Tin, typename Tout, bool ACC>
-__global__ __launch_bounds__(256) void rope_kernel(const Tin* __restrict__ x, Tout* __restrict__ y,
-                                                   const int32_t* __restrict__ depth, int32_t row0,
-                                                   int32_t n_rows, int32_t heads, int32_t d, double base,
-                                                   double sign) {
+__global__ __launch_bounds__(256) void rope_kernel(const Tin* __restrict__ x, Tout* __restrict__ y, PlanPtrs P,
+                                                   int32_t row0, int32_t n_rows, int32_t heads, int32_t d,
+                                                   double base, double sign) {
+  if (!plan_matches(P)) return;
+  const int32_t* __restrict__ depth = P.depth;
   const int half = d >> 1;
   const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
   if (idx >= int64_t(n_rows) * half) return;
@@ -55,6 +56,7 @@ template <typename T, int DMAX>
 __global__ __launch_bounds__(256) void fwd_generic(const T* __restrict__ q, const T* __restrict__ k,
                                                    const T* __restrict__ v, T* __restrict__ o,
                                                    float* __restrict__ lse, PlanPtrs P, AttnGeom g) {
+  if (!plan_matches(P)) return;
   constexpr int NT = DMAX / kWave;
   __shared__ float qs[4][DMAX];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -139,6 +141,7 @@ __global__ __launch_bounds__(256) void dq_generic(const T* __restrict__ q, const
                                                   const T* __restrict__ v, const T* __restrict__ d_o,
                                                   const float* __restrict__ lse, const float* __restrict__ D,
                                                   float* __restrict__ dq_acc, PlanPtrs P, AttnGeom g) {
+  if (!plan_matches(P)) return;
   constexpr int NT = DMAX / kWave;
   __shared__ float qs[4][DMAX];
   __shared__ float ds_[4][DMAX];
@@ -210,6 +213,7 @@ __global__ __launch_bounds__(256) void dkdv_generic(const T* __restrict__ q, con
                                                     const float* __restrict__ lse, const float* __restrict__ D,
                                                     TG* __restrict__ d_k, TG* __restrict__ d_v, PlanPtrs P,
                                                     AttnGeom g) {
+  if (!plan_matches(P)) return;
   constexpr int NT = DMAX / kWave;
   __shared__ float ks[4][DMAX];
   __shared__ float vs[4][DMAX];
@@ -308,7 +312,7 @@ inline unsigned blocks_for(int64_t n, int per) { return unsigned((n + per - 1) /
 }  // namespace
 
 // ---------------------------------------------------------------- launchers
-int launch_rope(const void* x, void* y, tt_dtype tin, tt_dtype tout, bool acc, const int32_t* depth, int32_t row0,
+int launch_rope(const void* x, void* y, tt_dtype tin, tt_dtype tout, bool acc, const PlanPtrs& P, int32_t row0,
                 int32_t n_rows, int32_t heads, int32_t d, float base, bool inverse, hipStream_t st) {
   const int64_t n = int64_t(n_rows) * (d / 2);
   if (n == 0) return 0;
@@ -316,13 +320,13 @@ int launch_rope(const void* x, void* y, tt_dtype tin, tt_dtype tout, bool acc, c
   const double sg = inverse ? -1.0 : 1.0;
   const double b = double(base);
   if (tin == TT_F32 && tout == TT_F32 && !acc)
-    rope_kernel<float, float, false><<<grid, block, 0, st>>>((const float*)x, (float*)y, depth, row0, n_rows, heads, d, b, sg);
+    rope_kernel<float, float, false><<<grid, block, 0, st>>>((const float*)x, (float*)y, P, row0, n_rows, heads, d, b, sg);
   else if (tin == TT_F32 && tout == TT_F32 && acc)
-    rope_kernel<float, float, true><<<grid, block, 0, st>>>((const float*)x, (float*)y, depth, row0, n_rows, heads, d, b, sg);
+    rope_kernel<float, float, true><<<grid, block, 0, st>>>((const float*)x, (float*)y, P, row0, n_rows, heads, d, b, sg);
   else if (tin == TT_BF16 && tout == TT_BF16 && !acc)
-    rope_kernel<uint16_t, uint16_t, false><<<grid, block, 0, st>>>((const uint16_t*)x, (uint16_t*)y, depth, row0, n_rows, heads, d, b, sg);
+    rope_kernel<uint16_t, uint16_t, false><<<grid, block, 0, st>>>((const uint16_t*)x, (uint16_t*)y, P, row0, n_rows, heads, d, b, sg);
   else if (tin == TT_F32 && tout == TT_BF16 && !acc)
-    rope_kernel<float, uint16_t, false><<<grid, block, 0, st>>>((const float*)x, (uint16_t*)y, depth, row0, n_rows, heads, d, b, sg);
+    rope_kernel<float, uint16_t, false><<<grid, block, 0, st>>>((const float*)x, (uint16_t*)y, P, row0, n_rows, heads, d, b, sg);
   else
     return -1;
   return hipGetLastError() == hipSuccess ? 0 : -1;

@@ -46,6 +46,7 @@ __global__ __launch_bounds__(FwdCfg<G>::THREADS, FwdCfg<G>::MINB) void fwd_mfma_
   using C = FwdCfg<G>;
   constexpr int NT = C::NT;
   __shared__ FwdStage st[2];
+  if (!plan_matches(P)) return;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r = lane & 31, hh = lane >> 5;
   const int kvh = blockIdx.x % g.h_kv;

@@ -51,6 +51,7 @@ __global__ __launch_bounds__(DqCfg<G>::THREADS) void dq_mfma_kernel(
     float* __restrict__ dq_acc, PlanPtrs P, AttnGeom g, int full_range, int qb_first, int n_qb) {
   using C = DqCfg<G>;
   __shared__ DqStage st[2];
+  if (!plan_matches(P)) return;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r = lane & 31, hh = lane >> 5;
   const int kvh = blockIdx.x % g.h_kv;
   const int idx = blockIdx.x / g.h_kv;
@@ -211,6 +212,7 @@ __global__ __launch_bounds__(KV_THREADS, 2) void dkdv_mfma_kernel(
     const uint16_t* __restrict__ d_o, const float* __restrict__ lse, const float* __restrict__ Dv,
     TG* __restrict__ d_k, TG* __restrict__ d_v, PlanPtrs P, AttnGeom g) {
   __shared__ KvLds L;
+  if (!plan_matches(P)) return;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r = lane & 31, hh = lane >> 5;
   const int ks = wave & 3;  // key sub-tile
   const int mt = wave >> 2; // query half of each staged tile

@@ -227,13 +227,13 @@ extern "C" int tree_attn_fwd(const tt_attn_args* a, tt_stream stream) {
   if (w.rope) {
     {
       KTimer t("rope_q", st);
-      if (launch_rope(a->q, ws + w.q_rot, a->dtype, a->dtype, false, P.depth, a->q_off, a->n_q, a->h_q, a->d,
+      if (launch_rope(a->q, ws + w.q_rot, a->dtype, a->dtype, false, P, a->q_off, a->n_q, a->h_q, a->d,
                       a->rope_base, false, st))
         return dev_fail(fn, "rope(q)");
     }
     {
       KTimer t("rope_k", st);
-      if (launch_rope(a->k, ws + w.k_rot, a->dtype, a->dtype, false, P.depth, 0, a->n_k, a->h_kv, a->d,
+      if (launch_rope(a->k, ws + w.k_rot, a->dtype, a->dtype, false, P, 0, a->n_k, a->h_kv, a->d,
                       a->rope_base, false, st))
         return dev_fail(fn, "rope(k)");
     }
@@ -270,13 +270,13 @@ extern "C" int tree_attn_bwd(const tt_attn_bwd_args* b, tt_stream stream) {
   if (w.rope) {
     if (a->n_q > 0) {
       KTimer t("rope_q", st);
-      if (launch_rope(a->q, ws + w.q_rot, a->dtype, a->dtype, false, P.depth, a->q_off, a->n_q, a->h_q, a->d,
+      if (launch_rope(a->q, ws + w.q_rot, a->dtype, a->dtype, false, P, a->q_off, a->n_q, a->h_q, a->d,
                       a->rope_base, false, st))
         return dev_fail(fn, "rope(q)");
     }
     {
       KTimer t("rope_k", st);
-      if (launch_rope(a->k, ws + w.k_rot, a->dtype, a->dtype, false, P.depth, 0, a->n_k, a->h_kv, a->d,
+      if (launch_rope(a->k, ws + w.k_rot, a->dtype, a->dtype, false, P, 0, a->n_k, a->h_kv, a->d,
                       a->rope_base, false, st))
         return dev_fail(fn, "rope(k)");
     }
@@ -292,7 +292,7 @@ extern "C" int tree_attn_bwd(const tt_attn_bwd_args* b, tt_stream stream) {
   // dQ: rotate back at the query rows' depths, convert to the output dtype
   if (a->n_q > 0) {
     KTimer t("dq_finalize", st);
-    if (launch_rope(dq, b->d_q, TT_F32, a->dtype, false, P.depth, a->q_off, a->n_q, a->h_q, a->d, a->rope_base, true,
+    if (launch_rope(dq, b->d_q, TT_F32, a->dtype, false, P, a->q_off, a->n_q, a->h_q, a->d, a->rope_base, true,
                     st))
       return dev_fail(fn, "dq finalize");
   }

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "internal.h"
 #include "tt.h"
 
 namespace ttd {
@@ -57,8 +58,21 @@ struct PlanPtrs {
   const int32_t* kb_qhi;
   const int32_t* kb_minend;
   const int32_t* kb_order;
+  const int32_t* hdr;  // image header
   int32_t N, bq, bk, nqb, nkb;
+  int32_t id;  // the tree's image identity (header word H_ID of its host copy)
 };
+
+// True when the device image at P.hdr is the one built for the tree these
+// pointers were resolved from: magic word, row count and identity as the host
+// recorded them.  Kernels that index plan arrays return at once otherwise, so
+// a plan uploaded for another tree cannot make them read past its arrays.
+// P is a kernel argument, so the loads are uniform (scalar unit).
+__device__ __forceinline__ bool plan_matches(const PlanPtrs& P) {
+  typedef __attribute__((address_space(4))) const int32_t cword;
+  const cword* h = (const cword*)P.hdr;
+  return h[ttp::H_MAGIC] == ttp::kMagic && h[ttp::H_N] == P.N && h[ttp::H_ID] == P.id;
+}
 
 // Geometry of one attention call after validation.
 struct AttnGeom {

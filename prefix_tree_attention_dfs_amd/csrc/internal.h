@@ -16,6 +16,7 @@ enum : int32_t {
   H_MAGIC = 0, H_N, H_BQ, H_BK, H_NQB, H_NKB, H_NTILES, H_BYTES,
   H_DEPTH, H_END, H_QB_PTR, H_QB_TILES, H_QB_ORDER,
   H_KB_QLO, H_KB_QHI, H_KB_MINEND, H_KB_ORDER,
+  H_ID,  // FNV-1a hash of the image (this word 0 while hashing): which tree it belongs to
   H_WORDS = 64
 };
 constexpr int32_t kFullBit = int32_t(0x40000000);  // tile entry: kb | kFullBit if FULL

@@ -9,7 +9,7 @@
 #include "tt.h"
 
 // RoPE (and its transpose) at the rows' depths; acc adds into an fp32 output.
-int launch_rope(const void* x, void* y, tt_dtype tin, tt_dtype tout, bool acc, const int32_t* depth, int32_t row0,
+int launch_rope(const void* x, void* y, tt_dtype tin, tt_dtype tout, bool acc, const PlanPtrs& P, int32_t row0,
                 int32_t n_rows, int32_t heads, int32_t d, float base, bool inverse, hipStream_t st);
 
 // Generic (any d <= 256) path, fp32 or bf16 storage.

@@ -135,7 +135,6 @@ extern "C" int tree_attn_path(const tt_path_args* a, tt_stream stream) {
                      hipMemcpyHostToDevice, st) != hipSuccess)
     return dev_fail(fn, "plan upload");
   const PlanPtrs P = ttc::plan_ptrs(p->chain, ws + w.plan);
-  const int32_t* pos = P.depth;  // chain depth = stack position
   AttnGeom g;
   g.h_q = a->h_q;
   g.h_kv = a->h_kv;
@@ -172,9 +171,9 @@ extern "C" int tree_attn_path(const tt_path_args* a, tt_stream stream) {
       const size_t r0 = size_t(s.row0), n = size_t(s.len), d0 = size_t(s.depth0);
       {
         KTimer t("path_push", st);
-        if (launch_rope(q + r0 * qrow, Qp + d0 * qrow, dt, dt, false, pos, s.depth0, s.len, a->h_q, a->d, rb, false,
+        if (launch_rope(q + r0 * qrow, Qp + d0 * qrow, dt, dt, false, P, s.depth0, s.len, a->h_q, a->d, rb, false,
                         st) ||
-            launch_rope(k + r0 * krow, Kp + d0 * krow, dt, dt, false, pos, s.depth0, s.len, a->h_kv, a->d, rb, false,
+            launch_rope(k + r0 * krow, Kp + d0 * krow, dt, dt, false, P, s.depth0, s.len, a->h_kv, a->d, rb, false,
                         st) ||
             hipMemcpyAsync(Vp + d0 * krow, v + r0 * krow, n * krow, hipMemcpyDeviceToDevice, st) != hipSuccess)
           return dev_fail(fn, "push");
@@ -214,14 +213,14 @@ extern "C" int tree_attn_path(const tt_path_args* a, tt_stream stream) {
                                      LSEp + size_t(qo) * hq, D, dq, dKa, dVa, true, false, st)))
           return rc;
         KTimer t("dq_finalize", st);
-        if (launch_rope(dq + pad * hq * d, d_q + row * qrow, TT_F32, dt, false, pos, c0, c1 - c0, a->h_q, a->d, rb,
+        if (launch_rope(dq + pad * hq * d, d_q + row * qrow, TT_F32, dt, false, P, c0, c1 - c0, a->h_q, a->d, rb,
                         true, st))
           return dev_fail(fn, "dq finalize");
       }
       KTimer t("path_pop", st);
-      if (launch_rope(dKa + d0 * hk * d, d_k + r0 * krow, TT_F32, dt, false, pos, s.depth0, s.len, a->h_kv, a->d, rb,
+      if (launch_rope(dKa + d0 * hk * d, d_k + r0 * krow, TT_F32, dt, false, P, s.depth0, s.len, a->h_kv, a->d, rb,
                       true, st) ||
-          launch_rope(dVa + d0 * hk * d, d_v + r0 * krow, TT_F32, dt, false, pos, s.depth0, s.len, a->h_kv, a->d, 0.f,
+          launch_rope(dVa + d0 * hk * d, d_v + r0 * krow, TT_F32, dt, false, P, s.depth0, s.len, a->h_kv, a->d, 0.f,
                       false, st) ||
           launch_fill_zero(dKa + d0 * hk * d, n * hk * d * 4, st) ||
           launch_fill_zero(dVa + d0 * hk * d, n * hk * d * 4, st))

@@ -164,6 +164,10 @@ void build_schedule(tt_tree* t) {
   std::copy(qhi.begin(), qhi.end(), p + o_qhi);
   std::copy(minend.begin(), minend.end(), p + o_minend);
   std::copy(korder.begin(), korder.end(), p + o_korder);
+  uint32_t h = 2166136261u;  // FNV-1a over every byte of the image
+  for (const int32_t x : t->plan)
+    for (int b = 0; b < 4; ++b) h = (h ^ ((uint32_t(x) >> (8 * b)) & 0xFFu)) * 16777619u;
+  p[ttp::H_ID] = int32_t(h);
 }
 
 int build(const int32_t* tokens, const int64_t* offs, int32_t B, tt_tree* t) {

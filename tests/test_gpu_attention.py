@@ -4,6 +4,8 @@ Tolerance: max |gpu - oracle| / max |oracle| per tensor, 1e-5 for float32
 inputs and 2e-2 for bf16 inputs.  Every input comes from treesynth with a
 fixed seed; both sides get the same values.
 """
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -131,3 +133,35 @@ def test_probe_mfma_rate_plausible():
     rate = tt.probe_mfma(n_blocks=512, iters=500, reps=2)
     print(f"sustained bf16 MFMA: {rate:.1f} TFLOP/s", flush=True)
     assert 625.0 < rate < 2520.0, rate
+
+
+def test_plan_of_another_tree_is_ignored():
+    """A plan image uploaded for another tree fails the kernels' header check:
+    every kernel that reads the plan returns at once and the outputs keep
+    their previous contents.  The buffer is sized for the tree of the call, so
+    every address the kernels could form lies inside it."""
+    small = tt.Tree([[1, 2, 3, 4], [1, 2, 5]])
+    big_case = ts.random_small_tree(11, n_seqs=8, max_len=300, vocab=3)
+    big = tt.Tree(big_case.seqs)
+    buf = torch.zeros(big.plan_bytes(), dtype=torch.uint8, device="cuda")
+    assert tt.lib().tree_plan_upload(small.handle, ctypes.c_void_p(buf.data_ptr()), buf.numel(),
+                                     ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)) == tt.TT_OK
+    torch.cuda.synchronize()
+    for dtype, hq, hkv, d in ((torch.float32, 4, 2, 64), (torch.bfloat16, 8, 2, 128)):
+        print(f"wrong plan: N={big.N} dtype={dtype} d={d}", flush=True)
+        (q, _), (k, _), (v, _), (do, _) = inputs(dtype, 5, big.N, big.N, hq, hkv, d, d ** -0.5)
+        o = torch.full_like(q, 7.0)
+        lse = torch.full((big.N, hq), 7.0, dtype=torch.float32, device="cuda")
+        tt.tree_attn_fwd(big, buf, q, k, v, o=o, lse=lse)
+        dq = torch.full_like(q, 7.0)
+        dk, dv = torch.full_like(k, 7.0), torch.full_like(v, 7.0)
+        tt.tree_attn_bwd(big, buf, q, k, v, o, lse, do, d_q=dq, d_k=dk, d_v=dv)
+        torch.cuda.synchronize()
+        for t_ in (o, lse, dq, dk, dv):
+            assert bool((t_.float() == 7.0).all())
+    # the right plan in the same kind of buffer works
+    good = big.upload_plan()
+    (q, qn), (k, kn), (v, vn), _ = inputs(torch.float32, 5, big.N, big.N, 4, 2, 64, 64 ** -0.5)
+    O, L = tt.tree_attn_fwd(big, good, q, k, v)
+    Or, Lr, _ = OA.forward(dfs_arrays(big_case.seqs), qn, kn, vn, which="leaves")
+    assert rel_err(O, Or) < 1e-4 and rel_err(L, Lr) < 1e-4

@@ -258,3 +258,30 @@ def test_probe_mfma_validates_before_launch():
     assert lib.tt_probe_mfma(4, 10, None, None, ctypes.byref(fl)) == tt.TT_EINVAL
     assert lib.tt_probe_mfma(4, 10, dummy, None, None) == tt.TT_EINVAL
     assert b"tt_probe_mfma" in lib.tt_last_error()
+
+
+def _fnv1a_words(words):
+    h = 2166136261
+    for b in np.asarray(words, dtype="<i4").tobytes():
+        h = ((h ^ b) * 16777619) & 0xFFFFFFFF
+    return h
+
+
+def test_plan_identity_word():
+    """Header word 17 of the plan image is the FNV-1a hash of the image with
+    that word zeroed (the kernels compare it with the tree's own copy before
+    reading any plan array).  The image holds structure only, so trees of
+    different shape get different identities and trees of one shape (other
+    token ids) share one, together with identical, interchangeable images."""
+    ids = {}
+    for name, seqs in (("tiny", ts.tiny_tree(0).seqs), ("fork", [[1, 2, 3], [1, 2, 4]]),
+                       ("fork_other_tokens", [[1, 2, 3], [1, 2, 5]]), ("chain", [[1, 2, 3, 4]]),
+                       ("random", ts.random_small_tree(3, n_seqs=6, max_len=90, vocab=4).seqs)):
+        p = tt.Tree(seqs).plan_host()
+        q = p.copy()
+        q[17] = 0
+        assert (int(p[17]) & 0xFFFFFFFF) == _fnv1a_words(q)
+        ids[name] = (int(p[17]), p.tobytes())
+    assert ids["fork"] == ids["fork_other_tokens"]
+    shapes = [ids[n][0] for n in ("tiny", "fork", "chain", "random")]
+    assert len(set(shapes)) == 4
