@@ -349,6 +349,10 @@ __global__ __launch_bounds__(KV_THREADS, 2) void dkdv_mfma_kernel(
       dp = mfma(lds_read16(&S.O[soff(mt * 32 + r, dc * 16 + 8 * hh)]), lds_read16(Vt + dc * 16), dp);
     }
     f32x16 ds;
+    // the softmax step runs at raised wave priority: the SIMD's other wave,
+    // usually issuing MFMAs, yields issue slots to it, which shortens the gap
+    // before this wave's own dV/dK products (measured 2% on this kernel)
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int i4 = 0; i4 < 4; ++i4) {
       const int ql = mt * 32 + 8 * i4 + 4 * hh;
@@ -374,6 +378,7 @@ __global__ __launch_bounds__(KV_THREADS, 2) void dkdv_mfma_kernel(
     }
     const bf16x8 p0 = c_to_b(s, 0), p1 = c_to_b(s, 1);
     const bf16x8 s0 = c_to_b(ds, 0), s1 = c_to_b(ds, 1);
+    __builtin_amdgcn_s_setprio(0);
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
       dv[dt] = mfma(tr_frag_swz(S.O, mt * 32, dt * 32, lane), p0, dv[dt]);
