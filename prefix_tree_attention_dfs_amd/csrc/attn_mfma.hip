@@ -133,9 +133,8 @@ __global__ __launch_bounds__(FwdCfg<G>::THREADS, FwdCfg<G>::MINB) void fwd_mfma_
     if (e + 1 < e1) load_tile(cur & kKbMask);
     const FwdStage& S = st[sidx];
 
-    // S^T = K Q^T for both 32-key halves first, then for each half: mask,
-    // online softmax (rows = lanes), O^T += V^T P^T -- the second half's
-    // products run on the matrix pipe while the first half's softmax runs.
+    // S^T = K Q^T for both 32-key halves, mask, one online-softmax update
+    // (rows = lanes) for the 64-key tile, then O^T += V^T P^T.
     f32x16 sv[2][NT];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
@@ -148,10 +147,10 @@ __global__ __launch_bounds__(FwdCfg<G>::THREADS, FwdCfg<G>::MINB) void fwd_mfma_
         for (int nt = 0; nt < NT; ++nt) sv[kt][nt] = mfma(a, qf[nt][dc], sv[kt][nt]);
       }
     }
+    // mask (PARTIAL tiles), then one running-max update for the whole tile
+    if (!full) {
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      f32x16(&sacc)[NT] = sv[kt];
-      if (!full) {
+      for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
           const int qpos = qb * BQ + pos0 + nt * 32 + r;
@@ -159,52 +158,64 @@ __global__ __launch_bounds__(FwdCfg<G>::THREADS, FwdCfg<G>::MINB) void fwd_mfma_
           for (int i = 0; i < 16; ++i) {
             const int kl = kt * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
             const bool vis = (kb * BK + kl <= qpos) & (qpos < S.end[kl]);
-            sacc[nt][i] = vis ? sacc[nt][i] : -INFINITY;
+            sv[kt][nt][i] = vis ? sv[kt][nt][i] : -INFINITY;
           }
         }
+    }
+    float mexp[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sv[kt][nt][i]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      // the running max moves only when a row's tile max exceeds it by more
+      // than tau (2^8 in probability); until then p may reach 2^8, which the
+      // fp32 sums and the bf16 P operand carry without loss of relative precision.
+      const bool grow = mx > m[nt] + tau;
+      if (__any(grow)) {
+        const float mnew = grow ? mx : m[nt];
+        const float alpha = (mnew == m[nt]) ? 1.f : exp2_fast((m[nt] - mnew) * c2);
+        lpart[nt] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) oacc[nt][dt][i] *= alpha;
+        m[nt] = mnew;
       }
-      bf16x8 pf[2][NT];
+      mexp[nt] = m[nt] == -INFINITY ? 0.f : m[nt] * c2;
+    }
+    // one straight block: both halves' exponentials and P, then O^T += V^T P^T;
+    // the scheduler overlaps the first half's products with the second half's
+    // exponentials
+    bf16x8 pf[2][2][NT];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-        float mx = -INFINITY;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[nt][i]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        // The running max moves only when a row's tile max exceeds it by more
-        // than tau (2^8 in probability); until then p may reach 2^8, which the
-        // fp32 sums and the bf16 P operand carry without loss of relative precision.
-        const bool grow = mx > m[nt] + tau;
-        if (__any(grow)) {
-          const float mnew = grow ? mx : m[nt];
-          const float alpha = (mnew == m[nt]) ? 1.f : exp2_fast((m[nt] - mnew) * c2);
-          lpart[nt] *= alpha;
-#pragma unroll
-          for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) oacc[nt][dt][i] *= alpha;
-          m[nt] = mnew;
-        }
-        const float mexp = m[nt] == -INFINITY ? 0.f : m[nt] * c2;
         float ls = 0.f;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const float p = exp2_fast(sacc[nt][i] * c2 - mexp);
-          sacc[nt][i] = p;
+          const float p = exp2_fast(sv[kt][nt][i] * c2 - mexp[nt]);
+          sv[kt][nt][i] = p;
           ls += p;
         }
         lpart[nt] += ls;
 #pragma unroll
-        for (int c = 0; c < 2; ++c) pf[c][nt] = c_to_b(sacc[nt], c);
+        for (int c = 0; c < 2; ++c) pf[kt][c][nt] = c_to_b(sv[kt][nt], c);
       }
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
           const bf16x8 a = tr_frag(S.V, VSTR, kt * 32 + 16 * c, dt * 32, lane);
 #pragma unroll
-          for (int nt = 0; nt < NT; ++nt) oacc[nt][dt] = mfma(a, pf[c][nt], oacc[nt][dt]);
+          for (int nt = 0; nt < NT; ++nt) oacc[nt][dt] = mfma(a, pf[kt][c][nt], oacc[nt][dt]);
         }
-    }
 
     if (e + 1 < e1) store_tile(st[sidx ^ 1]);
     __syncthreads();
