@@ -407,8 +407,8 @@ def main():
         print(json.dumps({"copy_bytes": x.numel() * 2, "launches": 5}), flush=True)
         return
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 (the multi-GPU dispatcher "
-                                   "is design-only)"}), flush=True)
+        print(json.dumps({"error": "the library runs on one GPU; --gpus must be 1 (sharding across GPUs is "
+                                   "described in the design notes, not implemented)"}), flush=True)
         sys.exit(2)
 
     import numpy as np
