@@ -15,8 +15,9 @@
 //                    4 key slices of 32 x 2 query halves.  It streams 64-row
 //                    Q / dO tiles of every query head of the group over the
 //                    contiguous range of query rows that see its keys, top
-//                    down:  S = Q K^T, P, dP = dO V^T, dS, dV^T += dO^T P,
-//                    dK^T += Q^T dS.
+//                    down, loaded straight from global memory into LDS (no
+//                    staging registers):  S = Q K^T, P, dP = dO V^T, dS,
+//                    dV^T += dO^T P, dK^T += Q^T dS.
 // Recomputing S and dP in both kernels costs 14 d MFMA flops per visible pair
 // instead of 10 d, in exchange for no fp32 atomic traffic on dQ.
 #include "device.h"
@@ -269,61 +270,60 @@ __global__ __launch_bounds__(KV_THREADS, 2) void dkdv_mfma_kernel(
   const int n_qt = hi > lo ? (hi - 1) / QT - qt_first + 1 : 0;
   const int n_steps = n_qt * G;
 
-  bf16x8 qreg[QCH], oreg[QCH];
   float lreg = 0.f, dreg = 0.f;
-  // buffer loads: query rows past n_q read zeros (tiles start at or after
-  // q_off, which is a multiple of 64, so rows are never below the buffer)
+  // query rows past n_q read zeros (tiles start at or after q_off, which is
+  // a multiple of 64, so rows are never below the buffer)
   const uint32_t q_bytes = uint32_t(g.n_q) * uint32_t(g.h_q) * D * 2;
   const rsrc_t rq = make_rsrc(q, q_bytes), ro = make_rsrc(d_o, q_bytes);
   const rsrc_t rl = make_rsrc(lse, uint32_t(g.n_q) * g.h_q * 4), rd = make_rsrc(Dv, uint32_t(g.n_q) * g.h_q * 4);
-  uint32_t voff[QCH];
+  // Q and dO tiles (64 rows x 128 bf16 = 16 KB each) go from global memory
+  // straight into LDS: 16 loads of 1 KB per tile, two per wave.  Lane l of
+  // load j fills LDS slot 64 j + l = (row, stored chunk) = ((64 j + l) / 16,
+  // (64 j + l) % 16), so it fetches global chunk (stored chunk ^ swz(row)) of
+  // that row and the tile lands in the swizzled layout the reads expect.
+  uint32_t dvoff[2];
 #pragma unroll
-  for (int u = 0; u < QCH; ++u) {
-    const int c = tid + u * KV_THREADS;
-    voff[u] = (uint32_t(c >> 4) * g.h_q * D + (c & 15) * 8) * 2;
+  for (int i = 0; i < 2; ++i) {
+    const int p = (wave * 2 + i) * 64 + lane;
+    const int row = p >> 4, c = (p & 15) ^ swz(p >> 4);
+    dvoff[i] = (uint32_t(row) * g.h_q * D + c * 8) * 2;
   }
-  auto load_tile = [&](int step) {
+  auto load_tile = [&](int step, KvStage& s) {
     // query tiles from the top down: workgroups over a shared prefix have the
     // same upper end, so they walk the same tiles together and share them in L2
     const int rev = n_steps - 1 - step;
     const int qt = qt_first + rev / G, head = kvh * G + rev % G;
     const uint32_t rowh = uint32_t(qt * QT - g.q_off) * g.h_q + head;  // (row, head) of the tile's first row
+    const uint32_t qb = lds_u32(s.Q) + wave * 2048, ob = lds_u32(s.O) + wave * 2048;
 #pragma unroll
-    for (int u = 0; u < QCH; ++u) {
-      qreg[u] = bload16(rq, voff[u], rowh * D * 2);
-      oreg[u] = bload16(ro, voff[u], rowh * D * 2);
+    for (int i = 0; i < 2; ++i) {
+      dma16(rq, dvoff[i], rowh * D * 2, qb + i * 1024);
+      dma16(ro, dvoff[i], rowh * D * 2, ob + i * 1024);
     }
     if (tid < QT) {
       lreg = bloadf(rl, uint32_t(tid) * g.h_q * 4, rowh * 4);
       dreg = bloadf(rd, uint32_t(tid) * g.h_q * 4, rowh * 4);
     }
   };
-  auto store_tile = [&](KvStage& s) {
-#pragma unroll
-    for (int u = 0; u < QCH; ++u) {
-      const int c = tid + u * KV_THREADS;
-      const int rr = c >> 4, dch = c & 15;
-      *reinterpret_cast<bf16x8*>(&s.Q[soff(rr, dch * 8)]) = qreg[u];
-      *reinterpret_cast<bf16x8*>(&s.O[soff(rr, dch * 8)]) = oreg[u];
-    }
+  auto store_rows = [&](KvStage& s) {
     if (tid < QT) {
-      s.s0[tid] = -lreg * inv_scale;  // scaled here, not at the load: no wait in the loop head
+      s.s0[tid] = -lreg * inv_scale;
       s.d0[tid] = -dreg;
     }
   };
 
   if (n_steps > 0) {
-    load_tile(0);
-    store_tile(L.run.st[0]);
+    load_tile(0, L.run.st[0]);
+    store_rows(L.run.st[0]);
   }
-  wait_vmem();
+  wait_vmem();  // also the direct-to-LDS loads, which the compiler does not track
   __syncthreads();
   const uint16_t* Kt = L.run.K + (ks * 32 + r) * KSTR + 8 * hh;
   const uint16_t* Vt = L.run.V + (ks * 32 + r) * KSTR + 8 * hh;
   for (int step = 0; step < n_steps; ++step) {
     const int sidx = step & 1;
     const int qt = qt_first + (n_steps - 1 - step) / G;
-    if (step + 1 < n_steps) load_tile(step + 1);
+    if (step + 1 < n_steps) load_tile(step + 1, L.run.st[sidx ^ 1]);  // that stage was last read in the previous step
     const KvStage& S = L.run.st[sidx];
     const int q0 = qt * QT + mt * 32;  // tree row of this wave's first query
     // every (query, key) pair of this wave's 32 x 32 block visible and in range?
@@ -386,7 +386,8 @@ __global__ __launch_bounds__(KV_THREADS, 2) void dkdv_mfma_kernel(
       dk[dt] = mfma(tr_frag_swz(S.Q, mt * 32, dt * 32, lane), s0, dk[dt]);
       dk[dt] = mfma(tr_frag_swz(S.Q, mt * 32 + 16, dt * 32, lane), s1, dk[dt]);
     }
-    if (step + 1 < n_steps) store_tile(L.run.st[sidx ^ 1]);
+    if (step + 1 < n_steps) store_rows(L.run.st[sidx ^ 1]);
+    wait_vmem();  // this wave's direct-to-LDS loads of the next tile have landed
     __syncthreads();
   }
 

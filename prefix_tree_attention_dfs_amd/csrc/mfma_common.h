@@ -81,6 +81,22 @@ __device__ __forceinline__ int32_t ld_uniform(const int32_t* p, int i) {
   return ((const_i32*)p)[i];
 }
 
+// LDS byte address of a __shared__ object (the low 32 bits of its generic
+// address are its offset in the LDS aperture).
+__device__ __forceinline__ uint32_t lds_u32(const void* p) { return uint32_t(reinterpret_cast<uintptr_t>(p)); }
+
+// 16 bytes per lane from a buffer straight into LDS: lane l's chunk lands at
+// LDS address lds_base + 16 l (lds_base wave-uniform, via M0); lanes past the
+// buffer's size write zeros.  Issued from assembly, so the compiler inserts
+// no wait for it: the caller waits with wait_vmem() before the barrier that
+// publishes the data.
+__device__ __forceinline__ void dma16(rsrc_t r, uint32_t voff, uint32_t soff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :: "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(voff), "s"(r),
+                  "s"(__builtin_amdgcn_readfirstlane(soff))
+               : "memory", "m0");
+}
+
 // Wait until every vector-memory load issued so far has returned
 // (s_waitcnt vmcnt(0); expcnt and lgkmcnt left at their maxima).  Placed
 // after a kernel's prologue, it tells the compiler's wait insertion that the
