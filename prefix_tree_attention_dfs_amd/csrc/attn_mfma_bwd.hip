@@ -320,6 +320,11 @@ __global__ __launch_bounds__(KV_THREADS, 2) void dkdv_mfma_kernel(
   __syncthreads();
   const uint16_t* Kt = L.run.K + (ks * 32 + r) * KSTR + 8 * hh;
   const uint16_t* Vt = L.run.V + (ks * 32 + r) * KSTR + 8 * hh;
+  // this wave's 32 keys as B operands of S = Q K^T, read once: they are the
+  // same in every step (V's are read from LDS each step; holding both spills)
+  bf16x8 kf[8];
+#pragma unroll
+  for (int dc = 0; dc < 8; ++dc) kf[dc] = lds_read16(Kt + dc * 16);
   for (int step = 0; step < n_steps; ++step) {
     const int sidx = step & 1;
     const int qt = qt_first + (n_steps - 1 - step) / G;
@@ -345,7 +350,7 @@ __global__ __launch_bounds__(KV_THREADS, 2) void dkdv_mfma_kernel(
     }
 #pragma unroll
     for (int dc = 0; dc < 8; ++dc) {
-      s = mfma(lds_read16(&S.Q[soff(mt * 32 + r, dc * 16 + 8 * hh)]), lds_read16(Kt + dc * 16), s);
+      s = mfma(lds_read16(&S.Q[soff(mt * 32 + r, dc * 16 + 8 * hh)]), kf[dc], s);
       dp = mfma(lds_read16(&S.O[soff(mt * 32 + r, dc * 16 + 8 * hh)]), lds_read16(Vt + dc * 16), dp);
     }
     f32x16 ds;
