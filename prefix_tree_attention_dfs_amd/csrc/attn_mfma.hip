@@ -7,8 +7,8 @@
 // One workgroup = one 64-row query block x one key/value head, i.e. the G
 // query heads that share that K/V (GQA).  It walks the block's list of
 // non-empty 64-key tiles (the plan's CSR); FULL tiles skip the mask.  K and V
-// tiles are staged global -> registers -> LDS, double buffered, one barrier
-// per tile.  Per wave: NT sub-tiles of 32 query rows of one head, Q held in
+// tiles go from global memory straight into LDS (swizzled layout), double
+// buffered, one barrier per tile.  Per wave: NT sub-tiles of 32 query rows of one head, Q held in
 // registers as B operands.
 //   S^T  = K Q^T        (A = K rows from LDS, B = Q)
 //   online softmax over keys (columns are lanes: row statistics are per lane)
@@ -33,8 +33,8 @@ struct FwdCfg {
 };
 
 struct __align__(16) FwdStage {
-  uint16_t K[BK * KSTR];
-  uint16_t V[BK * VSTR];
+  uint16_t K[BK * D];  // swizzled (soff): row reads for S^T
+  uint16_t V[BK * D];  // swizzled: transposed reads for O^T
   int32_t end[BK];
 };
 
@@ -83,31 +83,32 @@ __global__ __launch_bounds__(FwdCfg<G>::THREADS, FwdCfg<G>::MINB) void fwd_mfma_
   const rsrc_t rk = make_rsrc(k, kv_bytes), rv = make_rsrc(v, kv_bytes);
   const rsrc_t re = make_rsrc(P.end, uint32_t(g.n_k) * 4);
   const uint32_t tile_bytes = uint32_t(BK) * g.h_kv * D * 2;  // one 64-key tile of K (or V)
-  uint32_t voff[C::CH];
+  // K and V tiles (64 keys x 128 bf16 = 16 KB each) go from global memory
+  // straight into LDS: 16 loads of 1 KB per tile, NL per wave.  Lane l of
+  // load j fills LDS slot 64 j + l = (key, stored chunk) = ((64 j + l) / 16,
+  // (64 j + l) % 16) and fetches global chunk (stored chunk ^ swz(key)), so
+  // the tile lands in the swizzled layout.
+  constexpr int NL = (BK * D * 2 / 1024) / C::WAVES;  // 1 KB loads per wave per tile
+  static_assert(NL * C::WAVES * 1024 == BK * D * 2, "the waves' 1 KB loads cover a tile");
+  uint32_t dvoff[NL];
 #pragma unroll
-  for (int u = 0; u < C::CH; ++u) {
-    const int c = tid + u * C::THREADS;
-    voff[u] = (uint32_t((c >> 4) * g.h_kv + kvh) * D + (c & 15) * 8) * 2;
+  for (int i = 0; i < NL; ++i) {
+    const int p = (wave * NL + i) * 64 + lane;
+    const int key = p >> 4, c = (p & 15) ^ swz(p >> 4);
+    dvoff[i] = (uint32_t(key * g.h_kv + kvh) * D + c * 8) * 2;
   }
-  bf16x8 kreg[C::CH], vreg[C::CH];
   int32_t ereg = 0;
-  auto load_tile = [&](int kb) {
+  auto load_tile = [&](int kb, FwdStage& s) {
     const uint32_t so = uint32_t(kb) * tile_bytes;
+    const uint32_t kbase = lds_u32(s.K) + wave * NL * 1024, vbase = lds_u32(s.V) + wave * NL * 1024;
 #pragma unroll
-    for (int u = 0; u < C::CH; ++u) {
-      kreg[u] = bload16(rk, voff[u], so);
-      vreg[u] = bload16(rv, voff[u], so);
+    for (int i = 0; i < NL; ++i) {
+      dma16(rk, dvoff[i], so, kbase + i * 1024);
+      dma16(rv, dvoff[i], so, vbase + i * 1024);
     }
     if (tid < BK) ereg = bloadi(re, uint32_t(tid) * 4, uint32_t(kb) * BK * 4);
   };
-  auto store_tile = [&](FwdStage& s) {
-#pragma unroll
-    for (int u = 0; u < C::CH; ++u) {
-      const int c = tid + u * C::THREADS;
-      const int key = c >> 4, dch = c & 15;
-      *reinterpret_cast<bf16x8*>(&s.K[key * KSTR + dch * 8]) = kreg[u];
-      *reinterpret_cast<bf16x8*>(&s.V[key * VSTR + dch * 8]) = vreg[u];
-    }
+  auto store_end = [&](FwdStage& s) {
     if (tid < BK) s.end[tid] = ereg;
   };
 
@@ -117,10 +118,10 @@ __global__ __launch_bounds__(FwdCfg<G>::THREADS, FwdCfg<G>::MINB) void fwd_mfma_
   int cur = e0 < e1 ? ld_uniform(P.qb_tiles, e0) : 0;
   int nxt = e0 + 1 < e1 ? ld_uniform(P.qb_tiles, e0 + 1) : 0;
   if (e0 < e1) {
-    load_tile(cur & kKbMask);
-    store_tile(st[0]);
+    load_tile(cur & kKbMask, st[0]);
+    store_end(st[0]);
   }
-  wait_vmem();
+  wait_vmem();  // also the direct-to-LDS loads, which the compiler does not track
   __syncthreads();
 
   for (int e = e0; e < e1; ++e) {
@@ -130,7 +131,7 @@ __global__ __launch_bounds__(FwdCfg<G>::THREADS, FwdCfg<G>::MINB) void fwd_mfma_
     const bool full = (ent & kFull) != 0;
     cur = nxt;
     if (e + 2 < e1) nxt = ld_uniform(P.qb_tiles, e + 2);
-    if (e + 1 < e1) load_tile(cur & kKbMask);
+    if (e + 1 < e1) load_tile(cur & kKbMask, st[sidx ^ 1]);  // that stage was last read in the previous tile
     const FwdStage& S = st[sidx];
 
     // S^T = K Q^T for both 32-key halves, mask, one online-softmax update
@@ -142,7 +143,7 @@ __global__ __launch_bounds__(FwdCfg<G>::THREADS, FwdCfg<G>::MINB) void fwd_mfma_
       for (int nt = 0; nt < NT; ++nt) sv[kt][nt] = zero16();
 #pragma unroll
       for (int dc = 0; dc < 8; ++dc) {
-        const bf16x8 a = lds_read16(&S.K[(kt * 32 + r) * KSTR + dc * 16 + 8 * hh]);
+        const bf16x8 a = lds_read16(&S.K[soff(kt * 32 + r, dc * 16 + 8 * hh)]);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) sv[kt][nt] = mfma(a, qf[nt][dc], sv[kt][nt]);
       }
@@ -212,12 +213,13 @@ __global__ __launch_bounds__(FwdCfg<G>::THREADS, FwdCfg<G>::MINB) void fwd_mfma_
       for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-          const bf16x8 a = tr_frag(S.V, VSTR, kt * 32 + 16 * c, dt * 32, lane);
+          const bf16x8 a = tr_frag_swz(S.V, kt * 32 + 16 * c, dt * 32, lane);
 #pragma unroll
           for (int nt = 0; nt < NT; ++nt) oacc[nt][dt] = mfma(a, pf[kt][c][nt], oacc[nt][dt]);
         }
 
-    if (e + 1 < e1) store_tile(st[sidx ^ 1]);
+    if (e + 1 < e1) store_end(st[sidx ^ 1]);
+    wait_vmem();  // this wave's direct-to-LDS loads of the next tile have landed
     __syncthreads();
   }
 
