@@ -40,8 +40,8 @@ struct DqCfg {
 };
 
 struct __align__(16) DqStage {
-  uint16_t K[BK * D];     // swizzled: row reads (S^T) and transposed reads (dQ^T)
-  uint16_t V[BK * KSTR];  // padded: row reads only (dP^T)
+  uint16_t K[BK * D];  // swizzled: row reads (S^T) and transposed reads (dQ^T)
+  uint16_t V[BK * D];  // swizzled: row reads (dP^T)
   int32_t end[BK];
 };
 
@@ -83,31 +83,29 @@ __global__ __launch_bounds__(DqCfg<G>::THREADS) void dq_mfma_kernel(
   const rsrc_t rk = make_rsrc(k, kv_bytes), rv = make_rsrc(v, kv_bytes);
   const rsrc_t re = make_rsrc(P.end, uint32_t(g.n_k) * 4);
   const uint32_t tile_bytes = uint32_t(BK) * g.h_kv * D * 2;
-  uint32_t voff[C::CH];
+  // K and V tiles go from global memory straight into LDS in the swizzled
+  // layout, NL loads of 1 KB per wave each, as in the forward
+  constexpr int NL = (BK * D * 2 / 1024) / C::WAVES;
+  static_assert(NL * C::WAVES * 1024 == BK * D * 2, "the waves' 1 KB loads cover a tile");
+  uint32_t dvoff[NL];
 #pragma unroll
-  for (int u = 0; u < C::CH; ++u) {
-    const int c = tid + u * C::THREADS;
-    voff[u] = (uint32_t((c >> 4) * g.h_kv + kvh) * D + (c & 15) * 8) * 2;
+  for (int i = 0; i < NL; ++i) {
+    const int p = (wave * NL + i) * 64 + lane;
+    const int key = p >> 4, c = (p & 15) ^ swz(p >> 4);
+    dvoff[i] = (uint32_t(key * g.h_kv + kvh) * D + c * 8) * 2;
   }
-  bf16x8 kreg[C::CH], vreg[C::CH];
   int32_t ereg = 0;
-  auto load_tile = [&](int kb) {
+  auto load_tile = [&](int kb, DqStage& s) {
     const uint32_t so = uint32_t(kb) * tile_bytes;
+    const uint32_t kbase = lds_u32(s.K) + wave * NL * 1024, vbase = lds_u32(s.V) + wave * NL * 1024;
 #pragma unroll
-    for (int u = 0; u < C::CH; ++u) {
-      kreg[u] = bload16(rk, voff[u], so);
-      vreg[u] = bload16(rv, voff[u], so);
+    for (int i = 0; i < NL; ++i) {
+      dma16(rk, dvoff[i], so, kbase + i * 1024);
+      dma16(rv, dvoff[i], so, vbase + i * 1024);
     }
     if (tid < BK) ereg = bloadi(re, uint32_t(tid) * 4, uint32_t(kb) * BK * 4);
   };
-  auto store_tile = [&](DqStage& s) {
-#pragma unroll
-    for (int u = 0; u < C::CH; ++u) {
-      const int c = tid + u * C::THREADS;
-      const int key = c >> 4, dch = c & 15;
-      *reinterpret_cast<bf16x8*>(&s.K[soff(key, dch * 8)]) = kreg[u];
-      *reinterpret_cast<bf16x8*>(&s.V[key * KSTR + dch * 8]) = vreg[u];
-    }
+  auto store_end = [&](DqStage& s) {
     if (tid < BK) s.end[tid] = ereg;
   };
 
@@ -116,10 +114,10 @@ __global__ __launch_bounds__(DqCfg<G>::THREADS) void dq_mfma_kernel(
   int cur = e0 < e1 ? ld_uniform(P.qb_tiles, e0) : 0;
   int nxt = e0 + 1 < e1 ? ld_uniform(P.qb_tiles, e0 + 1) : 0;
   if (e0 < e1) {
-    load_tile(cur & kKbMask);
-    store_tile(st[0]);
+    load_tile(cur & kKbMask, st[0]);
+    store_end(st[0]);
   }
-  wait_vmem();
+  wait_vmem();  // also the direct-to-LDS loads, which the compiler does not track
   __syncthreads();
   for (int e = e0; e < e1; ++e) {
     const int sidx = (e - e0) & 1;
@@ -128,7 +126,7 @@ __global__ __launch_bounds__(DqCfg<G>::THREADS) void dq_mfma_kernel(
     const bool full = (ent & kFull) != 0;
     cur = nxt;
     if (e + 2 < e1) nxt = ld_uniform(P.qb_tiles, e + 2);
-    if (e + 1 < e1) load_tile(cur & kKbMask);
+    if (e + 1 < e1) load_tile(cur & kKbMask, st[sidx ^ 1]);  // that stage was last read in the previous tile
     const DqStage& S = st[sidx];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
@@ -137,7 +135,7 @@ __global__ __launch_bounds__(DqCfg<G>::THREADS) void dq_mfma_kernel(
       for (int dc = 0; dc < 8; ++dc) {
         const bf16x8 a = lds_read16(&S.K[soff(kt * 32 + r, dc * 16 + 8 * hh)]);
         s = mfma(a, qf[dc], s);
-        const bf16x8 b = lds_read16(&S.V[(kt * 32 + r) * KSTR + dc * 16 + 8 * hh]);
+        const bf16x8 b = lds_read16(&S.V[soff(kt * 32 + r, dc * 16 + 8 * hh)]);
         dp = mfma(b, of[dc], dp);
       }
       if (full) {
@@ -159,7 +157,8 @@ __global__ __launch_bounds__(DqCfg<G>::THREADS) void dq_mfma_kernel(
         acc[dt] = mfma(tr_frag_swz(S.K, kt * 32 + 16, dt * 32, lane), d1, acc[dt]);
       }
     }
-    if (e + 1 < e1) store_tile(st[sidx ^ 1]);
+    if (e + 1 < e1) store_end(st[sidx ^ 1]);
+    wait_vmem();  // this wave's direct-to-LDS loads of the next tile have landed
     __syncthreads();
   }
   if (!rok) return;
