@@ -29,7 +29,6 @@ constexpr int D = 128;     // head dim
 constexpr int BQ = 64;     // query rows per plan block
 constexpr int BK = 64;     // key rows per plan block
 constexpr int KSTR = 136;  // LDS row stride (bf16) of tiles read with ds_read_b128
-constexpr int VSTR = 160;  // LDS row stride (bf16) of tiles read with ds_read_tr16_b64
 constexpr int32_t kFull = 0x40000000;
 constexpr int32_t kKbMask = 0x3FFFFFFF;
 
@@ -134,8 +133,7 @@ __device__ __forceinline__ bf16x8 tr_frag(const uint16_t* tile, int stride, int 
 // is free of bank conflicts when each such group of lanes covers distinct banks.
 //
 // Padded tiles: a row stride of 272 bytes (KSTR) puts 16 consecutive rows of a
-// 16-byte column read on distinct banks; 320 bytes (VSTR) puts the 4 rows x
-// 64 bytes of a 32-lane transposed read on distinct banks.
+// 16-byte column read on distinct banks.
 //
 // Swizzled 128-column tiles (256-byte rows, no padding): 16-byte chunk c of
 // row k lives at chunk c ^ swz(k), swz(k) = the two low 2-bit fields of k
