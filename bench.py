@@ -31,8 +31,8 @@ METRIC = "tree attn fwd+bwd unique tokens/s + useful TFLOP/s (% bf16 MFMA peak),
 # HBM traffic of the roofline kernel from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE
 # runs (scaled by the same counters' reading for a plain copy of known size),
 # valid only for the kernel source it was measured on.
-MEASURED_TRAFFIC = {"kernel": "attn_bwd_dkdv_mfma", "source_sha1": "25f136851ec96f8032d4ece88f73f0745567a9e9",
-                    "bytes_per_launch": 20447005149}
+MEASURED_TRAFFIC = {"kernel": "attn_bwd_dkdv_mfma", "source_sha1": "8a483042142e91344d31e3932ccb608c2d8cce28",
+                    "bytes_per_launch": 19649364404}
 
 
 def _source_sha(path):
