@@ -93,6 +93,6 @@ int attn_fwd_core(tt_dtype dt, const PlanPtrs& P, const AttnGeom& g, const void*
 // and added to when acc).
 int attn_bwd_core(tt_dtype dt, const PlanPtrs& P, const AttnGeom& g, const void* q, const void* k, const void* v,
                   const void* o, const void* d_o, const float* lse, float* D, float* dq, void* d_k, void* d_v,
-                  bool acc, bool full_range, hipStream_t st);
+                  bool acc, bool full_range, const float2* cs_tab, hipStream_t st);
 
 }  // namespace ttc

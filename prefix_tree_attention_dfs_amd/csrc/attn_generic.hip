@@ -49,6 +49,20 @@ __global__ __launch_bounds__(256) void rope_kernel(const Tin* __restrict__ x, To
   }
 }
 
+// (cos, sin) of p * theta_k for every position p < n_pos and pair k < half,
+// in fp64, rounded once to fp32 (the table the dK/dV epilogue rotates with).
+__global__ __launch_bounds__(256) void rope_table_kernel(float2* __restrict__ tab, int32_t n_pos, int32_t half,
+                                                         double base) {
+  const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx >= int64_t(n_pos) * half) return;
+  const int64_t p = idx / half;
+  const int k = int(idx - p * half);
+  const double theta = pow(base, -2.0 * double(k) / double(2 * half));
+  double sn, cs;
+  sincos(double(p) * theta, &sn, &cs);
+  tab[idx] = make_float2(float(cs), float(sn));
+}
+
 // ---------------------------------------------------------------- forward
 // One wave per (query row, query head).  Keys are visited tile by tile
 // through the q-block's list of non-empty k-blocks; lane = key.
@@ -329,6 +343,13 @@ int launch_rope(const void* x, void* y, tt_dtype tin, tt_dtype tout, bool acc, c
     rope_kernel<float, uint16_t, false><<<grid, block, 0, st>>>((const float*)x, (uint16_t*)y, P, row0, n_rows, heads, d, b, sg);
   else
     return -1;
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int launch_rope_table(float2* tab, int32_t n_pos, int32_t half, float base, hipStream_t st) {
+  const int64_t n = int64_t(n_pos) * half;
+  if (n == 0) return 0;
+  rope_table_kernel<<<dim3(blocks_for(n, 256)), dim3(256), 0, st>>>(tab, n_pos, half, double(base));
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

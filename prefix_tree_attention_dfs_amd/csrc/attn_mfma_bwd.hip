@@ -210,7 +210,7 @@ template <int G, bool ACC, typename TG>
 __global__ __launch_bounds__(KV_THREADS, 2) void dkdv_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ d_o, const float* __restrict__ lse, const float* __restrict__ Dv,
-    TG* __restrict__ d_k, TG* __restrict__ d_v, PlanPtrs P, AttnGeom g) {
+    TG* __restrict__ d_k, TG* __restrict__ d_v, const float2* __restrict__ cs_tab, PlanPtrs P, AttnGeom g) {
   __shared__ KvLds L;
   if (!plan_matches(P)) return;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r = lane & 31, hh = lane >> 5;
@@ -415,9 +415,10 @@ __global__ __launch_bounds__(KV_THREADS, 2) void dkdv_mfma_kernel(
       dv[dt][i] += L.part[ks][4 + dt][i][lane];
     }
 
-  // dK = R^T (scale * dK') at the key's depth; coordinates (c, c+64) are the
-  // same register of blocks dt and dt+2.
-  const int depth = P.depth[j];
+  // dK = R^T (scale * dK') at the key's depth, with (cos, sin) of depth *
+  // theta_c from the caller's table (none: no rotation); coordinates (c, c+64)
+  // are the same register of blocks dt and dt+2.
+  const float2* __restrict__ cs_row = cs_tab ? cs_tab + int64_t(P.depth[j]) * (D / 2) : nullptr;
   const int64_t base = (int64_t(j) * g.h_kv + kvh) * D;
 #pragma unroll
   for (int dt = 0; dt < 2; ++dt)
@@ -427,14 +428,15 @@ __global__ __launch_bounds__(KV_THREADS, 2) void dkdv_mfma_kernel(
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int c = dt * 32 + 8 * i4 + 4 * hh + e;
-        const double x1 = double(dk[dt][4 * i4 + e]) * g.scale, x2 = double(dk[dt + 2][4 * i4 + e]) * g.scale;
-        double cs = 1.0, sn = 0.0;
-        if (g.rope_base != 0.f) {
-          const double theta = pow(double(g.rope_base), -2.0 * double(c) / double(D));
-          sincos(double(depth) * theta, &sn, &cs);
+        const float x1 = dk[dt][4 * i4 + e] * g.scale, x2 = dk[dt + 2][4 * i4 + e] * g.scale;
+        float cs = 1.f, sn = 0.f;
+        if (cs_row) {
+          const float2 t = cs_row[c];
+          cs = t.x;
+          sn = t.y;
         }
-        lo4[e] = float(x1 * cs + x2 * sn);
-        hi4[e] = float(x2 * cs - x1 * sn);
+        lo4[e] = x1 * cs + x2 * sn;
+        hi4[e] = x2 * cs - x1 * sn;
       }
       const int c0 = dt * 32 + 8 * i4 + 4 * hh;
 #pragma unroll
@@ -475,18 +477,19 @@ int launch_dq_g(const void* q, const void* k, const void* v, const void* d_o, co
 
 template <int G>
 int launch_dkdv_g(const void* q, const void* k, const void* v, const void* d_o, const float* lse, const float* D_,
-                  void* d_k, void* d_v, bool acc, const PlanPtrs& P, const AttnGeom& g, hipStream_t st) {
+                  void* d_k, void* d_v, bool acc, const float2* cs_tab, const PlanPtrs& P, const AttnGeom& g,
+                  hipStream_t st) {
   const int nkb2 = (g.n_k + KV_KEYS - 1) / KV_KEYS;
   if (nkb2 <= 0) return 0;
   const dim3 grid(unsigned(nkb2) * unsigned(g.h_kv)), block(KV_THREADS);
   if (acc)
     dkdv_mfma_kernel<G, true, float><<<grid, block, 0, st>>>((const uint16_t*)q, (const uint16_t*)k,
                                                               (const uint16_t*)v, (const uint16_t*)d_o, lse, D_,
-                                                              (float*)d_k, (float*)d_v, P, g);
+                                                              (float*)d_k, (float*)d_v, cs_tab, P, g);
   else
     dkdv_mfma_kernel<G, false, uint16_t><<<grid, block, 0, st>>>((const uint16_t*)q, (const uint16_t*)k,
                                                                   (const uint16_t*)v, (const uint16_t*)d_o, lse, D_,
-                                                                  (uint16_t*)d_k, (uint16_t*)d_v, P, g);
+                                                                  (uint16_t*)d_k, (uint16_t*)d_v, cs_tab, P, g);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
@@ -511,11 +514,12 @@ int launch_dq_mfma(const void* q, const void* k, const void* v, const void* d_o,
 }
 
 int launch_dkdv_mfma(const void* q, const void* k, const void* v, const void* d_o, const float* lse, const float* D_,
-                     void* d_k, void* d_v, bool acc, const PlanPtrs& P, const AttnGeom& g, hipStream_t st) {
+                     void* d_k, void* d_v, bool acc, const float2* cs_tab, const PlanPtrs& P, const AttnGeom& g,
+                     hipStream_t st) {
   switch (g.h_q / g.h_kv) {
-    case 1: return launch_dkdv_g<1>(q, k, v, d_o, lse, D_, d_k, d_v, acc, P, g, st);
-    case 2: return launch_dkdv_g<2>(q, k, v, d_o, lse, D_, d_k, d_v, acc, P, g, st);
-    case 4: return launch_dkdv_g<4>(q, k, v, d_o, lse, D_, d_k, d_v, acc, P, g, st);
+    case 1: return launch_dkdv_g<1>(q, k, v, d_o, lse, D_, d_k, d_v, acc, cs_tab, P, g, st);
+    case 2: return launch_dkdv_g<2>(q, k, v, d_o, lse, D_, d_k, d_v, acc, cs_tab, P, g, st);
+    case 4: return launch_dkdv_g<4>(q, k, v, d_o, lse, D_, d_k, d_v, acc, cs_tab, P, g, st);
     default: return -1;
   }
 }

@@ -25,8 +25,9 @@ size_t dsize(tt_dtype t) { return t == TT_F32 ? 4 : 2; }
 
 // Workspace carve-up, identical for the size query and the calls.
 struct AttnWs {
-  size_t q_rot = 0, k_rot = 0, D = 0, dq = 0, total = 0;
+  size_t q_rot = 0, k_rot = 0, D = 0, dq = 0, cs = 0, total = 0;
   bool rope = false;
+  int32_t cs_pos = 0;  // rows of the (cos, sin) table: every depth of the tree
 };
 
 AttnWs attn_ws(const tt_attn_args* a, bool bwd) {
@@ -45,6 +46,11 @@ AttnWs attn_ws(const tt_attn_args* a, bool bwd) {
     off = align_up(off + size_t(a->n_q) * a->h_q * 4);
     w.dq = off;
     off = align_up(off + size_t(a->n_q) * a->h_q * a->d * 4);
+    if (w.rope) {
+      w.cs_pos = a->tree->max_depth + 1;
+      w.cs = off;
+      off = align_up(off + size_t(w.cs_pos) * (a->d / 2) * 8);
+    }
   }
   w.total = off;
   return w;
@@ -122,7 +128,7 @@ int attn_fwd_core(tt_dtype dt, const PlanPtrs& P, const AttnGeom& g, const void*
 
 int attn_bwd_core(tt_dtype dt, const PlanPtrs& P, const AttnGeom& g, const void* q, const void* k, const void* v,
                   const void* o, const void* d_o, const float* lse, float* D, float* dq, void* d_k, void* d_v,
-                  bool acc, bool full_range, hipStream_t st) {
+                  bool acc, bool full_range, const float2* cs_tab, hipStream_t st) {
   const char* fn = "attention backward";
   {
     KTimer t("attn_bwd_pre", st);
@@ -135,7 +141,7 @@ int attn_bwd_core(tt_dtype dt, const PlanPtrs& P, const AttnGeom& g, const void*
     }
     {
       KTimer t("attn_bwd_dkdv_mfma", st);
-      if (launch_dkdv_mfma(q, k, v, d_o, lse, D, d_k, d_v, acc, P, g, st)) return dev_fail(fn, "dk/dv kernel");
+      if (launch_dkdv_mfma(q, k, v, d_o, lse, D, d_k, d_v, acc, cs_tab, P, g, st)) return dev_fail(fn, "dk/dv kernel");
     }
   } else {
     {
@@ -285,9 +291,15 @@ extern "C" int tree_attn_bwd(const tt_attn_bwd_args* b, tt_stream stream) {
   }
   float* D = reinterpret_cast<float*>(ws + w.D);
   float* dq = reinterpret_cast<float*>(ws + w.dq);
+  float2* cs_tab = nullptr;
+  if (w.rope && w.cs_pos > 0) {
+    cs_tab = reinterpret_cast<float2*>(ws + w.cs);
+    KTimer t("rope_table", st);
+    if (launch_rope_table(cs_tab, w.cs_pos, a->d / 2, a->rope_base, st)) return dev_fail(fn, "rope table");
+  }
   const bool full_range = a->q_off == 0 && a->n_q == P.N;
   if ((rc = ttc::attn_bwd_core(a->dtype, P, g, q, k, a->v, a->o, b->d_o, a->lse, D, dq, b->d_k, b->d_v, acc,
-                               full_range, st)))
+                               full_range, cs_tab, st)))
     return rc;
   // dQ: rotate back at the query rows' depths, convert to the output dtype
   if (a->n_q > 0) {

@@ -30,7 +30,11 @@ int launch_fwd_mfma(const void* q, const void* k, const void* v, void* o, float*
 int launch_dq_mfma(const void* q, const void* k, const void* v, const void* d_o, const float* lse, const float* D,
                    float* dq_acc, const PlanPtrs& P, const AttnGeom& g, bool full_range, hipStream_t st);
 int launch_dkdv_mfma(const void* q, const void* k, const void* v, const void* d_o, const float* lse, const float* D,
-                     void* d_k, void* d_v, bool acc, const PlanPtrs& P, const AttnGeom& g, hipStream_t st);
+                     void* d_k, void* d_v, bool acc, const float2* cs_tab, const PlanPtrs& P, const AttnGeom& g,
+                     hipStream_t st);
+// (cos, sin) of p * theta_k, theta_k = base^(-2k / (2 half)), for p < n_pos and
+// k < half, computed in fp64 and rounded to fp32: tab[p * half + k]
+int launch_rope_table(float2* tab, int32_t n_pos, int32_t half, float base, hipStream_t st);
 
 // Zeroes `bytes` (a multiple of 4) at p.
 int launch_fill_zero(void* p, size_t bytes, hipStream_t st);

@@ -210,7 +210,7 @@ extern "C" int tree_attn_path(const tt_path_args* a, tt_stream stream) {
         g.n_q = c1 - qo;
         g.n_k = c1;
         if ((rc = ttc::attn_bwd_core(dt, P, g, Qp + size_t(qo) * qrow, Kp, Vp, Op + size_t(qo) * qrow, dOc,
-                                     LSEp + size_t(qo) * hq, D, dq, dKa, dVa, true, false, st)))
+                                     LSEp + size_t(qo) * hq, D, dq, dKa, dVa, true, false, nullptr, st)))
           return rc;
         KTimer t("dq_finalize", st);
         if (launch_rope(dq + pad * hq * d, d_q + row * qrow, TT_F32, dt, false, P, c0, c1 - c0, a->h_q, a->d, rb,
