@@ -191,7 +191,9 @@ typedef struct {
   const void* v;           /* device [n_k, h_kv, d] dtype */
   void* o;                 /* device [n_q, h_q, d] dtype: output of fwd, input of bwd */
   float* lse;              /* device [n_q, h_q] float32: output of fwd, input of bwd */
-  void* workspace;         /* device scratch, >= tree_attn_workspace_bytes */
+  void* workspace;         /* device scratch, >= tree_attn_workspace_bytes: rotated q and k
+                              (with RoPE); for the backward also D, fp32 dQ and a (cos, sin)
+                              table of the tree's depths; contents are not kept between calls */
   size_t workspace_bytes;
 } tt_attn_args;
 
