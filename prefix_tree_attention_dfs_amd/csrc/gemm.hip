@@ -6,15 +6,32 @@
 //   dH = dZ W^T        (NT: A = dZ [M][K'], B stored [N][K'] = W)
 //   dW = H^T dZ        (TN: A stored [K][M] = H, B = dZ [K][N])
 //
-// Block tile 256 x 256, k-step 64, 16 waves of 64 x 64 (2 x 2 tiles of
-// v_mfma_f32_32x32x16_bf16, 64 accumulator registers, at most 128 VGPRs), so
-// that four waves share each SIMD and some issue products while others wait
-// on loads, the barrier or the epilogue; double-buffered LDS.  Operands whose reduction
-// index is contiguous in memory are read with ds_read_b128 (or two b64 reads
-// matching the permuted reduction order below); operands stored with the
-// reduction index strided are read with ds_read_tr16_b64, which returns rows
-// k0 + {4h..4h+3, 8+4h..8+4h+3} for lane half h -- when one operand is read
-// that way, the other is read in the same reduction order.
+// Block tile 256 x 256, 8 waves of 128 x 64 (4 x 2 tiles of
+// v_mfma_f32_32x32x16_bf16, two waves per SIMD).  The reduction is staged 32
+// at a time through four LDS buffers of 32 KB, filled by 16-byte buffer loads
+// that write straight into LDS, three stages ahead of the one being
+// multiplied: one stage is ~1000 cycles of matrix work per SIMD, so about
+// three of them cover a load's latency from HBM.  One barrier per stage
+// publishes it and frees the buffer its loads go into.
+//
+// A tile operand is stored one of two ways, each swizzled at 16-byte chunks
+// so that its reads are free of LDS bank conflicts (64 banks of 4 bytes;
+// 16-byte reads are served 16 lanes per cycle, 8-byte reads 32):
+//   * k contiguous (rows = m or n, 32 k = 64-byte rows): chunk c of row q at
+//     chunk c ^ ((q >> 2) & 3).  A fragment is a 16-byte read per lane at row
+//     row0 + r, chunk 2 ks + h; 16 consecutive rows cover all 16 bank groups.
+//   * k strided (rows = k, 256 m or n = 512-byte rows): chunk c of row k at
+//     chunk c ^ ((k & 3) << 2).  A fragment is two ds_read_tr16_b64, rows
+//     8h..8h+3 and 8h+4..8h+7 of the 16-row step, so every operand comes out
+//     in the natural reduction order (lane (r, h) holds k = 8h .. 8h+7); the
+//     32 lanes of a read cover 4 consecutive rows x 4 adjacent chunks, which
+//     the swizzle spreads over all 16 bank groups.
+// The buffer descriptor of a stage is built from the tile's own origin, so
+// matrices above 4 GB (Z) need no 64-bit offsets; a lane whose chunk lies
+// outside the matrix gets an offset past the descriptor's record count, for
+// which the load writes zeros.  Every column count of a k-strided operand and
+// the reduction length of a k-contiguous one are multiples of 8 (checked by
+// the caller), so a chunk is either wholly inside or wholly outside.
 #include "device.h"
 #include "kernels.h"
 #include "mfma_common.h"
@@ -23,111 +40,108 @@ using namespace ttm;
 
 namespace {
 
-constexpr int GBM = 256, GBN = 256, GBK = 64;
-constexpr int GTHREADS = 1024;  // 16 waves: 4 (m) x 4 (n), each 64 x 64
-constexpr int WTN = 2;          // 32-column tiles per wave
-constexpr int WTM = 2;          // 32-row tiles per wave
-// LDS row strides (elements), chosen for gfx950's 64 banks: 16-byte reads are
-// served 16 lanes per cycle, 8-byte and transposed reads 32 lanes per cycle.
-constexpr int KROW = GBK + 8;    // rows along k, read 16 bytes per lane (144-byte rows)
-constexpr int KROW8 = GBK + 4;   // rows along k, read 8 bytes per lane (136 bytes: 32 rows on distinct banks)
-constexpr int XROW = GBN + 32;   // rows along m or n, read transposed (576 bytes: 4 rows x 64 bytes on distinct banks)
+constexpr int GBM = 256, GBN = 256, GBK = 32;
+constexpr int GSTAGES = 4;
+constexpr int GWAVES = 8;  // 2 (m) x 4 (n), each 128 x 64
+constexpr int GTHREADS = GWAVES * 64;
+constexpr int WTM = 4;  // 32-row tiles per wave
+constexpr int WTN = 2;  // 32-column tiles per wave
+constexpr uint32_t TILE_BYTES = 256 * GBK * 2;          // 16 KB, either layout
+constexpr uint32_t STAGE_BYTES = 2 * TILE_BYTES;        // A then B
+constexpr int LOADS_PER_WAVE = TILE_BYTES / 1024 / GWAVES;  // 1 KB per load instruction
+static_assert(LOADS_PER_WAVE == 2, "staging assumes two loads per wave per operand");
+constexpr uint32_t kRecords = 0x7FFFFFF0u;  // descriptor size: every in-matrix offset is below it
+constexpr uint32_t kOut = 0x80000000u;      // offset past it: the load writes zeros
 
-template <bool A_T, bool B_T>
-struct GemmLds {
-  static constexpr bool PERM = A_T || !B_T;  // some operand is read transposed: permuted reduction order
-  static constexpr int A_STRIDE = A_T ? XROW : (PERM ? KROW8 : KROW);
-  static constexpr int B_STRIDE = B_T ? KROW : XROW;
-  // A tile: [GBM][A_STRIDE] (m rows, k contiguous) or [GBK][XROW] (k rows, m contiguous)
-  static constexpr int A_ELEMS = A_T ? GBK * XROW : GBM * A_STRIDE;
-  static constexpr int B_ELEMS = B_T ? GBN * KROW : GBK * XROW;
-};
-
-// Loads a 256 x 64 (or 64 x 256) bf16 tile of a row-major matrix in 16-byte
-// chunks; out-of-range rows/chunks read a clamped address and are zeroed.
-// Every column count here is a multiple of 8 (checked by the caller), so a
-// chunk is either wholly inside or wholly outside the matrix.
-template <bool KROWS>  // true: tile rows are the matrix rows (k contiguous, 64 wide)
-__device__ __forceinline__ void load_tile(const uint16_t* __restrict__ X, int64_t ld, int64_t r0, int64_t c0,
-                                          int64_t nrows, int64_t ncols, int tid, bf16x8 (&reg)[2]) {
-  // KROWS: tile = 256 rows x 64 cols (8 chunks per row); else 64 rows x 256 cols (32 chunks per row)
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int c = tid + u * GTHREADS;
-    const int row = KROWS ? (c >> 3) : (c >> 5);
-    const int col = KROWS ? ((c & 7) << 3) : ((c & 31) << 3);
-    const int64_t gr = r0 + row, gc = c0 + col;
-    const bool ok = gr < nrows && gc + 8 <= ncols;
-    const int64_t cr = gr < nrows ? gr : nrows - 1;
-    const int64_t cc = gc + 8 <= ncols ? gc : 0;
-    const bf16x8 x = ld16(X + cr * ld + cc);
-    reg[u] = ok ? x : zero8();
-  }
+// s_waitcnt with vmcnt = n (n < 16), expcnt and lgkmcnt left at their maxima
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 16, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
 }
 
-template <bool KROWS, int STRIDE>
-__device__ __forceinline__ void store_tile(uint16_t* s, int tid, const bf16x8 (&reg)[2]) {
+// Per-lane staging of one operand tile.  Lane l of the wave's load u fills
+// LDS slot p = 64 (2 wave + u) + l; `off` is the byte offset of the global
+// chunk it fetches relative to the stage's tile origin (kOut when the chunk's
+// row or column is outside the matrix), `kpos` the chunk's reduction index
+// within the stage (checked only in a ragged last stage).
+template <bool KCONTIG>
+__device__ __forceinline__ void stage_lane(int wave, int lane, int64_t ld, int64_t rc0, int64_t nrc, uint32_t (&off)[2],
+                                           int (&kpos)[2]) {
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int c = tid + u * GTHREADS;
-    const int row = KROWS ? (c >> 3) : (c >> 5);
-    const int col = KROWS ? ((c & 7) << 3) : ((c & 31) << 3);
-    if constexpr (STRIDE % 8 == 0) {
-      *reinterpret_cast<bf16x8*>(s + row * STRIDE + col) = reg[u];
-    } else {  // rows only 8-byte aligned: two 8-byte stores
-      bf16x4 lo, hi;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        lo[e] = reg[u][e];
-        hi[e] = reg[u][4 + e];
-      }
-      *reinterpret_cast<bf16x4*>(s + row * STRIDE + col) = lo;
-      *reinterpret_cast<bf16x4*>(s + row * STRIDE + col + 4) = hi;
+  for (int u = 0; u < LOADS_PER_WAVE; ++u) {
+    const int p = 64 * (LOADS_PER_WAVE * wave + u) + lane;
+    if (KCONTIG) {  // row q (m or n) holds 4 chunks of k
+      const int q = p >> 2, c = (p & 3) ^ ((q >> 2) & 3);
+      off[u] = rc0 + q < nrc ? uint32_t(q * ld * 2 + 16 * c) : kOut;
+      kpos[u] = 8 * c;
+    } else {  // row k holds 32 chunks of m or n
+      const int k = p >> 5, c = (p & 31) ^ ((k & 3) << 2);
+      off[u] = rc0 + 8 * c < nrc ? uint32_t(k * ld * 2 + 16 * c) : kOut;
+      kpos[u] = k;
     }
   }
 }
 
 // OUT: 0 = bf16 store, 1 = f32 store
 template <bool A_T, bool B_T, int OUT>
-__global__ __launch_bounds__(GTHREADS) void gemm_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
-                                                        void* __restrict__ Cv, int64_t M, int64_t N, int64_t K,
-                                                        int tiles_n) {
-  using L = GemmLds<A_T, B_T>;
+// 128 KB of LDS allows one workgroup per CU, i.e. two waves per SIMD: the
+// compiler may use all 256 VGPRs to issue fragment reads early.
+__global__ __launch_bounds__(GTHREADS) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
+                                                        void* __restrict__ Cv, int64_t M, int64_t N, int64_t K) {
   extern __shared__ __align__(16) uint16_t smem[];
-  constexpr int STAGE = L::A_ELEMS + L::B_ELEMS;  // stage s: A at s*STAGE, B right after
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r = lane & 31, hh = lane >> 5;
-  const int wm = wave >> 2, wn = wave & 3;  // 4 x 4
-  // block -> tile; consecutive blocks share a B column panel
-  const int tm = blockIdx.x % ((M + GBM - 1) / GBM);
-  const int tn = blockIdx.x / ((M + GBM - 1) / GBM);
-  (void)tiles_n;
+  const int wm = wave >> 2, wn = wave & 3;
+  // block -> tile: consecutive blocks share a B column panel, and the 32
+  // workgroups an XCD holds at once (every 8th block) span 8 row and 4 column
+  // panels
+  const int tiles_m = int((M + GBM - 1) / GBM);
+  const int tm = blockIdx.x % tiles_m, tn = blockIdx.x / tiles_m;
   const int64_t m0 = int64_t(tm) * GBM, n0 = int64_t(tn) * GBN;
-  // leading dimensions (row-major storage)
   const int64_t lda = A_T ? M : K;  // A stored [M][K] or [K][M]
   const int64_t ldb = B_T ? K : N;  // B stored [K][N] or [N][K]
 
-  bf16x8 ra[2], rb[2];
-  auto gload = [&](int64_t k0) {
-    if (A_T)
-      load_tile<false>(A, lda, k0, m0, K, M, tid, ra);
-    else
-      load_tile<true>(A, lda, m0, k0, M, K, tid, ra);
-    if (B_T)
-      load_tile<true>(B, ldb, n0, k0, N, K, tid, rb);
-    else
-      load_tile<false>(B, ldb, k0, n0, K, N, tid, rb);
+  uint32_t offa[2], offb[2];
+  int kpa[2], kpb[2];
+  stage_lane<!A_T>(wave, lane, lda, m0, M, offa, kpa);
+  stage_lane<B_T>(wave, lane, ldb, n0, N, offb, kpb);
+  const uint32_t lds0 = lds_u32(smem);
+
+  // loads of reduction stage kt into buffer kt % GSTAGES (four per wave)
+  const int nk = int((K + GBK - 1) / GBK);
+  auto issue = [&](int kt) {
+    const int64_t k0 = int64_t(kt) * GBK, krem = K - k0;
+    const uint32_t la = lds0 + uint32_t(kt % GSTAGES) * STAGE_BYTES + uint32_t(LOADS_PER_WAVE * wave) * 1024u;
+    const uint32_t lb = la + TILE_BYTES;
+    const rsrc_t ra = make_rsrc(A_T ? A + k0 * lda + m0 : A + m0 * lda + k0, kRecords);
+    const rsrc_t rb = make_rsrc(B_T ? B + n0 * ldb + k0 : B + k0 * ldb + n0, kRecords);
+    if (krem >= GBK) {
+#pragma unroll
+      for (int u = 0; u < LOADS_PER_WAVE; ++u) dma16(ra, offa[u], 0, la + 1024u * u);
+#pragma unroll
+      for (int u = 0; u < LOADS_PER_WAVE; ++u) dma16(rb, offb[u], 0, lb + 1024u * u);
+    } else {
+#pragma unroll
+      for (int u = 0; u < LOADS_PER_WAVE; ++u) dma16(ra, kpa[u] < krem ? offa[u] : kOut, 0, la + 1024u * u);
+#pragma unroll
+      for (int u = 0; u < LOADS_PER_WAVE; ++u) dma16(rb, kpb[u] < krem ? offb[u] : kOut, 0, lb + 1024u * u);
+    }
   };
-  auto sstore = [&](int s) {
-    uint16_t* sa = smem + s * STAGE;
-    uint16_t* sb = sa + L::A_ELEMS;
-    if (A_T)
-      store_tile<false, XROW>(sa, tid, ra);
-    else
-      store_tile<true, L::A_STRIDE>(sa, tid, ra);
-    if (B_T)
-      store_tile<true, KROW>(sb, tid, rb);
-    else
-      store_tile<false, XROW>(sb, tid, rb);
+
+  // Fragment addresses (bytes within a tile) of this lane.  k contiguous:
+  // row row0 + r, chunk 2 ks + hh; the swizzle term depends on r alone since
+  // row0 is a multiple of 32.  k strided: group g = lane / 16 reads rows
+  // 16 ks + 8 (g / 2) + (lane % 16) / 4 (+4 for the second half), columns
+  // col0 + 16 (g % 2) + 4 (lane % 4) .. +3.
+  const int rsw = (r >> 2) & 3;
+  const uint32_t rowfrag0 = uint32_t(r * 64 + ((hh ^ rsw) << 4));        // ks = 0: chunk hh
+  const uint32_t rowfrag1 = uint32_t(r * 64 + (((2 + hh) ^ rsw) << 4));  // ks = 1: chunk 2 + hh
+  const int g = lane >> 4, rr = lane & 15;
+  const int csw = ((rr >> 2) & 3) << 2;
+  const uint32_t colrow = uint32_t((8 * (g >> 1) + (rr >> 2)) * 512 + (rr & 1) * 8);
+  const int clow = 2 * (g & 1) + ((rr & 3) >> 1);  // chunk within the 4-chunk group
+  auto colfrag_off = [&](int col0) {  // col0: multiple of 32
+    return colrow + uint32_t((((col0 >> 3) ^ csw) + clow) << 4);
   };
 
   f32x16 acc[WTM][WTN];
@@ -136,55 +150,71 @@ __global__ __launch_bounds__(GTHREADS) void gemm_kernel(const uint16_t* __restri
 #pragma unroll
     for (int j = 0; j < WTN; ++j) acc[i][j] = zero16();
 
-  const int nk = int((K + GBK - 1) / GBK);
-  if (nk > 0) {
-    gload(0);
-    sstore(0);
+  // byte offsets of this wave's fragments within the A and B tiles
+  uint32_t afo[WTM][2], bfo[WTN][2];
+#pragma unroll
+  for (int i = 0; i < WTM; ++i) {
+    const int mrow = wm * 128 + i * 32;
+    if (A_T) {
+      afo[i][0] = colfrag_off(mrow);
+      afo[i][1] = afo[i][0] + 16 * 512;
+    } else {
+      afo[i][0] = uint32_t(mrow * 64) + rowfrag0;
+      afo[i][1] = uint32_t(mrow * 64) + rowfrag1;
+    }
   }
-  __syncthreads();
-  // reduction order: natural (8h + s) unless some operand is read transposed
-  constexpr bool PERM = L::PERM;
+#pragma unroll
+  for (int j = 0; j < WTN; ++j) {
+    const int ncol = wn * 64 + j * 32;
+    if (B_T) {
+      bfo[j][0] = uint32_t(ncol * 64) + rowfrag0;
+      bfo[j][1] = uint32_t(ncol * 64) + rowfrag1;
+    } else {
+      bfo[j][0] = colfrag_off(ncol);
+      bfo[j][1] = bfo[j][0] + 16 * 512;
+    }
+  }
+  const char* lds_c = reinterpret_cast<const char*>(smem);
+  auto frag = [&](bool tr, uint32_t byte) -> bf16x8 {
+    const uint16_t* p = reinterpret_cast<const uint16_t*>(lds_c + byte);
+    if (!tr) return lds_read16(p);
+    const bf16x4 lo = lds_tr4(p), hi = lds_tr4(p + 4 * 256);  // rows +4: same swizzle, 2 KB further
+    bf16x8 a;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      a[e] = lo[e];
+      a[4 + e] = hi[e];
+    }
+    return a;
+  };
+
+#pragma unroll
+  for (int s = 0; s < GSTAGES - 1; ++s)
+    if (s < nk) issue(s);
   for (int kt = 0; kt < nk; ++kt) {
-    const int s = kt & 1;
-    if (kt + 1 < nk) gload(int64_t(kt + 1) * GBK);
-    const uint16_t* a_s = smem + s * STAGE;
-    const uint16_t* b_s = a_s + L::A_ELEMS;
+    // stage kt has landed once at most the later stages' loads are pending
+    const int ahead = nk - 1 - kt;
+    if (ahead >= 2)
+      wait_vm<4 * LOADS_PER_WAVE>();
+    else if (ahead == 1)
+      wait_vm<2 * LOADS_PER_WAVE>();
+    else
+      wait_vm<0>();
+    __syncthreads();
+    if (kt + GSTAGES - 1 < nk) issue(kt + GSTAGES - 1);
+    const uint32_t sa = uint32_t(kt % GSTAGES) * STAGE_BYTES, sb = sa + TILE_BYTES;
 #pragma unroll
     for (int ks = 0; ks < GBK / 16; ++ks) {
       bf16x8 af[WTM], bfr[WTN];
 #pragma unroll
-      for (int i = 0; i < WTM; ++i) {
-        const int mrow = wm * 64 + i * 32;
-        if (A_T) {
-          af[i] = tr_frag(a_s, XROW, ks * 16, mrow, lane);
-        } else if (PERM) {
-          const uint16_t* p = a_s + (mrow + r) * L::A_STRIDE + ks * 16 + 4 * hh;
-          const bf16x4 lo = *reinterpret_cast<const bf16x4*>(p);
-          const bf16x4 hi = *reinterpret_cast<const bf16x4*>(p + 8);
+      for (int i = 0; i < WTM; ++i) af[i] = frag(A_T, sa + afo[i][ks]);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            af[i][e] = lo[e];
-            af[i][4 + e] = hi[e];
-          }
-        } else {
-          af[i] = lds_read16(a_s + (mrow + r) * L::A_STRIDE + ks * 16 + 8 * hh);
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < WTN; ++j) {
-        const int ncol = wn * 64 + j * 32;
-        if (B_T)
-          bfr[j] = lds_read16(b_s + (ncol + r) * KROW + ks * 16 + 8 * hh);
-        else
-          bfr[j] = tr_frag(b_s, XROW, ks * 16, ncol, lane);
-      }
+      for (int j = 0; j < WTN; ++j) bfr[j] = frag(!B_T, sb + bfo[j][ks]);
 #pragma unroll
       for (int i = 0; i < WTM; ++i)
 #pragma unroll
         for (int j = 0; j < WTN; ++j) acc[i][j] = mfma(af[i], bfr[j], acc[i][j]);
     }
-    if (kt + 1 < nk) sstore(s ^ 1);
-    __syncthreads();
   }
 
   // epilogue: lane holds C[m = 8*(e/4) + 4hh + e%4][n = r] of each 32 x 32 tile
@@ -196,7 +226,7 @@ __global__ __launch_bounds__(GTHREADS) void gemm_kernel(const uint16_t* __restri
       if (n >= N) continue;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int64_t m = m0 + wm * 64 + i * 32 + 8 * (e >> 2) + 4 * hh + (e & 3);
+        const int64_t m = m0 + wm * 128 + i * 32 + 8 * (e >> 2) + 4 * hh + (e & 3);
         if (m >= M) continue;
         if (OUT == 0)
           static_cast<uint16_t*>(Cv)[m * N + n] = ttd::f2bf(acc[i][j][e]);
@@ -211,8 +241,10 @@ int launch_gemm(const uint16_t* A, const uint16_t* B, void* C, int64_t M, int64_
   if (M <= 0 || N <= 0) return 0;
   const int64_t tm = (M + GBM - 1) / GBM, tn = (N + GBN - 1) / GBN;
   if (tm * tn >= (int64_t(1) << 31)) return -1;
-  using L = GemmLds<A_T, B_T>;
-  const size_t lds = size_t(2) * (L::A_ELEMS + L::B_ELEMS) * sizeof(uint16_t);
+  // per-lane offsets are 32-bit: 256 rows (or 32 k rows) of the widest operand
+  const int64_t lda = A_T ? M : K, ldb = B_T ? K : N;
+  if (int64_t(GBM) * (lda > ldb ? lda : ldb) * 2 >= int64_t(kRecords)) return -1;
+  const size_t lds = size_t(GSTAGES) * STAGE_BYTES;
   static bool attr_set = false;
   if (!attr_set) {
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel<A_T, B_T, OUT>),
@@ -220,7 +252,7 @@ int launch_gemm(const uint16_t* A, const uint16_t* B, void* C, int64_t M, int64_
       return -1;
     attr_set = true;
   }
-  gemm_kernel<A_T, B_T, OUT><<<dim3(unsigned(tm * tn)), dim3(GTHREADS), lds, st>>>(A, B, C, M, N, K, int(tn));
+  gemm_kernel<A_T, B_T, OUT><<<dim3(unsigned(tm * tn)), dim3(GTHREADS), lds, st>>>(A, B, C, M, N, K);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
