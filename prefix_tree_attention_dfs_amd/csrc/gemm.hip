@@ -89,6 +89,10 @@ template <bool A_T, bool B_T, int OUT>
 // compiler may use all 256 VGPRs to issue fragment reads early.
 __global__ __launch_bounds__(GTHREADS) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
                                                         void* __restrict__ Cv, int64_t M, int64_t N, int64_t K) {
+  // The output pointer is consumed here, so its scalar load completes in the
+  // prologue: a scalar load still in flight would make every LDS wait in the
+  // loop a wait for all outstanding LDS reads.
+  if (Cv == nullptr) return;
   extern __shared__ __align__(16) uint16_t smem[];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r = lane & 31, hh = lane >> 5;
   const int wm = wave >> 2, wn = wave & 3;
@@ -188,11 +192,22 @@ __global__ __launch_bounds__(GTHREADS) __attribute__((amdgpu_waves_per_eu(2, 2))
     return a;
   };
 
+  // fragments of one 16-deep step of the stage in buffer b
+  auto load_frags = [&](int b, int ks, bf16x8 (&af)[WTM], bf16x8 (&bfr)[WTN]) {
+    const uint32_t sa = uint32_t(b) * STAGE_BYTES, sb = sa + TILE_BYTES;
 #pragma unroll
-  for (int s = 0; s < GSTAGES - 1; ++s)
-    if (s < nk) issue(s);
-  for (int kt = 0; kt < nk; ++kt) {
-    // stage kt has landed once at most the later stages' loads are pending
+    for (int i = 0; i < WTM; ++i) af[i] = frag(A_T, sa + afo[i][ks]);
+#pragma unroll
+    for (int j = 0; j < WTN; ++j) bfr[j] = frag(!B_T, sb + bfo[j][ks]);
+  };
+  auto mma = [&](const bf16x8 (&af)[WTM], const bf16x8 (&bfr)[WTN]) {
+#pragma unroll
+    for (int i = 0; i < WTM; ++i)
+#pragma unroll
+      for (int j = 0; j < WTN; ++j) acc[i][j] = mfma(af[i], bfr[j], acc[i][j]);
+  };
+  // stage kt has landed once at most the later stages' loads are pending
+  auto wait_stage = [&](int kt) {
     const int ahead = nk - 1 - kt;
     if (ahead >= 2)
       wait_vm<4 * LOADS_PER_WAVE>();
@@ -200,21 +215,40 @@ __global__ __launch_bounds__(GTHREADS) __attribute__((amdgpu_waves_per_eu(2, 2))
       wait_vm<2 * LOADS_PER_WAVE>();
     else
       wait_vm<0>();
+  };
+
+  // Software pipeline across the barrier: the second step's fragments of
+  // stage kt are read before the barrier that publishes stage kt + 1, and
+  // their products are issued after it, behind the first reads of stage
+  // kt + 1.  The buffer the new loads go into held stage kt, whose reads
+  // have all completed at the barrier.
+#pragma unroll
+  for (int s = 0; s < GSTAGES - 1; ++s)
+    if (s < nk) issue(s);
+  bf16x8 a0[WTM], b0[WTN], a1[WTM], b1[WTN];
+  if (nk > 0) {
+    wait_stage(0);
     __syncthreads();
-    if (kt + GSTAGES - 1 < nk) issue(kt + GSTAGES - 1);
-    const uint32_t sa = uint32_t(kt % GSTAGES) * STAGE_BYTES, sb = sa + TILE_BYTES;
-#pragma unroll
-    for (int ks = 0; ks < GBK / 16; ++ks) {
-      bf16x8 af[WTM], bfr[WTN];
-#pragma unroll
-      for (int i = 0; i < WTM; ++i) af[i] = frag(A_T, sa + afo[i][ks]);
-#pragma unroll
-      for (int j = 0; j < WTN; ++j) bfr[j] = frag(!B_T, sb + bfo[j][ks]);
-#pragma unroll
-      for (int i = 0; i < WTM; ++i)
-#pragma unroll
-        for (int j = 0; j < WTN; ++j) acc[i][j] = mfma(af[i], bfr[j], acc[i][j]);
-    }
+    if (GSTAGES - 1 < nk) issue(GSTAGES - 1);
+    load_frags(0, 0, a0, b0);
+  }
+  // (the last stage is peeled off, so that no path into the products after
+  // the barrier carries reads of the current stage still in flight)
+  for (int kt = 0; kt < nk - 1; ++kt) {
+    load_frags(kt % GSTAGES, 1, a1, b1);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(a0, b0);
+    wait_stage(kt + 1);
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    if (kt + GSTAGES < nk) issue(kt + GSTAGES);
+    load_frags((kt + 1) % GSTAGES, 0, a0, b0);
+    mma(a1, b1);
+  }
+  if (nk > 0) {
+    load_frags((nk - 1) % GSTAGES, 1, a1, b1);
+    mma(a0, b0);
+    mma(a1, b1);
   }
 
   // epilogue: lane holds C[m = 8*(e/4) + 4hh + e%4][n = r] of each 32 x 32 tile
