@@ -7,19 +7,21 @@
 //   dW = H^T dZ        (TN: A stored [K][M] = H, B = dZ [K][N])
 //
 // Block tile 256 x 256, 8 waves of 128 x 64 (4 x 2 tiles of
-// v_mfma_f32_32x32x16_bf16, two waves per SIMD).  The reduction is staged 32
-// at a time through four LDS buffers of 32 KB, filled by 16-byte buffer loads
-// that write straight into LDS, three stages ahead of the one being
-// multiplied: one stage is ~1000 cycles of matrix work per SIMD, so about
-// three of them cover a load's latency from HBM.  One barrier per stage
-// publishes it and frees the buffer its loads go into.
+// v_mfma_f32_32x32x16_bf16, two waves per SIMD).  The reduction is staged 64
+// at a time through two LDS buffers of 64 KB, filled by 16-byte buffer loads
+// that write straight into LDS one stage ahead of the one being multiplied
+// (a stage is ~2000 cycles of matrix work per SIMD).  One barrier per stage
+// publishes it and frees the buffer its loads go into; 32-deep stages with
+// three in flight took twice the barriers and ran 7% slower.
 //
 // A tile operand is stored one of two ways, each swizzled at 16-byte chunks
 // so that its reads are free of LDS bank conflicts (64 banks of 4 bytes;
 // 16-byte reads are served 16 lanes per cycle, 8-byte reads 32):
-//   * k contiguous (rows = m or n, 32 k = 64-byte rows): chunk c of row q at
-//     chunk c ^ ((q >> 2) & 3).  A fragment is a 16-byte read per lane at row
-//     row0 + r, chunk 2 ks + h; 16 consecutive rows cover all 16 bank groups.
+//   * k contiguous (rows = m or n, 64 k = 128-byte rows): chunk c of row q
+//     at chunk c ^ ((q >> 1) & 7).  A fragment is a 16-byte read per lane at
+//     row row0 + r, chunk 2 ks + h; 16 consecutive rows, (q & 1) choosing the
+//     half of the bank space and the swizzle the chunk, cover all 16 bank
+//     groups.
 //   * k strided (rows = k, 256 m or n = 512-byte rows): chunk c of row k at
 //     chunk c ^ ((k & 3) << 2).  A fragment is two ds_read_tr16_b64, rows
 //     8h..8h+3 and 8h+4..8h+7 of the 16-row step, so every operand comes out
@@ -40,8 +42,8 @@ using namespace ttm;
 
 namespace {
 
-constexpr int GBM = 256, GBN = 256, GBK = 32;
-constexpr int GSTAGES = 4;
+constexpr int GBM = 256, GBN = 256, GBK = 64;
+constexpr int GSTAGES = 2;
 constexpr int GWAVES = 8;  // 2 (m) x 4 (n), each 128 x 64
 constexpr int GTHREADS = GWAVES * 64;
 constexpr int WTM = 4;  // 32-row tiles per wave
@@ -49,7 +51,7 @@ constexpr int WTN = 2;  // 32-column tiles per wave
 constexpr uint32_t TILE_BYTES = 256 * GBK * 2;          // 16 KB, either layout
 constexpr uint32_t STAGE_BYTES = 2 * TILE_BYTES;        // A then B
 constexpr int LOADS_PER_WAVE = TILE_BYTES / 1024 / GWAVES;  // 1 KB per load instruction
-static_assert(LOADS_PER_WAVE == 2, "staging assumes two loads per wave per operand");
+static_assert(LOADS_PER_WAVE == 4, "staging assumes four loads per wave per operand");
 constexpr uint32_t kRecords = 0x7FFFFFF0u;  // descriptor size: every in-matrix offset is below it
 constexpr uint32_t kOut = 0x80000000u;      // offset past it: the load writes zeros
 
@@ -61,18 +63,18 @@ __device__ __forceinline__ void wait_vm() {
 }
 
 // Per-lane staging of one operand tile.  Lane l of the wave's load u fills
-// LDS slot p = 64 (2 wave + u) + l; `off` is the byte offset of the global
+// LDS slot p = 64 (4 wave + u) + l; `off` is the byte offset of the global
 // chunk it fetches relative to the stage's tile origin (kOut when the chunk's
 // row or column is outside the matrix), `kpos` the chunk's reduction index
 // within the stage (checked only in a ragged last stage).
 template <bool KCONTIG>
-__device__ __forceinline__ void stage_lane(int wave, int lane, int64_t ld, int64_t rc0, int64_t nrc, uint32_t (&off)[2],
-                                           int (&kpos)[2]) {
+__device__ __forceinline__ void stage_lane(int wave, int lane, int64_t ld, int64_t rc0, int64_t nrc, uint32_t (&off)[LOADS_PER_WAVE],
+                                           int (&kpos)[LOADS_PER_WAVE]) {
 #pragma unroll
   for (int u = 0; u < LOADS_PER_WAVE; ++u) {
     const int p = 64 * (LOADS_PER_WAVE * wave + u) + lane;
-    if (KCONTIG) {  // row q (m or n) holds 4 chunks of k
-      const int q = p >> 2, c = (p & 3) ^ ((q >> 2) & 3);
+    if (KCONTIG) {  // row q (m or n) holds 8 chunks of k
+      const int q = p >> 3, c = (p & 7) ^ ((q >> 1) & 7);
       off[u] = rc0 + q < nrc ? uint32_t(q * ld * 2 + 16 * c) : kOut;
       kpos[u] = 8 * c;
     } else {  // row k holds 32 chunks of m or n
@@ -83,10 +85,10 @@ __device__ __forceinline__ void stage_lane(int wave, int lane, int64_t ld, int64
   }
 }
 
-// OUT: 0 = bf16 store, 1 = f32 store
+// OUT: 0 = bf16 store, 1 = f32 store.  128 KB of LDS allows one workgroup
+// per CU, i.e. two waves per SIMD: the compiler may use all 256 VGPRs to
+// issue fragment reads early.
 template <bool A_T, bool B_T, int OUT>
-// 128 KB of LDS allows one workgroup per CU, i.e. two waves per SIMD: the
-// compiler may use all 256 VGPRs to issue fragment reads early.
 __global__ __launch_bounds__(GTHREADS) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
                                                         void* __restrict__ Cv, int64_t M, int64_t N, int64_t K) {
   // The output pointer is consumed here, so its scalar load completes in the
@@ -105,13 +107,13 @@ __global__ __launch_bounds__(GTHREADS) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int64_t lda = A_T ? M : K;  // A stored [M][K] or [K][M]
   const int64_t ldb = B_T ? K : N;  // B stored [K][N] or [N][K]
 
-  uint32_t offa[2], offb[2];
-  int kpa[2], kpb[2];
+  uint32_t offa[LOADS_PER_WAVE], offb[LOADS_PER_WAVE];
+  int kpa[LOADS_PER_WAVE], kpb[LOADS_PER_WAVE];
   stage_lane<!A_T>(wave, lane, lda, m0, M, offa, kpa);
   stage_lane<B_T>(wave, lane, ldb, n0, N, offb, kpb);
   const uint32_t lds0 = lds_u32(smem);
 
-  // loads of reduction stage kt into buffer kt % GSTAGES (four per wave)
+  // loads of reduction stage kt into buffer kt % GSTAGES (eight per wave)
   const int nk = int((K + GBK - 1) / GBK);
   auto issue = [&](int kt) {
     const int64_t k0 = int64_t(kt) * GBK, krem = K - k0;
@@ -137,9 +139,11 @@ __global__ __launch_bounds__(GTHREADS) __attribute__((amdgpu_waves_per_eu(2, 2))
   // row0 is a multiple of 32.  k strided: group g = lane / 16 reads rows
   // 16 ks + 8 (g / 2) + (lane % 16) / 4 (+4 for the second half), columns
   // col0 + 16 (g % 2) + 4 (lane % 4) .. +3.
-  const int rsw = (r >> 2) & 3;
-  const uint32_t rowfrag0 = uint32_t(r * 64 + ((hh ^ rsw) << 4));        // ks = 0: chunk hh
-  const uint32_t rowfrag1 = uint32_t(r * 64 + (((2 + hh) ^ rsw) << 4));  // ks = 1: chunk 2 + hh
+  constexpr int NKS = GBK / 16;
+  const int rsw = (r >> 1) & 7;
+  uint32_t rowfrag[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) rowfrag[ks] = uint32_t(r * 128 + (((2 * ks + hh) ^ rsw) << 4));
   const int g = lane >> 4, rr = lane & 15;
   const int csw = ((rr >> 2) & 3) << 2;
   const uint32_t colrow = uint32_t((8 * (g >> 1) + (rr >> 2)) * 512 + (rr & 1) * 8);
@@ -155,28 +159,20 @@ __global__ __launch_bounds__(GTHREADS) __attribute__((amdgpu_waves_per_eu(2, 2))
     for (int j = 0; j < WTN; ++j) acc[i][j] = zero16();
 
   // byte offsets of this wave's fragments within the A and B tiles
-  uint32_t afo[WTM][2], bfo[WTN][2];
+  uint32_t afo[WTM][NKS], bfo[WTN][NKS];
 #pragma unroll
   for (int i = 0; i < WTM; ++i) {
     const int mrow = wm * 128 + i * 32;
-    if (A_T) {
-      afo[i][0] = colfrag_off(mrow);
-      afo[i][1] = afo[i][0] + 16 * 512;
-    } else {
-      afo[i][0] = uint32_t(mrow * 64) + rowfrag0;
-      afo[i][1] = uint32_t(mrow * 64) + rowfrag1;
-    }
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+      afo[i][ks] = A_T ? colfrag_off(mrow) + ks * 16 * 512 : uint32_t(mrow * 128) + rowfrag[ks];
   }
 #pragma unroll
   for (int j = 0; j < WTN; ++j) {
     const int ncol = wn * 64 + j * 32;
-    if (B_T) {
-      bfo[j][0] = uint32_t(ncol * 64) + rowfrag0;
-      bfo[j][1] = uint32_t(ncol * 64) + rowfrag1;
-    } else {
-      bfo[j][0] = colfrag_off(ncol);
-      bfo[j][1] = bfo[j][0] + 16 * 512;
-    }
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+      bfo[j][ks] = B_T ? uint32_t(ncol * 128) + rowfrag[ks] : colfrag_off(ncol) + ks * 16 * 512;
   }
   const char* lds_c = reinterpret_cast<const char*>(smem);
   auto frag = [&](bool tr, uint32_t byte) -> bf16x8 {
@@ -206,47 +202,44 @@ __global__ __launch_bounds__(GTHREADS) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
       for (int j = 0; j < WTN; ++j) acc[i][j] = mfma(af[i], bfr[j], acc[i][j]);
   };
-  // stage kt has landed once at most the later stages' loads are pending
-  auto wait_stage = [&](int kt) {
-    const int ahead = nk - 1 - kt;
-    if (ahead >= 2)
-      wait_vm<4 * LOADS_PER_WAVE>();
-    else if (ahead == 1)
-      wait_vm<2 * LOADS_PER_WAVE>();
-    else
-      wait_vm<0>();
-  };
-
-  // Software pipeline across the barrier: the second step's fragments of
-  // stage kt are read before the barrier that publishes stage kt + 1, and
-  // their products are issued after it, behind the first reads of stage
-  // kt + 1.  The buffer the new loads go into held stage kt, whose reads
-  // have all completed at the barrier.
-#pragma unroll
-  for (int s = 0; s < GSTAGES - 1; ++s)
-    if (s < nk) issue(s);
+  // Two 64-deep stages: the loads of stage kt + 1 are issued right after
+  // the barrier that publishes stage kt, and the products of stage kt's last
+  // 16-deep step are issued after the next barrier, behind the first reads
+  // of stage kt + 1.
   bf16x8 a0[WTM], b0[WTN], a1[WTM], b1[WTN];
   if (nk > 0) {
-    wait_stage(0);
+    issue(0);
+    wait_vm<0>();
     __syncthreads();
-    if (GSTAGES - 1 < nk) issue(GSTAGES - 1);
+    if (1 < nk) issue(1);
     load_frags(0, 0, a0, b0);
   }
-  // (the last stage is peeled off, so that no path into the products after
-  // the barrier carries reads of the current stage still in flight)
   for (int kt = 0; kt < nk - 1; ++kt) {
-    load_frags(kt % GSTAGES, 1, a1, b1);
+    const int b = kt & 1;
+    load_frags(b, 1, a1, b1);
     __builtin_amdgcn_sched_barrier(0);
     mma(a0, b0);
-    wait_stage(kt + 1);
+    load_frags(b, 2, a0, b0);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(a1, b1);
+    load_frags(b, 3, a1, b1);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(a0, b0);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vm<0>();
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
-    if (kt + GSTAGES < nk) issue(kt + GSTAGES);
-    load_frags((kt + 1) % GSTAGES, 0, a0, b0);
+    if (kt + 2 < nk) issue(kt + 2);
+    load_frags(b ^ 1, 0, a0, b0);
     mma(a1, b1);
   }
   if (nk > 0) {
-    load_frags((nk - 1) % GSTAGES, 1, a1, b1);
+    const int b = (nk - 1) & 1;
+    load_frags(b, 1, a1, b1);
+    mma(a0, b0);
+    load_frags(b, 2, a0, b0);
+    mma(a1, b1);
+    load_frags(b, 3, a1, b1);
     mma(a0, b0);
     mma(a1, b1);
   }
