@@ -147,6 +147,32 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ o, c
   if (lane == 0) D[r] = a;
 }
 
+// bf16 rows of length d = 8 L (L a power of two, at most 64): L lanes per
+// row, each with one 16-byte load of O and of dO, then a reduction over the
+// row's L lanes.  Rows start 16-byte aligned (checked by the launcher).
+template <int L>
+__global__ __launch_bounds__(256) void bwd_pre_vec_kernel(const uint16_t* __restrict__ o,
+                                                          const uint16_t* __restrict__ d_o, float* __restrict__ D,
+                                                          int64_t rows) {
+  const int64_t t = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t r = t / L;
+  const int sub = int(t % L);
+  float a = 0.f;
+  if (r < rows) {
+    const uint4 x = *reinterpret_cast<const uint4*>(o + r * (8 * L) + 8 * sub);
+    const uint4 y = *reinterpret_cast<const uint4*>(d_o + r * (8 * L) + 8 * sub);
+    const uint32_t xs[4] = {x.x, x.y, x.z, x.w}, ys[4] = {y.x, y.y, y.z, y.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      a += __uint_as_float(xs[e] << 16) * __uint_as_float(ys[e] << 16);
+      a += __uint_as_float(xs[e] & 0xFFFF0000u) * __uint_as_float(ys[e] & 0xFFFF0000u);
+    }
+  }
+#pragma unroll
+  for (int m = L / 2; m >= 1; m >>= 1) a += __shfl_xor(a, m, kWave);
+  if (r < rows && sub == 0) D[r] = a;
+}
+
 // ---------------------------------------------------------------- dQ
 // One wave per (query row, head); writes scale * sum_j dS_ij k'_j (rotated
 // frame, fp32) into dq_acc.
@@ -373,6 +399,20 @@ int launch_fwd_generic(tt_dtype dt, const void* q, const void* k, const void* v,
 
 int launch_bwd_pre(tt_dtype dt, const void* o, const void* d_o, float* D, int64_t rows, int d, hipStream_t st) {
   if (rows == 0) return 0;
+  const int L = d / 8;
+  const bool vec = dt == TT_BF16 && d % 8 == 0 && L <= 64 && (L & (L - 1)) == 0 &&
+                   (reinterpret_cast<uintptr_t>(o) & 15u) == 0 && (reinterpret_cast<uintptr_t>(d_o) & 15u) == 0;
+  if (vec) {
+    const dim3 vgrid(blocks_for(rows * L, 256)), vblock(256);
+    const uint16_t *ob = static_cast<const uint16_t*>(o), *db = static_cast<const uint16_t*>(d_o);
+    switch (L) {
+#define PRE(LL) \
+  case LL: bwd_pre_vec_kernel<LL><<<vgrid, vblock, 0, st>>>(ob, db, D, rows); break;
+      PRE(1) PRE(2) PRE(4) PRE(8) PRE(16) PRE(32) PRE(64)
+#undef PRE
+    }
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+  }
   const dim3 grid(blocks_for(rows, 4)), block(256);
   if (dt == TT_F32)
     bwd_pre_kernel<float><<<grid, block, 0, st>>>((const float*)o, (const float*)d_o, D, rows, d);
