@@ -90,9 +90,12 @@ int attn_fwd_core(tt_dtype dt, const PlanPtrs& P, const AttnGeom& g, const void*
 
 // Backward on rotated q, k: D = rowsum(dO o O) into D, dQ (rotated frame,
 // float32, not yet rotated back) into dq, dK and dV into d_k, d_v (float32
-// and added to when acc).
+// and added to when acc).  When dq_final is set and the bf16 matrix-core
+// kernels run, dQ is instead rotated back with cs_tab and stored in bf16 to
+// dq_final, and *dq_done is set (dq is then not written).
 int attn_bwd_core(tt_dtype dt, const PlanPtrs& P, const AttnGeom& g, const void* q, const void* k, const void* v,
                   const void* o, const void* d_o, const float* lse, float* D, float* dq, void* d_k, void* d_v,
-                  bool acc, bool full_range, const float2* cs_tab, hipStream_t st);
+                  bool acc, bool full_range, const float2* cs_tab, hipStream_t st, void* dq_final = nullptr,
+                  bool* dq_done = nullptr);
 
 }  // namespace ttc

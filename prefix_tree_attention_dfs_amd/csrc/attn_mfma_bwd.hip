@@ -45,11 +45,15 @@ struct __align__(16) DqStage {
   int32_t end[BK];
 };
 
-template <int G>
+// FIN: the epilogue rotates dQ back at the query's depth (R^T with the
+// caller's (cos, sin) table; none: no rotation) and stores it in bf16 to
+// dq_out; otherwise it stores the rotated-frame dQ in fp32 to dq_acc.
+template <int G, bool FIN>
 __global__ __launch_bounds__(DqCfg<G>::THREADS) void dq_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ d_o, const float* __restrict__ lse, const float* __restrict__ Dv,
-    float* __restrict__ dq_acc, PlanPtrs P, AttnGeom g, int full_range, int qb_first, int n_qb) {
+    float* __restrict__ dq_acc, uint16_t* __restrict__ dq_out, const float2* __restrict__ cs_tab, PlanPtrs P,
+    AttnGeom g, int full_range, int qb_first, int n_qb) {
   using C = DqCfg<G>;
   __shared__ DqStage st[2];
   if (!plan_matches(P)) return;
@@ -166,6 +170,34 @@ __global__ __launch_bounds__(DqCfg<G>::THREADS) void dq_mfma_kernel(
     __syncthreads();
   }
   if (!rok) return;
+  if (FIN) {
+    // coordinates (c, c+64) of a rotation pair are the same register of
+    // blocks dt and dt+2: dQ = R^T (scale * dQ') in registers, one bf16 rounding
+    const float2* __restrict__ cs_row = cs_tab ? cs_tab + int64_t(P.depth[qpos]) * (D / 2) : nullptr;
+    uint16_t* orow = dq_out + (int64_t(row) * g.h_q + head) * D;
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int c0 = dt * 32 + 8 * i4 + 4 * hh;
+        bf16x4 lo4, hi4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float x1 = acc[dt][4 * i4 + e] * g.scale, x2 = acc[dt + 2][4 * i4 + e] * g.scale;
+          float cs = 1.f, sn = 0.f;
+          if (cs_row) {
+            const float2 t = cs_row[c0 + e];
+            cs = t.x;
+            sn = t.y;
+          }
+          lo4[e] = __bf16(x1 * cs + x2 * sn);
+          hi4[e] = __bf16(x2 * cs - x1 * sn);
+        }
+        *reinterpret_cast<bf16x4*>(orow + c0) = lo4;
+        *reinterpret_cast<bf16x4*>(orow + c0 + 64) = hi4;
+      }
+    return;
+  }
   float* out = dq_acc + (int64_t(row) * g.h_q + head) * D;
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
@@ -468,14 +500,21 @@ __global__ __launch_bounds__(KV_THREADS, 2) void dkdv_mfma_kernel(
 
 template <int G>
 int launch_dq_g(const void* q, const void* k, const void* v, const void* d_o, const float* lse, const float* D_,
-                float* dq_acc, const PlanPtrs& P, const AttnGeom& g, bool full_range, hipStream_t st) {
+                float* dq_acc, void* dq_out, const float2* cs_tab, const PlanPtrs& P, const AttnGeom& g,
+                bool full_range, hipStream_t st) {
   const int qb_first = g.q_off / BQ;
   const int qb_end = (g.q_off + g.n_q + BQ - 1) / BQ;
   const int n_qb = qb_end - qb_first;
   if (n_qb <= 0) return 0;
-  dq_mfma_kernel<G><<<dim3(unsigned(n_qb) * unsigned(g.h_kv)), dim3(DqCfg<G>::THREADS), 0, st>>>(
-      (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)d_o, lse, D_, dq_acc, P, g,
-      full_range ? 1 : 0, qb_first, n_qb);
+  const dim3 grid(unsigned(n_qb) * unsigned(g.h_kv)), block(DqCfg<G>::THREADS);
+  if (dq_out)
+    dq_mfma_kernel<G, true><<<grid, block, 0, st>>>((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
+                                                    (const uint16_t*)d_o, lse, D_, nullptr, (uint16_t*)dq_out,
+                                                    cs_tab, P, g, full_range ? 1 : 0, qb_first, n_qb);
+  else
+    dq_mfma_kernel<G, false><<<grid, block, 0, st>>>((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
+                                                     (const uint16_t*)d_o, lse, D_, dq_acc, nullptr, nullptr, P,
+                                                     g, full_range ? 1 : 0, qb_first, n_qb);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
@@ -508,11 +547,12 @@ bool mfma_bwd_supported(const AttnGeom& g, const PlanPtrs& P) {
 }
 
 int launch_dq_mfma(const void* q, const void* k, const void* v, const void* d_o, const float* lse, const float* D_,
-                   float* dq_acc, const PlanPtrs& P, const AttnGeom& g, bool full_range, hipStream_t st) {
+                   float* dq_acc, void* dq_out, const float2* cs_tab, const PlanPtrs& P, const AttnGeom& g,
+                   bool full_range, hipStream_t st) {
   switch (g.h_q / g.h_kv) {
-    case 1: return launch_dq_g<1>(q, k, v, d_o, lse, D_, dq_acc, P, g, full_range, st);
-    case 2: return launch_dq_g<2>(q, k, v, d_o, lse, D_, dq_acc, P, g, full_range, st);
-    case 4: return launch_dq_g<4>(q, k, v, d_o, lse, D_, dq_acc, P, g, full_range, st);
+    case 1: return launch_dq_g<1>(q, k, v, d_o, lse, D_, dq_acc, dq_out, cs_tab, P, g, full_range, st);
+    case 2: return launch_dq_g<2>(q, k, v, d_o, lse, D_, dq_acc, dq_out, cs_tab, P, g, full_range, st);
+    case 4: return launch_dq_g<4>(q, k, v, d_o, lse, D_, dq_acc, dq_out, cs_tab, P, g, full_range, st);
     default: return -1;
   }
 }

@@ -128,8 +128,9 @@ int attn_fwd_core(tt_dtype dt, const PlanPtrs& P, const AttnGeom& g, const void*
 
 int attn_bwd_core(tt_dtype dt, const PlanPtrs& P, const AttnGeom& g, const void* q, const void* k, const void* v,
                   const void* o, const void* d_o, const float* lse, float* D, float* dq, void* d_k, void* d_v,
-                  bool acc, bool full_range, const float2* cs_tab, hipStream_t st) {
+                  bool acc, bool full_range, const float2* cs_tab, hipStream_t st, void* dq_final, bool* dq_done) {
   const char* fn = "attention backward";
+  if (dq_done) *dq_done = false;
   {
     KTimer t("attn_bwd_pre", st);
     if (launch_bwd_pre(dt, o, d_o, D, int64_t(g.n_q) * g.h_q, g.d, st)) return dev_fail(fn, "preprocess");
@@ -137,7 +138,9 @@ int attn_bwd_core(tt_dtype dt, const PlanPtrs& P, const AttnGeom& g, const void*
   if (dt == TT_BF16 && mfma_bwd_supported(g, P)) {
     {
       KTimer t("attn_bwd_dq_mfma", st);
-      if (launch_dq_mfma(q, k, v, d_o, lse, D, dq, P, g, full_range, st)) return dev_fail(fn, "dq kernel");
+      if (launch_dq_mfma(q, k, v, d_o, lse, D, dq, dq_final, cs_tab, P, g, full_range, st))
+        return dev_fail(fn, "dq kernel");
+      if (dq_final && dq_done) *dq_done = true;
     }
     {
       KTimer t("attn_bwd_dkdv_mfma", st);
@@ -298,11 +301,15 @@ extern "C" int tree_attn_bwd(const tt_attn_bwd_args* b, tt_stream stream) {
     if (launch_rope_table(cs_tab, w.cs_pos, a->d / 2, a->rope_base, st)) return dev_fail(fn, "rope table");
   }
   const bool full_range = a->q_off == 0 && a->n_q == P.N;
+  // the bf16 dQ kernel rotates back and converts in its epilogue (table
+  // built above whenever RoPE is on); other paths finalize from fp32 below
+  bool dq_done = false;
+  void* dq_final = (a->dtype == TT_BF16 && (!w.rope || cs_tab)) ? b->d_q : nullptr;
   if ((rc = ttc::attn_bwd_core(a->dtype, P, g, q, k, a->v, a->o, b->d_o, a->lse, D, dq, b->d_k, b->d_v, acc,
-                               full_range, cs_tab, st)))
+                               full_range, cs_tab, st, dq_final, &dq_done)))
     return rc;
   // dQ: rotate back at the query rows' depths, convert to the output dtype
-  if (a->n_q > 0) {
+  if (a->n_q > 0 && !dq_done) {
     KTimer t("dq_finalize", st);
     if (launch_rope(dq, b->d_q, TT_F32, a->dtype, false, P, a->q_off, a->n_q, a->h_q, a->d, a->rope_base, true,
                     st))

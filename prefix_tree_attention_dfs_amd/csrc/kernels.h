@@ -27,8 +27,11 @@ bool mfma_attn_supported(const AttnGeom& g, const PlanPtrs& P);
 bool mfma_bwd_supported(const AttnGeom& g, const PlanPtrs& P);
 int launch_fwd_mfma(const void* q, const void* k, const void* v, void* o, float* lse, const PlanPtrs& P,
                     const AttnGeom& g, bool full_range, hipStream_t st);
+// dQ into dq_acc (fp32, rotated frame), or, when dq_out is set, rotated back
+// with cs_tab (may be null: no rotation) and stored in bf16 to dq_out.
 int launch_dq_mfma(const void* q, const void* k, const void* v, const void* d_o, const float* lse, const float* D,
-                   float* dq_acc, const PlanPtrs& P, const AttnGeom& g, bool full_range, hipStream_t st);
+                   float* dq_acc, void* dq_out, const float2* cs_tab, const PlanPtrs& P, const AttnGeom& g,
+                   bool full_range, hipStream_t st);
 int launch_dkdv_mfma(const void* q, const void* k, const void* v, const void* d_o, const float* lse, const float* D,
                      void* d_k, void* d_v, bool acc, const float2* cs_tab, const PlanPtrs& P, const AttnGeom& g,
                      hipStream_t st);
