@@ -49,6 +49,57 @@ __global__ __launch_bounds__(256) void rope_kernel(const Tin* __restrict__ x, To
   }
 }
 
+// The bf16 -> bf16 rotation of rope_kernel with 16-byte accesses: one thread
+// per (row, 8 consecutive pairs), the same fp64 angles and arithmetic (results
+// are bit-identical), looping over the heads.  Needs half % 8 == 0 and
+// 16-byte aligned rows.
+__global__ __launch_bounds__(256) void rope_bf16x8_kernel(const uint16_t* __restrict__ x, uint16_t* __restrict__ y,
+                                                          PlanPtrs P, int32_t row0, int32_t n_rows, int32_t heads,
+                                                          int32_t d, double base, double sign) {
+  if (!plan_matches(P)) return;
+  const int half = d >> 1, oct = half >> 3;
+  const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx >= int64_t(n_rows) * oct) return;
+  const int64_t r = idx / oct;
+  const int k0 = int(idx - r * oct) * 8;
+  double c[8], sn[8];
+  const double pos = double(P.depth[row0 + r]);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    c[e] = 1.0;
+    sn[e] = 0.0;
+    if (base != 0.0) {
+      const double theta = pow(base, -2.0 * double(k0 + e) / double(d));
+      sincos(pos * theta, &sn[e], &c[e]);
+      sn[e] *= sign;
+    }
+  }
+#pragma unroll 2
+  for (int h = 0; h < heads; ++h) {
+    const int64_t b = (r * heads + h) * d + k0;
+    const uint4 a1 = *reinterpret_cast<const uint4*>(x + b);
+    const uint4 a2 = *reinterpret_cast<const uint4*>(x + b + half);
+    const uint32_t w1[4] = {a1.x, a1.y, a1.z, a1.w}, w2[4] = {a2.x, a2.y, a2.z, a2.w};
+    uint32_t o1[4], o2[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      uint32_t lo1 = 0, lo2 = 0;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int e = 2 * u + t;
+        const double x1 = bf2f(uint16_t(w1[u] >> (16 * t))), x2 = bf2f(uint16_t(w2[u] >> (16 * t)));
+        const float y1 = float(x1 * c[e] - x2 * sn[e]), y2 = float(x2 * c[e] + x1 * sn[e]);
+        lo1 |= uint32_t(f2bf(y1)) << (16 * t);
+        lo2 |= uint32_t(f2bf(y2)) << (16 * t);
+      }
+      o1[u] = lo1;
+      o2[u] = lo2;
+    }
+    *reinterpret_cast<uint4*>(y + b) = make_uint4(o1[0], o1[1], o1[2], o1[3]);
+    *reinterpret_cast<uint4*>(y + b + half) = make_uint4(o2[0], o2[1], o2[2], o2[3]);
+  }
+}
+
 // (cos, sin) of p * theta_k for every position p < n_pos and pair k < half,
 // in fp64, rounded once to fp32 (the table the dK/dV epilogue rotates with).
 __global__ __launch_bounds__(256) void rope_table_kernel(float2* __restrict__ tab, int32_t n_pos, int32_t half,
@@ -363,7 +414,12 @@ int launch_rope(const void* x, void* y, tt_dtype tin, tt_dtype tout, bool acc, c
     rope_kernel<float, float, false><<<grid, block, 0, st>>>((const float*)x, (float*)y, P, row0, n_rows, heads, d, b, sg);
   else if (tin == TT_F32 && tout == TT_F32 && acc)
     rope_kernel<float, float, true><<<grid, block, 0, st>>>((const float*)x, (float*)y, P, row0, n_rows, heads, d, b, sg);
-  else if (tin == TT_BF16 && tout == TT_BF16 && !acc)
+  else if (tin == TT_BF16 && tout == TT_BF16 && !acc && (d % 16) == 0 &&
+           ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(y)) & 15) == 0) {
+    const int64_t nv = int64_t(n_rows) * (d / 16);
+    rope_bf16x8_kernel<<<dim3(blocks_for(nv, 256)), block, 0, st>>>((const uint16_t*)x, (uint16_t*)y, P, row0, n_rows,
+                                                                      heads, d, b, sg);
+  } else if (tin == TT_BF16 && tout == TT_BF16 && !acc)
     rope_kernel<uint16_t, uint16_t, false><<<grid, block, 0, st>>>((const uint16_t*)x, (uint16_t*)y, P, row0, n_rows, heads, d, b, sg);
   else if (tin == TT_F32 && tout == TT_BF16 && !acc)
     rope_kernel<float, uint16_t, false><<<grid, block, 0, st>>>((const float*)x, (uint16_t*)y, P, row0, n_rows, heads, d, b, sg);
