@@ -157,6 +157,23 @@ def test_mfma_backward_peaky(name):
         assert rel_err(g_, r_) < TOL, (n, rel_err(g_, r_))
 
 
+def test_mfma_backward_no_rope_custom_scale():
+    """rope_base = 0: no rotation anywhere (the dQ and dK/dV epilogues only
+    scale and convert); a scale other than 1/sqrt(d)."""
+    case = TREES["beam_small"]()
+    tree = tt.Tree(case.seqs)
+    o = dfs_arrays(case.seqs)
+    plan = tree.upload_plan()
+    (q, qn), (k, kn), (v, vn), (do, don) = inputs(torch.bfloat16, 43, tree.N, tree.N, 8, 2, 128, 128 ** -0.5)
+    O, L = tt.tree_attn_fwd(tree, plan, q, k, v, scale=0.05, rope_base=0.0)
+    dq, dk, dv = tt.tree_attn_bwd(tree, plan, q, k, v, O, L, do, scale=0.05, rope_base=0.0)
+    Or, Lr, _ = OA.forward(o, qn, kn, vn, scale=0.05, rope_base=0, which="leaves")
+    dQr, dKr, dVr = OA.backward(o, qn, kn, vn, don, scale=0.05, rope_base=0, which="leaves")
+    assert rel_err(O, Or) < TOL and rel_err(L, Lr) < TOL
+    for n, g_, r_ in zip(("dq", "dk", "dv"), (dq, dk, dv), (dQr, dKr, dVr)):
+        assert rel_err(g_, r_) < TOL, (n, rel_err(g_, r_))
+
+
 def test_mfma_backward_chunks_accumulate():
     """Right-to-left chunks of a suffix against a cached prefix, dK/dV added
     into fp32 buffers across chunks == oracle backward with dO = 0 on the prefix."""
