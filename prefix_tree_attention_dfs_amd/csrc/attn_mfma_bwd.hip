@@ -10,9 +10,9 @@
 //   dq_mfma_kernel   query-stationary (the forward's walk over the block's
 //                    non-empty key tiles):  S^T = K Q^T, P^T, dP^T = V dO^T,
 //                    dS^T = P^T (dP^T - D), dQ^T += K^T dS^T.
-//   dkdv_mfma_kernel key-stationary: one workgroup per 128 keys x kv head,
-//                    K and V of those keys loaded once into LDS; 8 waves =
-//                    4 key slices of 32 x 2 query halves.  It streams 64-row
+//   dkdv_mfma_kernel key-stationary: one workgroup per 256 keys x kv head,
+//                    each of its 8 waves owning 32 keys (K in registers, V
+//                    in LDS, both loaded once).  It streams 64-row
 //                    Q / dO tiles of every query head of the group over the
 //                    contiguous range of query rows that see its keys, top
 //                    down, loaded straight from global memory into LDS (no
@@ -211,17 +211,18 @@ __global__ __launch_bounds__(DqCfg<G>::THREADS) void dq_mfma_kernel(
 }
 
 // ------------------------------------------------------------------ dK, dV
-// One workgroup per 128 keys x kv head, 8 waves (two per SIMD).  K and V of
-// the 128 keys stay in LDS for the whole kernel; query tiles of 64 rows (Q,
-// dO, LSE, D of one head) stream through a double-buffered stage.  Wave w
-// owns keys 32*(w%4) .. +32 and the query half w/4 of every staged tile; the
-// two waves that share keys add their partial dK, dV through LDS at the end.
+// One workgroup per 256 keys x kv head, 8 waves (two per SIMD); wave w owns
+// keys 32 w .. +32 for the whole kernel: its K fragments (B operands of S)
+// sit in registers, loaded once from global memory, and V of the 256 keys in
+// LDS.  Query tiles of 64 rows (Q, dO, LSE, D of one head) stream through a
+// double-buffered stage; every wave runs both 32-row halves of each staged
+// tile, so a stage (32 KB) feeds 512 MFMAs and each wave's dK, dV are
+// complete at the end (no exchange between waves).
 constexpr int KV_WAVES = 8;
 constexpr int KV_THREADS = KV_WAVES * 64;
-constexpr int KV_KEYS = 128;                       // keys per workgroup
+constexpr int KV_KEYS = 32 * KV_WAVES;             // keys per workgroup
 constexpr int QT = 64;                             // query rows per staged tile
-constexpr int QCH = (QT * D / 8) / KV_THREADS;     // 16-byte chunks per thread per Q (or dO) tile
-constexpr int KCH = (KV_KEYS * D / 8) / KV_THREADS;
+constexpr int VCH = (KV_KEYS * D / 8) / KV_THREADS;  // 16-byte chunks of V per thread
 
 struct __align__(16) KvStage {
   uint16_t Q[QT * D];  // swizzled (row reads for S, transposed reads for dK^T)
@@ -231,15 +232,9 @@ struct __align__(16) KvStage {
 };
 
 struct __align__(16) KvLds {
-  union {
-    struct {
-      uint16_t K[KV_KEYS * KSTR];  // padded: row reads only
-      uint16_t V[KV_KEYS * KSTR];
-      KvStage st[2];
-    } run;
-    float part[4][8][16][64];  // epilogue: partial dK^T, dV^T of the upper query halves
-  };
-  int32_t red[2][KV_WAVES];
+  uint16_t V[KV_KEYS * KSTR];  // padded: row reads only
+  KvStage st[2];
+  int32_t red[KV_WAVES];
 };
 
 template <int G, bool ACC, typename TG>
@@ -250,27 +245,31 @@ __global__ __launch_bounds__(KV_THREADS, 2) void dkdv_mfma_kernel(
   __shared__ KvLds L;
   if (!plan_matches(P)) return;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r = lane & 31, hh = lane >> 5;
-  const int ks = wave & 3;  // key sub-tile
-  const int mt = wave >> 2; // query half of each staged tile
   const int kvh = blockIdx.x % g.h_kv;
   const int kb2 = blockIdx.x / g.h_kv;
   const int kbase = kb2 * KV_KEYS;
-  const int j = kbase + ks * 32 + r;  // this lane's key (lane column of S, dP, dK^T, dV^T)
+  const int j = kbase + wave * 32 + r;  // this lane's key (lane column of S, dP, dK^T, dV^T)
   const bool jok = j < g.n_k;
   const float c2 = g.scale * kLog2e;
   const float inv_scale = 1.f / g.scale;
 
-  // K, V of the workgroup's keys -> LDS (rows past n_k are zero)
+  // V of the workgroup's keys -> LDS (rows past n_k are zero)
 #pragma unroll
-  for (int u = 0; u < KCH; ++u) {
+  for (int u = 0; u < VCH; ++u) {
     const int c = tid + u * KV_THREADS;
     const int key = c >> 4, dch = c & 15;
     const int jj = kbase + key;
     const bool ok = jj < g.n_k;
-    const int64_t off = (int64_t(ok ? jj : g.n_k - 1) * g.h_kv + kvh) * D + dch * 8;
-    const bf16x8 kx = ld16(k + off), vx = ld16(v + off);
-    *reinterpret_cast<bf16x8*>(&L.run.K[key * KSTR + dch * 8]) = ok ? kx : zero8();
-    *reinterpret_cast<bf16x8*>(&L.run.V[key * KSTR + dch * 8]) = ok ? vx : zero8();
+    const bf16x8 vx = ld16(v + (int64_t(ok ? jj : g.n_k - 1) * g.h_kv + kvh) * D + dch * 8);
+    *reinterpret_cast<bf16x8*>(&L.V[key * KSTR + dch * 8]) = ok ? vx : zero8();
+  }
+  // this wave's 32 keys as B operands of S = Q K^T, straight from global
+  // memory: lane (r, hh) holds K[j][16 dc + 8 hh .. +8]
+  bf16x8 kf[8];
+  {
+    const uint16_t* krow = k + (int64_t(jok ? j : 0) * g.h_kv + kvh) * D + 8 * hh;
+#pragma unroll
+    for (int dc = 0; dc < 8; ++dc) kf[dc] = jok ? ld16(krow + dc * 16) : zero8();
   }
   const int endj = jok ? P.end[j] : -1;
 
@@ -281,18 +280,15 @@ __global__ __launch_bounds__(KV_THREADS, 2) void dkdv_mfma_kernel(
     mx = max(mx, __shfl_xor(mx, o, 64));
     mn = min(mn, __shfl_xor(mn, o, 64));
   }
-  if (lane == 0) {
-    L.red[0][wave] = mx;
-    L.red[1][wave] = mn;
-  }
+  if (lane == 0) L.red[wave] = mx;
   __syncthreads();
   int hi = 0;
 #pragma unroll
-  for (int w = 0; w < 4; ++w) hi = max(hi, L.red[0][w]);
-  const int wave_min_end = L.red[1][ks];
+  for (int w = 0; w < KV_WAVES; ++w) hi = max(hi, L.red[w]);
+  const int wave_min_end = __builtin_amdgcn_readfirstlane(mn);
   const int lo = max(kbase, g.q_off);
   hi = min(hi, g.q_off + g.n_q);
-  const int wave_kmax = kbase + ks * 32 + 31;
+  const int wave_kmax = kbase + wave * 32 + 31;
 
   f32x16 dk[4], dv[4];
 #pragma unroll
@@ -348,108 +344,86 @@ __global__ __launch_bounds__(KV_THREADS, 2) void dkdv_mfma_kernel(
   };
 
   if (n_steps > 0) {
-    load_tile(0, L.run.st[0]);
-    store_rows(L.run.st[0]);
+    load_tile(0, L.st[0]);
+    store_rows(L.st[0]);
   }
   wait_vmem();  // also the direct-to-LDS loads, which the compiler does not track
   __syncthreads();
-  const uint16_t* Kt = L.run.K + (ks * 32 + r) * KSTR + 8 * hh;
-  const uint16_t* Vt = L.run.V + (ks * 32 + r) * KSTR + 8 * hh;
-  // this wave's 32 keys as B operands of S = Q K^T, read once: they are the
-  // same in every step (V's are read from LDS each step; holding both spills)
-  bf16x8 kf[8];
-#pragma unroll
-  for (int dc = 0; dc < 8; ++dc) kf[dc] = lds_read16(Kt + dc * 16);
+  const uint16_t* Vt = L.V + (wave * 32 + r) * KSTR + 8 * hh;
   for (int step = 0; step < n_steps; ++step) {
     const int sidx = step & 1;
     const int qt = qt_first + (n_steps - 1 - step) / G;
-    if (step + 1 < n_steps) load_tile(step + 1, L.run.st[sidx ^ 1]);  // that stage was last read in the previous step
-    const KvStage& S = L.run.st[sidx];
-    const int q0 = qt * QT + mt * 32;  // tree row of this wave's first query
-    // every (query, key) pair of this wave's 32 x 32 block visible and in range?
-    const bool full =
-        __builtin_amdgcn_readfirstlane(wave_kmax <= q0 && wave_min_end > q0 + 31 && q0 >= lo && q0 + 31 < hi);
-    // S starts at -LSE/scale and dP at -D (both per query = per register), so
-    // that the products below give c2 S - LSE log2(e) and dP - D directly
-    f32x16 s, dp;
+    if (step + 1 < n_steps) load_tile(step + 1, L.st[sidx ^ 1]);  // that stage was last read in the previous step
+    const KvStage& S = L.st[sidx];
 #pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) {
-      const int ql = mt * 32 + 8 * i4 + 4 * hh;
-      const f32x4 l4 = *reinterpret_cast<const f32x4*>(&S.s0[ql]);
-      const f32x4 d4 = *reinterpret_cast<const f32x4*>(&S.d0[ql]);
+    for (int mt = 0; mt < 2; ++mt) {
+      const int q0 = qt * QT + mt * 32;  // tree row of this half's first query
+      // every (query, key) pair of this wave's 32 x 32 block visible and in range?
+      const bool full =
+          __builtin_amdgcn_readfirstlane(wave_kmax <= q0 && wave_min_end > q0 + 31 && q0 >= lo && q0 + 31 < hi);
+      // S starts at -LSE/scale and dP at -D (both per query = per register), so
+      // that the products below give c2 S - LSE log2(e) and dP - D directly
+      f32x16 s, dp;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        s[4 * i4 + e] = l4[e];
-        dp[4 * i4 + e] = d4[e];
-      }
-    }
-#pragma unroll
-    for (int dc = 0; dc < 8; ++dc) {
-      s = mfma(lds_read16(&S.Q[soff(mt * 32 + r, dc * 16 + 8 * hh)]), kf[dc], s);
-      dp = mfma(lds_read16(&S.O[soff(mt * 32 + r, dc * 16 + 8 * hh)]), lds_read16(Vt + dc * 16), dp);
-    }
-    f32x16 ds;
-    // the softmax step runs at raised wave priority: the SIMD's other wave,
-    // usually issuing MFMAs, yields issue slots to it, which shortens the gap
-    // before this wave's own dV/dK products (measured 2% on this kernel)
-    __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) {
-      const int ql = mt * 32 + 8 * i4 + 4 * hh;
-      if (full) {
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int ql = mt * 32 + 8 * i4 + 4 * hh;
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&S.s0[ql]);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&S.d0[ql]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int i = 4 * i4 + e;
-          const float p = exp2_fast(s[i] * c2);
-          s[i] = p;
-          ds[i] = p * dp[i];
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = 4 * i4 + e;
-          const int qq = qt * QT + ql + e;
-          const bool vis = (j <= qq) & (qq < endj) & (qq >= lo) & (qq < hi);
-          const float p = vis ? exp2_fast(s[i] * c2) : 0.f;
-          s[i] = p;
-          ds[i] = p * dp[i];
+          s[4 * i4 + e] = l4[e];
+          dp[4 * i4 + e] = d4[e];
         }
       }
-    }
-    const bf16x8 p0 = c_to_b(s, 0), p1 = c_to_b(s, 1);
-    const bf16x8 s0 = c_to_b(ds, 0), s1 = c_to_b(ds, 1);
-    __builtin_amdgcn_s_setprio(0);
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
-      dv[dt] = mfma(tr_frag_swz(S.O, mt * 32, dt * 32, lane), p0, dv[dt]);
-      dv[dt] = mfma(tr_frag_swz(S.O, mt * 32 + 16, dt * 32, lane), p1, dv[dt]);
-      dk[dt] = mfma(tr_frag_swz(S.Q, mt * 32, dt * 32, lane), s0, dk[dt]);
-      dk[dt] = mfma(tr_frag_swz(S.Q, mt * 32 + 16, dt * 32, lane), s1, dk[dt]);
+      for (int dc = 0; dc < 8; ++dc) {
+        s = mfma(lds_read16(&S.Q[soff(mt * 32 + r, dc * 16 + 8 * hh)]), kf[dc], s);
+        dp = mfma(lds_read16(&S.O[soff(mt * 32 + r, dc * 16 + 8 * hh)]), lds_read16(Vt + dc * 16), dp);
+      }
+      f32x16 ds;
+      // the softmax step runs at raised wave priority: the SIMD's other wave,
+      // usually issuing MFMAs, yields issue slots to it, which shortens the gap
+      // before this wave's own dV/dK products
+      __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int ql = mt * 32 + 8 * i4 + 4 * hh;
+        if (full) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int i = 4 * i4 + e;
+            const float p = exp2_fast(s[i] * c2);
+            s[i] = p;
+            ds[i] = p * dp[i];
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int i = 4 * i4 + e;
+            const int qq = qt * QT + ql + e;
+            const bool vis = (j <= qq) & (qq < endj) & (qq >= lo) & (qq < hi);
+            const float p = vis ? exp2_fast(s[i] * c2) : 0.f;
+            s[i] = p;
+            ds[i] = p * dp[i];
+          }
+        }
+      }
+      const bf16x8 p0 = c_to_b(s, 0), p1 = c_to_b(s, 1);
+      const bf16x8 s0 = c_to_b(ds, 0), s1 = c_to_b(ds, 1);
+      __builtin_amdgcn_s_setprio(0);
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        dv[dt] = mfma(tr_frag_swz(S.O, mt * 32, dt * 32, lane), p0, dv[dt]);
+        dv[dt] = mfma(tr_frag_swz(S.O, mt * 32 + 16, dt * 32, lane), p1, dv[dt]);
+        dk[dt] = mfma(tr_frag_swz(S.Q, mt * 32, dt * 32, lane), s0, dk[dt]);
+        dk[dt] = mfma(tr_frag_swz(S.Q, mt * 32 + 16, dt * 32, lane), s1, dk[dt]);
+      }
     }
-    if (step + 1 < n_steps) store_rows(L.run.st[sidx ^ 1]);
+    if (step + 1 < n_steps) store_rows(L.st[sidx ^ 1]);
     wait_vmem();  // this wave's direct-to-LDS loads of the next tile have landed
     __syncthreads();
   }
-
-  // sum the two query halves: the upper half's waves hand their partials over LDS
-  if (mt == 1) {
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        L.part[ks][dt][i][lane] = dk[dt][i];
-        L.part[ks][4 + dt][i][lane] = dv[dt][i];
-      }
-  }
-  __syncthreads();
-  if (mt == 1 || !jok) return;
-#pragma unroll
-  for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      dk[dt][i] += L.part[ks][dt][i][lane];
-      dv[dt][i] += L.part[ks][4 + dt][i][lane];
-    }
+  if (!jok) return;
 
   // dK = R^T (scale * dK') at the key's depth, with (cos, sin) of depth *
   // theta_c from the caller's table (none: no rotation); coordinates (c, c+64)
