@@ -60,7 +60,8 @@ def _make_inputs(N, hq, hkv, d, seed, device="cuda"):
 
 
 class Step:
-    """Preallocated fwd+bwd over one tree (or one chunk of a path)."""
+    """Preallocated fwd+bwd over one tree (or one chunk of a path); the
+    backward takes the forward's rotated q and k from the shared workspace."""
 
     def __init__(self, tt, tree, plan, q, k, v, do, q_off=0, accumulate=False, d_k=None, d_v=None):
         import torch
@@ -83,7 +84,7 @@ class Step:
     def bwd(self):
         self.tt.tree_attn_bwd(self.tree, self.plan, self.q, self.k, self.v, self.o, self.lse, self.do,
                               q_off=self.q_off, d_q=self.dq, d_k=self.dk, d_v=self.dv,
-                              accumulate=self.accumulate, workspace=self.ws)
+                              accumulate=self.accumulate, workspace=self.ws, reuse_rotated=True)
 
 
 def _time(fn, steps, warmup):

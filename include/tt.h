@@ -65,6 +65,9 @@ typedef void* tt_stream;
 
 /* Flags of tree_attn_bwd. */
 #define TT_ACCUMULATE_DKDV 1u /* d_k, d_v are float32 and the call ADDS into them */
+#define TT_BWD_REUSE_ROTATED 2u /* the workspace still holds the rotated q and k that
+                                   tree_attn_fwd wrote for the same arguments: skip
+                                   rotating them again */
 
 typedef struct tt_tree tt_tree; /* opaque, host memory owned by the library */
 
@@ -192,8 +195,11 @@ typedef struct {
   void* o;                 /* device [n_q, h_q, d] dtype: output of fwd, input of bwd */
   float* lse;              /* device [n_q, h_q] float32: output of fwd, input of bwd */
   void* workspace;         /* device scratch, >= tree_attn_workspace_bytes: rotated q and k
-                              (with RoPE); for the backward also D, fp32 dQ and a (cos, sin)
-                              table of the tree's depths; contents are not kept between calls */
+                              (with RoPE) first, at the same offsets for both calls; for the
+                              backward also D, fp32 dQ and a (cos, sin) table of the tree's
+                              depths.  The library keeps nothing there between calls; a
+                              caller that passes the forward's workspace, unmodified, to the
+                              backward may set TT_BWD_REUSE_ROTATED */
   size_t workspace_bytes;
 } tt_attn_args;
 
@@ -220,6 +226,10 @@ int tree_attn_fwd(const tt_attn_args* args, tt_stream stream);
  *   d_k, d_v    device [n_k, h_kv, d]: dtype and overwritten, or float32 and
  *               added into with TT_ACCUMULATE_DKDV (chunked path mode: the
  *               prefix keys collect every chunk's contribution)
+ *   flags       TT_ACCUMULATE_DKDV, TT_BWD_REUSE_ROTATED (the caller vouches
+ *               that the workspace holds what tree_attn_fwd wrote there for
+ *               these q, k, tree, q_off, rope_base; results are then those of a
+ *               call without the flag).  Other bits: TT_EINVAL.
  */
 typedef struct {
   tt_attn_args a;

@@ -21,6 +21,7 @@ LIB_PATH = os.environ.get("TT_LIB_PATH") or os.path.join(_PKG, "libtreeattn.so")
 TT_OK, TT_EINVAL, TT_ENOMEM, TT_EWORKSPACE, TT_EUNSUPPORTED, TT_EDEVICE, TT_EOVERFLOW = 0, -1, -2, -3, -4, -5, -6
 TT_F32, TT_BF16 = 0, 1
 TT_ACCUMULATE_DKDV = 1
+TT_BWD_REUSE_ROTATED = 2
 
 EXPORTED = ("tree_build", "tree_free", "tree_info", "tree_export", "tree_plan_bytes", "tree_plan_upload",
             "tree_plan_copy",
@@ -358,8 +359,13 @@ def tree_attn_fwd(tree, plan, q, k, v, q_off=0, scale=0.0, rope_base=10000.0, o=
 
 
 def tree_attn_bwd(tree, plan, q, k, v, o, lse, d_o, q_off=0, scale=0.0, rope_base=10000.0, d_q=None, d_k=None,
-                  d_v=None, accumulate=False, workspace=None):
-    """dQ, dK, dV (dK/dV are float32 and added into when accumulate=True)."""
+                  d_v=None, accumulate=False, workspace=None, reuse_rotated=False):
+    """dQ, dK, dV (dK/dV are float32 and added into when accumulate=True).
+
+    reuse_rotated: `workspace` is the one tree_attn_fwd used for these same
+    arguments, unmodified since; the backward then takes its rotated q and k."""
+    if reuse_rotated and workspace is None:
+        raise ValueError("reuse_rotated needs the forward's workspace")
     import torch
     if d_q is None:
         d_q = torch.empty_like(q)
@@ -374,7 +380,7 @@ def tree_attn_bwd(tree, plan, q, k, v, o, lse, d_o, q_off=0, scale=0.0, rope_bas
     a.workspace = ctypes.c_void_p(ws.data_ptr())
     a.workspace_bytes = ws.numel()
     b = AttnBwdArgs(a=a, d_o=_p(d_o), d_q=_p(d_q), d_k=_p(d_k), d_v=_p(d_v),
-                    flags=TT_ACCUMULATE_DKDV if accumulate else 0)
+                    flags=(TT_ACCUMULATE_DKDV if accumulate else 0) | (TT_BWD_REUSE_ROTATED if reuse_rotated else 0))
     _check(lib().tree_attn_bwd(ctypes.byref(b), _stream()))
     return d_q, d_k, d_v
 

@@ -260,8 +260,10 @@ extern "C" int tree_attn_bwd(const tt_attn_bwd_args* b, tt_stream stream) {
   const tt_attn_args* a = &b->a;
   int rc = check_attn(a, fn);
   if (rc) return rc;
-  if (b->flags & ~TT_ACCUMULATE_DKDV) return tt::fail(TT_EINVAL, "tree_attn_bwd: unknown flags");
+  if (b->flags & ~(TT_ACCUMULATE_DKDV | TT_BWD_REUSE_ROTATED))
+    return tt::fail(TT_EINVAL, "tree_attn_bwd: unknown flags");
   const bool acc = (b->flags & TT_ACCUMULATE_DKDV) != 0;
+  const bool reuse = (b->flags & TT_BWD_REUSE_ROTATED) != 0;
   if (a->n_q > 0 && (!b->d_o || !b->d_q)) return tt::fail(TT_EINVAL, "tree_attn_bwd: d_o and d_q are required");
   if (a->n_k > 0 && (!b->d_k || !b->d_v)) return tt::fail(TT_EINVAL, "tree_attn_bwd: d_k and d_v are required");
   for (const void* p : {b->d_o, static_cast<const void*>(b->d_q), static_cast<const void*>(b->d_k),
@@ -277,13 +279,14 @@ extern "C" int tree_attn_bwd(const tt_attn_bwd_args* b, tt_stream stream) {
   const void* q = a->q;
   const void* k = a->k;
   if (w.rope) {
-    if (a->n_q > 0) {
+    // the forward wrote them at the same offsets (tree_attn_workspace_bytes layout)
+    if (a->n_q > 0 && !reuse) {
       KTimer t("rope_q", st);
       if (launch_rope(a->q, ws + w.q_rot, a->dtype, a->dtype, false, P, a->q_off, a->n_q, a->h_q, a->d,
                       a->rope_base, false, st))
         return dev_fail(fn, "rope(q)");
     }
-    {
+    if (!reuse) {
       KTimer t("rope_k", st);
       if (launch_rope(a->k, ws + w.k_rot, a->dtype, a->dtype, false, P, 0, a->n_k, a->h_kv, a->d,
                       a->rope_base, false, st))

@@ -174,6 +174,24 @@ def test_mfma_backward_no_rope_custom_scale():
         assert rel_err(g_, r_) < TOL, (n, rel_err(g_, r_))
 
 
+def test_mfma_backward_reuses_forward_rotation():
+    """TT_BWD_REUSE_ROTATED with the forward's workspace gives the same bits
+    as a backward that rotates q and k itself; a q_off chunk too."""
+    case = TREES["forest"]()
+    tree = tt.Tree(case.seqs)
+    plan = tree.upload_plan()
+    (q, _), (k, _), (v, _), (do, _) = inputs(torch.bfloat16, 44, tree.N, tree.N, 8, 2, 128, 128 ** -0.5)
+    for q_off in (0, 128):
+        qc, doc = q[q_off:], do[q_off:]
+        nb = max(tt.attn_workspace_bytes(tree, plan, qc, k, v, fb, q_off=q_off) for fb in (True, False))
+        ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+        O, L = tt.tree_attn_fwd(tree, plan, qc, k, v, q_off=q_off, workspace=ws)
+        got = tt.tree_attn_bwd(tree, plan, qc, k, v, O, L, doc, q_off=q_off, workspace=ws, reuse_rotated=True)
+        ref = tt.tree_attn_bwd(tree, plan, qc, k, v, O, L, doc, q_off=q_off)
+        for n, g_, r_ in zip(("dq", "dk", "dv"), got, ref):
+            assert torch.equal(g_, r_), (q_off, n)
+
+
 def test_mfma_backward_chunks_accumulate():
     """Right-to-left chunks of a suffix against a cached prefix, dK/dV added
     into fp32 buffers across chunks == oracle backward with dO = 0 on the prefix."""
