@@ -126,6 +126,10 @@ __global__ __launch_bounds__(kThreads) void nll_rows_kernel(const T* z, T* dz, i
 constexpr int kRegThreads = 1024;
 constexpr int kRegChunks = 19;  // 8 * 1024 * 19 = 155,648 logits per row
 typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 b16x8 __attribute__((ext_vector_type(8)));
+constexpr float kL2e = 1.4426950408889634f;
+// exp(x - c) as one FMA and v_exp_f32: 2^(x log2 e - c log2 e), cl = c log2 e
+__device__ __forceinline__ float exp_shift(float x, float cl) { return __builtin_amdgcn_exp2f(fmaf(x, kL2e, -cl)); }
 
 __global__ __launch_bounds__(kRegThreads) void nll_rows_reg_kernel(const uint16_t* z, uint16_t* dz, int32_t vocab,
                                                                    int64_t ldz, const int32_t* __restrict__ row_ptr,
@@ -160,11 +164,12 @@ __global__ __launch_bounds__(kRegThreads) void nll_rows_reg_kernel(const uint16_
   m = red_a[0];
   for (int w = 1; w < kRegThreads / kWave; ++w) m = fmaxf(m, red_a[w]);
   float s = 0.f;
+  const float ml = m * kL2e;
 #pragma unroll
   for (int c = 0; c < kRegChunks; ++c)
     if (c * kRegThreads + tid < nchunk)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) s += __expf(bf2f(x[c][e]) - m);
+      for (int e = 0; e < 8; ++e) s += exp_shift(bf2f(x[c][e]), ml);
   s = wave_sum(s);
   __syncthreads();  // red_a reused
   if (lane == 0) red_b[wv] = s;
@@ -205,15 +210,18 @@ __global__ __launch_bounds__(kRegThreads) void nll_rows_reg_kernel(const uint16_
   if (tid == 0) row_loss[r] = loss;
   if (dz == nullptr) return;
   uint16_t* dr = dz + int64_t(r) * ldz;
-  // pass 3a: every non-target position, 16 bytes at a time where a chunk holds no target
+  const float lsel = lse * kL2e;
+  // pass 3a: every non-target position, 16 bytes at a time where a chunk holds
+  // no target; rounded to bf16 (nearest even) two at a time by the hardware
 #pragma unroll
   for (int c = 0; c < kRegChunks; ++c) {
     const int ch = c * kRegThreads + tid;
     if (ch >= nchunk) continue;
     const uint32_t bits = (bitmap[ch >> 2] >> ((ch & 3) * 8)) & 0xFFu;  // the chunk's 8 target bits
-    u16x8 y;
+    b16x8 yb;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) y[e] = f2bf(W * __expf(bf2f(x[c][e]) - lse));
+    for (int e = 0; e < 8; ++e) yb[e] = __bf16(W * exp_shift(bf2f(x[c][e]), lsel));
+    const u16x8 y = __builtin_bit_cast(u16x8, yb);
     if (bits == 0u) {
       *reinterpret_cast<u16x8*>(dr + 8 * int64_t(ch)) = y;
     } else {
@@ -232,7 +240,7 @@ __global__ __launch_bounds__(kRegThreads) void nll_rows_reg_kernel(const uint16_
     float ws = 0.f;
     for (int u = t0; u < t1; ++u)
       if (tgt_id[u] == xi) ws += tgt_w[u];
-    dr[xi] = f2bf(W * __expf(bf2f(zr[xi]) - lse) - ws);
+    dr[xi] = f2bf(W * exp_shift(bf2f(zr[xi]), lsel) - ws);
   }
 }
 
