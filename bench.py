@@ -206,7 +206,8 @@ def path_mode_bench(tt, tree, plan, q, k, v, do, steps, tree_ms):
             max_path=inf["max_path"], pad_rows=inf["pad_rows"], pad_pairs_per_head=inf["pad_pairs"],
             recompute_pct=round(100.0 * inf["pad_pairs"] / P, 3),
             useful_tflops=round(useful / ms / 1e9, 1),
-            pct_bf16_peak=round(useful / ms / 1e9 / PEAK_BF16_TFLOPS * 100, 2), workspace_bytes=nbytes)
+            pct_bf16_peak=round(useful / ms / 1e9 / PEAK_BF16_TFLOPS * 100, 2), workspace_bytes=nbytes,
+            kernels={n_: {"launches": x[0], "total_ms": round(x[1], 3)} for n_, x in kt.items()})
         del ws, path
     return out
 
