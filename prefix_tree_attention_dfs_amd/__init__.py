@@ -22,7 +22,6 @@ TT_OK, TT_EINVAL, TT_ENOMEM, TT_EWORKSPACE, TT_EUNSUPPORTED, TT_EDEVICE, TT_EOVE
 TT_F32, TT_BF16 = 0, 1
 TT_ACCUMULATE_DKDV = 1
 TT_BWD_REUSE_ROTATED = 2
-KEY_GROUP = 256  # key rows per dK/dV workgroup (the plan orders these groups)
 
 EXPORTED = ("tree_build", "tree_free", "tree_info", "tree_export", "tree_plan_bytes", "tree_plan_upload",
             "tree_plan_copy",
@@ -278,7 +277,7 @@ class Tree:
         """Decoded tile schedule: dict {(qb, kb): full}, per-k-block (qlo, qhi, minend), orders."""
         p = self.plan_host()
         H = dict(N=1, BQ=2, BK=3, NQB=4, NKB=5, NTILES=6, DEPTH=8, END=9, QB_PTR=10, QB_TILES=11,
-                 QB_ORDER=12, KB_QLO=13, KB_QHI=14, KB_MINEND=15, KB_ORDER=16, KG_ORDER=18)
+                 QB_ORDER=12, KB_QLO=13, KB_QHI=14, KB_MINEND=15, KB_ORDER=16)
         nqb, nkb = int(p[H["NQB"]]), int(p[H["NKB"]])
         ptr = p[p[H["QB_PTR"]]:p[H["QB_PTR"]] + nqb + 1]
         tl = p[p[H["QB_TILES"]]:p[H["QB_TILES"]] + int(p[H["NTILES"]])]
@@ -290,7 +289,6 @@ class Tree:
         return dict(tiles=tiles, qb_ptr=ptr.copy(), depth=sec("DEPTH", self.N), end=sec("END", self.N),
                     qb_order=sec("QB_ORDER", nqb), kb_qlo=sec("KB_QLO", nkb), kb_qhi=sec("KB_QHI", nkb),
                     kb_minend=sec("KB_MINEND", nkb), kb_order=sec("KB_ORDER", nkb),
-                    kg_order=sec("KG_ORDER", (self.N + KEY_GROUP - 1) // KEY_GROUP),
                     bq=int(p[H["BQ"]]), bk=int(p[H["BK"]]))
 
     def upload_plan(self, device="cuda"):

@@ -26,7 +26,6 @@ inline PlanPtrs plan_ptrs(const tt_tree* t, const void* dev_plan) {
   P.kb_qhi = base + h[ttp::H_KB_QHI];
   P.kb_minend = base + h[ttp::H_KB_MINEND];
   P.kb_order = base + h[ttp::H_KB_ORDER];
-  P.kg_order = base + h[ttp::H_KG_ORDER];
   P.N = t->N;
   P.bq = t->bq;
   P.bk = t->bk;

@@ -221,7 +221,6 @@ __global__ __launch_bounds__(DqCfg<G>::THREADS) void dq_mfma_kernel(
 constexpr int KV_WAVES = 8;
 constexpr int KV_THREADS = KV_WAVES * 64;
 constexpr int KV_KEYS = 32 * KV_WAVES;             // keys per workgroup
-static_assert(KV_KEYS == ttp::kKeyGroup, "the plan orders key groups of this size");
 constexpr int QT = 64;                             // query rows per staged tile
 constexpr int VCH = (KV_KEYS * D / 8) / KV_THREADS;  // 16-byte chunks of V per thread
 
@@ -242,14 +241,12 @@ template <int G, bool ACC, typename TG>
 __global__ __launch_bounds__(KV_THREADS, 2) void dkdv_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ d_o, const float* __restrict__ lse, const float* __restrict__ Dv,
-    TG* __restrict__ d_k, TG* __restrict__ d_v, const float2* __restrict__ cs_tab, PlanPtrs P, AttnGeom g,
-    int full_range) {
+    TG* __restrict__ d_k, TG* __restrict__ d_v, const float2* __restrict__ cs_tab, PlanPtrs P, AttnGeom g) {
   __shared__ KvLds L;
   if (!plan_matches(P)) return;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r = lane & 31, hh = lane >> 5;
   const int kvh = blockIdx.x % g.h_kv;
-  // whole-tree calls take the key groups largest first (the plan's order)
-  const int kb2 = full_range ? ld_uniform(P.kg_order, blockIdx.x / g.h_kv) : blockIdx.x / g.h_kv;
+  const int kb2 = blockIdx.x / g.h_kv;
   const int kbase = kb2 * KV_KEYS;
   const int j = kbase + wave * 32 + r;  // this lane's key (lane column of S, dP, dK^T, dV^T)
   const bool jok = j < g.n_k;
@@ -498,20 +495,18 @@ int launch_dq_g(const void* q, const void* k, const void* v, const void* d_o, co
 template <int G>
 int launch_dkdv_g(const void* q, const void* k, const void* v, const void* d_o, const float* lse, const float* D_,
                   void* d_k, void* d_v, bool acc, const float2* cs_tab, const PlanPtrs& P, const AttnGeom& g,
-                  bool full_range, hipStream_t st) {
+                  hipStream_t st) {
   const int nkb2 = (g.n_k + KV_KEYS - 1) / KV_KEYS;
   if (nkb2 <= 0) return 0;
   const dim3 grid(unsigned(nkb2) * unsigned(g.h_kv)), block(KV_THREADS);
   if (acc)
     dkdv_mfma_kernel<G, true, float><<<grid, block, 0, st>>>((const uint16_t*)q, (const uint16_t*)k,
                                                               (const uint16_t*)v, (const uint16_t*)d_o, lse, D_,
-                                                              (float*)d_k, (float*)d_v, cs_tab, P, g,
-                                                              full_range ? 1 : 0);
+                                                              (float*)d_k, (float*)d_v, cs_tab, P, g);
   else
     dkdv_mfma_kernel<G, false, uint16_t><<<grid, block, 0, st>>>((const uint16_t*)q, (const uint16_t*)k,
                                                                   (const uint16_t*)v, (const uint16_t*)d_o, lse, D_,
-                                                                  (uint16_t*)d_k, (uint16_t*)d_v, cs_tab, P, g,
-                                                                  full_range ? 1 : 0);
+                                                                  (uint16_t*)d_k, (uint16_t*)d_v, cs_tab, P, g);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
@@ -538,11 +533,11 @@ int launch_dq_mfma(const void* q, const void* k, const void* v, const void* d_o,
 
 int launch_dkdv_mfma(const void* q, const void* k, const void* v, const void* d_o, const float* lse, const float* D_,
                      void* d_k, void* d_v, bool acc, const float2* cs_tab, const PlanPtrs& P, const AttnGeom& g,
-                     bool full_range, hipStream_t st) {
+                     hipStream_t st) {
   switch (g.h_q / g.h_kv) {
-    case 1: return launch_dkdv_g<1>(q, k, v, d_o, lse, D_, d_k, d_v, acc, cs_tab, P, g, full_range, st);
-    case 2: return launch_dkdv_g<2>(q, k, v, d_o, lse, D_, d_k, d_v, acc, cs_tab, P, g, full_range, st);
-    case 4: return launch_dkdv_g<4>(q, k, v, d_o, lse, D_, d_k, d_v, acc, cs_tab, P, g, full_range, st);
+    case 1: return launch_dkdv_g<1>(q, k, v, d_o, lse, D_, d_k, d_v, acc, cs_tab, P, g, st);
+    case 2: return launch_dkdv_g<2>(q, k, v, d_o, lse, D_, d_k, d_v, acc, cs_tab, P, g, st);
+    case 4: return launch_dkdv_g<4>(q, k, v, d_o, lse, D_, d_k, d_v, acc, cs_tab, P, g, st);
     default: return -1;
   }
 }

@@ -144,8 +144,7 @@ int attn_bwd_core(tt_dtype dt, const PlanPtrs& P, const AttnGeom& g, const void*
     }
     {
       KTimer t("attn_bwd_dkdv_mfma", st);
-      if (launch_dkdv_mfma(q, k, v, d_o, lse, D, d_k, d_v, acc, cs_tab, P, g, full_range, st))
-        return dev_fail(fn, "dk/dv kernel");
+      if (launch_dkdv_mfma(q, k, v, d_o, lse, D, d_k, d_v, acc, cs_tab, P, g, st)) return dev_fail(fn, "dk/dv kernel");
     }
   } else {
     {

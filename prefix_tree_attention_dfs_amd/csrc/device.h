@@ -58,7 +58,6 @@ struct PlanPtrs {
   const int32_t* kb_qhi;
   const int32_t* kb_minend;
   const int32_t* kb_order;
-  const int32_t* kg_order;  // key groups of ttp::kKeyGroup rows, largest first
   const int32_t* hdr;  // image header
   int32_t N, bq, bk, nqb, nkb;
   int32_t id;  // the tree's image identity (header word H_ID of its host copy)

@@ -11,16 +11,14 @@
 // words (256 bytes) so every section is a naturally aligned device array.
 namespace ttp {
 enum : int32_t {
-  kMagic = 0x32505454,  // "TTP2"
+  kMagic = 0x31505454,  // "TTP1"
   // header word indices
   H_MAGIC = 0, H_N, H_BQ, H_BK, H_NQB, H_NKB, H_NTILES, H_BYTES,
   H_DEPTH, H_END, H_QB_PTR, H_QB_TILES, H_QB_ORDER,
   H_KB_QLO, H_KB_QHI, H_KB_MINEND, H_KB_ORDER,
   H_ID,  // FNV-1a hash of the image (this word 0 while hashing): which tree it belongs to
-  H_KG_ORDER,  // key groups of kKeyGroup rows (one dK/dV workgroup each), largest first
   H_WORDS = 64
 };
-constexpr int32_t kKeyGroup = 256;  // key rows per dK/dV workgroup of the matrix-core backward
 constexpr int32_t kFullBit = int32_t(0x40000000);  // tile entry: kb | kFullBit if FULL
 }  // namespace ttp
 

@@ -32,11 +32,9 @@ int launch_fwd_mfma(const void* q, const void* k, const void* v, void* o, float*
 int launch_dq_mfma(const void* q, const void* k, const void* v, const void* d_o, const float* lse, const float* D,
                    float* dq_acc, void* dq_out, const float2* cs_tab, const PlanPtrs& P, const AttnGeom& g,
                    bool full_range, hipStream_t st);
-// full_range: the call covers the plan's whole tree (n_k = N), so key groups
-// run in the plan's largest-first order
 int launch_dkdv_mfma(const void* q, const void* k, const void* v, const void* d_o, const float* lse, const float* D,
                      void* d_k, void* d_v, bool acc, const float2* cs_tab, const PlanPtrs& P, const AttnGeom& g,
-                     bool full_range, hipStream_t st);
+                     hipStream_t st);
 // (cos, sin) of p * theta_k, theta_k = base^(-2k / (2 half)), for p < n_pos and
 // k < half, computed in fp64 and rounded to fp32: tab[p * half + k]
 int launch_rope_table(float2* tab, int32_t n_pos, int32_t half, float base, hipStream_t st);

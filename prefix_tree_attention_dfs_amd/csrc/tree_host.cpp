@@ -125,17 +125,6 @@ void build_schedule(tt_tree* t) {
   std::stable_sort(korder.begin(), korder.end(), [&](int32_t a, int32_t b) {
     return qhi[a] - qlo[a] > qhi[b] - qlo[b];
   });
-  // key groups of kKeyGroup rows: query tiles in [first key, max end), largest first
-  const int32_t ngroups = (N + ttp::kKeyGroup - 1) / ttp::kKeyGroup;
-  std::vector<int32_t> gwork(ngroups), gorder(ngroups);
-  for (int32_t g = 0; g < ngroups; ++g) {
-    const int32_t j0 = g * ttp::kKeyGroup, j1 = std::min(N, j0 + ttp::kKeyGroup);
-    int32_t hi = 0;
-    for (int32_t j = j0; j < j1; ++j) hi = std::max(hi, t->end[j]);
-    gwork[g] = hi > j0 ? (hi - 1) / bq - j0 / bq + 1 : 0;
-    gorder[g] = g;
-  }
-  std::stable_sort(gorder.begin(), gorder.end(), [&](int32_t a, int32_t b) { return gwork[a] > gwork[b]; });
 
   // plan image
   int64_t w = ttp::H_WORDS;
@@ -146,8 +135,7 @@ void build_schedule(tt_tree* t) {
   };
   const int64_t o_depth = place(N), o_end = place(N), o_qptr = place(t->nqb + 1),
                 o_qtiles = place(ntiles), o_qorder = place(t->nqb), o_qlo = place(t->nkb),
-                o_qhi = place(t->nkb), o_minend = place(t->nkb), o_korder = place(t->nkb),
-                o_gorder = place(ngroups);
+                o_qhi = place(t->nkb), o_minend = place(t->nkb), o_korder = place(t->nkb);
   t->plan.assign(size_t(w), 0);
   int32_t* p = t->plan.data();
   p[ttp::H_MAGIC] = ttp::kMagic;
@@ -167,7 +155,6 @@ void build_schedule(tt_tree* t) {
   p[ttp::H_KB_QHI] = int32_t(o_qhi);
   p[ttp::H_KB_MINEND] = int32_t(o_minend);
   p[ttp::H_KB_ORDER] = int32_t(o_korder);
-  p[ttp::H_KG_ORDER] = int32_t(o_gorder);
   std::copy(t->depth.begin(), t->depth.end(), p + o_depth);
   std::copy(t->end.begin(), t->end.end(), p + o_end);
   std::copy(cnt.begin(), cnt.end(), p + o_qptr);
@@ -177,7 +164,6 @@ void build_schedule(tt_tree* t) {
   std::copy(qhi.begin(), qhi.end(), p + o_qhi);
   std::copy(minend.begin(), minend.end(), p + o_minend);
   std::copy(korder.begin(), korder.end(), p + o_korder);
-  std::copy(gorder.begin(), gorder.end(), p + o_gorder);
   uint32_t h = 2166136261u;  // FNV-1a over every byte of the image
   for (const int32_t x : t->plan)
     for (int b = 0; b < 4; ++b) h = (h ^ ((uint32_t(x) >> (8 * b)) & 0xFFu)) * 16777619u;

@@ -99,12 +99,6 @@ def test_schedule_equals_bruteforce(case, blocks):
     assert sorted(s["qb_order"]) == list(range(len(cnt)))
     assert all(cnt[s["qb_order"][i]] >= cnt[s["qb_order"][i + 1]] for i in range(len(cnt) - 1))
     assert sorted(s["kb_order"]) == list(range(len(s["kb_qlo"])))
-    # key groups of the dK/dV kernel: query tiles in [first key, max end) of
-    # each group, recomputed from end[]; the plan lists them largest first
-    G = tt.KEY_GROUP
-    gw = [((max(int(e) for e in o["end"][g0:g0 + G]) - 1) // bq - g0 // bq + 1) for g0 in range(0, N, G)]
-    assert sorted(s["kg_order"]) == list(range(len(gw)))
-    assert all(gw[s["kg_order"][i]] >= gw[s["kg_order"][i + 1]] for i in range(len(gw) - 1))
 
 
 def test_schedule_workload_chain_and_tiny():
