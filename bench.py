@@ -184,7 +184,7 @@ def path_mode_bench(tt, tree, plan, q, k, v, do, steps, tree_ms):
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     out = {"tree_mode_ms": round(tree_ms, 3),
            "tree_mode_workspace_bytes": tt.attn_workspace_bytes(tree, plan, q, k, v, True)}
-    for chunk, order in ((2048, 0), (4096, 0), (2048, 1)):
+    for chunk, order in ((2048, 0), (4096, 0), (2048, 1), (4096, 1)):
         path = tt.Path(tree, chunk, order)
         nbytes = tt.path_workspace_bytes(path, q, k, v, True)
         ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
@@ -200,11 +200,11 @@ def path_mode_bench(tt, tree, plan, q, k, v, do, steps, tree_ms):
         tt.timing_enable(False)
         kt = tt.timing_collect()
         inf = path.info
-        out[f"chunk{chunk}_{'dfs' if order == 0 else 'largest_first'}"] = dict(
+        out[f"chunk{chunk}_{'dfs' if order == 0 else 'greedy'}"] = dict(
             ms=round(ms, 3), vs_tree_mode=round(ms / tree_ms, 3), kernel_ms=round(sum(x[1] for x in kt.values()), 3),
             launches=int(sum(x[0] for x in kt.values())), segments=inf["n_segments"], calls=inf["fwd_calls"],
-            max_path=inf["max_path"], pad_rows=inf["pad_rows"], pad_pairs_per_head=inf["pad_pairs"],
-            recompute_pct=round(100.0 * inf["pad_pairs"] / P, 3),
+            bwd_calls=inf["bwd_calls"], max_path=inf["max_path"], pad_rows=inf["pad_rows"],
+            pad_pairs_per_head=inf["pad_pairs"], recompute_pct=round(100.0 * inf["pad_pairs"] / (2 * P), 3),
             useful_tflops=round(useful / ms / 1e9, 1),
             pct_bf16_peak=round(useful / ms / 1e9 / PEAK_BF16_TFLOPS * 100, 2), workspace_bytes=nbytes,
             kernels={n_: {"launches": x[0], "total_ms": round(x[1], 3)} for n_, x in kt.items()})
@@ -289,7 +289,7 @@ def per_branch_dense(tt, ts, tree, case, q, k, v, do, steps):
                 branch_tokens_per_s=round(branch_tokens / ms * 1e3))
 
 
-def compression_study(tt, ts, steps):
+def compression_study(tt, ts, steps, prefixes=(7168, 6144, 4096, 2048, 1024, 512, 0)):
     """Where the tree stops paying off: 8 branches of 8192 tokens sharing a
     prefix of p tokens, p from 7168 down to 0 (compression to exactly 1).
     Tree mode (one fwd+bwd over the tree) against the same kernels per branch
@@ -298,7 +298,7 @@ def compression_study(tt, ts, steps):
     import torch
     B, L, hq, hkv, d = 8, 8192, 32, 8, 128
     points = []
-    for p in (7168, 6144, 4096, 2048, 1024, 512, 0):
+    for p in prefixes:
         prefix = list(range(p))
         seqs = [prefix + [200000 + b * L + j for j in range(L - p)] for b in range(B)]
         tree = tt.Tree(seqs)
@@ -322,63 +322,68 @@ def compression_study(tt, ts, steps):
 
 
 def cpu_baseline(ts, case, seed, budget_s):
-    """The fp64 oracle on sampled rows of the same tree: per-row forward and dQ
-    (each row from the branch ending at it), rows drawn uniformly at random."""
+    """The fp64 oracle's whole step (forward + backward) on a bounded sample of
+    the headline tree, extrapolated to the full step.
+
+    The oracle computes every branch on its own (textbook causal attention of
+    L x L per head), so its cost grows with sum over branches of L^2 times
+    the query heads.  Sample: a prefix of the longest branch, of L rows, for
+    one kv head's group of 4 query heads, forward then backward; L doubles
+    from 1024 until one call takes a quarter of the budget, then calls repeat
+    until the budget is spent.  Full step = mean call time x (sum_s |s|^2 /
+    L^2) x 8 groups; value = unique tree tokens / that time.  A second,
+    shorter sample on one BLAS thread gives value_1core the same way."""
     import numpy as np
     from oracle import attention as OA
     from oracle.tree import dfs_arrays
     try:
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_info, threadpool_limits
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
+        threadpool_limits = None
         threads = 1
-    o = dfs_arrays(case.seqs)
-    N = o["N"]
+    N = len(dfs_arrays(case.seqs)["token"])
+    longest = max(case.seqs, key=len)
     rng = ts.rng_for(seed + 77)
+    sq = float(sum(len(x) ** 2 for x in case.seqs))
+    draw = lambda shape, std: ts.bf16_bits_to_f64(ts.normal_bf16(rng, shape, std))  # noqa: E731
 
-    def rowbits(shape_h, std, rows):
-        # the same distribution as the GPU inputs, drawn per sampled row set
-        return ts.bf16_bits_to_f64(ts.normal_bf16(rng, (len(rows),) + shape_h, std))
-
-    def run(budget):
-        done = 0
+    def one(L):
+        o = dfs_arrays([longest[:L]])
+        q, k, v, do = draw((L, 4, 128), 128 ** -0.5), draw((L, 1, 128), 128 ** -0.5), \
+            draw((L, 1, 128), 128 ** -0.5), draw((L, 4, 128), 1.0)
         t0 = time.perf_counter()
-        while time.perf_counter() - t0 < budget:
-            one_row()
-            done += 1
-        return done, time.perf_counter() - t0
+        OA.forward(o, q, k, v)
+        OA.backward(o, q, k, v, do)
+        return time.perf_counter() - t0
 
-    def one_row():
-        i = int(rng.integers(0, N))
-        br = OA.ancestors(o, i)
-        qv = rowbits((32, 128), 128 ** -0.5, br)
-        kv = rowbits((8, 128), 128 ** -0.5, br)
-        vv = rowbits((8, 128), 128 ** -0.5, br)
-        dov = rowbits((32, 128), 1.0, br)
-        idx = {int(r): n for n, r in enumerate(br)}
+    def measure(budget, L_max):
+        L = min(1024, len(longest))
+        t = one(L)
+        while t < budget / 4 and 2 * L <= min(len(longest), L_max):
+            L *= 2
+            t = one(L)
+        times, t_all = [t], t
+        while t_all + t < budget:
+            times.append(one(L))
+            t_all += times[-1]
+        mean = float(np.mean(times))
+        full = mean * (sq / L ** 2) * 8
+        return L, len(times), mean, full
 
-        def get(name, ix, qv=qv, kv=kv, vv=vv, dov=dov, idx=idx):
-            src = {"q": qv, "k": kv, "v": vv, "do": dov}[name]
-            return src[[idx[int(x)] for x in ix]]
-
-        OA.forward_rows(o, None, None, None, [i], get=get)
-        OA.dq_rows(o, None, None, None, None, [i], get=get)
-
-    done, el = run(budget_s)
-    one = None
-    try:  # the same sample on one BLAS thread
-        from threadpoolctl import threadpool_limits
+    L, n, mean, full = measure(budget_s, 8192)
+    one_core = None
+    if threadpool_limits is not None:
         with threadpool_limits(limits=1):
-            d1, e1 = run(budget_s / 3)
-        one = round(d1 / e1, 3)
-    except Exception:  # pragma: no cover
-        pass
-    return {"value": round(done / el, 3), "unit": "unique tokens/s (forward + dQ only)", "cores": threads,
-            "value_1core": one, "kind": "oracle",
-            "sample": f"{done} rows drawn uniformly from the {N}-row agentic tree; per row the oracle's per-branch "
-                      f"forward and dQ over all 32 heads (forward_rows + dq_rows, fp64 numpy) in {el:.1f} s; "
-                      "dK/dV are not included (the oracle's per-key form costs the key's whole subtree), so this "
-                      "overstates the oracle's full forward+backward rate"}
+            L1, n1, mean1, full1 = measure(budget_s / 3, 4096)
+        one_core = round(N / full1, 3)
+    return {"value": round(N / full, 3), "unit": "unique tokens/s (forward + backward, extrapolated)",
+            "cores": threads, "value_1core": one_core, "kind": "oracle",
+            "extrapolated_step_s": round(full, 1),
+            "sample": f"{n} oracle calls (fp64 numpy per-branch forward + backward) on the first {L} rows of the "
+                      f"longest branch for one kv head's 4 query heads, {mean:.2f} s each; the full step (all "
+                      f"{len(case.seqs)} branches of the {N}-row tree, 32 heads) is extrapolated by "
+                      f"sum_s |s|^2 / L^2 = {sq / L ** 2:.1f} and 8 head groups to {full:.0f} s"}
 
 
 def main():
@@ -515,6 +520,9 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_secondary:
         result["secondary"] = secondary(tt, ts, args.steps)
+        result["study"] = {"name": "compression_sweep", "workload": "8 branches x 8192 tokens sharing a prefix of "
+                           "p tokens, Hq 32, Hkv 8, d 128, bf16 fwd+bwd; tree mode vs the same kernels per branch",
+                           "points": compression_study(tt, ts, args.steps, prefixes=(7168, 4096, 1024, 0))}
     if not args.no_cpu_baseline:
         cb = cpu_baseline(ts, case, args.seed, args.cpu_seconds)
         cb["gpu_over_cpu"] = round(value / cb["value"], 1)

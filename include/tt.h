@@ -63,6 +63,11 @@ typedef enum { TT_F32 = 0, TT_BF16 = 1 } tt_dtype;
 /* hipStream_t, passed as an opaque pointer (NULL = the null stream). */
 typedef void* tt_stream;
 
+/* Flags of tt_attn_args (and tt_path_args). */
+#define TT_ALLOW_GENERIC 1u /* bf16 shapes the matrix-core kernels do not take (head dim other than
+                               128, schedule blocks other than 64) run on the vector kernels, many
+                               times slower, instead of failing with TT_EUNSUPPORTED */
+
 /* Flags of tree_attn_bwd. */
 #define TT_ACCUMULATE_DKDV 1u /* d_k, d_v are float32 and the call ADDS into them */
 #define TT_BWD_REUSE_ROTATED 2u /* the workspace still holds the rotated q and k that
@@ -158,13 +163,15 @@ int tree_target_weights(const tt_tree* tree, const float* seq_scale, const uint8
  * `stream`) into the caller's device buffer of at least that many bytes.
  * Errors: TT_EINVAL, TT_EWORKSPACE (buffer too small), TT_EDEVICE.
  * The image's header carries its row count and an identity word (a hash of
- * the image, which holds structure only, not token ids).  Every kernel that
- * reads the plan first compares them with the tree of the call and returns
- * without writing anything when they differ: a plan uploaded for another
- * tree leaves the call's outputs unchanged instead of being read out of
- * bounds.  That mismatch is not reported (detecting it would need a device
- * synchronisation); passing the plan of the call's own tree is the caller's
- * contract.
+ * the image, which holds structure only, not token ids: trees of one shape
+ * have interchangeable plans).  The library records, per device address, the
+ * identity of the image last uploaded there; an attention call whose plan
+ * address holds no upload, or the upload of a tree of another shape, fails
+ * with TT_EINVAL before anything is launched.  As a backstop for device
+ * memory the host cannot see (a plan buffer overwritten by other work), every
+ * kernel that reads the plan first compares the header with the tree of the
+ * call and returns without writing when they differ, so a wrong plan is
+ * never read out of bounds.
  */
 int tree_plan_bytes(const tt_tree* tree, size_t* bytes);
 int tree_plan_upload(const tt_tree* tree, void* dev_plan, size_t bytes, tt_stream stream);
@@ -201,7 +208,13 @@ typedef struct {
                               caller that passes the forward's workspace, unmodified, to the
                               backward may set TT_BWD_REUSE_ROTATED */
   size_t workspace_bytes;
+  uint32_t flags;          /* 0 or TT_ALLOW_GENERIC; other bits: TT_EINVAL */
 } tt_attn_args;
+
+/* Kernels.  bf16 with head dim 128 (and the default 64-row schedule blocks)
+ * runs on the hand-written matrix-core kernels for any GQA group size and any
+ * tensor size; other bf16 shapes fail with TT_EUNSUPPORTED unless
+ * TT_ALLOW_GENERIC is set.  float32 runs on the vector kernels. */
 
 /* Workspace size for tree_attn_fwd (for_bwd = 0) or tree_attn_bwd (for_bwd = 1). */
 int tree_attn_workspace_bytes(const tt_attn_args* args, int for_bwd, size_t* bytes);
@@ -294,23 +307,32 @@ int tree_weighted_nll(const tt_nll_args* args, tt_stream stream);
  *
  * A segment is a maximal run of DFS rows in which every row but the last has
  * exactly one child; the segments form a tree.  Entering a segment pushes its
- * Q, K (rotated at their depths) and V onto the stack at positions = depths
- * and runs its forward in chunks against stack positions [0, end of chunk).
- * Leaving it (after all descendants) runs its backward chunk by chunk from the
- * right, adding dK, dV into float32 stack accumulators, then writes the
- * segment's dK, dV rows out and clears their stack slots.  Each call starts at
- * the 64-aligned position at or below its first query; the ancestor rows below
- * the chunk are recomputed with a zero upstream gradient ("pad rows", counted
- * in tt_path_info), so results equal tree mode (tree_attn_fwd/bwd) up to the
- * order of floating-point sums.
+ * Q, K (rotated at their depths) and V onto the stack at positions = depths;
+ * leaving it (after all descendants) pops it.  Consecutive enters form a
+ * forward round and consecutive leaves a backward round: the round's
+ * segments lie one on the next on the stack, so a round is one chunked pass
+ * over its positions -- one forward and one backward round per leaf
+ * (AReaL-DTA, Key Contributions 2: push-pop execution, about one regular
+ * forward/backward round per leaf).  A forward round runs its chunks against
+ * stack positions [0, end of chunk); a backward round runs them from the
+ * right, adding dK, dV into float32 stack accumulators, then writes each
+ * popped segment's dK, dV rows out and clears their stack slots.  Each call
+ * starts at the 64-aligned position at or below its first query; the
+ * ancestor rows below the chunk are recomputed with a zero upstream gradient
+ * ("pad rows", counted in tt_path_info), so results equal tree mode
+ * (tree_attn_fwd/bwd) up to the order of floating-point sums.
  *
  * tree_path_build
  *   tree    built tree; must outlive the path object
  *   chunk   queries per call, a positive multiple of 64 (Key Contributions 2
  *           gives 2048 as the default and 4096 as the faster setting)
- *   order   child visiting order: 0 = DFS (ascending token id), 1 = largest
- *           subtree first (the pages name a greedy ordering heuristic without
- *           defining it; this is one reading, offered for comparison)
+ *   order   child visiting order: 0 = DFS (ascending token id); 1 = greedy:
+ *           a node's last child is the one whose chain of last descendants
+ *           is shortest (children by descending chain length, ties in DFS
+ *           order), so short segments extend their parent's backward round
+ *           instead of forming short rounds of their own (AReaL-DTA, Key
+ *           Contributions 2 names a greedy DFS ordering that avoids short
+ *           backward steps without defining it; this is that reading)
  *   out     receives the path object; free with tree_path_free
  * Errors: TT_EINVAL (NULL, chunk, order), TT_ENOMEM.  Host only.
  */
@@ -320,10 +342,10 @@ typedef struct {
   int32_t n_segments;
   int32_t max_path;      /* longest root-to-leaf path in rows (max depth + 1): the stack size */
   int32_t chunk, order;
-  int64_t fwd_calls;     /* attention calls of one forward traversal */
-  int64_t bwd_calls;     /* attention calls of one backward traversal */
-  int64_t pad_rows;      /* ancestor query rows recomputed per traversal (64-alignment of calls) */
-  int64_t query_rows;    /* rows the calls compute in total: N + pad_rows */
+  int64_t fwd_calls;     /* attention calls of the forward rounds */
+  int64_t bwd_calls;     /* attention calls of the backward rounds */
+  int64_t pad_rows;      /* ancestor query rows recomputed by all calls (64-alignment of a round's first call) */
+  int64_t query_rows;    /* query rows all calls compute: 2 N + pad_rows */
   int64_t pad_pairs;     /* visible (query, key) pairs per head of the pad rows: recompute cost */
 } tt_path_info;
 
@@ -348,14 +370,16 @@ int tree_path_segments(const tt_path* path, int32_t* row0, int32_t* len, int32_t
  *   d_o           [N,h_q,d] upstream gradient, or NULL for forward only
  *   d_q, d_k, d_v [N,h_q,d], [N,h_kv,d], [N,h_kv,d] outputs in dtype,
  *                 overwritten (ignored when d_o is NULL)
+ *   plan          from tree_path_plan_upload for this path
  *   workspace     tree_path_workspace_bytes bytes, 256-byte aligned: the
  *                 stack (Q, K, V, O, LSE and, with d_o, float32 dK, dV) of
- *                 max_path positions plus per-call buffers of chunk + 64 rows
- *                 and the chain plan; proportional to the longest path, not N
+ *                 max_path positions plus per-call buffers of chunk + 64 rows;
+ *                 proportional to the longest path, not N
  * Errors: TT_EINVAL, TT_EUNSUPPORTED, TT_EWORKSPACE, TT_EOVERFLOW, TT_EDEVICE.
  */
 typedef struct {
   const tt_path* path;
+  const void* plan;        /* device plan of the walk, filled once by tree_path_plan_upload */
   int32_t h_q, h_kv, d;
   tt_dtype dtype;
   float scale;
@@ -367,7 +391,16 @@ typedef struct {
   void *d_q, *d_k, *d_v;
   void* workspace;
   size_t workspace_bytes;
+  uint32_t flags;          /* 0 or TT_ALLOW_GENERIC */
 } tt_path_args;
+
+/* The walk's device plan: the schedule of one chain of max_path rows, which
+ * serves every attention call of the walk (stack position = depth).  Upload it
+ * once per path object (hipMemcpyAsync on `stream`, like tree_plan_upload);
+ * tree_attn_path then copies nothing from the host.
+ * Errors: TT_EINVAL, TT_EWORKSPACE (buffer too small), TT_EDEVICE. */
+int tree_path_plan_bytes(const tt_path* path, size_t* bytes);
+int tree_path_plan_upload(const tt_path* path, void* dev_plan, size_t bytes, tt_stream stream);
 
 int tree_path_workspace_bytes(const tt_path_args* args, size_t* bytes);
 int tree_attn_path(const tt_path_args* args, tt_stream stream);

@@ -104,6 +104,58 @@ def lmhead_rows(hidden_rows, w_vocab, targets):
     return out
 
 
+def lmhead_lse(hidden, w_vocab, row_block=256):
+    """Log-sum-exp of every row of z = H W (fp64), z formed one block of rows
+    at a time so that the whole [rows, vocab] matrix is never held at once
+    (the fused lm-head at full vocabulary size)."""
+    H = np.asarray(hidden, dtype=np.float64)
+    W = np.asarray(w_vocab, dtype=np.float64)
+    out = np.empty(H.shape[0])
+    for r0 in range(0, H.shape[0], row_block):
+        out[r0:r0 + row_block] = _lse(H[r0:r0 + row_block] @ W)
+    return out
+
+
+def lmhead_target_logp(hidden, w_vocab, lse, parent, token, weight):
+    """Loss and per-target log-probabilities from per-row LSE (fp64).
+
+    Target t is predicted from row parent[t]: logp_t = z[parent t][x_t] -
+    lse[parent t] with z[r][x] = H_r . W[:, x]; loss = -sum_t w_t logp_t.
+    Returns (loss, logp [N] with nan at roots)."""
+    H = np.asarray(hidden, dtype=np.float64)
+    W = np.asarray(w_vocab, dtype=np.float64)
+    parent = np.asarray(parent)
+    t = np.nonzero(parent >= 0)[0]
+    r = parent[t]
+    x = np.asarray(token)[t]
+    z = np.einsum("td,dt->t", H[r], W[:, x])
+    logp = np.full(len(parent), np.nan)
+    logp[t] = z - np.asarray(lse)[r]
+    loss = -float(np.sum(np.asarray(weight, dtype=np.float64)[t] * logp[t]))
+    return loss, logp
+
+
+def lmhead_dw_columns(hidden, w_vocab, lse, parent, token, weight, cols):
+    """Columns `cols` of dW = H^T dZ (fp64), where row r of dZ is
+    (sum of its targets' weights) softmax(z_r) - sum over its targets t of
+    w_t e_{x_t}; only the selected columns of z and dZ are formed."""
+    H = np.asarray(hidden, dtype=np.float64)
+    W = np.asarray(w_vocab, dtype=np.float64)
+    cols = np.asarray(cols)
+    parent = np.asarray(parent)
+    weight = np.asarray(weight, dtype=np.float64)
+    wsum = np.zeros(H.shape[0])
+    for t in np.nonzero(parent >= 0)[0]:
+        wsum[parent[t]] += weight[t]
+    dz = wsum[:, None] * np.exp(H @ W[:, cols] - np.asarray(lse)[:, None])
+    where = {int(c): n for n, c in enumerate(cols)}
+    for t in np.nonzero(parent >= 0)[0]:
+        n = where.get(int(token[t]))
+        if n is not None:
+            dz[parent[t], n] -= weight[t]
+    return H.T @ dz
+
+
 def rl_weights(seq_pos_to_dfs, seq_lens, N, seq_scale=None, token_mask=None):
     """Per-row target weights for per-sequence scalars and per-token masks (fp64).
 

@@ -22,13 +22,15 @@ TT_OK, TT_EINVAL, TT_ENOMEM, TT_EWORKSPACE, TT_EUNSUPPORTED, TT_EDEVICE, TT_EOVE
 TT_F32, TT_BF16 = 0, 1
 TT_ACCUMULATE_DKDV = 1
 TT_BWD_REUSE_ROTATED = 2
+TT_ALLOW_GENERIC = 1
 
 EXPORTED = ("tree_build", "tree_free", "tree_info", "tree_export", "tree_plan_bytes", "tree_plan_upload",
             "tree_plan_copy",
             "tree_attn_workspace_bytes", "tree_attn_fwd", "tree_attn_bwd", "tree_nll_workspace_bytes",
             "tree_weighted_nll", "tt_last_error", "tt_timing_enable", "tt_timing_collect",
-            "tree_target_weights", "tree_path_build", "tree_path_free", "tree_path_info", "tree_path_segments", "tree_path_workspace_bytes",
-            "tree_attn_path", "tt_probe_mfma")
+            "tree_target_weights", "tree_path_build", "tree_path_free", "tree_path_info", "tree_path_segments",
+            "tree_path_plan_bytes", "tree_path_plan_upload", "tree_path_workspace_bytes", "tree_attn_path",
+            "tt_probe_mfma")
 
 
 class TTError(RuntimeError):
@@ -61,7 +63,8 @@ class AttnArgs(ctypes.Structure):
                 ("dtype", ctypes.c_int), ("scale", ctypes.c_float), ("rope_base", ctypes.c_float),
                 ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
                 ("o", ctypes.c_void_p), ("lse", ctypes.c_void_p),
-                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+                ("flags", ctypes.c_uint32)]
 
 
 class AttnBwdArgs(ctypes.Structure):
@@ -96,12 +99,13 @@ class PathInfo(ctypes.Structure):
 
 
 class PathArgs(ctypes.Structure):
-    _fields_ = [("path", ctypes.c_void_p), ("h_q", ctypes.c_int32), ("h_kv", ctypes.c_int32), ("d", ctypes.c_int32),
+    _fields_ = [("path", ctypes.c_void_p), ("plan", ctypes.c_void_p), ("h_q", ctypes.c_int32),
+                ("h_kv", ctypes.c_int32), ("d", ctypes.c_int32),
                 ("dtype", ctypes.c_int32), ("scale", ctypes.c_float), ("rope_base", ctypes.c_float),
                 ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("o", ctypes.c_void_p),
                 ("lse", ctypes.c_void_p), ("d_o", ctypes.c_void_p), ("d_q", ctypes.c_void_p),
                 ("d_k", ctypes.c_void_p), ("d_v", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
-                ("workspace_bytes", ctypes.c_size_t)]
+                ("workspace_bytes", ctypes.c_size_t), ("flags", ctypes.c_uint32)]
 
 
 def _setup(lib):
@@ -127,6 +131,8 @@ def _setup(lib):
     lib.tree_path_free.restype = None
     lib.tree_path_info.argtypes = [ctypes.c_void_p, ctypes.POINTER(PathInfo)]
     lib.tree_path_segments.argtypes = [ctypes.c_void_p] + [_i32p] * 5
+    lib.tree_path_plan_bytes.argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_size_t)]
+    lib.tree_path_plan_upload.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     lib.tree_path_workspace_bytes.argtypes = [ctypes.POINTER(PathArgs), ctypes.POINTER(ctypes.c_size_t)]
     lib.tree_attn_path.argtypes = [ctypes.POINTER(PathArgs), ctypes.c_void_p]
     lib.tt_last_error.restype = ctypes.c_char_p
@@ -138,7 +144,8 @@ def _setup(lib):
                                   ctypes.POINTER(ctypes.c_double)]
     lib.tt_probe_mfma.restype = ctypes.c_int
     for _n in ("tree_info", "tree_export", "tree_plan_bytes", "tree_plan_upload", "tree_plan_copy", "tree_attn_workspace_bytes",
-               "tree_attn_fwd", "tree_attn_bwd", "tree_nll_workspace_bytes", "tree_weighted_nll"):
+               "tree_attn_fwd", "tree_attn_bwd", "tree_nll_workspace_bytes", "tree_weighted_nll",
+               "tree_path_plan_bytes", "tree_path_plan_upload", "tree_path_workspace_bytes", "tree_attn_path"):
         getattr(lib, _n).restype = ctypes.c_int
 
 
@@ -319,12 +326,71 @@ def _p(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p()
 
 
-def _attn_args(tree, plan, q, k, v, o, lse, q_off, scale, rope_base):
+def _fail(msg):
+    raise ValueError(msg)
+
+
+def _check_tensor(t, name, dtypes=None, shape=None):
+    """Type, dtype, shape and contiguity of one tensor argument (ValueError)."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        _fail(f"{name} must be a torch.Tensor")
+    if dtypes is not None and t.dtype not in dtypes:
+        _fail(f"{name} has dtype {t.dtype}; expected {' or '.join(str(d) for d in dtypes)}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        _fail(f"{name} has shape {tuple(t.shape)}; expected {tuple(shape)}")
+    if not t.is_contiguous():
+        _fail(f"{name} must be contiguous (a strided view is read as if it were dense)")
+
+
+def _check_devices(**named):
+    """Every given tensor on one CUDA (HIP) device (checked after the layouts)."""
+    ref = None
+    for name, t in named.items():
+        if t is None:
+            continue
+        if not t.is_cuda:
+            _fail(f"{name} must be on a CUDA (HIP) device, not {t.device}")
+        if ref is None:
+            ref = (name, t.device)
+        elif t.device != ref[1]:
+            _fail(f"{name} is on {t.device} but {ref[0]} is on {ref[1]}")
+
+
+def _check_plan(tree, plan):
+    import torch
+    _check_tensor(plan, "plan", (torch.uint8,))
+    if plan.numel() < tree.plan_bytes():
+        _fail(f"plan holds {plan.numel()} bytes; this tree's plan needs {tree.plan_bytes()}")
+
+
+def _check_workspace(ws):
+    import torch
+    if ws is not None:
+        _check_tensor(ws, "workspace", (torch.uint8,))
+
+
+def _check_attn(tree, plan, q, k, v, workspace):
+    """q [n_q, h_q, d], k and v [n_k, h_kv, d], one dtype (float32 or bfloat16)."""
+    import torch
+    _check_tensor(q, "q", (torch.float32, torch.bfloat16))
+    if q.dim() != 3:
+        _fail(f"q must be [n_q, h_q, d]; got shape {tuple(q.shape)}")
+    _check_tensor(k, "k", (q.dtype,))
+    if k.dim() != 3 or k.shape[2] != q.shape[2]:
+        _fail(f"k must be [n_k, h_kv, {q.shape[2]}]; got shape {tuple(k.shape)}")
+    _check_tensor(v, "v", (q.dtype,), shape=k.shape)
+    _check_plan(tree, plan)
+    _check_workspace(workspace)
+
+
+def _attn_args(tree, plan, q, k, v, o, lse, q_off, scale, rope_base, allow_generic=False):
     n_q, h_q, d = q.shape
     n_k, h_kv, _ = k.shape
     return AttnArgs(tree=tree.handle, plan=ctypes.c_void_p(plan.data_ptr()), q_off=q_off, n_q=n_q, n_k=n_k,
                     h_q=h_q, h_kv=h_kv, d=d, dtype=_dt(q), scale=scale, rope_base=rope_base,
-                    q=_p(q), k=_p(k), v=_p(v), o=_p(o), lse=_p(lse), workspace=None, workspace_bytes=0)
+                    q=_p(q), k=_p(k), v=_p(v), o=_p(o), lse=_p(lse), workspace=None, workspace_bytes=0,
+                    flags=TT_ALLOW_GENERIC if allow_generic else 0)
 
 
 def attn_workspace_bytes(tree, plan, q, k, v, for_bwd, q_off=0, rope_base=10000.0):
@@ -341,14 +407,22 @@ def _workspace(nbytes, device, workspace):
     return workspace
 
 
-def tree_attn_fwd(tree, plan, q, k, v, q_off=0, scale=0.0, rope_base=10000.0, o=None, lse=None, workspace=None):
-    """O, LSE of tree attention for query rows [q_off, q_off + q.shape[0]) against key rows [0, k.shape[0])."""
+def tree_attn_fwd(tree, plan, q, k, v, q_off=0, scale=0.0, rope_base=10000.0, o=None, lse=None, workspace=None,
+                  allow_generic=False):
+    """O, LSE of tree attention for query rows [q_off, q_off + q.shape[0]) against key rows [0, k.shape[0]).
+
+    allow_generic: run bf16 shapes the matrix-core kernels do not take on the
+    vector kernels instead of raising (TT_ALLOW_GENERIC)."""
     import torch
+    _check_attn(tree, plan, q, k, v, workspace)
     if o is None:
         o = torch.empty_like(q)
     if lse is None:
         lse = torch.empty(q.shape[0], q.shape[1], dtype=torch.float32, device=q.device)
-    a = _attn_args(tree, plan, q, k, v, o, lse, q_off, scale, rope_base)
+    _check_tensor(o, "o", (q.dtype,), shape=q.shape)
+    _check_tensor(lse, "lse", (torch.float32,), shape=q.shape[:2])
+    _check_devices(q=q, k=k, v=v, o=o, lse=lse, plan=plan, workspace=workspace)
+    a = _attn_args(tree, plan, q, k, v, o, lse, q_off, scale, rope_base, allow_generic)
     n = ctypes.c_size_t()
     _check(lib().tree_attn_workspace_bytes(ctypes.byref(a), 0, ctypes.byref(n)))
     ws = _workspace(n.value, q.device, workspace)
@@ -359,7 +433,7 @@ def tree_attn_fwd(tree, plan, q, k, v, q_off=0, scale=0.0, rope_base=10000.0, o=
 
 
 def tree_attn_bwd(tree, plan, q, k, v, o, lse, d_o, q_off=0, scale=0.0, rope_base=10000.0, d_q=None, d_k=None,
-                  d_v=None, accumulate=False, workspace=None, reuse_rotated=False):
+                  d_v=None, accumulate=False, workspace=None, reuse_rotated=False, allow_generic=False):
     """dQ, dK, dV (dK/dV are float32 and added into when accumulate=True).
 
     reuse_rotated: `workspace` is the one tree_attn_fwd used for these same
@@ -367,13 +441,24 @@ def tree_attn_bwd(tree, plan, q, k, v, o, lse, d_o, q_off=0, scale=0.0, rope_bas
     if reuse_rotated and workspace is None:
         raise ValueError("reuse_rotated needs the forward's workspace")
     import torch
+    _check_attn(tree, plan, q, k, v, workspace)
+    _check_tensor(o, "o", (q.dtype,), shape=q.shape)
+    _check_tensor(lse, "lse", (torch.float32,), shape=q.shape[:2])
+    _check_tensor(d_o, "d_o", (q.dtype,), shape=q.shape)
+    gdt = torch.float32 if accumulate else k.dtype
+    for name, t in (("d_k", d_k), ("d_v", d_v)):
+        if t is not None:
+            _check_tensor(t, name, (gdt,), shape=k.shape)
+    if d_q is not None:
+        _check_tensor(d_q, "d_q", (q.dtype,), shape=q.shape)
+    _check_devices(q=q, k=k, v=v, o=o, lse=lse, d_o=d_o, d_q=d_q, d_k=d_k, d_v=d_v, plan=plan, workspace=workspace)
     if d_q is None:
         d_q = torch.empty_like(q)
     if d_k is None:
         d_k = (torch.zeros(k.shape, dtype=torch.float32, device=k.device) if accumulate else torch.empty_like(k))
     if d_v is None:
         d_v = (torch.zeros(v.shape, dtype=torch.float32, device=v.device) if accumulate else torch.empty_like(v))
-    a = _attn_args(tree, plan, q, k, v, o, lse, q_off, scale, rope_base)
+    a = _attn_args(tree, plan, q, k, v, o, lse, q_off, scale, rope_base, allow_generic)
     n = ctypes.c_size_t()
     _check(lib().tree_attn_workspace_bytes(ctypes.byref(a), 1, ctypes.byref(n)))
     ws = _workspace(n.value, q.device, workspace)
@@ -391,11 +476,31 @@ class Path:
 
     def __init__(self, tree, chunk=2048, order=0):
         self.tree = tree  # the walk reads the tree: keep it alive
+        self.plan = None  # device plan of the walk, uploaded on first use
         self.handle = ctypes.c_void_p()
         _check(lib().tree_path_build(tree.handle, int(chunk), int(order), ctypes.byref(self.handle)))
         inf = PathInfo()
         _check(lib().tree_path_info(self.handle, ctypes.byref(inf)))
         self.info = {n: int(getattr(inf, n)) for n, _ in PathInfo._fields_}
+
+    def plan_bytes(self):
+        n = ctypes.c_size_t()
+        _check(lib().tree_path_plan_bytes(self.handle, ctypes.byref(n)))
+        return n.value
+
+    def upload_plan(self, device="cuda"):
+        """The walk's device plan (uploaded once per path and device, kept on the object)."""
+        import torch
+        dev = torch.device(device)
+        if dev.type == "cuda" and dev.index is None:
+            dev = torch.device("cuda", torch.cuda.current_device())
+        if self.plan is None or self.plan.device != dev:
+            buf = torch.empty(max(self.plan_bytes(), 16), dtype=torch.uint8, device=dev)
+            _check(lib().tree_path_plan_upload(self.handle, ctypes.c_void_p(buf.data_ptr()), buf.numel(),
+                                               _stream()))
+            torch.cuda.current_stream().synchronize()  # the host image must outlive the copy
+            self.plan = buf
+        return self.plan
 
     def segments(self):
         """Segment table (row0, len, depth0, parent) and the walk's events, as host arrays."""
@@ -416,11 +521,12 @@ class Path:
             self.handle = None
 
 
-def _path_args(path, q, k, v, d_o, scale, rope_base):
+def _path_args(path, q, k, v, d_o, scale, rope_base, plan=None, allow_generic=False):
     _, h_q, d = q.shape
     h_kv = k.shape[1]
-    return PathArgs(path=path.handle, h_q=h_q, h_kv=h_kv, d=d, dtype=_dt(q), scale=scale, rope_base=rope_base,
-                    q=_p(q), k=_p(k), v=_p(v), d_o=_p(d_o))
+    return PathArgs(path=path.handle, plan=_p(plan), h_q=h_q, h_kv=h_kv, d=d, dtype=_dt(q), scale=scale,
+                    rope_base=rope_base, q=_p(q), k=_p(k), v=_p(v), d_o=_p(d_o),
+                    flags=TT_ALLOW_GENERIC if allow_generic else 0)
 
 
 def path_workspace_bytes(path, q, k, v, backward, scale=0.0, rope_base=10000.0):
@@ -431,9 +537,24 @@ def path_workspace_bytes(path, q, k, v, backward, scale=0.0, rope_base=10000.0):
 
 
 def tree_attn_path(path, q, k, v, d_o=None, scale=0.0, rope_base=10000.0, o=None, lse=None, d_q=None, d_k=None,
-                   d_v=None, workspace=None):
+                   d_v=None, workspace=None, allow_generic=False):
     """Path-mode walk of one layer: (o, lse), or (o, lse, d_q, d_k, d_v) when d_o is given."""
     import torch
+    N = path.tree.N
+    _check_tensor(q, "q", (torch.float32, torch.bfloat16))
+    if q.dim() != 3 or q.shape[0] != N:
+        _fail(f"q must be [{N}, h_q, d] (one row per tree row); got shape {tuple(q.shape)}")
+    _check_tensor(k, "k", (q.dtype,))
+    if k.dim() != 3 or k.shape[0] != N or k.shape[2] != q.shape[2]:
+        _fail(f"k must be [{N}, h_kv, {q.shape[2]}]; got shape {tuple(k.shape)}")
+    _check_tensor(v, "v", (q.dtype,), shape=k.shape)
+    _check_workspace(workspace)
+    for name, t, shp, dts in (("o", o, q.shape, (q.dtype,)), ("lse", lse, q.shape[:2], (torch.float32,)),
+                              ("d_o", d_o, q.shape, (q.dtype,)), ("d_q", d_q, q.shape, (q.dtype,)),
+                              ("d_k", d_k, k.shape, (q.dtype,)), ("d_v", d_v, k.shape, (q.dtype,))):
+        if t is not None:
+            _check_tensor(t, name, dts, shape=shp)
+    _check_devices(q=q, k=k, v=v, o=o, lse=lse, d_o=d_o, d_q=d_q, d_k=d_k, d_v=d_v, workspace=workspace)
     if o is None:
         o = torch.empty_like(q)
     if lse is None:
@@ -442,7 +563,8 @@ def tree_attn_path(path, q, k, v, d_o=None, scale=0.0, rope_base=10000.0, o=None
         d_q = torch.empty_like(q) if d_q is None else d_q
         d_k = torch.empty_like(k) if d_k is None else d_k
         d_v = torch.empty_like(v) if d_v is None else d_v
-    a = _path_args(path, q, k, v, d_o, scale, rope_base)
+    plan = path.upload_plan(q.device)
+    a = _path_args(path, q, k, v, d_o, scale, rope_base, plan, allow_generic)
     a.o, a.lse, a.d_q, a.d_k, a.d_v = _p(o), _p(lse), _p(d_q), _p(d_k), _p(d_v)
     n = ctypes.c_size_t()
     _check(lib().tree_path_workspace_bytes(ctypes.byref(a), ctypes.byref(n)))
@@ -461,7 +583,32 @@ def tree_weighted_nll(tgt_row_ptr, tgt_id, tgt_w, logits=None, hidden=None, w_vo
     Returns dict(loss=<0-d float32 tensor>, logp, d_logits | d_hidden, d_w_vocab)."""
     import torch
     fused = hidden is not None
+    if fused == (logits is not None):
+        _fail("give exactly one of logits or hidden (with w_vocab)")
+    if fused:
+        _check_tensor(hidden, "hidden", (torch.bfloat16,))
+        if hidden.dim() != 2:
+            _fail(f"hidden must be [n_rows, d_model]; got shape {tuple(hidden.shape)}")
+        _check_tensor(w_vocab, "w_vocab", (torch.bfloat16,))
+        if w_vocab.dim() != 2 or w_vocab.shape[0] != hidden.shape[1]:
+            _fail(f"w_vocab must be [{hidden.shape[1]}, vocab]; got shape {tuple(w_vocab.shape)}")
+    else:
+        if w_vocab is not None:
+            _fail("w_vocab needs hidden (fused mode)")
+        _check_tensor(logits, "logits", (torch.float32, torch.bfloat16))
+        if logits.dim() != 2:
+            _fail(f"logits must be [n_rows, vocab]; got shape {tuple(logits.shape)}")
+        if d_logits is not None:
+            _check_tensor(d_logits, "d_logits", (logits.dtype,), shape=logits.shape)
     ref = hidden if fused else logits
+    _check_tensor(tgt_row_ptr, "tgt_row_ptr", (torch.int32,), shape=(ref.shape[0] + 1,))
+    _check_tensor(tgt_id, "tgt_id", (torch.int32,))
+    if tgt_id.dim() != 1:
+        _fail(f"tgt_id must be one-dimensional; got shape {tuple(tgt_id.shape)}")
+    _check_tensor(tgt_w, "tgt_w", (torch.float32,), shape=tgt_id.shape)
+    _check_workspace(workspace)
+    _check_devices(hidden=hidden, w_vocab=w_vocab, logits=logits, d_logits=d_logits, tgt_row_ptr=tgt_row_ptr,
+                   tgt_id=tgt_id, tgt_w=tgt_w, workspace=workspace)
     dev = ref.device
     n_rows = ref.shape[0]
     vocab = w_vocab.shape[1] if fused else logits.shape[1]

@@ -84,6 +84,17 @@ class KTimer {
 };
 
 
+// Device plans the host has filled: tree_plan_upload (and the path-mode
+// upload) records each buffer's address with its image's identity word, and
+// every attention call checks that its plan is one of them and belongs to a
+// tree of the call's shape (TT_EINVAL otherwise).  The kernels' own header
+// check stays as the backstop for device memory the host cannot see.
+void plan_register(const void* dev_plan, int32_t id);
+int plan_check(const tt_tree* t, const void* dev_plan, const char* fn);
+
+// Shapes the bf16 matrix-core kernels take (any GQA group, any size).
+bool mfma_shape(int32_t d, int32_t bq, int32_t bk);
+
 // Forward on rotated q, k (no RoPE here).
 int attn_fwd_core(tt_dtype dt, const PlanPtrs& P, const AttnGeom& g, const void* q, const void* k, const void* v,
                   void* o, float* lse, bool full_range, hipStream_t st);

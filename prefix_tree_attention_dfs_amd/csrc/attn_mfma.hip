@@ -4,8 +4,9 @@
 // once and must get exactly its per-branch result; row i attends to row j iff
 // j <= i < end[j] (j is i or an ancestor of i in DFS order).
 //
-// One workgroup = one 64-row query block x one key/value head, i.e. the G
-// query heads that share that K/V (GQA).  It walks the block's list of
+// One workgroup = one 64-row query block x G query heads of one key/value
+// head's group (GQA; a group of more than 4 heads is split over several
+// workgroups, nsub per block, which read the same K/V tiles).  It walks the block's list of
 // non-empty 64-key tiles (the plan's CSR); FULL tiles skip the mask.  K and V
 // tiles go from global memory straight into LDS (swizzled layout), double
 // buffered, one barrier per tile.  Per wave: NT sub-tiles of 32 query rows of one head, Q held in
@@ -42,7 +43,7 @@ template <int G>
 __global__ __launch_bounds__(FwdCfg<G>::THREADS, FwdCfg<G>::MINB) void fwd_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     uint16_t* __restrict__ o, float* __restrict__ lse, PlanPtrs P, AttnGeom g, int full_range, int qb_first,
-    int n_qb) {
+    int n_qb, int nsub) {
   using C = FwdCfg<G>;
   constexpr int NT = C::NT;
   __shared__ FwdStage st[2];
@@ -50,9 +51,10 @@ __global__ __launch_bounds__(FwdCfg<G>::THREADS, FwdCfg<G>::MINB) void fwd_mfma_
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r = lane & 31, hh = lane >> 5;
   const int kvh = blockIdx.x % g.h_kv;
-  const int idx = blockIdx.x / g.h_kv;
+  const int rest = blockIdx.x / g.h_kv;
+  const int sub = rest % nsub, idx = rest / nsub;
   const int qb = full_range ? ld_uniform(P.qb_order, idx) : (qb_first + n_qb - 1 - idx);
-  const int head = kvh * G + wave / C::WPH;
+  const int head = (kvh * nsub + sub) * G + wave / C::WPH;
   const int pos0 = (wave % C::WPH) * 32 * NT;
   const int qrow0 = qb * BQ - g.q_off;  // q-buffer row of the block's first position
   const float c2 = g.scale * 1.4426950408889634f;
@@ -78,11 +80,12 @@ __global__ __launch_bounds__(FwdCfg<G>::THREADS, FwdCfg<G>::MINB) void fwd_mfma_
     for (int dt = 0; dt < 4; ++dt) oacc[nt][dt] = zero16();
   }
 
-  // tile staging: buffer loads, zero past n_k keys (end = 0 there: invisible)
-  const uint32_t kv_bytes = uint32_t(g.n_k) * uint32_t(g.h_kv) * D * 2;
-  const rsrc_t rk = make_rsrc(k, kv_bytes), rv = make_rsrc(v, kv_bytes);
+  // tile staging: buffer loads, zero past n_k keys (end = 0 there: invisible);
+  // each tile's descriptors start at the tile (64-bit base), so K and V may
+  // exceed the 4 GiB a 32-bit buffer offset reaches
+  const int64_t kv_elems = int64_t(g.n_k) * g.h_kv * D;
+  const int64_t tile_elems = int64_t(BK) * g.h_kv * D;  // one 64-key tile of K (or V)
   const rsrc_t re = make_rsrc(P.end, uint32_t(g.n_k) * 4);
-  const uint32_t tile_bytes = uint32_t(BK) * g.h_kv * D * 2;  // one 64-key tile of K (or V)
   // K and V tiles (64 keys x 128 bf16 = 16 KB each) go from global memory
   // straight into LDS: 16 loads of 1 KB per tile, NL per wave.  Lane l of
   // load j fills LDS slot 64 j + l = (key, stored chunk) = ((64 j + l) / 16,
@@ -99,12 +102,14 @@ __global__ __launch_bounds__(FwdCfg<G>::THREADS, FwdCfg<G>::MINB) void fwd_mfma_
   }
   int32_t ereg = 0;
   auto load_tile = [&](int kb, FwdStage& s) {
-    const uint32_t so = uint32_t(kb) * tile_bytes;
+    const int64_t t0 = int64_t(kb) * tile_elems;
+    const uint32_t bytes = tile_rec_bytes(kv_elems - t0);
+    const rsrc_t rk = make_rsrc(k + t0, bytes), rv = make_rsrc(v + t0, bytes);
     const uint32_t kbase = lds_u32(s.K) + wave * NL * 1024, vbase = lds_u32(s.V) + wave * NL * 1024;
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
-      dma16(rk, dvoff[i], so, kbase + i * 1024);
-      dma16(rv, dvoff[i], so, vbase + i * 1024);
+      dma16(rk, dvoff[i], 0, kbase + i * 1024);
+      dma16(rv, dvoff[i], 0, vbase + i * 1024);
     }
     if (tid < BK) ereg = bloadi(re, uint32_t(tid) * 4, uint32_t(kb) * BK * 4);
   };
@@ -251,25 +256,22 @@ int launch_fwd_g(const void* q, const void* k, const void* v, void* o, float* ls
   const int qb_end = (g.q_off + g.n_q + BQ - 1) / BQ;
   const int n_qb = qb_end - qb_first;
   if (n_qb <= 0) return 0;
-  const dim3 grid(unsigned(n_qb) * unsigned(g.h_kv)), block(FwdCfg<G>::THREADS);
+  const int nsub = (g.h_q / g.h_kv) / G;
+  const dim3 grid(unsigned(n_qb) * unsigned(g.h_kv) * unsigned(nsub)), block(FwdCfg<G>::THREADS);
   fwd_mfma_kernel<G><<<grid, block, 0, st>>>((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
-                                             (uint16_t*)o, lse, P, g, full_range ? 1 : 0, qb_first, n_qb);
+                                             (uint16_t*)o, lse, P, g, full_range ? 1 : 0, qb_first, n_qb, nsub);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 }  // namespace
 
 bool mfma_attn_supported(const AttnGeom& g, const PlanPtrs& P) {
-  const int G = g.h_q / g.h_kv;
-  // buffer loads address Q/dO and K/V with 32-bit byte offsets
-  const bool small = int64_t(g.n_q) * g.h_q * D * 2 < (int64_t(1) << 31) &&
-                     int64_t(g.n_k) * g.h_kv * D * 2 < (int64_t(1) << 31);
-  return g.d == D && P.bq == BQ && P.bk == BK && (G == 1 || G == 2 || G == 4) && small;
+  return g.d == D && P.bq == BQ && P.bk == BK && g.h_kv > 0 && g.h_q % g.h_kv == 0;
 }
 
 int launch_fwd_mfma(const void* q, const void* k, const void* v, void* o, float* lse, const PlanPtrs& P,
                     const AttnGeom& g, bool full_range, hipStream_t st) {
-  switch (g.h_q / g.h_kv) {
+  switch (group_split(g.h_q / g.h_kv)) {
     case 1: return launch_fwd_g<1>(q, k, v, o, lse, P, g, full_range, st);
     case 2: return launch_fwd_g<2>(q, k, v, o, lse, P, g, full_range, st);
     case 4: return launch_fwd_g<4>(q, k, v, o, lse, P, g, full_range, st);

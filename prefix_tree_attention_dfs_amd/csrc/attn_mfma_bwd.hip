@@ -53,15 +53,16 @@ __global__ __launch_bounds__(DqCfg<G>::THREADS) void dq_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ d_o, const float* __restrict__ lse, const float* __restrict__ Dv,
     float* __restrict__ dq_acc, uint16_t* __restrict__ dq_out, const float2* __restrict__ cs_tab, PlanPtrs P,
-    AttnGeom g, int full_range, int qb_first, int n_qb) {
+    AttnGeom g, int full_range, int qb_first, int n_qb, int nsub) {
   using C = DqCfg<G>;
   __shared__ DqStage st[2];
   if (!plan_matches(P)) return;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r = lane & 31, hh = lane >> 5;
   const int kvh = blockIdx.x % g.h_kv;
-  const int idx = blockIdx.x / g.h_kv;
+  const int rest = blockIdx.x / g.h_kv;
+  const int sub = rest % nsub, idx = rest / nsub;
   const int qb = full_range ? ld_uniform(P.qb_order, idx) : (qb_first + n_qb - 1 - idx);
-  const int head = kvh * G + (wave >> 1);
+  const int head = (kvh * nsub + sub) * G + (wave >> 1);
   const int pos0 = (wave & 1) * 32;
   const int row = qb * BQ - g.q_off + pos0 + r;  // q-buffer row of this lane's query
   const bool rok = row < g.n_q;
@@ -82,11 +83,11 @@ __global__ __launch_bounds__(DqCfg<G>::THREADS) void dq_mfma_kernel(
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) acc[dt] = zero16();
 
-  // tile staging: buffer loads, zero past n_k keys (end = 0 there: invisible)
-  const uint32_t kv_bytes = uint32_t(g.n_k) * uint32_t(g.h_kv) * D * 2;
-  const rsrc_t rk = make_rsrc(k, kv_bytes), rv = make_rsrc(v, kv_bytes);
+  // tile staging: buffer loads, zero past n_k keys (end = 0 there: invisible);
+  // descriptors start at each tile (64-bit base), as in the forward
+  const int64_t kv_elems = int64_t(g.n_k) * g.h_kv * D;
+  const int64_t tile_elems = int64_t(BK) * g.h_kv * D;
   const rsrc_t re = make_rsrc(P.end, uint32_t(g.n_k) * 4);
-  const uint32_t tile_bytes = uint32_t(BK) * g.h_kv * D * 2;
   // K and V tiles go from global memory straight into LDS in the swizzled
   // layout, NL loads of 1 KB per wave each, as in the forward
   constexpr int NL = (BK * D * 2 / 1024) / C::WAVES;
@@ -100,12 +101,14 @@ __global__ __launch_bounds__(DqCfg<G>::THREADS) void dq_mfma_kernel(
   }
   int32_t ereg = 0;
   auto load_tile = [&](int kb, DqStage& s) {
-    const uint32_t so = uint32_t(kb) * tile_bytes;
+    const int64_t t0 = int64_t(kb) * tile_elems;
+    const uint32_t bytes = tile_rec_bytes(kv_elems - t0);
+    const rsrc_t rk = make_rsrc(k + t0, bytes), rv = make_rsrc(v + t0, bytes);
     const uint32_t kbase = lds_u32(s.K) + wave * NL * 1024, vbase = lds_u32(s.V) + wave * NL * 1024;
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
-      dma16(rk, dvoff[i], so, kbase + i * 1024);
-      dma16(rv, dvoff[i], so, vbase + i * 1024);
+      dma16(rk, dvoff[i], 0, kbase + i * 1024);
+      dma16(rv, dvoff[i], 0, vbase + i * 1024);
     }
     if (tid < BK) ereg = bloadi(re, uint32_t(tid) * 4, uint32_t(kb) * BK * 4);
   };
@@ -237,6 +240,7 @@ struct __align__(16) KvLds {
   int32_t red[KV_WAVES];
 };
 
+// G: query heads per kv head (0: any group size, read from g at run time)
 template <int G, bool ACC, typename TG>
 __global__ __launch_bounds__(KV_THREADS, 2) void dkdv_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
@@ -299,14 +303,15 @@ __global__ __launch_bounds__(KV_THREADS, 2) void dkdv_mfma_kernel(
 
   const int qt_first = lo / QT;  // query tiles are aligned to 64 tree rows
   const int n_qt = hi > lo ? (hi - 1) / QT - qt_first + 1 : 0;
-  const int n_steps = n_qt * G;
+  const int GG = G > 0 ? G : g.h_q / g.h_kv;
+  const int n_steps = n_qt * GG;
 
   float lreg = 0.f, dreg = 0.f;
   // query rows past n_q read zeros (tiles start at or after q_off, which is
-  // a multiple of 64, so rows are never below the buffer)
-  const uint32_t q_bytes = uint32_t(g.n_q) * uint32_t(g.h_q) * D * 2;
-  const rsrc_t rq = make_rsrc(q, q_bytes), ro = make_rsrc(d_o, q_bytes);
-  const rsrc_t rl = make_rsrc(lse, uint32_t(g.n_q) * g.h_q * 4), rd = make_rsrc(Dv, uint32_t(g.n_q) * g.h_q * 4);
+  // a multiple of 64, so rows are never below the buffer); each tile's
+  // descriptors start at the tile (64-bit base), so Q and dO may exceed the
+  // 4 GiB a 32-bit buffer offset reaches
+  const int64_t q_elems = int64_t(g.n_q) * g.h_q * D, r_elems = int64_t(g.n_q) * g.h_q;
   // Q and dO tiles (64 rows x 128 bf16 = 16 KB each) go from global memory
   // straight into LDS: 16 loads of 1 KB per tile, two per wave.  Lane l of
   // load j fills LDS slot 64 j + l = (row, stored chunk) = ((64 j + l) / 16,
@@ -323,17 +328,21 @@ __global__ __launch_bounds__(KV_THREADS, 2) void dkdv_mfma_kernel(
     // query tiles from the top down: workgroups over a shared prefix have the
     // same upper end, so they walk the same tiles together and share them in L2
     const int rev = n_steps - 1 - step;
-    const int qt = qt_first + rev / G, head = kvh * G + rev % G;
-    const uint32_t rowh = uint32_t(qt * QT - g.q_off) * g.h_q + head;  // (row, head) of the tile's first row
+    const int qt = qt_first + rev / GG, head = kvh * GG + rev % GG;
+    const int64_t rowh = int64_t(qt * QT - g.q_off) * g.h_q + head;  // (row, head) of the tile's first row
+    const uint32_t qbytes = tile_rec_bytes(q_elems - rowh * D);
+    const uint32_t rbytes = tile_rec_bytes(2 * (r_elems - rowh));  // float32 entries
+    const rsrc_t rq = make_rsrc(q + rowh * D, qbytes), ro = make_rsrc(d_o + rowh * D, qbytes);
+    const rsrc_t rl = make_rsrc(lse + rowh, rbytes), rd = make_rsrc(Dv + rowh, rbytes);
     const uint32_t qb = lds_u32(s.Q) + wave * 2048, ob = lds_u32(s.O) + wave * 2048;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      dma16(rq, dvoff[i], rowh * D * 2, qb + i * 1024);
-      dma16(ro, dvoff[i], rowh * D * 2, ob + i * 1024);
+      dma16(rq, dvoff[i], 0, qb + i * 1024);
+      dma16(ro, dvoff[i], 0, ob + i * 1024);
     }
     if (tid < QT) {
-      lreg = bloadf(rl, uint32_t(tid) * g.h_q * 4, rowh * 4);
-      dreg = bloadf(rd, uint32_t(tid) * g.h_q * 4, rowh * 4);
+      lreg = bloadf(rl, uint32_t(tid) * g.h_q * 4, 0);
+      dreg = bloadf(rd, uint32_t(tid) * g.h_q * 4, 0);
     }
   };
   auto store_rows = [&](KvStage& s) {
@@ -352,7 +361,7 @@ __global__ __launch_bounds__(KV_THREADS, 2) void dkdv_mfma_kernel(
   const uint16_t* Vt = L.V + (wave * 32 + r) * KSTR + 8 * hh;
   for (int step = 0; step < n_steps; ++step) {
     const int sidx = step & 1;
-    const int qt = qt_first + (n_steps - 1 - step) / G;
+    const int qt = qt_first + (n_steps - 1 - step) / GG;
     if (step + 1 < n_steps) load_tile(step + 1, L.st[sidx ^ 1]);  // that stage was last read in the previous step
     const KvStage& S = L.st[sidx];
 #pragma unroll
@@ -480,15 +489,16 @@ int launch_dq_g(const void* q, const void* k, const void* v, const void* d_o, co
   const int qb_end = (g.q_off + g.n_q + BQ - 1) / BQ;
   const int n_qb = qb_end - qb_first;
   if (n_qb <= 0) return 0;
-  const dim3 grid(unsigned(n_qb) * unsigned(g.h_kv)), block(DqCfg<G>::THREADS);
+  const int nsub = (g.h_q / g.h_kv) / G;
+  const dim3 grid(unsigned(n_qb) * unsigned(g.h_kv) * unsigned(nsub)), block(DqCfg<G>::THREADS);
   if (dq_out)
     dq_mfma_kernel<G, true><<<grid, block, 0, st>>>((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
                                                     (const uint16_t*)d_o, lse, D_, nullptr, (uint16_t*)dq_out,
-                                                    cs_tab, P, g, full_range ? 1 : 0, qb_first, n_qb);
+                                                    cs_tab, P, g, full_range ? 1 : 0, qb_first, n_qb, nsub);
   else
     dq_mfma_kernel<G, false><<<grid, block, 0, st>>>((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
                                                      (const uint16_t*)d_o, lse, D_, dq_acc, nullptr, nullptr, P,
-                                                     g, full_range ? 1 : 0, qb_first, n_qb);
+                                                     g, full_range ? 1 : 0, qb_first, n_qb, nsub);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
@@ -513,17 +523,13 @@ int launch_dkdv_g(const void* q, const void* k, const void* v, const void* d_o, 
 }  // namespace
 
 bool mfma_bwd_supported(const AttnGeom& g, const PlanPtrs& P) {
-  const int G = g.h_q / g.h_kv;
-  // buffer loads address Q/dO and K/V with 32-bit byte offsets
-  const bool small = int64_t(g.n_q) * g.h_q * D * 2 < (int64_t(1) << 31) &&
-                     int64_t(g.n_k) * g.h_kv * D * 2 < (int64_t(1) << 31);
-  return g.d == D && P.bq == BQ && P.bk == BK && (G == 1 || G == 2 || G == 4) && small;
+  return g.d == D && P.bq == BQ && P.bk == BK && g.h_kv > 0 && g.h_q % g.h_kv == 0;
 }
 
 int launch_dq_mfma(const void* q, const void* k, const void* v, const void* d_o, const float* lse, const float* D_,
                    float* dq_acc, void* dq_out, const float2* cs_tab, const PlanPtrs& P, const AttnGeom& g,
                    bool full_range, hipStream_t st) {
-  switch (g.h_q / g.h_kv) {
+  switch (group_split(g.h_q / g.h_kv)) {
     case 1: return launch_dq_g<1>(q, k, v, d_o, lse, D_, dq_acc, dq_out, cs_tab, P, g, full_range, st);
     case 2: return launch_dq_g<2>(q, k, v, d_o, lse, D_, dq_acc, dq_out, cs_tab, P, g, full_range, st);
     case 4: return launch_dq_g<4>(q, k, v, d_o, lse, D_, dq_acc, dq_out, cs_tab, P, g, full_range, st);
@@ -538,6 +544,7 @@ int launch_dkdv_mfma(const void* q, const void* k, const void* v, const void* d_
     case 1: return launch_dkdv_g<1>(q, k, v, d_o, lse, D_, d_k, d_v, acc, cs_tab, P, g, st);
     case 2: return launch_dkdv_g<2>(q, k, v, d_o, lse, D_, d_k, d_v, acc, cs_tab, P, g, st);
     case 4: return launch_dkdv_g<4>(q, k, v, d_o, lse, D_, d_k, d_v, acc, cs_tab, P, g, st);
-    default: return -1;
+    case 8: return launch_dkdv_g<8>(q, k, v, d_o, lse, D_, d_k, d_v, acc, cs_tab, P, g, st);
+    default: return launch_dkdv_g<0>(q, k, v, d_o, lse, D_, d_k, d_v, acc, cs_tab, P, g, st);
   }
 }

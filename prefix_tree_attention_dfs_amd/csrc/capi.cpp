@@ -5,7 +5,9 @@
 #include <cmath>
 #include <algorithm>
 #include <cstring>
+#include <mutex>
 #include <string>
+#include <unordered_map>
 #include <vector>
 
 #include "attn_core.h"
@@ -67,7 +69,12 @@ int check_attn(const tt_attn_args* a, const char* fn) {
   if (a->d <= 0 || a->d % 2 != 0) return tt::fail(TT_EINVAL, string(fn) + ": d must be positive and even");
   if (a->d % 16 != 0 || a->d > 256)
     return tt::fail(TT_EUNSUPPORTED, string(fn) + ": head dim must be a multiple of 16 and <= 256");
+  if (a->flags & ~uint32_t(TT_ALLOW_GENERIC)) return tt::fail(TT_EINVAL, string(fn) + ": unknown flags");
   const tt_tree* t = a->tree;
+  if (a->dtype == TT_BF16 && !(a->flags & TT_ALLOW_GENERIC) && !ttc::mfma_shape(a->d, t->bq, t->bk))
+    return tt::fail(TT_EUNSUPPORTED, string(fn) +
+                                         ": bf16 attention runs on the matrix cores for head dim 128 and 64-row "
+                                         "schedule blocks only; TT_ALLOW_GENERIC selects the vector kernels");
   if (a->q_off < 0 || a->n_q < 0 || a->n_k < 0) return tt::fail(TT_EINVAL, string(fn) + ": negative q_off/n_q/n_k");
   if (int64_t(a->q_off) + a->n_q > a->n_k || a->n_k > t->N)
     return tt::fail(TT_EINVAL, string(fn) + ": need q_off + n_q <= n_k <= N");
@@ -112,6 +119,36 @@ AttnGeom geom(const tt_attn_args* a) {
 }  // namespace
 
 namespace ttc {
+
+namespace {
+std::mutex g_plan_mu;
+std::unordered_map<uintptr_t, int32_t> g_plan_owner;  // device plan address -> identity word of its image
+}  // namespace
+
+void plan_register(const void* dev_plan, int32_t id) {
+  std::lock_guard<std::mutex> lk(g_plan_mu);
+  g_plan_owner[reinterpret_cast<uintptr_t>(dev_plan)] = id;
+}
+
+int plan_check(const tt_tree* t, const void* dev_plan, const char* fn) {
+  int32_t id = 0;
+  bool known = false;
+  {
+    std::lock_guard<std::mutex> lk(g_plan_mu);
+    const auto it = g_plan_owner.find(reinterpret_cast<uintptr_t>(dev_plan));
+    if (it != g_plan_owner.end()) {
+      known = true;
+      id = it->second;
+    }
+  }
+  if (!known)
+    return tt::fail(TT_EINVAL, std::string(fn) + ": plan was not filled by tree_plan_upload (or tree_path_plan_upload)");
+  if (id != t->plan[ttp::H_ID])
+    return tt::fail(TT_EINVAL, std::string(fn) + ": plan was last uploaded from a tree of another shape");
+  return TT_OK;
+}
+
+bool mfma_shape(int32_t d, int32_t bq, int32_t bk) { return d == 128 && bq == 64 && bk == 64; }
 
 int attn_fwd_core(tt_dtype dt, const PlanPtrs& P, const AttnGeom& g, const void* q, const void* k, const void* v,
                   void* o, float* lse, bool full_range, hipStream_t st) {
@@ -206,6 +243,7 @@ extern "C" int tree_plan_upload(const tt_tree* t, void* dev_plan, size_t bytes, 
   if (bytes < need) return tt::fail(TT_EWORKSPACE, "tree_plan_upload: buffer smaller than tree_plan_bytes");
   if (hipMemcpyAsync(dev_plan, t->plan.data(), need, hipMemcpyHostToDevice, (hipStream_t)stream) != hipSuccess)
     return dev_fail("tree_plan_upload", "hipMemcpyAsync");
+  ttc::plan_register(dev_plan, t->plan[ttp::H_ID]);
   return TT_OK;
 }
 
@@ -225,6 +263,7 @@ extern "C" int tree_attn_fwd(const tt_attn_args* a, tt_stream stream) {
   int rc = check_attn(a, fn);
   if (rc) return rc;
   if ((rc = check_ws(a, false, fn))) return rc;
+  if ((rc = ttc::plan_check(a->tree, a->plan, fn))) return rc;
   if (a->n_q == 0) return TT_OK;
   hipStream_t st = (hipStream_t)stream;
   const PlanPtrs P = plan_ptrs(a->tree, a->plan);
@@ -270,6 +309,7 @@ extern "C" int tree_attn_bwd(const tt_attn_bwd_args* b, tt_stream stream) {
                         static_cast<const void*>(b->d_v)})
     if (p && !aligned16(p)) return tt::fail(TT_EINVAL, "tree_attn_bwd: device pointers must be 16-byte aligned");
   if ((rc = check_ws(a, true, fn))) return rc;
+  if ((rc = ttc::plan_check(a->tree, a->plan, fn))) return rc;
   if (a->n_k == 0) return TT_OK;
   hipStream_t st = (hipStream_t)stream;
   const PlanPtrs P = plan_ptrs(a->tree, a->plan);

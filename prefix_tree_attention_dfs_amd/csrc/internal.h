@@ -44,17 +44,26 @@ inline const int32_t* plan_section(const tt_tree* t, int hdr) { return t->plan.d
 
 // Path-mode traversal plan (tree_path_build).  Segments are maximal chains of
 // DFS rows; events list the walk: e >= 0 enters segment e, e < 0 leaves
-// segment -1 - e.  `chain` is a one-sequence tree of max_path rows whose plan
+// segment -1 - e.  A round is a maximal run of consecutive enters (a forward
+// round) or of consecutive leaves (a backward round): its segments lie
+// contiguously on the stack, positions [p0, p1), so one chunked pass serves
+// them all.  `chain` is a one-sequence tree of max_path rows whose plan
 // serves every attention call of the walk (stack position = depth).
 struct tt_path {
   struct Seg {
     int32_t row0, len, depth0, parent;
+  };
+  struct Round {
+    bool bwd;
+    int32_t p0, p1;    // stack positions covered
+    int32_t ev0, ev1;  // its events: events[ev0 .. ev1)
   };
   const tt_tree* tree = nullptr;
   tt_tree* chain = nullptr;
   int32_t chunk = 2048, order = 0, max_path = 0;
   std::vector<Seg> segs;
   std::vector<int32_t> events;
+  std::vector<Round> rounds;
   int64_t fwd_calls = 0, bwd_calls = 0, pad_rows = 0, pad_pairs = 0;
   ~tt_path();
 };

@@ -71,6 +71,20 @@ __device__ __forceinline__ int32_t bloadi(rsrc_t r, uint32_t voff, uint32_t soff
   return int32_t(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
 }
 
+// Byte size for the descriptor of a tile that starts `elems_left` bf16
+// elements before the end of its tensor: reads past the tensor return zeros,
+// and a tensor of 4 GiB or more is clamped to what a 32-bit offset reaches
+// (a tile never spans more than a few MB).
+__device__ __forceinline__ uint32_t tile_rec_bytes(int64_t elems_left) {
+  const int64_t b = elems_left > 0 ? elems_left * 2 : 0;
+  return b > int64_t(0xFFFFFFF0) ? 0xFFFFFFF0u : uint32_t(b);
+}
+
+// Query heads per workgroup of the forward and dQ kernels for a GQA group of
+// G heads: 4, 2 or 1, the largest that divides G (a larger group runs as
+// G / that many workgroups per block).
+__host__ __device__ inline int group_split(int G) { return G % 4 == 0 ? 4 : (G % 2 == 0 ? 2 : 1); }
+
 // One int32 of the plan (read-only for the kernel's whole life) at a
 // workgroup-uniform index, loaded through the scalar unit: the value lands in
 // an SGPR, so the loop head needs no vector-memory wait, and buffer loads

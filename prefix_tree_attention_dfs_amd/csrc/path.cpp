@@ -6,6 +6,7 @@
 // RoPE; gradients are rotated back as they leave the stack.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <string>
 #include <utility>
@@ -27,7 +28,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 // Workspace carve-up, identical for the size query and the call.
 struct PathWs {
-  size_t plan = 0, qp = 0, kp = 0, vp = 0, op = 0, lsep = 0;  // stack of max_path positions
+  size_t qp = 0, kp = 0, vp = 0, op = 0, lsep = 0;  // stack of max_path positions
   size_t dka = 0, dva = 0;                                   // float32 dK, dV accumulators (backward)
   size_t doc = 0, D = 0, dq = 0;                             // per-call buffers, chunk + 64 rows
   size_t total = 0;
@@ -44,7 +45,6 @@ PathWs path_ws(const tt_path_args* a, bool bwd) {
     off = align_up(off + bytes);
     return o;
   };
-  w.plan = take(p->chain ? p->chain->plan.size() * sizeof(int32_t) : 0);
   w.qp = take(L * hq * d * es);
   w.kp = take(L * hk * d * es);
   w.vp = take(L * hk * d * es);
@@ -71,6 +71,11 @@ int check_path(const tt_path_args* a, const char* fn) {
   if (a->d <= 0 || a->d % 2 != 0) return tt::fail(TT_EINVAL, string(fn) + ": d must be positive and even");
   if (a->d % 16 != 0 || a->d > 256)
     return tt::fail(TT_EUNSUPPORTED, string(fn) + ": head dim must be a multiple of 16 and <= 256");
+  if (a->flags & ~uint32_t(TT_ALLOW_GENERIC)) return tt::fail(TT_EINVAL, string(fn) + ": unknown flags");
+  if (a->dtype == TT_BF16 && !(a->flags & TT_ALLOW_GENERIC) && !ttc::mfma_shape(a->d, 64, 64))
+    return tt::fail(TT_EUNSUPPORTED, string(fn) +
+                                         ": bf16 attention runs on the matrix cores for head dim 128 only; "
+                                         "TT_ALLOW_GENERIC selects the vector kernels");
   if (!(a->scale >= 0.f) || !std::isfinite(a->scale)) return tt::fail(TT_EINVAL, string(fn) + ": bad scale");
   if (!(a->rope_base >= 0.f) || !std::isfinite(a->rope_base))
     return tt::fail(TT_EINVAL, string(fn) + ": bad rope_base");
@@ -80,9 +85,10 @@ int check_path(const tt_path_args* a, const char* fn) {
     return tt::fail(TT_EINVAL, string(fn) + ": q, k, v, o and lse are required");
   if (N > 0 && a->d_o && (!a->d_q || !a->d_k || !a->d_v))
     return tt::fail(TT_EINVAL, string(fn) + ": d_q, d_k and d_v are required with d_o");
+  if (a->path->max_path > 0 && !a->plan) return tt::fail(TT_EINVAL, string(fn) + ": plan is NULL");
   for (const void* p : {a->q, a->k, a->v, static_cast<const void*>(a->o), static_cast<const void*>(a->lse), a->d_o,
                         static_cast<const void*>(a->d_q), static_cast<const void*>(a->d_k),
-                        static_cast<const void*>(a->d_v)})
+                        static_cast<const void*>(a->d_v), a->plan})
     if (p && !aligned16(p)) return tt::fail(TT_EINVAL, string(fn) + ": device pointers must be 16-byte aligned");
   if (a->workspace && (reinterpret_cast<uintptr_t>(a->workspace) & (kAlign - 1)) != 0)
     return tt::fail(TT_EINVAL, string(fn) + ": workspace must be 256-byte aligned");
@@ -101,6 +107,20 @@ std::vector<std::pair<int32_t, int32_t>> chunks(int32_t p0, int32_t p1, int32_t 
 }
 
 }  // namespace
+
+extern "C" int tree_path_plan_bytes(const tt_path* p, size_t* bytes) {
+  tt::clear_error();
+  if (!p || !bytes) return tt::fail(TT_EINVAL, "tree_path_plan_bytes: NULL argument");
+  *bytes = p->chain ? p->chain->plan.size() * sizeof(int32_t) : 0;
+  return TT_OK;
+}
+
+extern "C" int tree_path_plan_upload(const tt_path* p, void* dev_plan, size_t bytes, tt_stream stream) {
+  tt::clear_error();
+  if (!p) return tt::fail(TT_EINVAL, "tree_path_plan_upload: path is NULL");
+  if (!p->chain) return TT_OK;  // an empty tree has no calls
+  return tree_plan_upload(p->chain, dev_plan, bytes, stream);
+}
 
 extern "C" int tree_path_workspace_bytes(const tt_path_args* a, size_t* bytes) {
   tt::clear_error();
@@ -124,6 +144,7 @@ extern "C" int tree_attn_path(const tt_path_args* a, tt_stream stream) {
     return tt::fail(TT_EWORKSPACE, std::string(fn) + ": workspace too small (need " + std::to_string(w.total) +
                                        " bytes)");
   if (p->tree->N == 0) return TT_OK;
+  if ((rc = ttc::plan_check(p->chain, a->plan, fn))) return rc;
   hipStream_t st = (hipStream_t)stream;
   char* ws = static_cast<char*>(a->workspace);
   const tt_dtype dt = a->dtype;
@@ -131,10 +152,7 @@ extern "C" int tree_attn_path(const tt_path_args* a, tt_stream stream) {
   const size_t qrow = hq * d * es, krow = hk * d * es;  // bytes per row
   const float rb = a->rope_base;
 
-  if (hipMemcpyAsync(ws + w.plan, p->chain->plan.data(), p->chain->plan.size() * sizeof(int32_t),
-                     hipMemcpyHostToDevice, st) != hipSuccess)
-    return dev_fail(fn, "plan upload");
-  const PlanPtrs P = ttc::plan_ptrs(p->chain, ws + w.plan);
+  const PlanPtrs P = ttc::plan_ptrs(p->chain, a->plan);
   AttnGeom g;
   g.h_q = a->h_q;
   g.h_kv = a->h_kv;
@@ -164,12 +182,17 @@ extern "C" int tree_attn_path(const tt_path_args* a, tt_stream stream) {
         launch_fill_zero(dVa, size_t(p->max_path) * hk * d * 4, st))
       return dev_fail(fn, "clear");
   }
-  for (const int32_t e : p->events) {
-    if (e >= 0) {
-      // enter: push the segment's rows, then its forward against the stack
-      const tt_path::Seg& s = p->segs[size_t(e)];
-      const size_t r0 = size_t(s.row0), n = size_t(s.len), d0 = size_t(s.depth0);
-      {
+  // the segments of a round and the part of [c0, c1) each one holds
+  const auto seg_of = [&](const tt_path::Round& rd, int32_t i) -> const tt_path::Seg& {
+    return p->segs[size_t(rd.bwd ? -1 - p->events[size_t(i)] : p->events[size_t(i)])];
+  };
+  for (const tt_path::Round& rd : p->rounds) {
+    if (!rd.bwd) {
+      // enter: push each segment's rows, then one chunked forward over the
+      // round's positions against the stack
+      for (int32_t i = rd.ev0; i < rd.ev1; ++i) {
+        const tt_path::Seg& s = seg_of(rd, i);
+        const size_t r0 = size_t(s.row0), n = size_t(s.len), d0 = size_t(s.depth0);
         KTimer t("path_push", st);
         if (launch_rope(q + r0 * qrow, Qp + d0 * qrow, dt, dt, false, P, s.depth0, s.len, a->h_q, a->d, rb, false,
                         st) ||
@@ -178,7 +201,7 @@ extern "C" int tree_attn_path(const tt_path_args* a, tt_stream stream) {
             hipMemcpyAsync(Vp + d0 * krow, v + r0 * krow, n * krow, hipMemcpyDeviceToDevice, st) != hipSuccess)
           return dev_fail(fn, "push");
       }
-      for (const auto& c : chunks(s.depth0, s.depth0 + s.len, p->chunk)) {
+      for (const auto& c : chunks(rd.p0, rd.p1, p->chunk)) {
         const int32_t qo = c.first & ~63;
         g.q_off = qo;
         g.n_q = c.second - qo;
@@ -187,24 +210,33 @@ extern "C" int tree_attn_path(const tt_path_args* a, tt_stream stream) {
                                      LSEp + size_t(qo) * hq, false, st)))
           return rc;
       }
-      KTimer t("path_out", st);
-      if (hipMemcpyAsync(o + r0 * qrow, Op + d0 * qrow, n * qrow, hipMemcpyDeviceToDevice, st) != hipSuccess ||
-          hipMemcpyAsync(a->lse + r0 * hq, LSEp + d0 * hq, n * hq * 4, hipMemcpyDeviceToDevice, st) != hipSuccess)
-        return dev_fail(fn, "forward outputs");
+      for (int32_t i = rd.ev0; i < rd.ev1; ++i) {
+        const tt_path::Seg& s = seg_of(rd, i);
+        const size_t r0 = size_t(s.row0), n = size_t(s.len), d0 = size_t(s.depth0);
+        KTimer t("path_out", st);
+        if (hipMemcpyAsync(o + r0 * qrow, Op + d0 * qrow, n * qrow, hipMemcpyDeviceToDevice, st) != hipSuccess ||
+            hipMemcpyAsync(a->lse + r0 * hq, LSEp + d0 * hq, n * hq * 4, hipMemcpyDeviceToDevice, st) != hipSuccess)
+          return dev_fail(fn, "forward outputs");
+      }
     } else if (bwd) {
-      // leave: the segment's backward, chunks right to left, then pop its dK, dV
-      const tt_path::Seg& s = p->segs[size_t(-1 - e)];
-      const size_t r0 = size_t(s.row0), n = size_t(s.len), d0 = size_t(s.depth0);
-      const auto cs = chunks(s.depth0, s.depth0 + s.len, p->chunk);
+      // leave: one backward over the round's positions, chunks right to left
+      // (every descendant's gradient has arrived), then pop each segment
+      const auto cs = chunks(rd.p0, rd.p1, p->chunk);
       for (auto it = cs.rbegin(); it != cs.rend(); ++it) {
         const int32_t c0 = it->first, c1 = it->second, qo = c0 & ~63;
-        const size_t pad = size_t(c0 - qo), nc = size_t(c1 - c0), row = r0 + size_t(c0) - d0;
+        const size_t pad = size_t(c0 - qo);
         {
           KTimer t("path_dout", st);
-          if (launch_fill_zero(dOc, pad * qrow, st) ||
-              hipMemcpyAsync(dOc + pad * qrow, d_o + row * qrow, nc * qrow, hipMemcpyDeviceToDevice, st) !=
-                  hipSuccess)
-            return dev_fail(fn, "upstream gradient");
+          if (launch_fill_zero(dOc, pad * qrow, st)) return dev_fail(fn, "upstream gradient");
+          for (int32_t i = rd.ev0; i < rd.ev1; ++i) {
+            const tt_path::Seg& s = seg_of(rd, i);
+            const int32_t lo = std::max(c0, s.depth0), hi = std::min(c1, s.depth0 + s.len);
+            if (lo >= hi) continue;
+            const size_t row = size_t(s.row0) + size_t(lo - s.depth0);
+            if (hipMemcpyAsync(dOc + size_t(lo - qo) * qrow, d_o + row * qrow, size_t(hi - lo) * qrow,
+                               hipMemcpyDeviceToDevice, st) != hipSuccess)
+              return dev_fail(fn, "upstream gradient");
+          }
         }
         g.q_off = qo;
         g.n_q = c1 - qo;
@@ -213,18 +245,28 @@ extern "C" int tree_attn_path(const tt_path_args* a, tt_stream stream) {
                                      LSEp + size_t(qo) * hq, D, dq, dKa, dVa, true, false, nullptr, st)))
           return rc;
         KTimer t("dq_finalize", st);
-        if (launch_rope(dq + pad * hq * d, d_q + row * qrow, TT_F32, dt, false, P, c0, c1 - c0, a->h_q, a->d, rb,
-                        true, st))
-          return dev_fail(fn, "dq finalize");
+        for (int32_t i = rd.ev0; i < rd.ev1; ++i) {
+          const tt_path::Seg& s = seg_of(rd, i);
+          const int32_t lo = std::max(c0, s.depth0), hi = std::min(c1, s.depth0 + s.len);
+          if (lo >= hi) continue;
+          const size_t row = size_t(s.row0) + size_t(lo - s.depth0);
+          if (launch_rope(dq + size_t(lo - qo) * hq * d, d_q + row * qrow, TT_F32, dt, false, P, lo, hi - lo, a->h_q,
+                          a->d, rb, true, st))
+            return dev_fail(fn, "dq finalize");
+        }
       }
-      KTimer t("path_pop", st);
-      if (launch_rope(dKa + d0 * hk * d, d_k + r0 * krow, TT_F32, dt, false, P, s.depth0, s.len, a->h_kv, a->d, rb,
-                      true, st) ||
-          launch_rope(dVa + d0 * hk * d, d_v + r0 * krow, TT_F32, dt, false, P, s.depth0, s.len, a->h_kv, a->d, 0.f,
-                      false, st) ||
-          launch_fill_zero(dKa + d0 * hk * d, n * hk * d * 4, st) ||
-          launch_fill_zero(dVa + d0 * hk * d, n * hk * d * 4, st))
-        return dev_fail(fn, "pop");
+      for (int32_t i = rd.ev0; i < rd.ev1; ++i) {
+        const tt_path::Seg& s = seg_of(rd, i);
+        const size_t r0 = size_t(s.row0), n = size_t(s.len), d0 = size_t(s.depth0);
+        KTimer t("path_pop", st);
+        if (launch_rope(dKa + d0 * hk * d, d_k + r0 * krow, TT_F32, dt, false, P, s.depth0, s.len, a->h_kv, a->d,
+                        rb, true, st) ||
+            launch_rope(dVa + d0 * hk * d, d_v + r0 * krow, TT_F32, dt, false, P, s.depth0, s.len, a->h_kv, a->d,
+                        0.f, false, st) ||
+            launch_fill_zero(dKa + d0 * hk * d, n * hk * d * 4, st) ||
+            launch_fill_zero(dVa + d0 * hk * d, n * hk * d * 4, st))
+          return dev_fail(fn, "pop");
+      }
     }
   }
   return TT_OK;

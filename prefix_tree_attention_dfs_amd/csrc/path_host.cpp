@@ -64,14 +64,21 @@ extern "C" int tree_path_build(const tt_tree* t, int32_t chunk, int32_t order, t
       const int32_t par = p->segs[size_t(s)].parent;
       (par < 0 ? roots : kids[size_t(par)]).push_back(s);
     }
-    if (order == 1) {  // largest subtree (rows) first; ties keep DFS order
-      auto rows = [&](int32_t s) {
-        const int32_t r = p->segs[size_t(s)].row0;
-        return t->end[size_t(r)] - r;
-      };
-      auto by_size = [&](int32_t a, int32_t b) { return rows(a) > rows(b); };
-      std::stable_sort(roots.begin(), roots.end(), by_size);
-      for (auto& k : kids) std::stable_sort(k.begin(), k.end(), by_size);
+    if (order == 1) {
+      // greedy: a segment's backward round continues into its parent only
+      // from the parent's last child, so the child whose own chain of last
+      // descendants is shortest goes last (it lengthens the parent's round
+      // instead of making a short round of its own); the others keep their
+      // longer rounds.  chain(s) = len(s) + chain(last child of s), bottom up
+      // (children have larger indices than their parent); ties keep DFS order.
+      std::vector<int64_t> chain_len(static_cast<size_t>(S), 0);
+      auto by_chain = [&](int32_t a, int32_t b) { return chain_len[size_t(a)] > chain_len[size_t(b)]; };
+      for (int32_t s = S - 1; s >= 0; --s) {
+        auto& k = kids[size_t(s)];
+        std::stable_sort(k.begin(), k.end(), by_chain);
+        chain_len[size_t(s)] = p->segs[size_t(s)].len + (k.empty() ? 0 : chain_len[size_t(k.back())]);
+      }
+      std::stable_sort(roots.begin(), roots.end(), by_chain);
     }
     p->events.reserve(size_t(2 * S));
     std::vector<std::pair<int32_t, size_t>> stack;  // (segment, next child index)
@@ -91,14 +98,29 @@ extern "C" int tree_path_build(const tt_tree* t, int32_t chunk, int32_t order, t
         }
       }
     }
-    for (const auto& sg : p->segs)
-      for_chunks(sg.depth0, sg.depth0 + sg.len, chunk, [&](int32_t c0, int32_t) {
-        ++p->fwd_calls;
+    // rounds: maximal runs of enters / of leaves; each run's segments are
+    // stacked one on the next (an enter run descends, a leave run ascends)
+    for (size_t e = 0; e < p->events.size();) {
+      const bool bwd = p->events[e] < 0;
+      size_t f = e;
+      while (f < p->events.size() && (p->events[f] < 0) == bwd) ++f;
+      const auto seg_at = [&](size_t i) { return p->segs[size_t(bwd ? -1 - p->events[i] : p->events[i])]; };
+      const tt_path::Seg first = seg_at(e), last = seg_at(f - 1);
+      tt_path::Round rd;
+      rd.bwd = bwd;
+      rd.ev0 = int32_t(e);
+      rd.ev1 = int32_t(f);
+      rd.p0 = bwd ? last.depth0 : first.depth0;
+      rd.p1 = bwd ? first.depth0 + first.len : last.depth0 + last.len;
+      p->rounds.push_back(rd);
+      for_chunks(rd.p0, rd.p1, chunk, [&](int32_t c0, int32_t) {
+        ++(bwd ? p->bwd_calls : p->fwd_calls);
         const int64_t qo = c0 & ~63;
         p->pad_rows += c0 - qo;
         p->pad_pairs += (int64_t(c0) * (c0 + 1) - qo * (qo + 1)) / 2;  // sum over rows r in [qo, c0) of r + 1
       });
-    p->bwd_calls = p->fwd_calls;
+      e = f;
+    }
     // the chain of the longest path: its plan serves every call
     if (p->max_path > 0) {
       std::vector<int32_t> tok(static_cast<size_t>(p->max_path));
@@ -130,7 +152,7 @@ extern "C" int tree_path_info(const tt_path* p, tt_path_info* out) {
   out->fwd_calls = p->fwd_calls;
   out->bwd_calls = p->bwd_calls;
   out->pad_rows = p->pad_rows;
-  out->query_rows = int64_t(p->tree->N) + p->pad_rows;
+  out->query_rows = 2 * int64_t(p->tree->N) + p->pad_rows;
   out->pad_pairs = p->pad_pairs;
   return TT_OK;
 }

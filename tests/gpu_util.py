@@ -15,6 +15,23 @@ def rel_err(gpu, ref):
     return float(np.max(np.abs(g - r)) / (den if den > 0 else 1.0))
 
 
+def row_rel_err(gpu, ref, floor=1e-3):
+    """Per-row error: max over rows (every index but the last) of
+    max |gpu - ref| / max |ref| within that row, so that small rows (the
+    gradient of a leaf key beside a root key) are judged on their own scale.
+    A row whose own maximum is below `floor` times the tensor's maximum is
+    normalised by that floor instead (an all-but-zero row has no scale)."""
+    g = gpu.detach().float().cpu().double().numpy() if isinstance(gpu, torch.Tensor) else np.asarray(gpu, np.float64)
+    r = np.asarray(ref, dtype=np.float64)
+    if r.size == 0:
+        return 0.0
+    g = g.reshape(-1, r.shape[-1])
+    r = r.reshape(-1, r.shape[-1])
+    top = np.max(np.abs(r))
+    den = np.maximum(np.max(np.abs(r), axis=1), floor * (top if top > 0 else 1.0))
+    return float(np.max(np.max(np.abs(g - r), axis=1) / den))
+
+
 def f32_input(rng, shape, std=1.0):
     """(device float32 tensor, exact fp64 numpy copy)."""
     x = ts.normal_f32(rng, shape, std)

@@ -21,13 +21,14 @@ pytestmark = pytest.mark.gpu
 TOL = {torch.float32: 1e-5, torch.bfloat16: 2e-2}
 
 
-def _run_tree(seqs, dtype, hq, hkv, d, seed, std=1.0, rope=10000.0, which="leaves", check_bwd=True):
+def _run_tree(seqs, dtype, hq, hkv, d, seed, std=1.0, rope=10000.0, which="leaves", check_bwd=True,
+              allow_generic=False):
     tree = tt.Tree(seqs)
     o = dfs_arrays(seqs)
     N = tree.N
     plan = tree.upload_plan()
     (q, qn), (k, kn), (v, vn), (do, don) = inputs(dtype, seed, N, N, hq, hkv, d, std)
-    O, L = tt.tree_attn_fwd(tree, plan, q, k, v, rope_base=rope)
+    O, L = tt.tree_attn_fwd(tree, plan, q, k, v, rope_base=rope, allow_generic=allow_generic)
     Or, Lr, _ = OA.forward(o, qn, kn, vn, rope_base=rope, which=which)
     tol = TOL[dtype]
     print(f"N={N} hq={hq} hkv={hkv} d={d} {dtype}", flush=True)
@@ -35,7 +36,7 @@ def _run_tree(seqs, dtype, hq, hkv, d, seed, std=1.0, rope=10000.0, which="leave
     assert rel_err(L, Lr) < tol, rel_err(L, Lr)
     if not check_bwd:
         return
-    dq, dk, dv = tt.tree_attn_bwd(tree, plan, q, k, v, O, L, do, rope_base=rope)
+    dq, dk, dv = tt.tree_attn_bwd(tree, plan, q, k, v, O, L, do, rope_base=rope, allow_generic=allow_generic)
     dQr, dKr, dVr = OA.backward(o, qn, kn, vn, don, rope_base=rope, which=which)
     assert rel_err(dq, dQr) < tol, ("dq", rel_err(dq, dQr))
     assert rel_err(dk, dKr) < tol, ("dk", rel_err(dk, dKr))
@@ -60,8 +61,12 @@ def test_random_trees_fp32(case, geom):
 
 @pytest.mark.parametrize("case", RANDOM[:3], ids=lambda c: f"seed{c.seed}")
 def test_random_trees_bf16_generic(case):
-    # head dim 64 in bf16 runs the generic kernels
-    _run_tree(case.seqs, torch.bfloat16, 4, 1, 64, seed=case.seed + 200)
+    # head dim 64 in bf16 runs the vector kernels, when asked for
+    _run_tree(case.seqs, torch.bfloat16, 4, 1, 64, seed=case.seed + 200, allow_generic=True)
+    tree = tt.Tree(case.seqs)
+    (q, _), (k, _), (v, _), _ = inputs(torch.bfloat16, 1, tree.N, tree.N, 4, 1, 64, 1.0)
+    with pytest.raises(tt.TTError, match="TT_ALLOW_GENERIC"):
+        tt.tree_attn_fwd(tree, tree.upload_plan(), q, k, v)
 
 
 def test_no_rope_and_custom_scale_fp32():
@@ -135,20 +140,39 @@ def test_probe_mfma_rate_plausible():
     assert 625.0 < rate < 2520.0, rate
 
 
-def test_plan_of_another_tree_is_ignored():
-    """A plan image uploaded for another tree fails the kernels' header check:
-    every kernel that reads the plan returns at once and the outputs keep
-    their previous contents.  The buffer is sized for the tree of the call, so
-    every address the kernels could form lies inside it."""
+def test_plan_of_another_tree():
+    """A plan address the library filled for a tree of another shape is
+    rejected on the host (TT_EINVAL, nothing launched, outputs untouched).  A
+    buffer whose device contents were overwritten behind the library's back
+    (here by a plain device copy of another tree's image) passes the host
+    check; the kernels' header check then returns without writing, so the
+    outputs keep their previous contents and nothing is read out of bounds
+    (the buffer is sized for the tree of the call)."""
     small = tt.Tree([[1, 2, 3, 4], [1, 2, 5]])
     big_case = ts.random_small_tree(11, n_seqs=8, max_len=300, vocab=3)
     big = tt.Tree(big_case.seqs)
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     buf = torch.zeros(big.plan_bytes(), dtype=torch.uint8, device="cuda")
-    assert tt.lib().tree_plan_upload(small.handle, ctypes.c_void_p(buf.data_ptr()), buf.numel(),
-                                     ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)) == tt.TT_OK
+    assert tt.lib().tree_plan_upload(small.handle, ctypes.c_void_p(buf.data_ptr()), buf.numel(), st) == tt.TT_OK
     torch.cuda.synchronize()
     for dtype, hq, hkv, d in ((torch.float32, 4, 2, 64), (torch.bfloat16, 8, 2, 128)):
-        print(f"wrong plan: N={big.N} dtype={dtype} d={d}", flush=True)
+        (q, _), (k, _), (v, _), (do, _) = inputs(dtype, 5, big.N, big.N, hq, hkv, d, d ** -0.5)
+        o = torch.full_like(q, 7.0)
+        lse = torch.full((big.N, hq), 7.0, dtype=torch.float32, device="cuda")
+        with pytest.raises(tt.TTError, match="another shape"):
+            tt.tree_attn_fwd(big, buf, q, k, v, o=o, lse=lse)
+        with pytest.raises(tt.TTError, match="another shape"):
+            tt.tree_attn_bwd(big, buf, q, k, v, o, lse, do)
+        assert bool((o.float() == 7.0).all()) and bool((lse == 7.0).all())
+    # the host records the big tree's upload; then the bytes are replaced on the device
+    good = big.upload_plan()
+    assert tt.lib().tree_plan_upload(big.handle, ctypes.c_void_p(buf.data_ptr()), buf.numel(), st) == tt.TT_OK
+    other = torch.zeros_like(buf)
+    assert tt.lib().tree_plan_upload(small.handle, ctypes.c_void_p(other.data_ptr()), other.numel(), st) == tt.TT_OK
+    buf.copy_(other)
+    torch.cuda.synchronize()
+    for dtype, hq, hkv, d in ((torch.float32, 4, 2, 64), (torch.bfloat16, 8, 2, 128)):
+        print(f"stale plan bytes: N={big.N} dtype={dtype} d={d}", flush=True)
         (q, _), (k, _), (v, _), (do, _) = inputs(dtype, 5, big.N, big.N, hq, hkv, d, d ** -0.5)
         o = torch.full_like(q, 7.0)
         lse = torch.full((big.N, hq), 7.0, dtype=torch.float32, device="cuda")
@@ -159,8 +183,7 @@ def test_plan_of_another_tree_is_ignored():
         torch.cuda.synchronize()
         for t_ in (o, lse, dq, dk, dv):
             assert bool((t_.float() == 7.0).all())
-    # the right plan in the same kind of buffer works
-    good = big.upload_plan()
+    # the right plan works
     (q, qn), (k, kn), (v, vn), _ = inputs(torch.float32, 5, big.N, big.N, 4, 2, 64, 64 ** -0.5)
     O, L = tt.tree_attn_fwd(big, good, q, k, v)
     Or, Lr, _ = OA.forward(dfs_arrays(big_case.seqs), qn, kn, vn, which="leaves")

@@ -63,6 +63,7 @@ def test_path_f32_vs_oracle(name):
     Or, Lr, _ = OA.forward(o, qn, kn, vn, which="leaves")
     dQr, dKr, dVr = OA.backward(o, qn, kn, vn, don, which="leaves")
     for n, g_, r_ in (("o", O, Or), ("lse", L, Lr), ("dq", dq, dQr), ("dk", dk, dKr), ("dv", dv, dVr)):
+        print(f"  {n}: {rel_err(g_, r_):.2e}", flush=True)
         assert rel_err(g_, r_) < 1e-4, (n, rel_err(g_, r_))
 
 

@@ -9,10 +9,13 @@ from the oracle's DFS arrays:
 * the events are a depth-first walk: each segment entered once, left once,
   children entered while their parent is on the stack, stack depth in rows
   never above max_path = max depth + 1;
-* order 0 visits children by ascending first row, order 1 by descending
-  subtree size (ties by first row);
-* call and pad-row counts follow the chunk rule (boundaries at multiples of
-  the chunk, each call starting at the 64-aligned row at or below its first).
+* order 0 visits children by ascending first row; order 1 by descending
+  length of the chain of last descendants (recomputed here from the walk
+  itself), ties by first row;
+* rounds are the maximal runs of enters and of leaves, each covering the
+  stack positions of its segments; call and pad-row counts follow the chunk
+  rule over the rounds (boundaries at multiples of the chunk, each call
+  starting at the 64-aligned position at or below its first).
 """
 import numpy as np
 import pytest
@@ -76,23 +79,43 @@ def _check(seqs, chunk, order):
             stack.pop()
             rows_on_stack -= s["len"][k]
     assert not stack and len(entered) == len(left) == S
-    size = lambda k: o["end"][s["row0"][k]] - s["row0"][k]  # noqa: E731
+    chain = {}
+
+    def chain_len(k):  # own length plus the chain of its last child in the walk
+        if k not in chain:
+            kids = kids_seen.get(k, [])
+            chain[k] = s["len"][k] + (chain_len(kids[-1]) if kids else 0)
+        return chain[k]
+
     for par, kids in kids_seen.items():
         want = sorted(kids, key=lambda k: s["row0"][k])
         if order == 1:
-            want = sorted(want, key=lambda k: -size(k))  # stable: ties stay in row order
+            want = sorted(want, key=lambda k: -chain_len(k))  # stable: ties stay in row order
         assert kids == want
-    # chunk accounting
-    calls = pad = pad_pairs = 0
-    for k in range(S):
-        c0, c1 = s["depth0"][k], s["depth0"][k] + s["len"][k]
-        while c0 < c1:
-            calls += 1
+    # rounds and chunk accounting
+    calls = {False: 0, True: 0}
+    pad = pad_pairs = 0
+    i = 0
+    while i < len(ev):
+        bwd = ev[i] < 0
+        j = i
+        while j < len(ev) and (ev[j] < 0) == bwd:
+            j += 1
+        segs = [(-1 - e if bwd else e) for e in ev[i:j]]
+        lo = min(s["depth0"][k] for k in segs)
+        hi = max(s["depth0"][k] + s["len"][k] for k in segs)
+        assert hi - lo == sum(s["len"][k] for k in segs)   # stacked one on the next
+        c0 = lo
+        while c0 < hi:
+            calls[bwd] += 1
             pad += c0 % 64
             pad_pairs += sum(r + 1 for r in range(c0 - c0 % 64, c0))  # a pad row at position r sees r + 1 keys
-            c0 = min(c1, (c0 // chunk + 1) * chunk)
-    assert inf["fwd_calls"] == inf["bwd_calls"] == calls
-    assert inf["pad_rows"] == pad and inf["query_rows"] == N + pad
+            c0 = min(hi, (c0 // chunk + 1) * chunk)
+        i = j
+    leaves = sum(1 for k in range(S) if k not in kids_seen)
+    assert inf["fwd_calls"] == calls[False] and inf["bwd_calls"] == calls[True]
+    assert calls[False] >= leaves and calls[True] >= leaves
+    assert inf["pad_rows"] == pad and inf["query_rows"] == 2 * N + pad
     assert inf["pad_pairs"] == pad_pairs
     return p
 
@@ -151,3 +174,17 @@ def test_path_build_errors():
     a = tt.PathArgs(path=p.handle, h_q=2, h_kv=1, d=128, dtype=tt.TT_BF16)  # q, k, v, o, lse missing
     assert lib.tree_attn_path(ctypes.byref(a), None) == tt.TT_EINVAL
     assert lib.tree_attn_path(None, None) == tt.TT_EINVAL
+    # every buffer given, but no plan / a plan the library never filled / bf16 head dim 64
+    F = 0x100000
+    full = dict(path=p.handle, h_q=2, h_kv=1, d=128, dtype=tt.TT_BF16, q=F, k=F, v=F, o=F, lse=F, workspace=F,
+                workspace_bytes=1 << 40)
+    a = tt.PathArgs(**full)
+    assert lib.tree_attn_path(ctypes.byref(a), None) == tt.TT_EINVAL and "plan is NULL" in tt.last_error()
+    a = tt.PathArgs(plan=F, **full)
+    assert lib.tree_attn_path(ctypes.byref(a), None) == tt.TT_EINVAL and "upload" in tt.last_error()
+    a = tt.PathArgs(plan=F, **dict(full, d=64))
+    assert lib.tree_attn_path(ctypes.byref(a), None) == tt.TT_EUNSUPPORTED
+    a = tt.PathArgs(plan=F, flags=tt.TT_ALLOW_GENERIC, **dict(full, d=64))
+    assert lib.tree_attn_path(ctypes.byref(a), None) == tt.TT_EINVAL and "upload" in tt.last_error()
+    # the walk's plan is the chain of the longest path (host copy size)
+    assert p.plan_bytes() > 0 and p.plan_bytes() % 256 == 0

@@ -285,3 +285,90 @@ def test_plan_identity_word():
     assert ids["fork"] == ids["fork_other_tokens"]
     shapes = [ids[n][0] for n in ("tiny", "fork", "chain", "random")]
     assert len(set(shapes)) == 4
+
+
+def test_kernel_envelope_and_plan_registry_on_host():
+    """Which shapes the bf16 matrix-core kernels take, decided on the host
+    before any launch: head dim 128 at 64-row blocks for any GQA group (1, 2,
+    3, 4, 8, 16) goes on to the plan check; another bf16 head dim fails with
+    TT_EUNSUPPORTED unless TT_ALLOW_GENERIC asks for the vector kernels;
+    float32 always runs the vector kernels.  A plan address the library never
+    filled is rejected (TT_EINVAL) after every other check passed."""
+    lib = tt.lib()
+    t = tt.Tree([np.arange(100), np.arange(50)])
+    t32 = tt.Tree([np.arange(100), np.arange(50)], block_q=32, block_k=32)
+
+    def both(a):
+        rf = lib.tree_attn_fwd(ctypes.byref(a), None)
+        b = tt.AttnBwdArgs(a=a, d_o=FAKE, d_q=FAKE, d_k=FAKE, d_v=FAKE, flags=0)
+        rb = lib.tree_attn_bwd(ctypes.byref(b), None)
+        assert rf == rb, (rf, rb)
+        return rf, tt.last_error()
+
+    for hq, hkv in ((4, 4), (4, 2), (6, 2), (8, 2), (32, 4), (32, 2)):
+        rc, msg = both(_attn(t, h_q=hq, h_kv=hkv))
+        assert rc == tt.TT_EINVAL and "tree_plan_upload" in msg, (hq, hkv, msg)
+    for kw in (dict(d=64), dict(d=256), dict(tree=t32.handle)):
+        rc, msg = both(_attn(t, **kw))
+        assert rc == tt.TT_EUNSUPPORTED and "TT_ALLOW_GENERIC" in msg, kw
+        rc, msg = both(_attn(t, flags=tt.TT_ALLOW_GENERIC, **kw))
+        assert rc == tt.TT_EINVAL and "tree_plan_upload" in msg, kw
+    rc, msg = both(_attn(t, d=64, dtype=tt.TT_F32))
+    assert rc == tt.TT_EINVAL and "tree_plan_upload" in msg
+    rc, _ = both(_attn(t, flags=2))
+    assert rc == tt.TT_EINVAL and "flags" in tt.last_error()
+
+
+def test_binding_rejects_bad_tensors_before_the_library():
+    """The Python binding checks dtype, shape, contiguity and device of every
+    tensor and raises ValueError before anything reaches the library (here
+    the tensors live on the CPU, so a check that slipped would fail later on
+    the device check, not pass)."""
+    import torch
+    t = tt.Tree([np.arange(70), np.arange(40)])
+    N = t.N
+    plan = torch.zeros(t.plan_bytes(), dtype=torch.uint8)
+    q = torch.zeros(N, 4, 128, dtype=torch.bfloat16)
+    k = torch.zeros(N, 2, 128, dtype=torch.bfloat16)
+    v = torch.zeros_like(k)
+
+    def raises(fn, text):
+        with pytest.raises(ValueError, match=text):
+            fn()
+
+    raises(lambda: tt.tree_attn_fwd(t, plan, q.float(), k, v), "k has dtype")
+    raises(lambda: tt.tree_attn_fwd(t, plan, q, k, v[:, :1].contiguous()), "v has shape")
+    raises(lambda: tt.tree_attn_fwd(t, plan, q, k[:, :, :64].contiguous(), v), "k must be")
+    raises(lambda: tt.tree_attn_fwd(t, plan, q.transpose(0, 1).contiguous().transpose(0, 1), k, v), "contiguous")
+    raises(lambda: tt.tree_attn_fwd(t, plan, q.half(), k.half(), v.half()), "q has dtype")
+    raises(lambda: tt.tree_attn_fwd(t, plan[:10], q, k, v), "device|plan holds")
+    raises(lambda: tt.tree_attn_fwd(t, plan, q, k, v), "CUDA")
+    lse = torch.zeros(N, 4)
+    o = torch.zeros_like(q)
+    raises(lambda: tt.tree_attn_bwd(t, plan, q, k, v, o, lse.double(), q), "lse has dtype")
+    raises(lambda: tt.tree_attn_bwd(t, plan, q, k, v, o, lse, q, d_k=torch.zeros_like(k), accumulate=True),
+           "d_k has dtype")
+    raises(lambda: tt.tree_attn_bwd(t, plan, q, k, v, o, lse, q, d_k=torch.zeros(N, 2, 128)), "d_k has dtype")
+    raises(lambda: tt.tree_attn_bwd(t, plan, q, k, v, o, lse, q[:-1]), "d_o has shape")
+    # weighted NLL: the target CSR must be int32 / float32, logits 2-D
+    z = torch.zeros(N, 50)
+    rp = torch.zeros(N + 1, dtype=torch.int32)
+    tid = torch.zeros(N - 2, dtype=torch.int32)
+    tw = torch.zeros(N - 2)
+    raises(lambda: tt.tree_weighted_nll(rp.long(), tid, tw, logits=z), "tgt_row_ptr has dtype")
+    raises(lambda: tt.tree_weighted_nll(rp, tid.long(), tw, logits=z), "tgt_id has dtype")
+    raises(lambda: tt.tree_weighted_nll(rp, tid, tw.double(), logits=z), "tgt_w has dtype")
+    raises(lambda: tt.tree_weighted_nll(rp[:-1], tid, tw, logits=z), "tgt_row_ptr has shape")
+    raises(lambda: tt.tree_weighted_nll(rp, tid, tw, logits=z.t()), "contiguous|shape")
+    raises(lambda: tt.tree_weighted_nll(rp, tid, tw, logits=z, hidden=z), "exactly one")
+    h = torch.zeros(N, 16, dtype=torch.bfloat16)
+    raises(lambda: tt.tree_weighted_nll(rp, tid, tw, hidden=h, w_vocab=torch.zeros(8, 64, dtype=torch.bfloat16)),
+           "w_vocab must be")
+    raises(lambda: tt.tree_weighted_nll(rp, tid, tw, hidden=h.float(), w_vocab=torch.zeros(16, 64)),
+           "hidden has dtype")
+    raises(lambda: tt.tree_weighted_nll(rp, tid, tw, logits=z), "CUDA")
+    # path mode: one row per tree row
+    p = tt.Path(t, 64, 0)
+    raises(lambda: tt.tree_attn_path(p, q[:-1], k, v), "one row per tree row")
+    raises(lambda: tt.tree_attn_path(p, q, k.float(), v), "k has dtype")
+    raises(lambda: tt.tree_attn_path(p, q, k, v, d_o=q, d_k=torch.zeros(N, 2, 128)), "d_k has dtype")

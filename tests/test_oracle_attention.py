@@ -189,3 +189,39 @@ def test_rope_closed_forms():
     e[0, 0, 1] = 1.0
     r = rotate(e, [3.0], 100.0)[0, 0]
     np.testing.assert_allclose(r, [0, np.cos(0.3), 0, np.sin(0.3)], atol=1e-15)
+
+
+@pytest.mark.parametrize("q_lo,q_hi", [(0, None), (7, None), (5, 19), (12, 13), (30, 30)])
+def test_dkdv_keys_query_range_is_backward_with_do_zeroed(q_lo, q_hi):
+    """dkdv_keys restricted to the queries [q_lo, q_hi) (the reference of the
+    chunked suffix mode) equals the full per-branch backward whose upstream
+    gradient is zero outside that range: attention is linear in dO, so the
+    queries outside it contribute nothing."""
+    case = ts.random_small_tree(21, n_seqs=6, max_len=24, vocab=3)
+    tree = dfs_arrays(case.seqs)
+    N = tree["N"]
+    q, k, v, do = _inputs(17, N, 4, 2, 8)
+    hi = N if q_hi is None else q_hi
+    masked = do.copy()
+    masked[:q_lo] = 0.0
+    masked[hi:] = 0.0
+    _, dK, dV = A.backward(tree, q, k, v, masked, rope_base=100.0)
+    keys = np.arange(N)
+    dk, dv = A.dkdv_keys(tree, q, k, v, do, keys, rope_base=100.0, q_lo=q_lo, q_hi=q_hi)
+    np.testing.assert_allclose(dk, dK, rtol=0, atol=1e-11)
+    np.testing.assert_allclose(dv, dV, rtol=0, atol=1e-11)
+
+
+def test_dkdv_keys_chain_suffix():
+    """The chunked path configuration in small: one chain, queries restricted
+    to its suffix; equal to the backward with dO = 0 on the prefix."""
+    L, prefix = 40, 26
+    tree = dfs_arrays([np.arange(L)])
+    q, k, v, do = _inputs(23, L, 2, 1, 8)
+    masked = do.copy()
+    masked[:prefix] = 0.0
+    _, dK, dV = A.backward(tree, q, k, v, masked)
+    keys = np.array([0, 5, prefix - 1, prefix, L - 2, L - 1])
+    dk, dv = A.dkdv_keys(tree, q, k, v, do, keys, q_lo=prefix)
+    np.testing.assert_allclose(dk, dK[keys], rtol=0, atol=1e-11)
+    np.testing.assert_allclose(dv, dV[keys], rtol=0, atol=1e-11)

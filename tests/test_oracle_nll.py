@@ -5,14 +5,17 @@
 * closed form with zero logits: loss = (sum_s (|s|-1) / B) ln V;
 * B = 1 is torch's summed cross entropy (fp64, CPU);
 * finite differences for dZ, dH, dW;
-* row-weight invariant: sum of a row's target weights = w_row - (#sequences ending at row)/B.
+* row-weight invariant: sum of a row's target weights = w_row - (#sequences ending at row)/B;
+* the row-blocked full-vocabulary helpers (per-row LSE, target logp, selected dW
+  columns) equal the whole-matrix lm-head on small sizes, with blocks that split the rows.
 """
 import numpy as np
 import pytest
 import torch
 
 import treesynth as ts
-from oracle.nll import tree_loss, branch_loss, lmhead, lmhead_rows
+from oracle.nll import (tree_loss, branch_loss, lmhead, lmhead_rows, lmhead_lse, lmhead_target_logp,
+                        lmhead_dw_columns)
 from oracle.tree import dfs_arrays
 
 CASES = [ts.random_small_tree(s, n_seqs=n, max_len=L, vocab=6)
@@ -110,3 +113,27 @@ def test_lmhead_finite_differences():
     for r, (lse, lps, dzr, dhr) in zip(rows, lmhead_rows(H[rows], W, tg)):
         np.testing.assert_allclose(dzr, dz[r], atol=1e-13)
         np.testing.assert_allclose(dhr, dH[r], atol=1e-12)
+
+
+@pytest.mark.parametrize("row_block", [1, 7, 1000])
+def test_lmhead_row_blocked_helpers(row_block):
+    """lmhead_lse / lmhead_target_logp / lmhead_dw_columns (used at the full
+    vocabulary size, where z cannot be held whole) against lmhead, which forms
+    z = H W at once and whose loss and gradients are pinned above."""
+    case = ts.random_small_tree(31, n_seqs=8, max_len=18, vocab=40)
+    tree = dfs_arrays(case.seqs)
+    N, dm, V = tree["N"], 12, 40
+    rng = np.random.default_rng(5)
+    H = rng.standard_normal((N, dm))
+    W = rng.standard_normal((dm, V)) * 0.3
+    w = _exact_w(tree)
+    loss, logp, dz, dH, dW = lmhead(H, W, tree["parent"], tree["token"], w)
+    lse = lmhead_lse(H, W, row_block=row_block)
+    l2, lp2 = lmhead_target_logp(H, W, lse, tree["parent"], tree["token"], w)
+    assert abs(l2 - loss) <= 1e-12 * abs(loss)
+    t = tree["parent"] >= 0
+    np.testing.assert_allclose(lp2[t], logp[t], rtol=0, atol=1e-12)
+    assert np.all(np.isnan(lp2[~t]))
+    cols = np.array([0, 3, int(tree["token"][1]), V - 1, 17])
+    np.testing.assert_allclose(lmhead_dw_columns(H, W, lse, tree["parent"], tree["token"], w, cols), dW[:, cols],
+                               rtol=0, atol=1e-12)

@@ -18,6 +18,7 @@ from .trees import (  # noqa: F401
     long_chain,
     lmhead_tree,
     random_small_tree,
+    nested_tree,
 )
 from .tensors import (  # noqa: F401
     rng_for,

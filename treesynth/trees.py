@@ -305,3 +305,30 @@ def random_small_tree(seed: int, n_seqs: int = 6, max_len: int = 40, vocab: int 
             seqs.append(s)
     return SynthTree("random_small", seqs, vocab, -1, seed,
                      dict(n_seqs=n_seqs, max_len=max_len, vocab=vocab))
+
+
+# ---------------------------------------------------------------- nested shape
+def nested_tree(seed: int, spec, vocab: int = 151936, name: str = "nested") -> SynthTree:
+    """A tree of segments with given lengths: spec = (length, [child specs]).
+    Every root-to-leaf chain of segments is one input sequence (leaves in the
+    spec's order); sibling segments start with distinct token ids.
+
+    Draw order: depth first through the spec -- a segment's tokens, then the
+    distinct first tokens of its children, then each child in turn."""
+    rng = rng_for(seed)
+    st = _SegTree()
+    ends = []
+
+    def grow(parent, sp, first):
+        length, kids = sp
+        seg = st.add(parent, _tokens(rng, length, vocab, first=first))
+        if not kids:
+            ends.append(seg)
+            return
+        firsts = _distinct_firsts(rng, len(kids), vocab)
+        for c, kid in enumerate(kids):
+            grow(seg, kid, int(firsts[c]))
+
+    grow(-1, spec, None)
+    seqs = [st.seq(e) for e in ends]
+    return SynthTree(name, seqs, vocab, st.used_length(range(len(st.toks))), seed, dict(spec=repr(spec)))
