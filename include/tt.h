@@ -297,6 +297,26 @@ int tree_nll_workspace_bytes(const tt_nll_args* args, size_t* bytes);
 int tree_weighted_nll(const tt_nll_args* args, tt_stream stream);
 
 /*
+ * tree_weighted_nll_noalloc -- for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): tree_weighted_nll in logits mode with its per-row partial
+ * losses in a static device array of TT_NOALLOC_MAX_ROWS float32 (4 MiB) per
+ * GPU, held until the process ends, instead of the workspace (workspace and
+ * workspace_bytes are ignored).  It calls no allocating routine; the first
+ * call on a device looks the array up once (hipGetSymbolAddress).  The
+ * stream's device must be the current device.  Every call on one GPU shares
+ * that GPU's array: calls that overlap on one GPU (other streams, other
+ * threads) race and must be serialised by the caller.  Every row's entry is
+ * written before it is summed, so nothing needs clearing between calls.
+ * Results equal tree_weighted_nll's bit for bit.
+ * Errors: those of tree_weighted_nll; TT_EUNSUPPORTED in fused mode;
+ * TT_EWORKSPACE when n_rows > TT_NOALLOC_MAX_ROWS; TT_EDEVICE if the array
+ * cannot be reached.
+ */
+#define TT_NOALLOC_MAX_ROWS (1 << 20)
+int tree_weighted_nll_noalloc(const tt_nll_args* args, tt_stream stream);
+
+/*
  * Path mode: one attention layer over the tree, walked depth-first with a
  * stack that holds only the current root-to-node path (AReaL-DTA, arXiv
  * 2602.00482, summary page, Methodology in Plain English: forward only the new

@@ -30,7 +30,7 @@ EXPORTED = ("tree_build", "tree_free", "tree_info", "tree_export", "tree_plan_by
             "tree_weighted_nll", "tt_last_error", "tt_timing_enable", "tt_timing_collect",
             "tree_target_weights", "tree_path_build", "tree_path_free", "tree_path_info", "tree_path_segments",
             "tree_path_plan_bytes", "tree_path_plan_upload", "tree_path_workspace_bytes", "tree_attn_path",
-            "tt_probe_mfma")
+            "tt_probe_mfma", "tree_weighted_nll_noalloc")
 
 
 class TTError(RuntimeError):
@@ -124,6 +124,7 @@ def _setup(lib):
     lib.tree_attn_bwd.argtypes = [ctypes.POINTER(AttnBwdArgs), ctypes.c_void_p]
     lib.tree_nll_workspace_bytes.argtypes = [ctypes.POINTER(NllArgs), ctypes.POINTER(ctypes.c_size_t)]
     lib.tree_weighted_nll.argtypes = [ctypes.POINTER(NllArgs), ctypes.c_void_p]
+    lib.tree_weighted_nll_noalloc.argtypes = [ctypes.POINTER(NllArgs), ctypes.c_void_p]
     lib.tree_target_weights.argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_float),
                                         ctypes.POINTER(ctypes.c_uint8), ctypes.POINTER(ctypes.c_float)]
     lib.tree_path_build.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(ctypes.c_void_p)]
@@ -145,7 +146,8 @@ def _setup(lib):
     lib.tt_probe_mfma.restype = ctypes.c_int
     for _n in ("tree_info", "tree_export", "tree_plan_bytes", "tree_plan_upload", "tree_plan_copy", "tree_attn_workspace_bytes",
                "tree_attn_fwd", "tree_attn_bwd", "tree_nll_workspace_bytes", "tree_weighted_nll",
-               "tree_path_plan_bytes", "tree_path_plan_upload", "tree_path_workspace_bytes", "tree_attn_path"):
+               "tree_path_plan_bytes", "tree_path_plan_upload", "tree_path_workspace_bytes", "tree_attn_path",
+               "tree_weighted_nll_noalloc"):
         getattr(lib, _n).restype = ctypes.c_int
 
 

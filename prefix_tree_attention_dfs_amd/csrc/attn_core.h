@@ -92,6 +92,10 @@ class KTimer {
 void plan_register(const void* dev_plan, int32_t id);
 int plan_check(const tt_tree* t, const void* dev_plan, const char* fn);
 
+// Validation of tree_weighted_nll's arguments shared by its entry points
+// (everything but the workspace); messages start with fn.
+int nll_check(const tt_nll_args* a, const char* fn);
+
 // Shapes the bf16 matrix-core kernels take (any GQA group, any size).
 bool mfma_shape(int32_t d, int32_t bq, int32_t bk);
 

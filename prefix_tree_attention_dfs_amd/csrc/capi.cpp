@@ -393,35 +393,47 @@ extern "C" int tree_nll_workspace_bytes(const tt_nll_args* a, size_t* bytes) {
   return TT_OK;
 }
 
-extern "C" int tree_weighted_nll(const tt_nll_args* a, tt_stream stream) {
-  tt::clear_error();
-  const char* fn = "tree_weighted_nll";
-  if (!a) return tt::fail(TT_EINVAL, "tree_weighted_nll: args is NULL");
+namespace ttc {
+
+int nll_check(const tt_nll_args* a, const char* fn) {
+  using std::string;
+  const string f(fn);
+  if (!a) return tt::fail(TT_EINVAL, f + ": args is NULL");
   const bool fused = a->hidden != nullptr || a->w_vocab != nullptr;
   const bool logits = a->logits != nullptr;
-  if (fused == logits) return tt::fail(TT_EINVAL, "tree_weighted_nll: give exactly one of logits or hidden+w_vocab");
-  if (fused && (!a->hidden || !a->w_vocab))
-    return tt::fail(TT_EINVAL, "tree_weighted_nll: fused mode needs hidden and w_vocab");
-  if (a->n_rows < 0 || a->vocab <= 0 || a->n_tgt < 0) return tt::fail(TT_EINVAL, "tree_weighted_nll: bad sizes");
-  if (fused && a->d_model <= 0) return tt::fail(TT_EINVAL, "tree_weighted_nll: bad d_model");
-  if (a->vocab > (1 << 18)) return tt::fail(TT_EUNSUPPORTED, "tree_weighted_nll: vocab > 262144");
+  if (fused == logits) return tt::fail(TT_EINVAL, f + ": give exactly one of logits or hidden+w_vocab");
+  if (fused && (!a->hidden || !a->w_vocab)) return tt::fail(TT_EINVAL, f + ": fused mode needs hidden and w_vocab");
+  if (a->n_rows < 0 || a->vocab <= 0 || a->n_tgt < 0) return tt::fail(TT_EINVAL, f + ": bad sizes");
+  if (fused && a->d_model <= 0) return tt::fail(TT_EINVAL, f + ": bad d_model");
+  if (a->vocab > (1 << 18)) return tt::fail(TT_EUNSUPPORTED, f + ": vocab > 262144");
   if (fused && (a->vocab % 8 != 0 || a->d_model % 8 != 0))
-    return tt::fail(TT_EUNSUPPORTED, "tree_weighted_nll: fused mode needs vocab and d_model multiples of 8");
+    return tt::fail(TT_EUNSUPPORTED, f + ": fused mode needs vocab and d_model multiples of 8");
   if (logits && a->logits_dtype != TT_F32 && a->logits_dtype != TT_BF16)
-    return tt::fail(TT_EINVAL, "tree_weighted_nll: bad logits dtype");
+    return tt::fail(TT_EINVAL, f + ": bad logits dtype");
   if (fused && a->d_w_vocab && a->dw_dtype != TT_F32 && a->dw_dtype != TT_BF16)
-    return tt::fail(TT_EINVAL, "tree_weighted_nll: bad dw dtype");
+    return tt::fail(TT_EINVAL, f + ": bad dw dtype");
   if (!a->loss || !a->tgt_row_ptr || (a->n_tgt > 0 && (!a->tgt_id || !a->tgt_w)))
-    return tt::fail(TT_EINVAL, "tree_weighted_nll: loss and the target CSR are required");
-  if (logits && a->d_hidden) return tt::fail(TT_EINVAL, "tree_weighted_nll: d_hidden needs fused mode");
-  if (logits && a->d_w_vocab) return tt::fail(TT_EINVAL, "tree_weighted_nll: d_w_vocab needs fused mode");
-  if (fused && a->d_logits) return tt::fail(TT_EINVAL, "tree_weighted_nll: d_logits needs logits mode");
+    return tt::fail(TT_EINVAL, f + ": loss and the target CSR are required");
+  if (logits && a->d_hidden) return tt::fail(TT_EINVAL, f + ": d_hidden needs fused mode");
+  if (logits && a->d_w_vocab) return tt::fail(TT_EINVAL, f + ": d_w_vocab needs fused mode");
+  if (fused && a->d_logits) return tt::fail(TT_EINVAL, f + ": d_logits needs logits mode");
   for (const void* p : {a->hidden, a->w_vocab, a->logits, static_cast<const void*>(a->tgt_row_ptr),
                         static_cast<const void*>(a->tgt_id), static_cast<const void*>(a->tgt_w),
                         static_cast<const void*>(a->loss), static_cast<const void*>(a->logp),
                         static_cast<const void*>(a->d_hidden), static_cast<const void*>(a->d_w_vocab),
                         static_cast<const void*>(a->d_logits), static_cast<const void*>(a->workspace)})
-    if (p && !aligned16(p)) return tt::fail(TT_EINVAL, "tree_weighted_nll: device pointers must be 16-byte aligned");
+    if (p && !aligned16(p)) return tt::fail(TT_EINVAL, f + ": device pointers must be 16-byte aligned");
+  return TT_OK;
+}
+
+}  // namespace ttc
+
+extern "C" int tree_weighted_nll(const tt_nll_args* a, tt_stream stream) {
+  tt::clear_error();
+  const char* fn = "tree_weighted_nll";
+  int rc = ttc::nll_check(a, fn);
+  if (rc) return rc;
+  const bool logits = a->logits != nullptr;
   const NllWs w = nll_ws(a);
   if (!a->workspace || a->workspace_bytes < w.total)
     return tt::fail(TT_EWORKSPACE, std::string(fn) + ": workspace too small (need " + std::to_string(w.total) +

@@ -283,3 +283,68 @@ int launch_sum_loss(const float* row_loss, int32_t n, float* loss, hipStream_t s
   sum_loss_kernel<<<1, kThreads, 0, st>>>(row_loss, n, loss);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
+
+// ---------------------------------------------------------------- no-allocation entry point
+// tree_weighted_nll_noalloc: the logits mode of tree_weighted_nll with its
+// per-row partial losses in a static device array instead of the caller's
+// workspace, for callers that cannot allocate (graph capture, tight loops).
+// Every GPU the library runs on holds its own copy of the array until the
+// process ends; host code reaches it only through the address
+// hipGetSymbolAddress returns for the current device.
+#include <mutex>
+
+#include "attn_core.h"
+
+namespace {
+
+constexpr int32_t kNoAllocMaxRows = 1 << 20;  // 4 MiB of float32 row losses per GPU
+constexpr int kMaxDevices = 64;
+
+static __device__ __align__(256) float scratch[kNoAllocMaxRows];
+
+std::mutex g_scratch_mu;
+float* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's copy of `scratch`, looked up once per device.
+int scratch_for_current_device(float** out, const char* fn) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return tt::fail(TT_EDEVICE, std::string(fn) + ": no usable current device");
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return tt::fail(TT_EDEVICE, std::string(fn) + ": hipGetSymbolAddress(scratch) failed: " + hipGetErrorString(e));
+    g_scratch_ptr[dev] = static_cast<float*>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return TT_OK;
+}
+
+}  // namespace
+
+extern "C" int tree_weighted_nll_noalloc(const tt_nll_args* a, tt_stream stream) {
+  tt::clear_error();
+  const char* fn = "tree_weighted_nll_noalloc";
+  int rc = ttc::nll_check(a, fn);
+  if (rc) return rc;
+  if (!a->logits)
+    return tt::fail(TT_EUNSUPPORTED, std::string(fn) + ": logits mode only (the fused mode needs a rows x vocab "
+                                                       "workspace; use tree_weighted_nll)");
+  if (a->n_rows > kNoAllocMaxRows)
+    return tt::fail(TT_EWORKSPACE, std::string(fn) + ": n_rows " + std::to_string(a->n_rows) + " exceeds the " +
+                                       std::to_string(kNoAllocMaxRows) + " rows of the static scratch");
+  float* row_loss = nullptr;
+  if ((rc = scratch_for_current_device(&row_loss, fn))) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  {
+    ttc::KTimer t("nll_rows", st);
+    if (launch_nll_rows(a->logits_dtype, a->logits, a->d_logits, a->n_rows, a->vocab, a->vocab, a->tgt_row_ptr,
+                        a->tgt_id, a->tgt_w, a->n_tgt, a->logp, row_loss, st))
+      return ttc::dev_fail(fn, "nll kernel launch");
+  }
+  ttc::KTimer t("nll_sum", st);
+  if (launch_sum_loss(row_loss, a->n_rows, a->loss, st)) return ttc::dev_fail(fn, "loss reduction");
+  return TT_OK;
+}

@@ -245,6 +245,21 @@ def test_nll_argument_errors():
     assert nll(logits=0, hidden=FAKE, w_vocab=FAKE, d_model=8, vocab=100) == tt.TT_EUNSUPPORTED  # vocab % 8
     assert nll(logits=0, hidden=FAKE, w_vocab=FAKE, d_model=12, vocab=104) == tt.TT_EUNSUPPORTED  # d_model % 8
 
+    # the no-allocation variant: the same checks, then logits mode only and at most TT_NOALLOC_MAX_ROWS rows
+    def noalloc(**kw):
+        a = tt.NllArgs(n_rows=10, d_model=0, vocab=100, n_tgt=9, logits=FAKE, logits_dtype=tt.TT_F32,
+                       tgt_row_ptr=FAKE, tgt_id=FAKE, tgt_w=FAKE, loss=FAKE)
+        for k_, v_ in kw.items():
+            setattr(a, k_, v_)
+        return lib.tree_weighted_nll_noalloc(ctypes.byref(a), None)
+
+    assert noalloc(loss=0) == tt.TT_EINVAL
+    assert noalloc(vocab=1 << 20) == tt.TT_EUNSUPPORTED
+    assert noalloc(logits=0, hidden=FAKE, w_vocab=FAKE, d_model=8, vocab=104) == tt.TT_EUNSUPPORTED
+    assert b"logits mode only" in lib.tt_last_error()
+    assert noalloc(n_rows=(1 << 20) + 1) == tt.TT_EWORKSPACE
+    assert b"static scratch" in lib.tt_last_error()
+
 
 def test_probe_mfma_validates_before_launch():
     """The matrix-core probe rejects bad sizes and NULL pointers on the host."""
