@@ -99,11 +99,17 @@ int nll_check(const tt_nll_args* a, const char* fn);
 // Shapes the bf16 matrix-core kernels take (any GQA group, any size).
 bool mfma_shape(int32_t d, int32_t bq, int32_t bk);
 
-// Forward on rotated q, k (no RoPE here).
+// Factor the query operand carries into the attention cores: the
+// matrix-core kernels take q (rotated) times scale * log2(e), so that q.k is
+// the score in log2 units and exp2 applies to it directly; the vector
+// kernels take the rotated q itself (1).
+double q_operand_scale(tt_dtype dt, const AttnGeom& g, const PlanPtrs& P);
+
+// Forward on rotated q (times q_operand_scale) and k (no RoPE here).
 int attn_fwd_core(tt_dtype dt, const PlanPtrs& P, const AttnGeom& g, const void* q, const void* k, const void* v,
                   void* o, float* lse, bool full_range, hipStream_t st);
 
-// Backward on rotated q, k: D = rowsum(dO o O) into D, dQ (rotated frame,
+// Backward on rotated q (times q_operand_scale) and k: D = rowsum(dO o O) into D, dQ (rotated frame,
 // float32, not yet rotated back) into dq, dK and dV into d_k, d_v (float32
 // and added to when acc).  When dq_final is set and the bf16 matrix-core
 // kernels run, dQ is instead rotated back with cs_tab and stored in bf16 to

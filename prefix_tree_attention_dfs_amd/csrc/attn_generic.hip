@@ -16,12 +16,14 @@ using namespace ttd;
 namespace {
 
 // ---------------------------------------------------------------- RoPE (K1/K5)
-// y = R(depth * theta) x (or R^T x), theta_k = base^(-2k/d), pairs (k, k+d/2).
-// One thread per (row, k); the angle is formed and rotated in fp64.
+// y = mul R(depth * theta) x (or mul R^T x), theta_k = base^(-2k/d), pairs
+// (k, k+d/2); mul is 1 except for the query copy of the matrix-core kernels,
+// which carries the softmax scale times log2(e).  One thread per (row, k);
+// the angle is formed and rotated in fp64, rounded once to the output type.
 template <typename Tin, typename Tout, bool ACC>
 __global__ __launch_bounds__(256) void rope_kernel(const Tin* __restrict__ x, Tout* __restrict__ y, PlanPtrs P,
                                                    int32_t row0, int32_t n_rows, int32_t heads, int32_t d,
-                                                   double base, double sign) {
+                                                   double base, double sign, double mul) {
   if (!plan_matches(P)) return;
   const int32_t* __restrict__ depth = P.depth;
   const int half = d >> 1;
@@ -35,6 +37,8 @@ __global__ __launch_bounds__(256) void rope_kernel(const Tin* __restrict__ x, To
     sincos(double(depth[row0 + r]) * theta, &s, &c);
     s *= sign;
   }
+  c *= mul;
+  s *= mul;
   for (int h = 0; h < heads; ++h) {
     const int64_t b = (r * heads + h) * d;
     const double x1 = Elem<Tin>::load(x, b + k), x2 = Elem<Tin>::load(x, b + k + half);
@@ -55,7 +59,7 @@ __global__ __launch_bounds__(256) void rope_kernel(const Tin* __restrict__ x, To
 // 16-byte aligned rows.
 __global__ __launch_bounds__(256) void rope_bf16x8_kernel(const uint16_t* __restrict__ x, uint16_t* __restrict__ y,
                                                           PlanPtrs P, int32_t row0, int32_t n_rows, int32_t heads,
-                                                          int32_t d, double base, double sign) {
+                                                          int32_t d, double base, double sign, double mul) {
   if (!plan_matches(P)) return;
   const int half = d >> 1, oct = half >> 3;
   const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
@@ -73,6 +77,8 @@ __global__ __launch_bounds__(256) void rope_bf16x8_kernel(const uint16_t* __rest
       sincos(pos * theta, &sn[e], &c[e]);
       sn[e] *= sign;
     }
+    c[e] *= mul;
+    sn[e] *= mul;
   }
 #pragma unroll 2
   for (int h = 0; h < heads; ++h) {
@@ -404,25 +410,25 @@ inline unsigned blocks_for(int64_t n, int per) { return unsigned((n + per - 1) /
 
 // ---------------------------------------------------------------- launchers
 int launch_rope(const void* x, void* y, tt_dtype tin, tt_dtype tout, bool acc, const PlanPtrs& P, int32_t row0,
-                int32_t n_rows, int32_t heads, int32_t d, float base, bool inverse, hipStream_t st) {
+                int32_t n_rows, int32_t heads, int32_t d, float base, bool inverse, hipStream_t st, double mul) {
   const int64_t n = int64_t(n_rows) * (d / 2);
   if (n == 0) return 0;
   const dim3 grid(blocks_for(n, 256)), block(256);
   const double sg = inverse ? -1.0 : 1.0;
   const double b = double(base);
   if (tin == TT_F32 && tout == TT_F32 && !acc)
-    rope_kernel<float, float, false><<<grid, block, 0, st>>>((const float*)x, (float*)y, P, row0, n_rows, heads, d, b, sg);
+    rope_kernel<float, float, false><<<grid, block, 0, st>>>((const float*)x, (float*)y, P, row0, n_rows, heads, d, b, sg, mul);
   else if (tin == TT_F32 && tout == TT_F32 && acc)
-    rope_kernel<float, float, true><<<grid, block, 0, st>>>((const float*)x, (float*)y, P, row0, n_rows, heads, d, b, sg);
+    rope_kernel<float, float, true><<<grid, block, 0, st>>>((const float*)x, (float*)y, P, row0, n_rows, heads, d, b, sg, mul);
   else if (tin == TT_BF16 && tout == TT_BF16 && !acc && (d % 16) == 0 &&
            ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(y)) & 15) == 0) {
     const int64_t nv = int64_t(n_rows) * (d / 16);
     rope_bf16x8_kernel<<<dim3(blocks_for(nv, 256)), block, 0, st>>>((const uint16_t*)x, (uint16_t*)y, P, row0, n_rows,
-                                                                      heads, d, b, sg);
+                                                                      heads, d, b, sg, mul);
   } else if (tin == TT_BF16 && tout == TT_BF16 && !acc)
-    rope_kernel<uint16_t, uint16_t, false><<<grid, block, 0, st>>>((const uint16_t*)x, (uint16_t*)y, P, row0, n_rows, heads, d, b, sg);
+    rope_kernel<uint16_t, uint16_t, false><<<grid, block, 0, st>>>((const uint16_t*)x, (uint16_t*)y, P, row0, n_rows, heads, d, b, sg, mul);
   else if (tin == TT_F32 && tout == TT_BF16 && !acc)
-    rope_kernel<float, uint16_t, false><<<grid, block, 0, st>>>((const float*)x, (uint16_t*)y, P, row0, n_rows, heads, d, b, sg);
+    rope_kernel<float, uint16_t, false><<<grid, block, 0, st>>>((const float*)x, (uint16_t*)y, P, row0, n_rows, heads, d, b, sg, mul);
   else
     return -1;
   return hipGetLastError() == hipSuccess ? 0 : -1;

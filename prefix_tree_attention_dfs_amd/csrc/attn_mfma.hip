@@ -11,7 +11,9 @@
 // tiles go from global memory straight into LDS (swizzled layout), double
 // buffered, one barrier per tile.  Per wave: NT sub-tiles of 32 query rows of one head, Q held in
 // registers as B operands.
-//   S^T  = K Q^T        (A = K rows from LDS, B = Q)
+//   S^T  = K Q^T        (A = K rows from LDS, B = Q; Q carries scale * log2(e),
+//                        so scores are in log2 units, and the accumulators
+//                        start at minus the running max: no per-score FMA)
 //   online softmax over keys (columns are lanes: row statistics are per lane)
 //   O^T += V^T P^T      (A = V^T via ds_read_tr16_b64, B = P^T straight from
 //                        the S^T accumulator registers)
@@ -39,7 +41,9 @@ struct __align__(16) FwdStage {
   int32_t end[BK];
 };
 
-template <int G>
+// WIDE: K/V of 2 GiB or more; each tile's descriptors then start at the tile
+// (64-bit base) instead of one descriptor with a 32-bit tile offset.
+template <int G, bool WIDE>
 __global__ __launch_bounds__(FwdCfg<G>::THREADS, FwdCfg<G>::MINB) void fwd_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     uint16_t* __restrict__ o, float* __restrict__ lse, PlanPtrs P, AttnGeom g, int full_range, int qb_first,
@@ -57,8 +61,10 @@ __global__ __launch_bounds__(FwdCfg<G>::THREADS, FwdCfg<G>::MINB) void fwd_mfma_
   const int head = (kvh * nsub + sub) * G + wave / C::WPH;
   const int pos0 = (wave % C::WPH) * 32 * NT;
   const int qrow0 = qb * BQ - g.q_off;  // q-buffer row of the block's first position
-  const float c2 = g.scale * 1.4426950408889634f;
-  const float tau = 8.f / c2;  // 8 in log2 units, in raw score units
+  // the running max (log2 units) moves only when a row's tile max exceeds it
+  // by more than tau (2^8 in probability); until then p may reach 2^8, which
+  // the fp32 sums and the bf16 P operand carry without loss of relative precision
+  constexpr float tau = 8.f;
 
   // Q fragments (B operands): lane holds Q[row][dc*16 + 8hh .. +8]
   bf16x8 qf[NT][8];
@@ -71,7 +77,7 @@ __global__ __launch_bounds__(FwdCfg<G>::THREADS, FwdCfg<G>::MINB) void fwd_mfma_
   }
 
   f32x16 oacc[NT][4];
-  float m[NT], lpart[NT];
+  float m[NT], lpart[NT];  // running max (log2 units, -inf before any visible key), partial row sum
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     m[nt] = -INFINITY;
@@ -80,12 +86,11 @@ __global__ __launch_bounds__(FwdCfg<G>::THREADS, FwdCfg<G>::MINB) void fwd_mfma_
     for (int dt = 0; dt < 4; ++dt) oacc[nt][dt] = zero16();
   }
 
-  // tile staging: buffer loads, zero past n_k keys (end = 0 there: invisible);
-  // each tile's descriptors start at the tile (64-bit base), so K and V may
-  // exceed the 4 GiB a 32-bit buffer offset reaches
+  // tile staging: buffer loads, zero past n_k keys (end = 0 there: invisible)
   const int64_t kv_elems = int64_t(g.n_k) * g.h_kv * D;
   const int64_t tile_elems = int64_t(BK) * g.h_kv * D;  // one 64-key tile of K (or V)
   const rsrc_t re = make_rsrc(P.end, uint32_t(g.n_k) * 4);
+  const rsrc_t rk0 = make_rsrc(k, WIDE ? 0u : uint32_t(kv_elems * 2)), rv0 = make_rsrc(v, WIDE ? 0u : uint32_t(kv_elems * 2));
   // K and V tiles (64 keys x 128 bf16 = 16 KB each) go from global memory
   // straight into LDS: 16 loads of 1 KB per tile, NL per wave.  Lane l of
   // load j fills LDS slot 64 j + l = (key, stored chunk) = ((64 j + l) / 16,
@@ -102,14 +107,23 @@ __global__ __launch_bounds__(FwdCfg<G>::THREADS, FwdCfg<G>::MINB) void fwd_mfma_
   }
   int32_t ereg = 0;
   auto load_tile = [&](int kb, FwdStage& s) {
-    const int64_t t0 = int64_t(kb) * tile_elems;
-    const uint32_t bytes = tile_rec_bytes(kv_elems - t0);
-    const rsrc_t rk = make_rsrc(k + t0, bytes), rv = make_rsrc(v + t0, bytes);
     const uint32_t kbase = lds_u32(s.K) + wave * NL * 1024, vbase = lds_u32(s.V) + wave * NL * 1024;
+    if constexpr (WIDE) {
+      const int64_t t0 = int64_t(kb) * tile_elems;
+      const uint32_t bytes = tile_rec_bytes(kv_elems - t0);
+      const rsrc_t rk = make_rsrc(k + t0, bytes), rv = make_rsrc(v + t0, bytes);
 #pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      dma16(rk, dvoff[i], 0, kbase + i * 1024);
-      dma16(rv, dvoff[i], 0, vbase + i * 1024);
+      for (int i = 0; i < NL; ++i) {
+        dma16(rk, dvoff[i], 0, kbase + i * 1024);
+        dma16(rv, dvoff[i], 0, vbase + i * 1024);
+      }
+    } else {
+      const uint32_t so = uint32_t(kb) * uint32_t(tile_elems * 2);
+#pragma unroll
+      for (int i = 0; i < NL; ++i) {
+        dma16(rk0, dvoff[i], so, kbase + i * 1024);
+        dma16(rv0, dvoff[i], so, vbase + i * 1024);
+      }
     }
     if (tid < BK) ereg = bloadi(re, uint32_t(tid) * 4, uint32_t(kb) * BK * 4);
   };
@@ -139,13 +153,18 @@ __global__ __launch_bounds__(FwdCfg<G>::THREADS, FwdCfg<G>::MINB) void fwd_mfma_
     if (e + 1 < e1) load_tile(cur & kKbMask, st[sidx ^ 1]);  // that stage was last read in the previous tile
     const FwdStage& S = st[sidx];
 
-    // S^T = K Q^T for both 32-key halves, mask, one online-softmax update
-    // (rows = lanes) for the 64-key tile, then O^T += V^T P^T.
+    // S^T = K Q^T - m for both 32-key halves (scores in log2 units relative to
+    // the running max), mask, one online-softmax update (rows = lanes) for the
+    // 64-key tile, then O^T += V^T P^T.
     f32x16 sv[2][NT];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) sv[kt][nt] = zero16();
+      for (int nt = 0; nt < NT; ++nt) {
+        const float neg = m[nt] == -INFINITY ? 0.f : -m[nt];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sv[kt][nt][i] = neg;
+      }
 #pragma unroll
       for (int dc = 0; dc < 8; ++dc) {
         const bf16x8 a = lds_read16(&S.K[soff(kt * 32 + r, dc * 16 + 8 * hh)]);
@@ -153,7 +172,7 @@ __global__ __launch_bounds__(FwdCfg<G>::THREADS, FwdCfg<G>::MINB) void fwd_mfma_
         for (int nt = 0; nt < NT; ++nt) sv[kt][nt] = mfma(a, qf[nt][dc], sv[kt][nt]);
       }
     }
-    // mask (PARTIAL tiles), then one running-max update for the whole tile
+    // mask (PARTIAL tiles)
     if (!full) {
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
@@ -168,7 +187,10 @@ __global__ __launch_bounds__(FwdCfg<G>::THREADS, FwdCfg<G>::MINB) void fwd_mfma_
           }
         }
     }
-    float mexp[NT];
+    // tile max relative to the running max; a row shifts its max by dlt only
+    // when that exceeds tau (or on its first visible key)
+    float dlt[NT];
+    bool grow_any = false;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       float mx = -INFINITY;
@@ -177,25 +199,33 @@ __global__ __launch_bounds__(FwdCfg<G>::THREADS, FwdCfg<G>::MINB) void fwd_mfma_
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sv[kt][nt][i]);
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      // the running max moves only when a row's tile max exceeds it by more
-      // than tau (2^8 in probability); until then p may reach 2^8, which the
-      // fp32 sums and the bf16 P operand carry without loss of relative precision.
-      const bool grow = mx > m[nt] + tau;
-      if (__any(grow)) {
-        const float mnew = grow ? mx : m[nt];
-        const float alpha = (mnew == m[nt]) ? 1.f : exp2_fast((m[nt] - mnew) * c2);
-        lpart[nt] *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) oacc[nt][dt][i] *= alpha;
-        m[nt] = mnew;
-      }
-      mexp[nt] = m[nt] == -INFINITY ? 0.f : m[nt] * c2;
+      const bool grow = m[nt] == -INFINITY ? mx > -INFINITY : mx > tau;
+      dlt[nt] = grow ? mx : 0.f;
+      grow_any |= grow;
     }
-    // one straight block: both halves' exponentials and P, then O^T += V^T P^T;
-    // the scheduler overlaps the first half's products with the second half's
-    // exponentials
+    if (__any(grow_any)) {
+      // rare: move the max of the rows that grew (rescale O and l) and shift
+      // their scores to it
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        if (dlt[nt] != 0.f && m[nt] != -INFINITY) {
+          const float alpha = exp2_fast(-dlt[nt]);
+          lpart[nt] *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) oacc[nt][dt][i] *= alpha;
+        }
+        m[nt] = m[nt] == -INFINITY ? dlt[nt] : m[nt] + dlt[nt];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) sv[kt][nt][i] -= dlt[nt];
+      }
+    }
+    // exponentials and P of both halves, then O^T += V^T P^T, in one straight
+    // block: the scheduler overlaps the first half's products with the second
+    // half's exponentials
     bf16x8 pf[2][2][NT];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
@@ -204,7 +234,7 @@ __global__ __launch_bounds__(FwdCfg<G>::THREADS, FwdCfg<G>::MINB) void fwd_mfma_
         float ls = 0.f;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const float p = exp2_fast(sv[kt][nt][i] * c2 - mexp[nt]);
+          const float p = exp2_fast(sv[kt][nt][i]);
           sv[kt][nt][i] = p;
           ls += p;
         }
@@ -245,7 +275,8 @@ __global__ __launch_bounds__(FwdCfg<G>::THREADS, FwdCfg<G>::MINB) void fwd_mfma_
         for (int e = 0; e < 4; ++e) w[e] = __bf16(oacc[nt][dt][4 * i4 + e] * inv);
         *reinterpret_cast<bf16x4*>(orow + dt * 32 + 8 * i4 + 4 * hh) = w;
       }
-    if (hh == 0) lse[int64_t(row) * g.h_q + head] = m[nt] * g.scale + logf(lt);  // ln sum exp(scale (s - m)) + scale m
+    // natural-log LSE from the log2-unit max: ln 2 (m + log2 sum 2^(s' - m))
+    if (hh == 0) lse[int64_t(row) * g.h_q + head] = (m[nt] + __log2f(lt)) * 0.6931471805599453f;
   }
 }
 
@@ -258,8 +289,15 @@ int launch_fwd_g(const void* q, const void* k, const void* v, void* o, float* ls
   if (n_qb <= 0) return 0;
   const int nsub = (g.h_q / g.h_kv) / G;
   const dim3 grid(unsigned(n_qb) * unsigned(g.h_kv) * unsigned(nsub)), block(FwdCfg<G>::THREADS);
-  fwd_mfma_kernel<G><<<grid, block, 0, st>>>((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
-                                             (uint16_t*)o, lse, P, g, full_range ? 1 : 0, qb_first, n_qb, nsub);
+  const bool wide = int64_t(g.n_k) * g.h_kv * D * 2 >= (int64_t(1) << 31);
+  if (wide)
+    fwd_mfma_kernel<G, true><<<grid, block, 0, st>>>((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
+                                                     (uint16_t*)o, lse, P, g, full_range ? 1 : 0, qb_first, n_qb,
+                                                     nsub);
+  else
+    fwd_mfma_kernel<G, false><<<grid, block, 0, st>>>((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
+                                                      (uint16_t*)o, lse, P, g, full_range ? 1 : 0, qb_first, n_qb,
+                                                      nsub);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -10,6 +10,9 @@
 //   dq_mfma_kernel   query-stationary (the forward's walk over the block's
 //                    non-empty key tiles):  S^T = K Q^T, P^T, dP^T = V dO^T,
 //                    dS^T = P^T (dP^T - D), dQ^T += K^T dS^T.
+// Q comes multiplied by scale * log2(e), so S is in log2 units; S's
+// accumulators start at -LSE log2(e) and dP's at -D, so P = exp2(S) and
+// dS = P dP come straight from the products.
 //   dkdv_mfma_kernel key-stationary: one workgroup per 256 keys x kv head,
 //                    each of its 8 waves owning 32 keys (K in registers, V
 //                    in LDS, both loaded once).  It streams 64-row
@@ -30,6 +33,7 @@ using ttd::Elem;
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 
 // ------------------------------------------------------------------ dQ
 template <int G>
@@ -48,7 +52,8 @@ struct __align__(16) DqStage {
 // FIN: the epilogue rotates dQ back at the query's depth (R^T with the
 // caller's (cos, sin) table; none: no rotation) and stores it in bf16 to
 // dq_out; otherwise it stores the rotated-frame dQ in fp32 to dq_acc.
-template <int G, bool FIN>
+// WIDE: K/V of 2 GiB or more (each tile's descriptors start at the tile).
+template <int G, bool FIN, bool WIDE>
 __global__ __launch_bounds__(DqCfg<G>::THREADS) void dq_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ d_o, const float* __restrict__ lse, const float* __restrict__ Dv,
@@ -67,7 +72,6 @@ __global__ __launch_bounds__(DqCfg<G>::THREADS) void dq_mfma_kernel(
   const int row = qb * BQ - g.q_off + pos0 + r;  // q-buffer row of this lane's query
   const bool rok = row < g.n_q;
   const int qpos = qb * BQ + pos0 + r;
-  const float c2 = g.scale * kLog2e;
 
   bf16x8 qf[8], of[8];
 #pragma unroll
@@ -76,18 +80,18 @@ __global__ __launch_bounds__(DqCfg<G>::THREADS) void dq_mfma_kernel(
     qf[dc] = rok ? ld16(q + off) : zero8();
     of[dc] = rok ? ld16(d_o + off) : zero8();
   }
-  const float lse2 = rok ? lse[int64_t(row) * g.h_q + head] * kLog2e : 0.f;
-  const float Dq = rok ? Dv[int64_t(row) * g.h_q + head] : 0.f;
+  const float neg_lse2 = rok ? -lse[int64_t(row) * g.h_q + head] * kLog2e : 0.f;
+  const float neg_D = rok ? -Dv[int64_t(row) * g.h_q + head] : 0.f;
 
   f32x16 acc[4];
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) acc[dt] = zero16();
 
-  // tile staging: buffer loads, zero past n_k keys (end = 0 there: invisible);
-  // descriptors start at each tile (64-bit base), as in the forward
+  // tile staging: buffer loads, zero past n_k keys (end = 0 there: invisible)
   const int64_t kv_elems = int64_t(g.n_k) * g.h_kv * D;
   const int64_t tile_elems = int64_t(BK) * g.h_kv * D;
   const rsrc_t re = make_rsrc(P.end, uint32_t(g.n_k) * 4);
+  const rsrc_t rk0 = make_rsrc(k, WIDE ? 0u : uint32_t(kv_elems * 2)), rv0 = make_rsrc(v, WIDE ? 0u : uint32_t(kv_elems * 2));
   // K and V tiles go from global memory straight into LDS in the swizzled
   // layout, NL loads of 1 KB per wave each, as in the forward
   constexpr int NL = (BK * D * 2 / 1024) / C::WAVES;
@@ -101,14 +105,23 @@ __global__ __launch_bounds__(DqCfg<G>::THREADS) void dq_mfma_kernel(
   }
   int32_t ereg = 0;
   auto load_tile = [&](int kb, DqStage& s) {
-    const int64_t t0 = int64_t(kb) * tile_elems;
-    const uint32_t bytes = tile_rec_bytes(kv_elems - t0);
-    const rsrc_t rk = make_rsrc(k + t0, bytes), rv = make_rsrc(v + t0, bytes);
     const uint32_t kbase = lds_u32(s.K) + wave * NL * 1024, vbase = lds_u32(s.V) + wave * NL * 1024;
+    if constexpr (WIDE) {
+      const int64_t t0 = int64_t(kb) * tile_elems;
+      const uint32_t bytes = tile_rec_bytes(kv_elems - t0);
+      const rsrc_t rk = make_rsrc(k + t0, bytes), rv = make_rsrc(v + t0, bytes);
 #pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      dma16(rk, dvoff[i], 0, kbase + i * 1024);
-      dma16(rv, dvoff[i], 0, vbase + i * 1024);
+      for (int i = 0; i < NL; ++i) {
+        dma16(rk, dvoff[i], 0, kbase + i * 1024);
+        dma16(rv, dvoff[i], 0, vbase + i * 1024);
+      }
+    } else {
+      const uint32_t so = uint32_t(kb) * uint32_t(tile_elems * 2);
+#pragma unroll
+      for (int i = 0; i < NL; ++i) {
+        dma16(rk0, dvoff[i], so, kbase + i * 1024);
+        dma16(rv0, dvoff[i], so, vbase + i * 1024);
+      }
     }
     if (tid < BK) ereg = bloadi(re, uint32_t(tid) * 4, uint32_t(kb) * BK * 4);
   };
@@ -137,7 +150,7 @@ __global__ __launch_bounds__(DqCfg<G>::THREADS) void dq_mfma_kernel(
     const DqStage& S = st[sidx];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
-      f32x16 s = zero16(), dp = zero16();
+      f32x16 s = splat16_here(neg_lse2), dp = splat16_here(neg_D);
 #pragma unroll
       for (int dc = 0; dc < 8; ++dc) {
         const bf16x8 a = lds_read16(&S.K[soff(kt * 32 + r, dc * 16 + 8 * hh)]);
@@ -150,14 +163,13 @@ __global__ __launch_bounds__(DqCfg<G>::THREADS) void dq_mfma_kernel(
       __builtin_amdgcn_s_setprio(1);
       if (full) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) s[i] = exp2_fast(s[i] * c2 - lse2) * (dp[i] - Dq);
+        for (int i = 0; i < 16; ++i) s[i] = exp2_fast(s[i]) * dp[i];
       } else {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int kl = kt * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
           const bool vis = (kb * BK + kl <= qpos) & (qpos < S.end[kl]);
-          const float p = exp2_fast(s[i] * c2 - lse2);
-          s[i] = vis ? p * (dp[i] - Dq) : 0.f;
+          s[i] = vis ? exp2_fast(s[i]) * dp[i] : 0.f;
         }
       }
       const bf16x8 d0 = c_to_b(s, 0), d1 = c_to_b(s, 1);
@@ -230,7 +242,7 @@ constexpr int VCH = (KV_KEYS * D / 8) / KV_THREADS;  // 16-byte chunks of V per 
 struct __align__(16) KvStage {
   uint16_t Q[QT * D];  // swizzled (row reads for S, transposed reads for dK^T)
   uint16_t O[QT * D];  // dO, swizzled (row reads for dP, transposed reads for dV^T)
-  float s0[QT];  // -LSE / scale: start value of the S accumulator, so that P = exp2(c2 S)
+  float s0[QT];  // -LSE log2(e): start value of the S accumulator (Q carries scale log2(e)), so P = exp2(S)
   float d0[QT];  // -D: start value of the dP accumulator, so that dS = P dP
 };
 
@@ -240,8 +252,9 @@ struct __align__(16) KvLds {
   int32_t red[KV_WAVES];
 };
 
-// G: query heads per kv head (0: any group size, read from g at run time)
-template <int G, bool ACC, typename TG>
+// G: query heads per kv head (0: any group size, read from g at run time).
+// WIDE: Q / dO of 2 GiB or more (each tile's descriptors start at the tile).
+template <int G, bool ACC, typename TG, bool WIDE>
 __global__ __launch_bounds__(KV_THREADS, 2) void dkdv_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ d_o, const float* __restrict__ lse, const float* __restrict__ Dv,
@@ -254,8 +267,6 @@ __global__ __launch_bounds__(KV_THREADS, 2) void dkdv_mfma_kernel(
   const int kbase = kb2 * KV_KEYS;
   const int j = kbase + wave * 32 + r;  // this lane's key (lane column of S, dP, dK^T, dV^T)
   const bool jok = j < g.n_k;
-  const float c2 = g.scale * kLog2e;
-  const float inv_scale = 1.f / g.scale;
 
   // V of the workgroup's keys -> LDS (rows past n_k are zero)
 #pragma unroll
@@ -308,10 +319,10 @@ __global__ __launch_bounds__(KV_THREADS, 2) void dkdv_mfma_kernel(
 
   float lreg = 0.f, dreg = 0.f;
   // query rows past n_q read zeros (tiles start at or after q_off, which is
-  // a multiple of 64, so rows are never below the buffer); each tile's
-  // descriptors start at the tile (64-bit base), so Q and dO may exceed the
-  // 4 GiB a 32-bit buffer offset reaches
+  // a multiple of 64, so rows are never below the buffer)
   const int64_t q_elems = int64_t(g.n_q) * g.h_q * D, r_elems = int64_t(g.n_q) * g.h_q;
+  const uint32_t qb0 = WIDE ? 0u : uint32_t(q_elems * 2), rb0 = WIDE ? 0u : uint32_t(r_elems * 4);
+  const rsrc_t rq0 = make_rsrc(q, qb0), ro0 = make_rsrc(d_o, qb0), rl0 = make_rsrc(lse, rb0), rd0 = make_rsrc(Dv, rb0);
   // Q and dO tiles (64 rows x 128 bf16 = 16 KB each) go from global memory
   // straight into LDS: 16 loads of 1 KB per tile, two per wave.  Lane l of
   // load j fills LDS slot 64 j + l = (row, stored chunk) = ((64 j + l) / 16,
@@ -330,24 +341,37 @@ __global__ __launch_bounds__(KV_THREADS, 2) void dkdv_mfma_kernel(
     const int rev = n_steps - 1 - step;
     const int qt = qt_first + rev / GG, head = kvh * GG + rev % GG;
     const int64_t rowh = int64_t(qt * QT - g.q_off) * g.h_q + head;  // (row, head) of the tile's first row
-    const uint32_t qbytes = tile_rec_bytes(q_elems - rowh * D);
-    const uint32_t rbytes = tile_rec_bytes(2 * (r_elems - rowh));  // float32 entries
-    const rsrc_t rq = make_rsrc(q + rowh * D, qbytes), ro = make_rsrc(d_o + rowh * D, qbytes);
-    const rsrc_t rl = make_rsrc(lse + rowh, rbytes), rd = make_rsrc(Dv + rowh, rbytes);
     const uint32_t qb = lds_u32(s.Q) + wave * 2048, ob = lds_u32(s.O) + wave * 2048;
+    if constexpr (WIDE) {
+      const uint32_t qbytes = tile_rec_bytes(q_elems - rowh * D);
+      const uint32_t rbytes = tile_rec_bytes(2 * (r_elems - rowh));  // float32 entries
+      const rsrc_t rq = make_rsrc(q + rowh * D, qbytes), ro = make_rsrc(d_o + rowh * D, qbytes);
+      const rsrc_t rl = make_rsrc(lse + rowh, rbytes), rd = make_rsrc(Dv + rowh, rbytes);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      dma16(rq, dvoff[i], 0, qb + i * 1024);
-      dma16(ro, dvoff[i], 0, ob + i * 1024);
-    }
-    if (tid < QT) {
-      lreg = bloadf(rl, uint32_t(tid) * g.h_q * 4, 0);
-      dreg = bloadf(rd, uint32_t(tid) * g.h_q * 4, 0);
+      for (int i = 0; i < 2; ++i) {
+        dma16(rq, dvoff[i], 0, qb + i * 1024);
+        dma16(ro, dvoff[i], 0, ob + i * 1024);
+      }
+      if (tid < QT) {
+        lreg = bloadf(rl, uint32_t(tid) * g.h_q * 4, 0);
+        dreg = bloadf(rd, uint32_t(tid) * g.h_q * 4, 0);
+      }
+    } else {
+      const uint32_t rh = uint32_t(rowh);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        dma16(rq0, dvoff[i], rh * D * 2, qb + i * 1024);
+        dma16(ro0, dvoff[i], rh * D * 2, ob + i * 1024);
+      }
+      if (tid < QT) {
+        lreg = bloadf(rl0, uint32_t(tid) * g.h_q * 4, rh * 4);
+        dreg = bloadf(rd0, uint32_t(tid) * g.h_q * 4, rh * 4);
+      }
     }
   };
   auto store_rows = [&](KvStage& s) {
     if (tid < QT) {
-      s.s0[tid] = -lreg * inv_scale;
+      s.s0[tid] = -lreg * kLog2e;
       s.d0[tid] = -dreg;
     }
   };
@@ -370,8 +394,8 @@ __global__ __launch_bounds__(KV_THREADS, 2) void dkdv_mfma_kernel(
       // every (query, key) pair of this wave's 32 x 32 block visible and in range?
       const bool full =
           __builtin_amdgcn_readfirstlane(wave_kmax <= q0 && wave_min_end > q0 + 31 && q0 >= lo && q0 + 31 < hi);
-      // S starts at -LSE/scale and dP at -D (both per query = per register), so
-      // that the products below give c2 S - LSE log2(e) and dP - D directly
+      // S starts at -LSE log2(e) and dP at -D (both per query = per register), so
+      // that the products below give S - LSE log2(e) (log2 units) and dP - D directly
       f32x16 s, dp;
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
@@ -401,7 +425,7 @@ __global__ __launch_bounds__(KV_THREADS, 2) void dkdv_mfma_kernel(
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int i = 4 * i4 + e;
-            const float p = exp2_fast(s[i] * c2);
+            const float p = exp2_fast(s[i]);
             s[i] = p;
             ds[i] = p * dp[i];
           }
@@ -411,7 +435,7 @@ __global__ __launch_bounds__(KV_THREADS, 2) void dkdv_mfma_kernel(
             const int i = 4 * i4 + e;
             const int qq = qt * QT + ql + e;
             const bool vis = (j <= qq) & (qq < endj) & (qq >= lo) & (qq < hi);
-            const float p = vis ? exp2_fast(s[i] * c2) : 0.f;
+            const float p = vis ? exp2_fast(s[i]) : 0.f;
             s[i] = p;
             ds[i] = p * dp[i];
           }
@@ -436,7 +460,8 @@ __global__ __launch_bounds__(KV_THREADS, 2) void dkdv_mfma_kernel(
 
   // dK = R^T (scale * dK') at the key's depth, with (cos, sin) of depth *
   // theta_c from the caller's table (none: no rotation); coordinates (c, c+64)
-  // are the same register of blocks dt and dt+2.
+  // are the same register of blocks dt and dt+2.  The Q operand carried
+  // scale * log2(e), so scale * dK' is the accumulator times ln 2.
   const float2* __restrict__ cs_row = cs_tab ? cs_tab + int64_t(P.depth[j]) * (D / 2) : nullptr;
   const int64_t base = (int64_t(j) * g.h_kv + kvh) * D;
 #pragma unroll
@@ -447,7 +472,7 @@ __global__ __launch_bounds__(KV_THREADS, 2) void dkdv_mfma_kernel(
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int c = dt * 32 + 8 * i4 + 4 * hh + e;
-        const float x1 = dk[dt][4 * i4 + e] * g.scale, x2 = dk[dt + 2][4 * i4 + e] * g.scale;
+        const float x1 = dk[dt][4 * i4 + e] * kLn2, x2 = dk[dt + 2][4 * i4 + e] * kLn2;
         float cs = 1.f, sn = 0.f;
         if (cs_row) {
           const float2 t = cs_row[c];
@@ -491,14 +516,18 @@ int launch_dq_g(const void* q, const void* k, const void* v, const void* d_o, co
   if (n_qb <= 0) return 0;
   const int nsub = (g.h_q / g.h_kv) / G;
   const dim3 grid(unsigned(n_qb) * unsigned(g.h_kv) * unsigned(nsub)), block(DqCfg<G>::THREADS);
-  if (dq_out)
-    dq_mfma_kernel<G, true><<<grid, block, 0, st>>>((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
-                                                    (const uint16_t*)d_o, lse, D_, nullptr, (uint16_t*)dq_out,
-                                                    cs_tab, P, g, full_range ? 1 : 0, qb_first, n_qb, nsub);
-  else
-    dq_mfma_kernel<G, false><<<grid, block, 0, st>>>((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
-                                                     (const uint16_t*)d_o, lse, D_, dq_acc, nullptr, nullptr, P,
-                                                     g, full_range ? 1 : 0, qb_first, n_qb, nsub);
+  const bool wide = int64_t(g.n_k) * g.h_kv * D * 2 >= (int64_t(1) << 31);
+#define TT_DQ(FIN, WIDE)                                                                                          \
+  dq_mfma_kernel<G, FIN, WIDE><<<grid, block, 0, st>>>(                                                           \
+      (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)d_o, lse, D_,                  \
+      FIN ? nullptr : dq_acc, FIN ? (uint16_t*)dq_out : nullptr, FIN ? cs_tab : nullptr, P, g, full_range ? 1 : 0, \
+      qb_first, n_qb, nsub)
+  if (dq_out) {
+    if (wide) TT_DQ(true, true); else TT_DQ(true, false);
+  } else {
+    if (wide) TT_DQ(false, true); else TT_DQ(false, false);
+  }
+#undef TT_DQ
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
@@ -509,14 +538,17 @@ int launch_dkdv_g(const void* q, const void* k, const void* v, const void* d_o, 
   const int nkb2 = (g.n_k + KV_KEYS - 1) / KV_KEYS;
   if (nkb2 <= 0) return 0;
   const dim3 grid(unsigned(nkb2) * unsigned(g.h_kv)), block(KV_THREADS);
-  if (acc)
-    dkdv_mfma_kernel<G, true, float><<<grid, block, 0, st>>>((const uint16_t*)q, (const uint16_t*)k,
-                                                              (const uint16_t*)v, (const uint16_t*)d_o, lse, D_,
-                                                              (float*)d_k, (float*)d_v, cs_tab, P, g);
-  else
-    dkdv_mfma_kernel<G, false, uint16_t><<<grid, block, 0, st>>>((const uint16_t*)q, (const uint16_t*)k,
-                                                                  (const uint16_t*)v, (const uint16_t*)d_o, lse, D_,
-                                                                  (uint16_t*)d_k, (uint16_t*)d_v, cs_tab, P, g);
+  const bool wide = int64_t(g.n_q) * g.h_q * D * 2 >= (int64_t(1) << 31);
+#define TT_KV(ACC, TG, WIDE)                                                                                    \
+  dkdv_mfma_kernel<G, ACC, TG, WIDE><<<grid, block, 0, st>>>((const uint16_t*)q, (const uint16_t*)k,             \
+                                                             (const uint16_t*)v, (const uint16_t*)d_o, lse, D_, \
+                                                             (TG*)d_k, (TG*)d_v, cs_tab, P, g)
+  if (acc) {
+    if (wide) TT_KV(true, float, true); else TT_KV(true, float, false);
+  } else {
+    if (wide) TT_KV(false, uint16_t, true); else TT_KV(false, uint16_t, false);
+  }
+#undef TT_KV
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -29,17 +29,28 @@ size_t dsize(tt_dtype t) { return t == TT_F32 ? 4 : 2; }
 struct AttnWs {
   size_t q_rot = 0, k_rot = 0, D = 0, dq = 0, cs = 0, total = 0;
   bool rope = false;
+  bool qcopy = false;  // q rotated (and, for the matrix-core kernels, scaled) into the workspace
   int32_t cs_pos = 0;  // rows of the (cos, sin) table: every depth of the tree
 };
+
+// The matrix-core kernels take the query already multiplied by scale * log2(e)
+// (their scores come out in log2 units); that copy lives in the workspace even
+// without RoPE.
+bool mfma_call(const tt_attn_args* a) {
+  return a->dtype == TT_BF16 && ttc::mfma_shape(a->d, a->tree->bq, a->tree->bk);
+}
 
 AttnWs attn_ws(const tt_attn_args* a, bool bwd) {
   AttnWs w;
   const size_t es = dsize(a->dtype);
   w.rope = a->rope_base != 0.f;
+  w.qcopy = w.rope || mfma_call(a);
   size_t off = 0;
-  if (w.rope) {
+  if (w.qcopy) {
     w.q_rot = off;
     off = align_up(off + size_t(a->n_q) * a->h_q * a->d * es);
+  }
+  if (w.rope) {
     w.k_rot = off;
     off = align_up(off + size_t(a->n_k) * a->h_kv * a->d * es);
   }
@@ -149,6 +160,10 @@ int plan_check(const tt_tree* t, const void* dev_plan, const char* fn) {
 }
 
 bool mfma_shape(int32_t d, int32_t bq, int32_t bk) { return d == 128 && bq == 64 && bk == 64; }
+
+double q_operand_scale(tt_dtype dt, const AttnGeom& g, const PlanPtrs& P) {
+  return dt == TT_BF16 && mfma_attn_supported(g, P) ? double(g.scale) * 1.4426950408889634 : 1.0;
+}
 
 int attn_fwd_core(tt_dtype dt, const PlanPtrs& P, const AttnGeom& g, const void* q, const void* k, const void* v,
                   void* o, float* lse, bool full_range, hipStream_t st) {
@@ -272,20 +287,18 @@ extern "C" int tree_attn_fwd(const tt_attn_args* a, tt_stream stream) {
   char* ws = static_cast<char*>(a->workspace);
   const void* q = a->q;
   const void* k = a->k;
-  if (w.rope) {
-    {
-      KTimer t("rope_q", st);
-      if (launch_rope(a->q, ws + w.q_rot, a->dtype, a->dtype, false, P, a->q_off, a->n_q, a->h_q, a->d,
-                      a->rope_base, false, st))
-        return dev_fail(fn, "rope(q)");
-    }
-    {
-      KTimer t("rope_k", st);
-      if (launch_rope(a->k, ws + w.k_rot, a->dtype, a->dtype, false, P, 0, a->n_k, a->h_kv, a->d,
-                      a->rope_base, false, st))
-        return dev_fail(fn, "rope(k)");
-    }
+  if (w.qcopy) {
+    KTimer t("rope_q", st);
+    if (launch_rope(a->q, ws + w.q_rot, a->dtype, a->dtype, false, P, a->q_off, a->n_q, a->h_q, a->d,
+                    a->rope_base, false, st, ttc::q_operand_scale(a->dtype, g, P)))
+      return dev_fail(fn, "rope(q)");
     q = ws + w.q_rot;
+  }
+  if (w.rope) {
+    KTimer t("rope_k", st);
+    if (launch_rope(a->k, ws + w.k_rot, a->dtype, a->dtype, false, P, 0, a->n_k, a->h_kv, a->d,
+                    a->rope_base, false, st))
+      return dev_fail(fn, "rope(k)");
     k = ws + w.k_rot;
   }
   const bool full_range = a->q_off == 0 && a->n_q == P.N;
@@ -318,21 +331,23 @@ extern "C" int tree_attn_bwd(const tt_attn_bwd_args* b, tt_stream stream) {
   char* ws = static_cast<char*>(a->workspace);
   const void* q = a->q;
   const void* k = a->k;
-  if (w.rope) {
-    // the forward wrote them at the same offsets (tree_attn_workspace_bytes layout)
+  // the forward wrote them at the same offsets (tree_attn_workspace_bytes layout)
+  if (w.qcopy) {
     if (a->n_q > 0 && !reuse) {
       KTimer t("rope_q", st);
       if (launch_rope(a->q, ws + w.q_rot, a->dtype, a->dtype, false, P, a->q_off, a->n_q, a->h_q, a->d,
-                      a->rope_base, false, st))
+                      a->rope_base, false, st, ttc::q_operand_scale(a->dtype, g, P)))
         return dev_fail(fn, "rope(q)");
     }
+    q = ws + w.q_rot;
+  }
+  if (w.rope) {
     if (!reuse) {
       KTimer t("rope_k", st);
       if (launch_rope(a->k, ws + w.k_rot, a->dtype, a->dtype, false, P, 0, a->n_k, a->h_kv, a->d,
                       a->rope_base, false, st))
         return dev_fail(fn, "rope(k)");
     }
-    q = ws + w.q_rot;
     k = ws + w.k_rot;
   }
   float* D = reinterpret_cast<float*>(ws + w.D);

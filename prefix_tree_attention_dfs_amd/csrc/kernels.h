@@ -10,7 +10,8 @@
 
 // RoPE (and its transpose) at the rows' depths; acc adds into an fp32 output.
 int launch_rope(const void* x, void* y, tt_dtype tin, tt_dtype tout, bool acc, const PlanPtrs& P, int32_t row0,
-                int32_t n_rows, int32_t heads, int32_t d, float base, bool inverse, hipStream_t st);
+                int32_t n_rows, int32_t heads, int32_t d, float base, bool inverse, hipStream_t st,
+                double mul = 1.0);
 
 // Generic (any d <= 256) path, fp32 or bf16 storage.
 int launch_fwd_generic(tt_dtype dt, const void* q, const void* k, const void* v, void* o, float* lse,

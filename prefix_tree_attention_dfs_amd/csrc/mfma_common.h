@@ -43,6 +43,20 @@ __device__ __forceinline__ bf16x8 zero8() {
   return z;
 }
 
+// 16 copies of x, each made by its own move where the call stands: a splat of
+// a loop-invariant value written this way is not hoisted out of the loop (a
+// hoisted splat would keep 16 more registers live through the loop).
+__device__ __forceinline__ f32x16 splat16_here(float x) {
+  f32x16 r;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    float t;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(t) : "v"(x));
+    r[i] = t;
+  }
+  return r;
+}
+
 __device__ __forceinline__ f32x16 zero16() {
   f32x16 z;
 #pragma unroll

@@ -159,6 +159,7 @@ extern "C" int tree_attn_path(const tt_path_args* a, tt_stream stream) {
   g.d = a->d;
   g.scale = a->scale == 0.f ? float(1.0 / std::sqrt(double(a->d))) : a->scale;
   g.rope_base = 0.f;  // the stack holds rotated rows
+  const double qmul = ttc::q_operand_scale(dt, g, P);  // and queries in the attention cores' operand form
 
   char *Qp = ws + w.qp, *Kp = ws + w.kp, *Vp = ws + w.vp, *Op = ws + w.op;
   float* LSEp = reinterpret_cast<float*>(ws + w.lsep);
@@ -195,7 +196,7 @@ extern "C" int tree_attn_path(const tt_path_args* a, tt_stream stream) {
         const size_t r0 = size_t(s.row0), n = size_t(s.len), d0 = size_t(s.depth0);
         KTimer t("path_push", st);
         if (launch_rope(q + r0 * qrow, Qp + d0 * qrow, dt, dt, false, P, s.depth0, s.len, a->h_q, a->d, rb, false,
-                        st) ||
+                        st, qmul) ||
             launch_rope(k + r0 * krow, Kp + d0 * krow, dt, dt, false, P, s.depth0, s.len, a->h_kv, a->d, rb, false,
                         st) ||
             hipMemcpyAsync(Vp + d0 * krow, v + r0 * krow, n * krow, hipMemcpyDeviceToDevice, st) != hipSuccess)

@@ -214,7 +214,11 @@ def test_attention_argument_errors():
     assert lib.tree_attn_workspace_bytes(ctypes.byref(_attn(t)), 1, ctypes.byref(n)) == 0
     q_bytes = t.N * 4 * 128 * 2
     assert n.value >= q_bytes + t.N * 2 * 128 * 2 + t.N * 4 * 4 + t.N * 4 * 128 * 4
+    # without RoPE the matrix-core forward still needs its scaled query copy; the vector kernels need nothing
     assert lib.tree_attn_workspace_bytes(ctypes.byref(_attn(t, rope_base=0.0)), 0, ctypes.byref(n)) == 0
+    assert n.value == (q_bytes + 255) // 256 * 256
+    assert lib.tree_attn_workspace_bytes(ctypes.byref(_attn(t, rope_base=0.0, dtype=tt.TT_F32)), 0,
+                                         ctypes.byref(n)) == 0
     assert n.value == 0
 
 
