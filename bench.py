@@ -472,7 +472,8 @@ def main():
     tflops_strict = 12 * d * hq * P / (ms * 1e-3) / 1e12  # backward counted as 8 d Hq P
     # roofline of the dominant kernel (largest share of the step's device time)
     algo = {"attn_fwd_mfma": 4 * d * hq * P, "attn_bwd_dkdv_mfma": 8 * d * hq * P,
-            "attn_bwd_dq_mfma": 6 * d * hq * P}
+            "attn_bwd_dq_mfma": 6 * d * hq * P,
+            "attn_bwd_mfma": 14 * d * hq * P}  # dQ (S, dP recomputed; dQ) and dK/dV (S, dP, dV, dK) in one launch
     dom = max(kt, key=lambda n: kt[n][1])
     launches, tot, mx = kt[dom]
     avg_ms = tot / launches

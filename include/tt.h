@@ -333,19 +333,21 @@ int tree_weighted_nll_noalloc(const tt_nll_args* args, tt_stream stream);
  * segments lie one on the next on the stack, so a round is one chunked pass
  * over its positions -- one forward and one backward round per leaf
  * (AReaL-DTA, Key Contributions 2: push-pop execution, about one regular
- * forward/backward round per leaf).  A forward round runs its chunks against
- * stack positions [0, end of chunk); a backward round runs them from the
- * right, adding dK, dV into float32 stack accumulators, then writes each
- * popped segment's dK, dV rows out and clears their stack slots.  Each call
- * starts at the 64-aligned position at or below its first query; the
- * ancestor rows below the chunk are recomputed with a zero upstream gradient
- * ("pad rows", counted in tt_path_info), so results equal tree mode
- * (tree_attn_fwd/bwd) up to the order of floating-point sums.
+ * forward/backward round per leaf).  A forward round is one call over its
+ * positions against the stack below them; a backward round runs in chunks
+ * (boundaries at multiples of the chunk length) from the right, adding dK, dV
+ * into float32 stack accumulators, then writes each popped segment's dK, dV
+ * rows out and clears their stack slots.  Each call starts at the 64-aligned
+ * position at or below its first query; the ancestor rows below it are
+ * recomputed (with a zero upstream gradient in the backward: "pad rows",
+ * counted in tt_path_info), so results equal tree mode (tree_attn_fwd/bwd)
+ * up to the order of floating-point sums.
  *
  * tree_path_build
  *   tree    built tree; must outlive the path object
- *   chunk   queries per call, a positive multiple of 64 (Key Contributions 2
- *           gives 2048 as the default and 4096 as the faster setting)
+ *   chunk   queries per backward call, a positive multiple of 64 (Key
+ *           Contributions 2 gives 2048 as the default and 4096 as the
+ *           faster setting)
  *   order   child visiting order: 0 = DFS (ascending token id); 1 = greedy:
  *           a node's last child is the one whose chain of last descendants
  *           is shortest (children by descending chain length, ties in DFS
@@ -362,7 +364,7 @@ typedef struct {
   int32_t n_segments;
   int32_t max_path;      /* longest root-to-leaf path in rows (max depth + 1): the stack size */
   int32_t chunk, order;
-  int64_t fwd_calls;     /* attention calls of the forward rounds */
+  int64_t fwd_calls;     /* attention calls of the forward rounds (one per round) */
   int64_t bwd_calls;     /* attention calls of the backward rounds */
   int64_t pad_rows;      /* ancestor query rows recomputed by all calls (64-alignment of a round's first call) */
   int64_t query_rows;    /* query rows all calls compute: 2 N + pad_rows */

@@ -53,18 +53,20 @@ struct __align__(16) DqStage {
 // caller's (cos, sin) table; none: no rotation) and stores it in bf16 to
 // dq_out; otherwise it stores the rotated-frame dQ in fp32 to dq_acc.
 // WIDE: K/V of 2 GiB or more (each tile's descriptors start at the tile).
+// The body of the dQ kernel for workgroup `bid` (the kernel below, or the
+// dQ part of the combined backward launch).
 template <int G, bool FIN, bool WIDE>
-__global__ __launch_bounds__(DqCfg<G>::THREADS) void dq_mfma_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const uint16_t* __restrict__ d_o, const float* __restrict__ lse, const float* __restrict__ Dv,
-    float* __restrict__ dq_acc, uint16_t* __restrict__ dq_out, const float2* __restrict__ cs_tab, PlanPtrs P,
-    AttnGeom g, int full_range, int qb_first, int n_qb, int nsub) {
+__device__ __forceinline__ void dq_body(
+    DqStage (&st)[2], const int bid, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, const uint16_t* __restrict__ d_o, const float* __restrict__ lse,
+    const float* __restrict__ Dv, float* __restrict__ dq_acc, uint16_t* __restrict__ dq_out,
+    const float2* __restrict__ cs_tab, const PlanPtrs& P, const AttnGeom& g, int full_range, int qb_first, int n_qb,
+    int nsub) {
   using C = DqCfg<G>;
-  __shared__ DqStage st[2];
   if (!plan_matches(P)) return;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r = lane & 31, hh = lane >> 5;
-  const int kvh = blockIdx.x % g.h_kv;
-  const int rest = blockIdx.x / g.h_kv;
+  const int kvh = bid % g.h_kv;
+  const int rest = bid / g.h_kv;
   const int sub = rest % nsub, idx = rest / nsub;
   const int qb = full_range ? ld_uniform(P.qb_order, idx) : (qb_first + n_qb - 1 - idx);
   const int head = (kvh * nsub + sub) * G + (wave >> 1);
@@ -252,18 +254,20 @@ struct __align__(16) KvLds {
   int32_t red[KV_WAVES];
 };
 
+// The body of the dK/dV kernel for workgroup `bid` (the kernel below, or the
+// dK/dV part of the combined backward launch).
 // G: query heads per kv head (0: any group size, read from g at run time).
 // WIDE: Q / dO of 2 GiB or more (each tile's descriptors start at the tile).
 template <int G, bool ACC, typename TG, bool WIDE>
-__global__ __launch_bounds__(KV_THREADS, 2) void dkdv_mfma_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const uint16_t* __restrict__ d_o, const float* __restrict__ lse, const float* __restrict__ Dv,
-    TG* __restrict__ d_k, TG* __restrict__ d_v, const float2* __restrict__ cs_tab, PlanPtrs P, AttnGeom g) {
-  __shared__ KvLds L;
+__device__ __forceinline__ void dkdv_body(
+    KvLds& L, const int bid, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, const uint16_t* __restrict__ d_o, const float* __restrict__ lse,
+    const float* __restrict__ Dv, TG* __restrict__ d_k, TG* __restrict__ d_v, const float2* __restrict__ cs_tab,
+    const PlanPtrs& P, const AttnGeom& g) {
   if (!plan_matches(P)) return;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r = lane & 31, hh = lane >> 5;
-  const int kvh = blockIdx.x % g.h_kv;
-  const int kb2 = blockIdx.x / g.h_kv;
+  const int kvh = bid % g.h_kv;
+  const int kb2 = bid / g.h_kv;
   const int kbase = kb2 * KV_KEYS;
   const int j = kbase + wave * 32 + r;  // this lane's key (lane column of S, dP, dK^T, dV^T)
   const bool jok = j < g.n_k;
@@ -506,6 +510,49 @@ __global__ __launch_bounds__(KV_THREADS, 2) void dkdv_mfma_kernel(
     }
 }
 
+template <int G, bool FIN, bool WIDE>
+__global__ __launch_bounds__(DqCfg<G>::THREADS) void dq_mfma_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const uint16_t* __restrict__ d_o, const float* __restrict__ lse, const float* __restrict__ Dv,
+    float* __restrict__ dq_acc, uint16_t* __restrict__ dq_out, const float2* __restrict__ cs_tab, PlanPtrs P,
+    AttnGeom g, int full_range, int qb_first, int n_qb, int nsub) {
+  __shared__ DqStage st[2];
+  dq_body<G, FIN, WIDE>(st, blockIdx.x, q, k, v, d_o, lse, Dv, dq_acc, dq_out, cs_tab, P, g, full_range, qb_first,
+                        n_qb, nsub);
+}
+
+template <int G, bool ACC, typename TG, bool WIDE>
+__global__ __launch_bounds__(KV_THREADS, 2) void dkdv_mfma_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const uint16_t* __restrict__ d_o, const float* __restrict__ lse, const float* __restrict__ Dv,
+    TG* __restrict__ d_k, TG* __restrict__ d_v, const float2* __restrict__ cs_tab, PlanPtrs P, AttnGeom g) {
+  __shared__ KvLds L;
+  dkdv_body<G, ACC, TG, WIDE>(L, blockIdx.x, q, k, v, d_o, lse, Dv, d_k, d_v, cs_tab, P, g);
+}
+
+// dQ and dK/dV in one launch: the first n_kv workgroups are the dK/dV
+// kernel's (longest first in key order), the rest the dQ kernel's (8 waves
+// each, four query heads per workgroup), so dQ workgroups fill the CUs the
+// last dK/dV workgroups leave idle.  Both read the same inputs and write
+// disjoint outputs; they share one LDS allocation.
+static_assert(sizeof(KvLds) >= 2 * sizeof(DqStage), "the dK/dV workgroups' LDS holds the dQ stages");
+static_assert(DqCfg<4>::THREADS == KV_THREADS, "the combined launch needs equal workgroup sizes");
+template <int GK, bool ACC, typename TG, bool WQ, bool FIN, bool WKV>
+__global__ __launch_bounds__(KV_THREADS, 2) void bwd_mfma_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const uint16_t* __restrict__ d_o, const float* __restrict__ lse, const float* __restrict__ Dv,
+    float* __restrict__ dq_acc, uint16_t* __restrict__ dq_out, TG* __restrict__ d_k, TG* __restrict__ d_v,
+    const float2* __restrict__ cs_tab, PlanPtrs P, AttnGeom g, int full_range, int qb_first, int n_qb, int nsub,
+    int n_kv) {
+  __shared__ __align__(16) unsigned char smem[sizeof(KvLds)];
+  const int b = blockIdx.x;
+  if (b < n_kv)
+    dkdv_body<GK, ACC, TG, WQ>(*reinterpret_cast<KvLds*>(smem), b, q, k, v, d_o, lse, Dv, d_k, d_v, cs_tab, P, g);
+  else
+    dq_body<4, FIN, WKV>(*reinterpret_cast<DqStage(*)[2]>(smem), b - n_kv, q, k, v, d_o, lse, Dv, dq_acc, dq_out,
+                         cs_tab, P, g, full_range, qb_first, n_qb, nsub);
+}
+
 template <int G>
 int launch_dq_g(const void* q, const void* k, const void* v, const void* d_o, const float* lse, const float* D_,
                 float* dq_acc, void* dq_out, const float2* cs_tab, const PlanPtrs& P, const AttnGeom& g,
@@ -552,7 +599,51 @@ int launch_dkdv_g(const void* q, const void* k, const void* v, const void* d_o, 
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
+template <int GK, bool ACC, typename TG, bool FIN>
+int launch_bwd_g(const void* q, const void* k, const void* v, const void* d_o, const float* lse, const float* D_,
+                 float* dq_acc, void* dq_out, void* d_k, void* d_v, const float2* cs_tab, const PlanPtrs& P,
+                 const AttnGeom& g, bool full_range, bool wide, hipStream_t st) {
+  const int qb_first = g.q_off / BQ;
+  const int n_qb = (g.q_off + g.n_q + BQ - 1) / BQ - qb_first;
+  const int nsub = (g.h_q / g.h_kv) / 4;
+  const int n_kv = (g.n_k + KV_KEYS - 1) / KV_KEYS * g.h_kv;
+  const int n_dq = n_qb > 0 ? n_qb * g.h_kv * nsub : 0;
+  if (n_kv + n_dq <= 0) return 0;
+  const dim3 grid(unsigned(n_kv + n_dq)), block(KV_THREADS);
+#define TT_BWD(WIDE)                                                                                              \
+  bwd_mfma_kernel<GK, ACC, TG, WIDE, FIN, WIDE><<<grid, block, 0, st>>>(                                          \
+      (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)d_o, lse, D_,                  \
+      FIN ? nullptr : dq_acc, FIN ? (uint16_t*)dq_out : nullptr, (TG*)d_k, (TG*)d_v, cs_tab, P, g,                \
+      full_range ? 1 : 0, qb_first, n_qb, nsub, n_kv)
+  if (wide)
+    TT_BWD(true);
+  else
+    TT_BWD(false);
+#undef TT_BWD
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
 }  // namespace
+
+int launch_bwd_mfma(const void* q, const void* k, const void* v, const void* d_o, const float* lse, const float* D_,
+                    float* dq_acc, void* dq_out, void* d_k, void* d_v, bool acc, const float2* cs_tab,
+                    const PlanPtrs& P, const AttnGeom& g, bool full_range, hipStream_t st) {
+  const int G = g.h_q / g.h_kv;
+  if (group_split(G) != 4) return -2;  // the dQ workgroups of smaller groups have fewer waves
+  const bool wide = int64_t(g.n_k) * g.h_kv * D * 2 >= (int64_t(1) << 31) ||
+                    int64_t(g.n_q) * g.h_q * D * 2 >= (int64_t(1) << 31);
+  const bool fin = dq_out != nullptr;
+#define TT_B(GK, ACC, TG, FIN) \
+  launch_bwd_g<GK, ACC, TG, FIN>(q, k, v, d_o, lse, D_, dq_acc, dq_out, d_k, d_v, cs_tab, P, g, full_range, wide, st)
+  if (!acc && !fin) return -2;
+  if (G == 4) {
+    if (!acc) return TT_B(4, false, uint16_t, true);
+    return fin ? TT_B(4, true, float, true) : TT_B(4, true, float, false);
+  }
+  if (!acc) return TT_B(0, false, uint16_t, true);
+  return fin ? TT_B(0, true, float, true) : TT_B(0, true, float, false);
+#undef TT_B
+}
 
 bool mfma_bwd_supported(const AttnGeom& g, const PlanPtrs& P) {
   return g.d == D && P.bq == BQ && P.bk == BK && g.h_kv > 0 && g.h_q % g.h_kv == 0;

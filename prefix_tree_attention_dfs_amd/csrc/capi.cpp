@@ -188,6 +188,20 @@ int attn_bwd_core(tt_dtype dt, const PlanPtrs& P, const AttnGeom& g, const void*
     if (launch_bwd_pre(dt, o, d_o, D, int64_t(g.n_q) * g.h_q, g.d, st)) return dev_fail(fn, "preprocess");
   }
   if (dt == TT_BF16 && mfma_bwd_supported(g, P)) {
+    // one launch for dQ and dK/dV when the dQ workgroups have the dK/dV
+    // workgroups' size (four query heads each: groups of a multiple of 4)
+    if ((g.h_q / g.h_kv) % 4 == 0 && (acc || dq_final)) {
+      int rc = -2;
+      {
+        KTimer t("attn_bwd_mfma", st);
+        rc = launch_bwd_mfma(q, k, v, d_o, lse, D, dq, dq_final, d_k, d_v, acc, cs_tab, P, g, full_range, st);
+      }
+      if (rc == -1) return dev_fail(fn, "backward kernel");
+      if (rc == 0) {
+        if (dq_final && dq_done) *dq_done = true;
+        return TT_OK;
+      }
+    }
     {
       KTimer t("attn_bwd_dq_mfma", st);
       if (launch_dq_mfma(q, k, v, d_o, lse, D, dq, dq_final, cs_tab, P, g, full_range, st))

@@ -36,6 +36,12 @@ int launch_dq_mfma(const void* q, const void* k, const void* v, const void* d_o,
 int launch_dkdv_mfma(const void* q, const void* k, const void* v, const void* d_o, const float* lse, const float* D,
                      void* d_k, void* d_v, bool acc, const float2* cs_tab, const PlanPtrs& P, const AttnGeom& g,
                      hipStream_t st);
+// dQ (as launch_dq_mfma) and dK/dV (as launch_dkdv_mfma) in one launch;
+// returns -2 (nothing launched) when the group size or output form is not
+// covered (then the two launches above apply)
+int launch_bwd_mfma(const void* q, const void* k, const void* v, const void* d_o, const float* lse, const float* D,
+                    float* dq_acc, void* dq_out, void* d_k, void* d_v, bool acc, const float2* cs_tab,
+                    const PlanPtrs& P, const AttnGeom& g, bool full_range, hipStream_t st);
 // (cos, sin) of p * theta_k, theta_k = base^(-2k / (2 half)), for p < n_pos and
 // k < half, computed in fp64 and rounded to fp32: tab[p * half + k]
 int launch_rope_table(float2* tab, int32_t n_pos, int32_t half, float base, hipStream_t st);

@@ -202,11 +202,13 @@ extern "C" int tree_attn_path(const tt_path_args* a, tt_stream stream) {
             hipMemcpyAsync(Vp + d0 * krow, v + r0 * krow, n * krow, hipMemcpyDeviceToDevice, st) != hipSuccess)
           return dev_fail(fn, "push");
       }
-      for (const auto& c : chunks(rd.p0, rd.p1, p->chunk)) {
-        const int32_t qo = c.first & ~63;
+      {
+        // one call over the whole round: the visibility rule keeps each query
+        // to the positions at or below it (only the backward is chunked)
+        const int32_t qo = rd.p0 & ~63;
         g.q_off = qo;
-        g.n_q = c.second - qo;
-        g.n_k = c.second;
+        g.n_q = rd.p1 - qo;
+        g.n_k = rd.p1;
         if ((rc = ttc::attn_fwd_core(dt, P, g, Qp + size_t(qo) * qrow, Kp, Vp, Op + size_t(qo) * qrow,
                                      LSEp + size_t(qo) * hq, false, st)))
           return rc;

@@ -113,12 +113,17 @@ extern "C" int tree_path_build(const tt_tree* t, int32_t chunk, int32_t order, t
       rd.p0 = bwd ? last.depth0 : first.depth0;
       rd.p1 = bwd ? first.depth0 + first.len : last.depth0 + last.len;
       p->rounds.push_back(rd);
-      for_chunks(rd.p0, rd.p1, chunk, [&](int32_t c0, int32_t) {
+      // a forward round is one call; a backward round runs in chunks
+      const auto count_call = [&](int32_t c0, int32_t) {
         ++(bwd ? p->bwd_calls : p->fwd_calls);
         const int64_t qo = c0 & ~63;
         p->pad_rows += c0 - qo;
         p->pad_pairs += (int64_t(c0) * (c0 + 1) - qo * (qo + 1)) / 2;  // sum over rows r in [qo, c0) of r + 1
-      });
+      };
+      if (bwd)
+        for_chunks(rd.p0, rd.p1, chunk, count_call);
+      else
+        count_call(rd.p0, rd.p1);
       e = f;
     }
     // the chain of the longest path: its plan serves every call

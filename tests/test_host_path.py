@@ -13,9 +13,10 @@ from the oracle's DFS arrays:
   length of the chain of last descendants (recomputed here from the walk
   itself), ties by first row;
 * rounds are the maximal runs of enters and of leaves, each covering the
-  stack positions of its segments; call and pad-row counts follow the chunk
-  rule over the rounds (boundaries at multiples of the chunk, each call
-  starting at the 64-aligned position at or below its first).
+  stack positions of its segments; a forward round is one call, a backward
+  round one call per chunk (boundaries at multiples of the chunk); each call
+  starts at the 64-aligned position at or below its first query, which sets
+  the pad-row counts.
 """
 import numpy as np
 import pytest
@@ -106,15 +107,15 @@ def _check(seqs, chunk, order):
         hi = max(s["depth0"][k] + s["len"][k] for k in segs)
         assert hi - lo == sum(s["len"][k] for k in segs)   # stacked one on the next
         c0 = lo
-        while c0 < hi:
+        while c0 < hi:  # a forward round is one call, a backward round one call per chunk
             calls[bwd] += 1
             pad += c0 % 64
             pad_pairs += sum(r + 1 for r in range(c0 - c0 % 64, c0))  # a pad row at position r sees r + 1 keys
-            c0 = min(hi, (c0 // chunk + 1) * chunk)
+            c0 = min(hi, (c0 // chunk + 1) * chunk) if bwd else hi
         i = j
     leaves = sum(1 for k in range(S) if k not in kids_seen)
     assert inf["fwd_calls"] == calls[False] and inf["bwd_calls"] == calls[True]
-    assert calls[False] >= leaves and calls[True] >= leaves
+    assert calls[False] == leaves and calls[True] >= leaves
     assert inf["pad_rows"] == pad and inf["query_rows"] == 2 * N + pad
     assert inf["pad_pairs"] == pad_pairs
     return p
