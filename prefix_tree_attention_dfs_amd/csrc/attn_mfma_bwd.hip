@@ -530,11 +530,12 @@ __global__ __launch_bounds__(KV_THREADS, 2) void dkdv_mfma_kernel(
   dkdv_body<G, ACC, TG, WIDE>(L, blockIdx.x, q, k, v, d_o, lse, Dv, d_k, d_v, cs_tab, P, g);
 }
 
-// dQ and dK/dV in one launch: the first n_kv workgroups are the dK/dV
-// kernel's (longest first in key order), the rest the dQ kernel's (8 waves
-// each, four query heads per workgroup), so dQ workgroups fill the CUs the
-// last dK/dV workgroups leave idle.  Both read the same inputs and write
-// disjoint outputs; they share one LDS allocation.
+// dQ and dK/dV in one launch: the kernel whose longest workgroup is longer
+// goes first (dK/dV in tree mode, where a shared root's keys walk every
+// query; dQ for a short chunk of queries against a long prefix), the other's
+// workgroups (8 waves each, four query heads per dQ workgroup) fill the CUs
+// the first leaves idle.  Both read the same inputs and write disjoint
+// outputs; they share one LDS allocation.
 static_assert(sizeof(KvLds) >= 2 * sizeof(DqStage), "the dK/dV workgroups' LDS holds the dQ stages");
 static_assert(DqCfg<4>::THREADS == KV_THREADS, "the combined launch needs equal workgroup sizes");
 template <int GK, bool ACC, typename TG, bool WQ, bool FIN, bool WKV>
@@ -543,14 +544,16 @@ __global__ __launch_bounds__(KV_THREADS, 2) void bwd_mfma_kernel(
     const uint16_t* __restrict__ d_o, const float* __restrict__ lse, const float* __restrict__ Dv,
     float* __restrict__ dq_acc, uint16_t* __restrict__ dq_out, TG* __restrict__ d_k, TG* __restrict__ d_v,
     const float2* __restrict__ cs_tab, PlanPtrs P, AttnGeom g, int full_range, int qb_first, int n_qb, int nsub,
-    int n_kv) {
+    int n_kv, int n_dq, int dq_first) {
   __shared__ __align__(16) unsigned char smem[sizeof(KvLds)];
   const int b = blockIdx.x;
-  if (b < n_kv)
-    dkdv_body<GK, ACC, TG, WQ>(*reinterpret_cast<KvLds*>(smem), b, q, k, v, d_o, lse, Dv, d_k, d_v, cs_tab, P, g);
+  const bool kv = dq_first ? b >= n_dq : b < n_kv;
+  if (kv)
+    dkdv_body<GK, ACC, TG, WQ>(*reinterpret_cast<KvLds*>(smem), dq_first ? b - n_dq : b, q, k, v, d_o, lse, Dv,
+                               d_k, d_v, cs_tab, P, g);
   else
-    dq_body<4, FIN, WKV>(*reinterpret_cast<DqStage(*)[2]>(smem), b - n_kv, q, k, v, d_o, lse, Dv, dq_acc, dq_out,
-                         cs_tab, P, g, full_range, qb_first, n_qb, nsub);
+    dq_body<4, FIN, WKV>(*reinterpret_cast<DqStage(*)[2]>(smem), dq_first ? b : b - n_kv, q, k, v, d_o, lse, Dv,
+                         dq_acc, dq_out, cs_tab, P, g, full_range, qb_first, n_qb, nsub);
 }
 
 template <int G>
@@ -609,12 +612,16 @@ int launch_bwd_g(const void* q, const void* k, const void* v, const void* d_o, c
   const int n_kv = (g.n_k + KV_KEYS - 1) / KV_KEYS * g.h_kv;
   const int n_dq = n_qb > 0 ? n_qb * g.h_kv * nsub : 0;
   if (n_kv + n_dq <= 0) return 0;
+  // longest workgroup of each: a dK/dV one walks up to n_q query rows x G
+  // heads (64 MFMAs per wave per 64 rows), a dQ one up to n_k keys (48 MFMAs
+  // per wave per 64 keys)
+  const int dq_first = 3 * int64_t(g.n_k) > 4 * int64_t(g.n_q) * (g.h_q / g.h_kv) ? 1 : 0;
   const dim3 grid(unsigned(n_kv + n_dq)), block(KV_THREADS);
 #define TT_BWD(WIDE)                                                                                              \
   bwd_mfma_kernel<GK, ACC, TG, WIDE, FIN, WIDE><<<grid, block, 0, st>>>(                                          \
       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)d_o, lse, D_,                  \
       FIN ? nullptr : dq_acc, FIN ? (uint16_t*)dq_out : nullptr, (TG*)d_k, (TG*)d_v, cs_tab, P, g,                \
-      full_range ? 1 : 0, qb_first, n_qb, nsub, n_kv)
+      full_range ? 1 : 0, qb_first, n_qb, nsub, n_kv, n_dq, dq_first)
   if (wide)
     TT_BWD(true);
   else

@@ -31,6 +31,7 @@ struct PathWs {
   size_t qp = 0, kp = 0, vp = 0, op = 0, lsep = 0;  // stack of max_path positions
   size_t dka = 0, dva = 0;                                   // float32 dK, dV accumulators (backward)
   size_t doc = 0, D = 0, dq = 0;                             // per-call buffers, chunk + 64 rows
+  size_t dqs = 0, cs = 0;  // matrix-core path: per-call bf16 dQ (rotated back) and the (cos, sin) table
   size_t total = 0;
 };
 
@@ -56,6 +57,10 @@ PathWs path_ws(const tt_path_args* a, bool bwd) {
     w.doc = take(C * hq * d * es);
     w.D = take(C * hq * 4);
     w.dq = take(C * hq * d * 4);
+    if (a->dtype == TT_BF16 && ttc::mfma_shape(a->d, 64, 64)) {
+      w.dqs = take(C * hq * d * 2);
+      w.cs = take(L * (d / 2) * 8);
+    }
   }
   w.total = off;
   return w;
@@ -183,6 +188,15 @@ extern "C" int tree_attn_path(const tt_path_args* a, tt_stream stream) {
         launch_fill_zero(dVa, size_t(p->max_path) * hk * d * 4, st))
       return dev_fail(fn, "clear");
   }
+  // matrix-core path: the dQ and dK/dV epilogues rotate back at the stack
+  // position (= depth) with this table (dQ stored as bf16 rows of the call)
+  char* dqs = bwd && w.dqs ? ws + w.dqs : nullptr;
+  float2* cs_tab = nullptr;
+  if (dqs && rb != 0.f) {
+    cs_tab = reinterpret_cast<float2*>(ws + w.cs);
+    KTimer t("rope_table", st);
+    if (launch_rope_table(cs_tab, p->max_path, a->d / 2, rb, st)) return dev_fail(fn, "rope table");
+  }
   // the segments of a round and the part of [c0, c1) each one holds
   const auto seg_of = [&](const tt_path::Round& rd, int32_t i) -> const tt_path::Seg& {
     return p->segs[size_t(rd.bwd ? -1 - p->events[size_t(i)] : p->events[size_t(i)])];
@@ -244,17 +258,24 @@ extern "C" int tree_attn_path(const tt_path_args* a, tt_stream stream) {
         g.q_off = qo;
         g.n_q = c1 - qo;
         g.n_k = c1;
+        bool dq_done = false;
         if ((rc = ttc::attn_bwd_core(dt, P, g, Qp + size_t(qo) * qrow, Kp, Vp, Op + size_t(qo) * qrow, dOc,
-                                     LSEp + size_t(qo) * hq, D, dq, dKa, dVa, true, false, nullptr, st)))
+                                     LSEp + size_t(qo) * hq, D, dq, dKa, dVa, true, false, cs_tab, st, dqs,
+                                     &dq_done)))
           return rc;
+        // dQ rows of the chunk to their tree rows, segment by segment: copied
+        // from the bf16 block the kernel rotated back, or rotated back here
+        // from the fp32 block (vector kernels)
         KTimer t("dq_finalize", st);
         for (int32_t i = rd.ev0; i < rd.ev1; ++i) {
           const tt_path::Seg& s = seg_of(rd, i);
           const int32_t lo = std::max(c0, s.depth0), hi = std::min(c1, s.depth0 + s.len);
           if (lo >= hi) continue;
           const size_t row = size_t(s.row0) + size_t(lo - s.depth0);
-          if (launch_rope(dq + size_t(lo - qo) * hq * d, d_q + row * qrow, TT_F32, dt, false, P, lo, hi - lo, a->h_q,
-                          a->d, rb, true, st))
+          if (dq_done ? hipMemcpyAsync(d_q + row * qrow, dqs + size_t(lo - qo) * qrow, size_t(hi - lo) * qrow,
+                                       hipMemcpyDeviceToDevice, st) != hipSuccess
+                      : launch_rope(dq + size_t(lo - qo) * hq * d, d_q + row * qrow, TT_F32, dt, false, P, lo, hi - lo,
+                                    a->h_q, a->d, rb, true, st) != 0)
             return dev_fail(fn, "dq finalize");
         }
       }
@@ -262,8 +283,11 @@ extern "C" int tree_attn_path(const tt_path_args* a, tt_stream stream) {
         const tt_path::Seg& s = seg_of(rd, i);
         const size_t r0 = size_t(s.row0), n = size_t(s.len), d0 = size_t(s.depth0);
         KTimer t("path_pop", st);
+        // with the table, the matrix-core dK/dV kernel already rotated each
+        // contribution back at the key's depth (rotation is linear, so the
+        // sums are in the output frame): convert only
         if (launch_rope(dKa + d0 * hk * d, d_k + r0 * krow, TT_F32, dt, false, P, s.depth0, s.len, a->h_kv, a->d,
-                        rb, true, st) ||
+                        cs_tab ? 0.f : rb, true, st) ||
             launch_rope(dVa + d0 * hk * d, d_v + r0 * krow, TT_F32, dt, false, P, s.depth0, s.len, a->h_kv, a->d,
                         0.f, false, st) ||
             launch_fill_zero(dKa + d0 * hk * d, n * hk * d * 4, st) ||
