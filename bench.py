@@ -31,8 +31,8 @@ METRIC = "tree attn fwd+bwd unique tokens/s + useful TFLOP/s (% bf16 MFMA peak),
 # HBM traffic of the roofline kernel from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE
 # runs (scaled by the same counters' reading for a plain copy of known size),
 # valid only for the kernel source it was measured on.
-MEASURED_TRAFFIC = {"kernel": "attn_bwd_dkdv_mfma", "source_sha1": "688487a3834ffe96edf0083b24ec9ddbda66a55c",
-                    "bytes_per_launch": 13942111250}
+MEASURED_TRAFFIC = {"kernel": "attn_bwd_mfma", "source_sha1": "56c62fd85bef18544cc881cc5585f2d5ea4357af",
+                    "bytes_per_launch": 39265645511}
 
 
 def _source_sha(path):
