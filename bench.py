@@ -138,6 +138,17 @@ def secondary(tt, ts, steps):
                                      ms=round(ms, 4), tokens_per_s=round(tree.N / ms * 1e3),
                                      useful_tflops=round(fl / ms / 1e9, 1),
                                      pct_bf16_peak=round(fl / ms / 1e9 / PEAK_BF16_TFLOPS * 100, 2))
+
+    def fwd_bwd():
+        st.fwd()
+        st.bwd()
+
+    # the same forest through forward + backward (not part of the forward-only
+    # configuration; the GQA-2 backward runs as separate dQ and dK/dV launches)
+    ms2 = _time(fwd_bwd, steps, 2)
+    fl2 = 14 * d * 16 * tree.info["pairs"]
+    out["rl_forest_1p7b_fwd_bwd"] = dict(ms=round(ms2, 4), useful_tflops=round(fl2 / ms2 / 1e9, 1),
+                                         pct_bf16_peak=round(fl2 / ms2 / 1e9 / PEAK_BF16_TFLOPS * 100, 2))
     del st, q, k, v, do
     # path mode: 49,152-token chain, 16k suffix in 2048-token chunks right to left against a 32k prefix
     case = ts.long_chain(0)

@@ -525,6 +525,43 @@ int launch_dkdv_generic(tt_dtype dt, bool acc, const void* q, const void* k, con
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
+// ---------------------------------------------------------------- accumulator pop
+// dK (y = 0) and dV (y = 1) rows leaving the path stack: the sum of nslot
+// fp32 accumulators (slot u at acc + u * slot_stride), rounded to bf16; the
+// accumulators' rows are cleared for the next segment at these positions.
+__global__ __launch_bounds__(256) void acc_pop_kernel(float* __restrict__ acc_k, float* __restrict__ acc_v,
+                                                      int64_t slot_stride, int nslot, uint16_t* __restrict__ out_k,
+                                                      uint16_t* __restrict__ out_v, int64_t n4) {
+  float* a = blockIdx.y ? acc_v : acc_k;
+  uint2* o = reinterpret_cast<uint2*>(blockIdx.y ? out_v : out_k);
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n4; i += int64_t(gridDim.x) * blockDim.x) {
+    float4 t = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int u = 0; u < nslot; ++u) {
+      float4* p = reinterpret_cast<float4*>(a + u * slot_stride) + i;
+      const float4 x = *p;
+      t.x += x.x;
+      t.y += x.y;
+      t.z += x.z;
+      t.w += x.w;
+      *p = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    o[i] = make_uint2(uint32_t(f2bf(t.x)) | (uint32_t(f2bf(t.y)) << 16),
+                      uint32_t(f2bf(t.z)) | (uint32_t(f2bf(t.w)) << 16));
+  }
+}
+
+int launch_acc_pop(float* acc_k, float* acc_v, int64_t slot_stride, int nslot, void* out_k, void* out_v, int64_t n,
+                   hipStream_t st) {
+  if (n <= 0) return 0;
+  if (n % 4 != 0 || slot_stride % 4 != 0 || nslot < 1) return -1;
+  const int64_t n4 = n / 4;
+  const int64_t blocks = std::min<int64_t>((n4 + 255) / 256, 2048);
+  acc_pop_kernel<<<dim3(unsigned(blocks), 2), dim3(256), 0, st>>>(acc_k, acc_v, slot_stride, nslot,
+                                                                   static_cast<uint16_t*>(out_k),
+                                                                   static_cast<uint16_t*>(out_v), n4);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
 // ---------------------------------------------------------------- fill
 // Zeroes a device buffer (bytes a multiple of 4) with plain vector stores, so
 // that code a caller may capture into a graph records no memset node.

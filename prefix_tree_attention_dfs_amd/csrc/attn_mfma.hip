@@ -32,7 +32,9 @@ struct FwdCfg {
   static constexpr int THREADS = WAVES * 64;
   static constexpr int CH = (BK * D / 8) / THREADS;      // 16-byte chunks per thread per K (or V) tile
   static constexpr int WPH = 2 / NT;                     // waves per head
-  static constexpr int MINB = WAVES >= 8 ? 1 : 8 / WAVES;  // workgroups per CU for two waves per SIMD
+  // waves per SIMD the register budget is set for: two, except at G = 1, where
+  // the LDS (two 33 KB stages per 2-wave workgroup) holds one wave per SIMD
+  static constexpr int MINB = G >= 2 ? 2 : 1;
 };
 
 struct __align__(16) FwdStage {

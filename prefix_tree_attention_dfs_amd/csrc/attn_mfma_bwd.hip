@@ -23,6 +23,8 @@
 //                    dV^T += dO^T P, dK^T += Q^T dS.
 // Recomputing S and dP in both kernels costs 14 d MFMA flops per visible pair
 // instead of 10 d, in exchange for no fp32 atomic traffic on dQ.
+#include <algorithm>
+
 #include "device.h"
 #include "kernels.h"
 #include "mfma_common.h"
@@ -510,8 +512,10 @@ __device__ __forceinline__ void dkdv_body(
     }
 }
 
+// two waves per SIMD, except at G = 1, where the LDS stages of 2-wave
+// workgroups hold one
 template <int G, bool FIN, bool WIDE>
-__global__ __launch_bounds__(DqCfg<G>::THREADS) void dq_mfma_kernel(
+__global__ __launch_bounds__(DqCfg<G>::THREADS, G >= 2 ? 2 : 1) void dq_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ d_o, const float* __restrict__ lse, const float* __restrict__ Dv,
     float* __restrict__ dq_acc, uint16_t* __restrict__ dq_out, const float2* __restrict__ cs_tab, PlanPtrs P,
@@ -530,14 +534,38 @@ __global__ __launch_bounds__(KV_THREADS, 2) void dkdv_mfma_kernel(
   dkdv_body<G, ACC, TG, WIDE>(L, blockIdx.x, q, k, v, d_o, lse, Dv, d_k, d_v, cs_tab, P, g);
 }
 
-// dQ and dK/dV in one launch: the kernel whose longest workgroup is longer
-// goes first (dK/dV in tree mode, where a shared root's keys walk every
-// query; dQ for a short chunk of queries against a long prefix), the other's
-// workgroups (8 waves each, four query heads per dQ workgroup) fill the CUs
-// the first leaves idle.  Both read the same inputs and write disjoint
-// outputs; they share one LDS allocation.
+// dQ and dK/dV in one launch, for one backward call or several independent
+// ones (each with its own query rows, dQ output and dK/dV accumulators; they
+// share K, V and the plan).  The grid is a list of segments, each the dQ or
+// the dK/dV workgroups of one call, ordered so that the segments with the
+// longest workgroups go first (dK/dV in tree mode, where a shared root's keys
+// walk every query; dQ for a short chunk of queries against a long prefix);
+// the rest fill the CUs the first leave idle.  Every workgroup has 8 waves
+// (four query heads per dQ workgroup); the two kinds share one LDS
+// allocation.
 static_assert(sizeof(KvLds) >= 2 * sizeof(DqStage), "the dK/dV workgroups' LDS holds the dQ stages");
 static_assert(DqCfg<4>::THREADS == KV_THREADS, "the combined launch needs equal workgroup sizes");
+
+struct BwdCall {
+  const uint16_t* q;
+  const uint16_t* d_o;
+  const float* lse;
+  const float* Dv;
+  float* dq_acc;
+  uint16_t* dq_out;
+  void* d_k;
+  void* d_v;
+  AttnGeom g;
+  int32_t qb_first, n_qb;
+};
+struct BwdGrid {
+  BwdCall c[kMaxBwdCalls];
+  int32_t b0[2 * kMaxBwdCalls + 1];  // segment s holds workgroups [b0[s], b0[s + 1])
+  int32_t what[2 * kMaxBwdCalls];    // 2 * call + (1: dK/dV, 0: dQ)
+  int32_t n_seg;
+};
+
+// One call: the segment order reduces to which kind goes first.
 template <int GK, bool ACC, typename TG, bool WQ, bool FIN, bool WKV>
 __global__ __launch_bounds__(KV_THREADS, 2) void bwd_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
@@ -554,6 +582,27 @@ __global__ __launch_bounds__(KV_THREADS, 2) void bwd_mfma_kernel(
   else
     dq_body<4, FIN, WKV>(*reinterpret_cast<DqStage(*)[2]>(smem), dq_first ? b : b - n_kv, q, k, v, d_o, lse, Dv,
                          dq_acc, dq_out, cs_tab, P, g, full_range, qb_first, n_qb, nsub);
+}
+
+// Several calls (a separate kernel: the per-call selection costs the
+// one-call case registers and about 1% of its time).
+template <int GK, bool ACC, typename TG, bool WQ, bool FIN, bool WKV>
+__global__ __launch_bounds__(KV_THREADS, 2) void bwd_multi_mfma_kernel(const uint16_t* __restrict__ k,
+                                                                 const uint16_t* __restrict__ v,
+                                                                 const float2* __restrict__ cs_tab, PlanPtrs P,
+                                                                 int full_range, int nsub, BwdGrid G) {
+  __shared__ __align__(16) unsigned char smem[sizeof(KvLds)];
+  const int b = blockIdx.x;
+  int s = 0;
+  for (int i = 1; i < G.n_seg; ++i) s += b >= G.b0[i] ? 1 : 0;
+  const BwdCall& c = G.c[G.what[s] >> 1];
+  const int lb = b - G.b0[s];
+  if (G.what[s] & 1)
+    dkdv_body<GK, ACC, TG, WQ>(*reinterpret_cast<KvLds*>(smem), lb, c.q, k, v, c.d_o, c.lse, c.Dv,
+                               static_cast<TG*>(c.d_k), static_cast<TG*>(c.d_v), cs_tab, P, c.g);
+  else
+    dq_body<4, FIN, WKV>(*reinterpret_cast<DqStage(*)[2]>(smem), lb, c.q, k, v, c.d_o, c.lse, c.Dv, c.dq_acc,
+                         c.dq_out, cs_tab, P, c.g, full_range, c.qb_first, c.n_qb, nsub);
 }
 
 template <int G>
@@ -603,46 +652,94 @@ int launch_dkdv_g(const void* q, const void* k, const void* v, const void* d_o, 
 }
 
 template <int GK, bool ACC, typename TG, bool FIN>
-int launch_bwd_g(const void* q, const void* k, const void* v, const void* d_o, const float* lse, const float* D_,
-                 float* dq_acc, void* dq_out, void* d_k, void* d_v, const float2* cs_tab, const PlanPtrs& P,
-                 const AttnGeom& g, bool full_range, bool wide, hipStream_t st) {
-  const int qb_first = g.q_off / BQ;
-  const int n_qb = (g.q_off + g.n_q + BQ - 1) / BQ - qb_first;
-  const int nsub = (g.h_q / g.h_kv) / 4;
-  const int n_kv = (g.n_k + KV_KEYS - 1) / KV_KEYS * g.h_kv;
-  const int n_dq = n_qb > 0 ? n_qb * g.h_kv * nsub : 0;
-  if (n_kv + n_dq <= 0) return 0;
-  // longest workgroup of each: a dK/dV one walks up to n_q query rows x G
-  // heads (64 MFMAs per wave per 64 rows), a dQ one up to n_k keys (48 MFMAs
-  // per wave per 64 keys)
-  const int dq_first = 3 * int64_t(g.n_k) > 4 * int64_t(g.n_q) * (g.h_q / g.h_kv) ? 1 : 0;
-  const dim3 grid(unsigned(n_kv + n_dq)), block(KV_THREADS);
-#define TT_BWD(WIDE)                                                                                              \
-  bwd_mfma_kernel<GK, ACC, TG, WIDE, FIN, WIDE><<<grid, block, 0, st>>>(                                          \
-      (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)d_o, lse, D_,                  \
-      FIN ? nullptr : dq_acc, FIN ? (uint16_t*)dq_out : nullptr, (TG*)d_k, (TG*)d_v, cs_tab, P, g,                \
-      full_range ? 1 : 0, qb_first, n_qb, nsub, n_kv, n_dq, dq_first)
-  if (wide)
-    TT_BWD(true);
-  else
-    TT_BWD(false);
+int launch_bwd_g(const BwdCallPtrs* calls, int n_calls, const void* k, const void* v, const float2* cs_tab,
+                 const PlanPtrs& P, bool full_range, bool wide, hipStream_t st) {
+  BwdGrid G{};
+  struct Seg {
+    int64_t len;  // longest workgroup of the segment, in MFMAs per wave / 16
+    int32_t what, count;
+  } seg[2 * kMaxBwdCalls];
+  int ns = 0;
+  const int nsub = (calls[0].g.h_q / calls[0].g.h_kv) / 4;
+  for (int i = 0; i < n_calls; ++i) {
+    const AttnGeom& g = calls[i].g;
+    BwdCall& c = G.c[i];
+    c.q = static_cast<const uint16_t*>(calls[i].q);
+    c.d_o = static_cast<const uint16_t*>(calls[i].d_o);
+    c.lse = calls[i].lse;
+    c.Dv = calls[i].D;
+    c.dq_acc = FIN ? nullptr : calls[i].dq_acc;
+    c.dq_out = FIN ? static_cast<uint16_t*>(calls[i].dq_out) : nullptr;
+    c.d_k = calls[i].d_k;
+    c.d_v = calls[i].d_v;
+    c.g = g;
+    c.qb_first = g.q_off / BQ;
+    c.n_qb = (g.q_off + g.n_q + BQ - 1) / BQ - c.qb_first;
+    const int n_kv = (g.n_k + KV_KEYS - 1) / KV_KEYS * g.h_kv;
+    const int n_dq = c.n_qb > 0 ? c.n_qb * g.h_kv * nsub : 0;
+    // a dK/dV workgroup walks up to n_q query rows x the group's heads (64
+    // MFMAs per wave per 64 rows and head), a dQ one up to n_k keys (48 MFMAs
+    // per wave per 64 keys); dK/dV is listed first, so it leads on a tie
+    if (n_kv > 0) seg[ns++] = {4 * int64_t(g.n_q) * (g.h_q / g.h_kv), 2 * i + 1, n_kv};
+    if (n_dq > 0) seg[ns++] = {3 * int64_t(g.n_k), 2 * i, n_dq};
+  }
+  std::stable_sort(seg, seg + ns, [](const Seg& x, const Seg& y) { return x.len > y.len; });
+  int64_t nb = 0;
+  for (int s = 0; s < ns; ++s) {
+    G.b0[s] = int32_t(nb);
+    G.what[s] = seg[s].what;
+    nb += seg[s].count;
+  }
+  G.b0[ns] = int32_t(nb);
+  G.n_seg = ns;
+  if (nb <= 0) return 0;
+  if (nb >= (int64_t(1) << 31)) return -1;
+  const dim3 grid(static_cast<unsigned>(nb)), block(KV_THREADS);
+  if (n_calls == 1) {
+    const BwdCall& c = G.c[0];
+    const int n_kv = (c.g.n_k + KV_KEYS - 1) / KV_KEYS * c.g.h_kv;
+    const int n_dq = int(nb) - n_kv, dq_first = ns > 0 && (G.what[0] & 1) == 0 ? 1 : 0;
+#define TT_BWD(WIDE)                                                                                          \
+  bwd_mfma_kernel<GK, ACC, TG, WIDE, FIN, WIDE><<<grid, block, 0, st>>>(                                      \
+      c.q, static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), c.d_o, c.lse, c.Dv, c.dq_acc,     \
+      c.dq_out, static_cast<TG*>(c.d_k), static_cast<TG*>(c.d_v), cs_tab, P, c.g, full_range ? 1 : 0,          \
+      c.qb_first, c.n_qb, nsub, n_kv, n_dq, dq_first)
+    if (wide)
+      TT_BWD(true);
+    else
+      TT_BWD(false);
 #undef TT_BWD
+  } else {
+#define TT_BWD(WIDE)                                                                          \
+  bwd_multi_mfma_kernel<GK, ACC, TG, WIDE, FIN, WIDE><<<grid, block, 0, st>>>(                \
+      static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), cs_tab, P, full_range ? 1 : 0, nsub, G)
+    if (wide)
+      TT_BWD(true);
+    else
+      TT_BWD(false);
+#undef TT_BWD
+  }
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 }  // namespace
 
-int launch_bwd_mfma(const void* q, const void* k, const void* v, const void* d_o, const float* lse, const float* D_,
-                    float* dq_acc, void* dq_out, void* d_k, void* d_v, bool acc, const float2* cs_tab,
-                    const PlanPtrs& P, const AttnGeom& g, bool full_range, hipStream_t st) {
-  const int G = g.h_q / g.h_kv;
+int launch_bwd_mfma_multi(const BwdCallPtrs* calls, int n_calls, const void* k, const void* v, bool acc,
+                          const float2* cs_tab, const PlanPtrs& P, bool full_range, hipStream_t st) {
+  if (n_calls < 1 || n_calls > kMaxBwdCalls) return -1;
+  const AttnGeom& g0 = calls[0].g;
+  const int G = g0.h_q / g0.h_kv;
   if (group_split(G) != 4) return -2;  // the dQ workgroups of smaller groups have fewer waves
-  const bool wide = int64_t(g.n_k) * g.h_kv * D * 2 >= (int64_t(1) << 31) ||
-                    int64_t(g.n_q) * g.h_q * D * 2 >= (int64_t(1) << 31);
-  const bool fin = dq_out != nullptr;
-#define TT_B(GK, ACC, TG, FIN) \
-  launch_bwd_g<GK, ACC, TG, FIN>(q, k, v, d_o, lse, D_, dq_acc, dq_out, d_k, d_v, cs_tab, P, g, full_range, wide, st)
+  const bool fin = calls[0].dq_out != nullptr;
   if (!acc && !fin) return -2;
+  bool wide = false;
+  for (int i = 0; i < n_calls; ++i) {
+    const AttnGeom& g = calls[i].g;
+    if (g.h_q != g0.h_q || g.h_kv != g0.h_kv || g.d != g0.d || (calls[i].dq_out != nullptr) != fin) return -1;
+    wide = wide || int64_t(g.n_k) * g.h_kv * D * 2 >= (int64_t(1) << 31) ||
+           int64_t(g.n_q) * g.h_q * D * 2 >= (int64_t(1) << 31);
+  }
+#define TT_B(GK, ACC, TG, FIN) launch_bwd_g<GK, ACC, TG, FIN>(calls, n_calls, k, v, cs_tab, P, full_range, wide, st)
   if (G == 4) {
     if (!acc) return TT_B(4, false, uint16_t, true);
     return fin ? TT_B(4, true, float, true) : TT_B(4, true, float, false);
@@ -650,6 +747,13 @@ int launch_bwd_mfma(const void* q, const void* k, const void* v, const void* d_o
   if (!acc) return TT_B(0, false, uint16_t, true);
   return fin ? TT_B(0, true, float, true) : TT_B(0, true, float, false);
 #undef TT_B
+}
+
+int launch_bwd_mfma(const void* q, const void* k, const void* v, const void* d_o, const float* lse, const float* D_,
+                    float* dq_acc, void* dq_out, void* d_k, void* d_v, bool acc, const float2* cs_tab,
+                    const PlanPtrs& P, const AttnGeom& g, bool full_range, hipStream_t st) {
+  const BwdCallPtrs c{q, d_o, lse, D_, dq_acc, dq_out, d_k, d_v, g};
+  return launch_bwd_mfma_multi(&c, 1, k, v, acc, cs_tab, P, full_range, st);
 }
 
 bool mfma_bwd_supported(const AttnGeom& g, const PlanPtrs& P) {

@@ -42,9 +42,35 @@ int launch_dkdv_mfma(const void* q, const void* k, const void* v, const void* d_
 int launch_bwd_mfma(const void* q, const void* k, const void* v, const void* d_o, const float* lse, const float* D,
                     float* dq_acc, void* dq_out, void* d_k, void* d_v, bool acc, const float2* cs_tab,
                     const PlanPtrs& P, const AttnGeom& g, bool full_range, hipStream_t st);
+// Several independent backward calls in one launch (as launch_bwd_mfma for
+// each): every call has its own query rows (q, d_o, lse and D at the call's
+// first row, g.q_off / n_q / n_k its geometry), dQ output and dK/dV outputs,
+// and all share k, v, cs_tab and the plan, the head counts and the output
+// form (acc, and dq_out set or not).  Calls may run in any order and side by
+// side, so no two may write the same output.  Returns -2 as launch_bwd_mfma.
+constexpr int kMaxBwdCalls = 4;
+struct BwdCallPtrs {
+  const void* q;
+  const void* d_o;
+  const float* lse;
+  const float* D;
+  float* dq_acc;
+  void* dq_out;
+  void* d_k;
+  void* d_v;
+  AttnGeom g;
+};
+int launch_bwd_mfma_multi(const BwdCallPtrs* calls, int n_calls, const void* k, const void* v, bool acc,
+                          const float2* cs_tab, const PlanPtrs& P, bool full_range, hipStream_t st);
 // (cos, sin) of p * theta_k, theta_k = base^(-2k / (2 half)), for p < n_pos and
 // k < half, computed in fp64 and rounded to fp32: tab[p * half + k]
 int launch_rope_table(float2* tab, int32_t n_pos, int32_t half, float base, hipStream_t st);
+
+// bf16 out_k / out_v (n elements each, a multiple of 4) = the sum of nslot
+// fp32 accumulators (slot u at acc + u * slot_stride elements); the
+// accumulators' n elements are zeroed.
+int launch_acc_pop(float* acc_k, float* acc_v, int64_t slot_stride, int nslot, void* out_k, void* out_v, int64_t n,
+                   hipStream_t st);
 
 // Zeroes `bytes` (a multiple of 4) at p.
 int launch_fill_zero(void* p, size_t bytes, hipStream_t st);

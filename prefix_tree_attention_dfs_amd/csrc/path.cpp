@@ -26,12 +26,20 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 size_t dsize(tt_dtype t) { return t == TT_F32 ? 4 : 2; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Backward chunk calls per launch on the matrix-core path: the calls of a
+// launch run side by side (each with its own dO copy, D, dQ block and dK/dV
+// accumulators), so one launch's grid holds the workgroups of several chunks.
+constexpr int kPathCalls = 2;
+
 // Workspace carve-up, identical for the size query and the call.
 struct PathWs {
   size_t qp = 0, kp = 0, vp = 0, op = 0, lsep = 0;  // stack of max_path positions
-  size_t dka = 0, dva = 0;                                   // float32 dK, dV accumulators (backward)
-  size_t doc = 0, D = 0, dq = 0;                             // per-call buffers, chunk + 64 rows
-  size_t dqs = 0, cs = 0;  // matrix-core path: per-call bf16 dQ (rotated back) and the (cos, sin) table
+  size_t dka = 0, dva = 0;  // float32 dK, dV accumulators (backward), `slots` of max_path rows each
+  size_t doc = 0, D = 0;    // per-call buffers, chunk + 64 rows, `slots` of each
+  size_t dq = 0;            // float32 dQ of one call (vector kernels)
+  size_t dqs = 0, cs = 0;   // matrix-core path: per-call bf16 dQ (rotated back, `slots`) and the (cos, sin) table
+  int slots = 1;            // chunk calls per backward launch
+  size_t acc_slot = 0, doc_slot = 0, D_slot = 0, dqs_slot = 0;  // bytes per slot
   size_t total = 0;
 };
 
@@ -39,7 +47,16 @@ PathWs path_ws(const tt_path_args* a, bool bwd) {
   const tt_path* p = a->path;
   const size_t L = size_t(p->max_path), C = size_t(p->chunk) + 64, es = dsize(a->dtype);
   const size_t hq = size_t(a->h_q), hk = size_t(a->h_kv), d = size_t(a->d);
+  const bool mfma = a->dtype == TT_BF16 && ttc::mfma_shape(a->d, 64, 64);
   PathWs w;
+  // several calls per launch where the combined matrix-core launch exists
+  // (the dQ workgroups take four query heads: groups of a multiple of 4)
+  w.slots = mfma && (a->h_q / a->h_kv) % 4 == 0 ? kPathCalls : 1;
+  const size_t S = size_t(w.slots);
+  w.acc_slot = align_up(L * hk * d * 4);
+  w.doc_slot = align_up(C * hq * d * es);
+  w.D_slot = align_up(C * hq * 4);
+  w.dqs_slot = align_up(C * hq * d * 2);
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t o = off;
@@ -52,13 +69,13 @@ PathWs path_ws(const tt_path_args* a, bool bwd) {
   w.op = take(L * hq * d * es);
   w.lsep = take(L * hq * 4);
   if (bwd) {
-    w.dka = take(L * hk * d * 4);
-    w.dva = take(L * hk * d * 4);
-    w.doc = take(C * hq * d * es);
-    w.D = take(C * hq * 4);
+    w.dka = take(S * w.acc_slot);
+    w.dva = take(S * w.acc_slot);
+    w.doc = take(S * w.doc_slot);
+    w.D = take(S * w.D_slot);
     w.dq = take(C * hq * d * 4);
-    if (a->dtype == TT_BF16 && ttc::mfma_shape(a->d, 64, 64)) {
-      w.dqs = take(C * hq * d * 2);
+    if (mfma) {
+      w.dqs = take(S * w.dqs_slot);
       w.cs = take(L * (d / 2) * 8);
     }
   }
@@ -184,8 +201,8 @@ extern "C" int tree_attn_path(const tt_path_args* a, tt_stream stream) {
 
   if (bwd) {
     KTimer t("path_clear", st);
-    if (launch_fill_zero(dKa, size_t(p->max_path) * hk * d * 4, st) ||
-        launch_fill_zero(dVa, size_t(p->max_path) * hk * d * 4, st))
+    if (launch_fill_zero(dKa, size_t(w.slots) * w.acc_slot, st) ||
+        launch_fill_zero(dVa, size_t(w.slots) * w.acc_slot, st))
       return dev_fail(fn, "clear");
   }
   // matrix-core path: the dQ and dK/dV epilogues rotate back at the stack
@@ -237,52 +254,90 @@ extern "C" int tree_attn_path(const tt_path_args* a, tt_stream stream) {
       }
     } else if (bwd) {
       // leave: one backward over the round's positions, chunks right to left
-      // (every descendant's gradient has arrived), then pop each segment
+      // (every descendant's gradient has arrived), then pop each segment.
+      // With several slots, consecutive chunks share a launch, each adding
+      // into its own accumulators (no two writers per key); the pops sum them.
       const auto cs = chunks(rd.p0, rd.p1, p->chunk);
-      for (auto it = cs.rbegin(); it != cs.rend(); ++it) {
-        const int32_t c0 = it->first, c1 = it->second, qo = c0 & ~63;
-        const size_t pad = size_t(c0 - qo);
-        {
-          KTimer t("path_dout", st);
-          if (launch_fill_zero(dOc, pad * qrow, st)) return dev_fail(fn, "upstream gradient");
+      const size_t nch = cs.size(), S = size_t(w.slots);
+      for (size_t i0 = 0; i0 < nch; i0 += S) {
+        const size_t nc = std::min(S, nch - i0);
+        BwdCallPtrs calls[kMaxBwdCalls];
+        for (size_t u = 0; u < nc; ++u) {
+          const int32_t c0 = cs[nch - 1 - i0 - u].first, c1 = cs[nch - 1 - i0 - u].second, qo = c0 & ~63;
+          const size_t pad = size_t(c0 - qo);
+          char* dOu = dOc + u * w.doc_slot;
+          {
+            KTimer t("path_dout", st);
+            if (launch_fill_zero(dOu, pad * qrow, st)) return dev_fail(fn, "upstream gradient");
+            for (int32_t i = rd.ev0; i < rd.ev1; ++i) {
+              const tt_path::Seg& s = seg_of(rd, i);
+              const int32_t lo = std::max(c0, s.depth0), hi = std::min(c1, s.depth0 + s.len);
+              if (lo >= hi) continue;
+              const size_t row = size_t(s.row0) + size_t(lo - s.depth0);
+              if (hipMemcpyAsync(dOu + size_t(lo - qo) * qrow, d_o + row * qrow, size_t(hi - lo) * qrow,
+                                 hipMemcpyDeviceToDevice, st) != hipSuccess)
+                return dev_fail(fn, "upstream gradient");
+            }
+          }
+          g.q_off = qo;
+          g.n_q = c1 - qo;
+          g.n_k = c1;
+          float* Du = reinterpret_cast<float*>(reinterpret_cast<char*>(D) + u * w.D_slot);
+          calls[u] = BwdCallPtrs{Qp + size_t(qo) * qrow, dOu, LSEp + size_t(qo) * hq, Du, nullptr,
+                                 dqs ? dqs + u * w.dqs_slot : nullptr,
+                                 reinterpret_cast<char*>(dKa) + u * w.acc_slot,
+                                 reinterpret_cast<char*>(dVa) + u * w.acc_slot, g};
+        }
+        bool dq_done = false;
+        if (S > 1) {
+          for (size_t u = 0; u < nc; ++u) {
+            KTimer t("attn_bwd_pre", st);
+            const AttnGeom& gu = calls[u].g;
+            if (launch_bwd_pre(dt, Op + size_t(gu.q_off) * qrow, calls[u].d_o, const_cast<float*>(calls[u].D),
+                               int64_t(gu.n_q) * gu.h_q, gu.d, st))
+              return dev_fail(fn, "backward preprocess");
+          }
+          KTimer t("attn_bwd_mfma", st);
+          if (launch_bwd_mfma_multi(calls, int(nc), Kp, Vp, true, cs_tab, P, false, st))
+            return dev_fail(fn, "backward kernel");
+          dq_done = true;
+        } else if ((rc = ttc::attn_bwd_core(dt, P, calls[0].g, calls[0].q, Kp, Vp,
+                                            Op + size_t(calls[0].g.q_off) * qrow, calls[0].d_o, calls[0].lse, D,
+                                            dq, dKa, dVa, true, false, cs_tab, st, dqs, &dq_done))) {
+          return rc;
+        }
+        // dQ rows of each chunk to their tree rows, segment by segment:
+        // copied from the bf16 block the kernel rotated back, or rotated back
+        // here from the fp32 block (vector kernels)
+        for (size_t u = 0; u < nc; ++u) {
+          const int32_t c0 = cs[nch - 1 - i0 - u].first, c1 = cs[nch - 1 - i0 - u].second, qo = c0 & ~63;
+          const char* dqu = dqs ? dqs + u * w.dqs_slot : nullptr;
+          KTimer t("dq_finalize", st);
           for (int32_t i = rd.ev0; i < rd.ev1; ++i) {
             const tt_path::Seg& s = seg_of(rd, i);
             const int32_t lo = std::max(c0, s.depth0), hi = std::min(c1, s.depth0 + s.len);
             if (lo >= hi) continue;
             const size_t row = size_t(s.row0) + size_t(lo - s.depth0);
-            if (hipMemcpyAsync(dOc + size_t(lo - qo) * qrow, d_o + row * qrow, size_t(hi - lo) * qrow,
-                               hipMemcpyDeviceToDevice, st) != hipSuccess)
-              return dev_fail(fn, "upstream gradient");
+            if (dq_done ? hipMemcpyAsync(d_q + row * qrow, dqu + size_t(lo - qo) * qrow, size_t(hi - lo) * qrow,
+                                         hipMemcpyDeviceToDevice, st) != hipSuccess
+                        : launch_rope(dq + size_t(lo - qo) * hq * d, d_q + row * qrow, TT_F32, dt, false, P, lo,
+                                      hi - lo, a->h_q, a->d, rb, true, st) != 0)
+              return dev_fail(fn, "dq finalize");
           }
-        }
-        g.q_off = qo;
-        g.n_q = c1 - qo;
-        g.n_k = c1;
-        bool dq_done = false;
-        if ((rc = ttc::attn_bwd_core(dt, P, g, Qp + size_t(qo) * qrow, Kp, Vp, Op + size_t(qo) * qrow, dOc,
-                                     LSEp + size_t(qo) * hq, D, dq, dKa, dVa, true, false, cs_tab, st, dqs,
-                                     &dq_done)))
-          return rc;
-        // dQ rows of the chunk to their tree rows, segment by segment: copied
-        // from the bf16 block the kernel rotated back, or rotated back here
-        // from the fp32 block (vector kernels)
-        KTimer t("dq_finalize", st);
-        for (int32_t i = rd.ev0; i < rd.ev1; ++i) {
-          const tt_path::Seg& s = seg_of(rd, i);
-          const int32_t lo = std::max(c0, s.depth0), hi = std::min(c1, s.depth0 + s.len);
-          if (lo >= hi) continue;
-          const size_t row = size_t(s.row0) + size_t(lo - s.depth0);
-          if (dq_done ? hipMemcpyAsync(d_q + row * qrow, dqs + size_t(lo - qo) * qrow, size_t(hi - lo) * qrow,
-                                       hipMemcpyDeviceToDevice, st) != hipSuccess
-                      : launch_rope(dq + size_t(lo - qo) * hq * d, d_q + row * qrow, TT_F32, dt, false, P, lo, hi - lo,
-                                    a->h_q, a->d, rb, true, st) != 0)
-            return dev_fail(fn, "dq finalize");
         }
       }
       for (int32_t i = rd.ev0; i < rd.ev1; ++i) {
         const tt_path::Seg& s = seg_of(rd, i);
         const size_t r0 = size_t(s.row0), n = size_t(s.len), d0 = size_t(s.depth0);
         KTimer t("path_pop", st);
+        if (w.slots > 1) {
+          // the matrix-core kernel rotated each contribution back at the
+          // key's depth (when there is RoPE): sum the slots and convert
+          if (launch_acc_pop(dKa + d0 * hk * d, dVa + d0 * hk * d, w.acc_slot / 4, w.slots, d_k + r0 * krow,
+                             d_v + r0 * krow, int64_t(n) * int64_t(hk * d), st))
+            return dev_fail(fn, "pop");
+          continue;
+        }
         // with the table, the matrix-core dK/dV kernel already rotated each
         // contribution back at the key's depth (rotation is linear, so the
         // sums are in the output frame): convert only

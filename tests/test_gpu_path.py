@@ -57,6 +57,19 @@ def test_path_bf16_vs_oracle_and_tree_mode(name, chunk, order):
         assert rel_err(g_, r) < 1e-2, (n, rel_err(g_, r))
 
 
+@pytest.mark.parametrize("name", ["beam_small", "chain"])
+def test_path_bf16_gqa2_vs_oracle(name):
+    """Groups of two query heads: each backward chunk is its own call (dQ and
+    dK/dV as separate launches, one accumulator); groups of four share a
+    launch between consecutive chunks (above)."""
+    _, o, _, (qn, kn, vn, don), (O, L, dq, dk, dv) = _run(name, torch.bfloat16, 128, 4, 2, 64, 0, 54)
+    Or, Lr, _ = OA.forward(o, qn, kn, vn, which="leaves")
+    dQr, dKr, dVr = OA.backward(o, qn, kn, vn, don, which="leaves")
+    for n, g_, r_ in (("o", O, Or), ("lse", L, Lr), ("dq", dq, dQr), ("dk", dk, dKr), ("dv", dv, dVr)):
+        print(f"  {n}: {rel_err(g_, r_):.2e}", flush=True)
+        assert rel_err(g_, r_) < 2e-2, (n, rel_err(g_, r_))
+
+
 @pytest.mark.parametrize("name", ["beam_small", "random"])
 def test_path_f32_vs_oracle(name):
     _, o, _, (qn, kn, vn, don), (O, L, dq, dk, dv) = _run(name, torch.float32, 64, 4, 2, 64, 0, 52)
