@@ -337,7 +337,11 @@ int tree_weighted_nll_noalloc(const tt_nll_args* args, tt_stream stream);
  * positions against the stack below them; a backward round runs in chunks
  * (boundaries at multiples of the chunk length) from the right, adding dK, dV
  * into float32 stack accumulators, then writes each popped segment's dK, dV
- * rows out and clears their stack slots.  Each call starts at the 64-aligned
+ * rows out and clears their stack slots.  On the matrix cores with groups of
+ * a multiple of 4 query heads, two consecutive chunk calls share one launch
+ * (each with its own dO copy, dQ block and pair of accumulators, summed when
+ * the segment is popped), so that one chunk's workgroups fill the CUs the
+ * other leaves idle.  Each call starts at the 64-aligned
  * position at or below its first query; the ancestor rows below it are
  * recomputed (with a zero upstream gradient in the backward: "pad rows",
  * counted in tt_path_info), so results equal tree mode (tree_attn_fwd/bwd)
@@ -394,8 +398,9 @@ int tree_path_segments(const tt_path* path, int32_t* row0, int32_t* len, int32_t
  *                 overwritten (ignored when d_o is NULL)
  *   plan          from tree_path_plan_upload for this path
  *   workspace     tree_path_workspace_bytes bytes, 256-byte aligned: the
- *                 stack (Q, K, V, O, LSE and, with d_o, float32 dK, dV) of
- *                 max_path positions plus per-call buffers of chunk + 64 rows;
+ *                 stack (Q, K, V, O, LSE and, with d_o, float32 dK, dV: two
+ *                 sets where chunk calls share a launch) of max_path
+ *                 positions plus per-call buffers of chunk + 64 rows;
  *                 proportional to the longest path, not N
  * Errors: TT_EINVAL, TT_EUNSUPPORTED, TT_EWORKSPACE, TT_EOVERFLOW, TT_EDEVICE.
  */
