@@ -31,8 +31,8 @@ METRIC = "tree attn fwd+bwd unique tokens/s + useful TFLOP/s (% bf16 MFMA peak),
 # HBM traffic of the roofline kernel from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE
 # runs (scaled by the same counters' reading for a plain copy of known size),
 # valid only for the kernel source it was measured on.
-MEASURED_TRAFFIC = {"kernel": "attn_bwd_mfma", "source_sha1": "56c62fd85bef18544cc881cc5585f2d5ea4357af",
-                    "bytes_per_launch": 39265645511}
+MEASURED_TRAFFIC = {"kernel": "attn_bwd_mfma", "source_sha1": "7b03347663d401791db682a3260c1ca47153eb90",
+                    "bytes_per_launch": 38936228577}
 
 
 def _source_sha(path):

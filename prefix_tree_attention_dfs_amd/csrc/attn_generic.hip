@@ -54,18 +54,22 @@ __global__ __launch_bounds__(256) void rope_kernel(const Tin* __restrict__ x, To
 }
 
 // The bf16 -> bf16 rotation of rope_kernel with 16-byte accesses: one thread
-// per (row, 8 consecutive pairs), the same fp64 angles and arithmetic (results
-// are bit-identical), looping over the heads.  Needs half % 8 == 0 and
-// 16-byte aligned rows.
+// per (row, 8 consecutive pairs, group of hpt heads), the same fp64 angles and
+// arithmetic (results are bit-identical), looping over its heads.  Few rows
+// (a path segment) split the heads over more threads so the grid still fills
+// the chip.  Needs half % 8 == 0, 16-byte aligned rows and hpt | heads.
 __global__ __launch_bounds__(256) void rope_bf16x8_kernel(const uint16_t* __restrict__ x, uint16_t* __restrict__ y,
                                                           PlanPtrs P, int32_t row0, int32_t n_rows, int32_t heads,
-                                                          int32_t d, double base, double sign, double mul) {
+                                                          int32_t d, double base, double sign, double mul,
+                                                          int32_t hpt) {
   if (!plan_matches(P)) return;
-  const int half = d >> 1, oct = half >> 3;
+  const int half = d >> 1, oct = half >> 3, hgroups = heads / hpt;
   const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (idx >= int64_t(n_rows) * oct) return;
-  const int64_t r = idx / oct;
-  const int k0 = int(idx - r * oct) * 8;
+  if (idx >= int64_t(n_rows) * oct * hgroups) return;
+  const int64_t rh = idx / oct;  // consecutive threads: consecutive octets of one head
+  const int k0 = int(idx - rh * oct) * 8;
+  const int64_t r = rh / hgroups;
+  const int h0 = int(rh - r * hgroups) * hpt;
   double c[8], sn[8];
   const double pos = double(P.depth[row0 + r]);
 #pragma unroll
@@ -81,7 +85,7 @@ __global__ __launch_bounds__(256) void rope_bf16x8_kernel(const uint16_t* __rest
     sn[e] *= mul;
   }
 #pragma unroll 2
-  for (int h = 0; h < heads; ++h) {
+  for (int h = h0; h < h0 + hpt; ++h) {
     const int64_t b = (r * heads + h) * d + k0;
     const uint4 a1 = *reinterpret_cast<const uint4*>(x + b);
     const uint4 a2 = *reinterpret_cast<const uint4*>(x + b + half);
@@ -422,9 +426,13 @@ int launch_rope(const void* x, void* y, tt_dtype tin, tt_dtype tout, bool acc, c
     rope_kernel<float, float, true><<<grid, block, 0, st>>>((const float*)x, (float*)y, P, row0, n_rows, heads, d, b, sg, mul);
   else if (tin == TT_BF16 && tout == TT_BF16 && !acc && (d % 16) == 0 &&
            ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(y)) & 15) == 0) {
+    // heads per thread: all of them, halved while the grid has fewer than
+    // 2^18 threads (1024 per CU) and the count stays a divisor
     const int64_t nv = int64_t(n_rows) * (d / 16);
-    rope_bf16x8_kernel<<<dim3(blocks_for(nv, 256)), block, 0, st>>>((const uint16_t*)x, (uint16_t*)y, P, row0, n_rows,
-                                                                      heads, d, b, sg, mul);
+    int hpt = heads;
+    while (hpt % 2 == 0 && nv * (heads / hpt) < (int64_t(1) << 18)) hpt /= 2;
+    rope_bf16x8_kernel<<<dim3(blocks_for(nv * (heads / hpt), 256)), block, 0, st>>>(
+        (const uint16_t*)x, (uint16_t*)y, P, row0, n_rows, heads, d, b, sg, mul, hpt);
   } else if (tin == TT_BF16 && tout == TT_BF16 && !acc)
     rope_kernel<uint16_t, uint16_t, false><<<grid, block, 0, st>>>((const uint16_t*)x, (uint16_t*)y, P, row0, n_rows, heads, d, b, sg, mul);
   else if (tin == TT_F32 && tout == TT_BF16 && !acc)
