@@ -30,6 +30,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // launch run side by side (each with its own dO copy, D, dQ block and dK/dV
 // accumulators), so one launch's grid holds the workgroups of several chunks.
 constexpr int kPathCalls = 2;
+static_assert(kPathCalls <= kMaxBwdCalls, "one launch takes at most kMaxBwdCalls calls");
 
 // Workspace carve-up, identical for the size query and the call.
 struct PathWs {
