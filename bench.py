@@ -139,6 +139,11 @@ def secondary(tt, ts, steps):
                                      useful_tflops=round(fl / ms / 1e9, 1),
                                      pct_bf16_peak=round(fl / ms / 1e9 / PEAK_BF16_TFLOPS * 100, 2))
 
+    dense = per_branch_dense(tt, ts, tree, case, q, k, v, do, steps, fwd_only=True)
+    out["rl_forest_1p7b_fwd"]["per_branch_dense"] = dict(dense, tree_speedup=round(dense["ms"] / ms, 3),
+                                                         pair_ratio=round(tree.info["dense_pairs"] /
+                                                                          tree.info["pairs"], 3))
+
     def fwd_bwd():
         st.fwd()
         st.bwd()
@@ -267,12 +272,56 @@ def lmhead_bench(tt, ts, steps):
                useful_tflops=round(fl / ms / 1e9, 1), pct_bf16_peak=round(fl / ms / 1e9 / PEAK_BF16_TFLOPS * 100, 2),
                nll_reduce_ms=round(red_ms, 3), nll_reduce_gbs=round(zbytes / red_ms / 1e6, 1),
                kernels={k_: {"launches": c, "avg_ms": round(t / c, 3)} for k_, (c, t, _) in kt.items()})
-    del H, W, ws
+    del ws
+    torch.cuda.empty_cache()
+    res["per_branch_dense"] = lmhead_dense(tt, tree, case, H, W, res["ms"], float(out_loss(rp, tid, tw, H, W, tt)))
+    del H, W
     torch.cuda.empty_cache()
     return res
 
 
-def per_branch_dense(tt, ts, tree, case, q, k, v, do, steps):
+def out_loss(rp, tid, tw, H, W, tt):
+    return tt.tree_weighted_nll(rp, tid, tw, hidden=H, w_vocab=W)["loss"].item()
+
+
+def lmhead_dense(tt, tree, case, H, W, tree_ms, tree_loss):
+    """The per-branch equivalent of the fused lm-head: every input sequence's
+    rows on their own (the tree rows gathered through seq_pos_to_dfs), each
+    position's target the sequence's next token with weight 1/B.  Its loss is
+    the tree loss (the branch average) up to rounding; the time is what the
+    tree saves."""
+    import numpy as np
+    import torch
+    a = tree.export()
+    B = len(case.seqs)
+    rows = torch.as_tensor(a["seq_pos_to_dfs"].astype("int64"), device="cuda")
+    Hd = H[rows].contiguous()
+    ptr, tok = [0], []
+    for s_ in case.seqs:
+        for k_ in range(len(s_)):
+            if k_ + 1 < len(s_):
+                tok.append(int(s_[k_ + 1]))
+            ptr.append(len(tok))
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()  # noqa: E731
+    rp = dev(np.asarray(ptr, dtype=np.int32))
+    tid = dev(np.asarray(tok, dtype=np.int32))
+    tw = dev(np.full(len(tok), np.float32(1.0) / np.float32(B), dtype=np.float32))
+    loss = tt.tree_weighted_nll(rp, tid, tw, hidden=Hd, w_vocab=W)["loss"].item()
+
+    def call():
+        tt.tree_weighted_nll(rp, tid, tw, hidden=Hd, w_vocab=W)
+
+    ms = _time(call, 2, 1)
+    n = int(rows.numel())
+    res = dict(rows=n, ms=round(ms, 3), rows_per_s=round(n / ms * 1e3), tree_speedup=round(ms / tree_ms, 3),
+               row_ratio=round(n / tree.N, 3), loss=round(loss, 4), tree_loss=round(tree_loss, 4),
+               loss_rel_diff=float(abs(loss - tree_loss) / abs(tree_loss)))
+    del Hd
+    torch.cuda.empty_cache()
+    return res
+
+
+def per_branch_dense(tt, ts, tree, case, q, k, v, do, steps, fwd_only=False):
     """The same kernels run on every input sequence as its own chain (no prefix sharing)."""
     import torch
     arr = tree.export()
@@ -290,7 +339,8 @@ def per_branch_dense(tt, ts, tree, case, q, k, v, do, steps):
     def run():
         for _, sb in steps_b:
             sb.fwd()
-            sb.bwd()
+            if not fwd_only:
+                sb.bwd()
 
     ms = _time(run, max(2, steps // 2), 1)
     branch_tokens = sum(len(s) for s in case.seqs)
