@@ -263,6 +263,7 @@ extern "C" int tree_attn_path(const tt_path_args* a, tt_stream stream) {
       for (size_t i0 = 0; i0 < nch; i0 += S) {
         const size_t nc = std::min(S, nch - i0);
         BwdCallPtrs calls[kMaxBwdCalls];
+        float* Ds[kMaxBwdCalls];
         for (size_t u = 0; u < nc; ++u) {
           const int32_t c0 = cs[nch - 1 - i0 - u].first, c1 = cs[nch - 1 - i0 - u].second, qo = c0 & ~63;
           const size_t pad = size_t(c0 - qo);
@@ -283,8 +284,8 @@ extern "C" int tree_attn_path(const tt_path_args* a, tt_stream stream) {
           g.q_off = qo;
           g.n_q = c1 - qo;
           g.n_k = c1;
-          float* Du = reinterpret_cast<float*>(reinterpret_cast<char*>(D) + u * w.D_slot);
-          calls[u] = BwdCallPtrs{Qp + size_t(qo) * qrow, dOu, LSEp + size_t(qo) * hq, Du, nullptr,
+          Ds[u] = reinterpret_cast<float*>(reinterpret_cast<char*>(D) + u * w.D_slot);
+          calls[u] = BwdCallPtrs{Qp + size_t(qo) * qrow, dOu, LSEp + size_t(qo) * hq, Ds[u], nullptr,
                                  dqs ? dqs + u * w.dqs_slot : nullptr,
                                  reinterpret_cast<char*>(dKa) + u * w.acc_slot,
                                  reinterpret_cast<char*>(dVa) + u * w.acc_slot, g};
@@ -294,8 +295,8 @@ extern "C" int tree_attn_path(const tt_path_args* a, tt_stream stream) {
           for (size_t u = 0; u < nc; ++u) {
             KTimer t("attn_bwd_pre", st);
             const AttnGeom& gu = calls[u].g;
-            if (launch_bwd_pre(dt, Op + size_t(gu.q_off) * qrow, calls[u].d_o, const_cast<float*>(calls[u].D),
-                               int64_t(gu.n_q) * gu.h_q, gu.d, st))
+            if (launch_bwd_pre(dt, Op + size_t(gu.q_off) * qrow, calls[u].d_o, Ds[u], int64_t(gu.n_q) * gu.h_q, gu.d,
+                               st))
               return dev_fail(fn, "backward preprocess");
           }
           KTimer t("attn_bwd_mfma", st);
