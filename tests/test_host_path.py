@@ -189,3 +189,42 @@ def test_path_build_errors():
     assert lib.tree_attn_path(ctypes.byref(a), None) == tt.TT_EINVAL and "upload" in tt.last_error()
     # the walk's plan is the chain of the longest path (host copy size)
     assert p.plan_bytes() > 0 and p.plan_bytes() % 256 == 0
+
+
+def _path_ws_expected(L, chunk, hq, hk, d, es, bwd, slots, mfma):
+    """The walk's workspace as tree_attn_path documents it: the stack of L
+    positions (Q, K, V, O in the data type, LSE fp32) and, with a backward,
+    `slots` sets of fp32 dK/dV accumulators, dO copies, D and bf16 dQ blocks of
+    chunk + 64 rows, one fp32 dQ block and the (cos, sin) table; every buffer
+    256-byte aligned."""
+    al = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    C = chunk + 64
+    n = al(L * hq * d * es) + 2 * al(L * hk * d * es) + al(L * hq * d * es) + al(L * hq * 4)
+    if bwd:
+        n += 2 * slots * al(L * hk * d * 4) + slots * al(C * hq * d * es) + slots * al(C * hq * 4)
+        n += al(C * hq * d * 4)
+        if mfma:
+            n += slots * al(C * hq * d * 2) + al(L * (d // 2) * 8)
+    return n
+
+
+@pytest.mark.parametrize("hq,hk,d,dtype,slots", [(8, 2, 128, "bf16", 2), (32, 8, 128, "bf16", 2),
+                                                 (4, 2, 128, "bf16", 1), (8, 2, 64, "bf16", 1),
+                                                 (8, 2, 64, "f32", 1)])
+def test_path_workspace_slots(hq, hk, d, dtype, slots):
+    """Matrix-core walks with groups of a multiple of 4 heads hold two sets of
+    per-call buffers and accumulators (two chunks per backward launch); other
+    shapes one."""
+    import ctypes
+    case = ts.random_small_tree(3, n_seqs=6, max_len=300, vocab=3)
+    t = tt.Tree(case.seqs)
+    p = tt.Path(t, 128, 0)
+    L = p.info["max_path"]
+    dt = tt.TT_BF16 if dtype == "bf16" else tt.TT_F32
+    es = 2 if dtype == "bf16" else 4
+    for bwd in (False, True):
+        args = tt.PathArgs(path=p.handle, h_q=hq, h_kv=hk, d=d, dtype=dt, d_o=0x100000 if bwd else None)
+        n = ctypes.c_size_t()
+        assert tt.lib().tree_path_workspace_bytes(ctypes.byref(args), ctypes.byref(n)) == tt.TT_OK
+        mfma = dtype == "bf16" and d == 128
+        assert n.value == _path_ws_expected(L, 128, hq, hk, d, es, bwd, slots, mfma), (bwd, n.value)
