@@ -419,6 +419,17 @@ __device__ __forceinline__ void dkdv_body(
         s = mfma(lds_read16(&S.Q[soff(mt * 32 + r, dc * 16 + 8 * hh)]), kf[dc], s);
         dp = mfma(lds_read16(&S.O[soff(mt * 32 + r, dc * 16 + 8 * hh)]), lds_read16(Vt + dc * 16), dp);
       }
+      // schedule: the start values and the first two steps' operands, then
+      // each step's two products followed by the reads two steps ahead (the
+      // compiler's own order reads one step ahead and waits before almost
+      // every product; measured 1.1-1.8% on the backward launch)
+      __builtin_amdgcn_sched_group_barrier(0x100, 14, 0);
+#pragma unroll
+      for (int i = 0; i < 6; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
       f32x16 ds;
       // the softmax step runs at raised wave priority: the SIMD's other wave,
       // usually issuing MFMAs, yields issue slots to it, which shortens the gap
