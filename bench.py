@@ -31,8 +31,8 @@ METRIC = "tree attn fwd+bwd unique tokens/s + useful TFLOP/s (% bf16 MFMA peak),
 # HBM traffic of the roofline kernel from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE
 # runs (scaled by the same counters' reading for a plain copy of known size),
 # valid only for the kernel source it was measured on.
-MEASURED_TRAFFIC = {"kernel": "attn_bwd_mfma", "source_sha1": "7b03347663d401791db682a3260c1ca47153eb90",
-                    "bytes_per_launch": 38936228577}
+MEASURED_TRAFFIC = {"kernel": "attn_bwd_mfma", "source_sha1": "b5cfaa8f96aee42cdb8bcec641acc33f05f0aa74",
+                    "bytes_per_launch": 37393555220}
 
 
 def _source_sha(path):
@@ -228,7 +228,7 @@ def path_mode_bench(tt, tree, plan, q, k, v, do, steps, tree_ms):
     return out
 
 
-def lmhead_bench(tt, ts, steps):
+def lmhead_bench(tt, ts, steps, dense=True):
     """Fused lm-head + weighted NLL: 16384 tree tokens x 4096 -> 151936 vocabulary,
     32-leaf tree (compression about 5.5); loss, dH and dW (fp32)."""
     import numpy as np
@@ -274,7 +274,9 @@ def lmhead_bench(tt, ts, steps):
                kernels={k_: {"launches": c, "avg_ms": round(t / c, 3)} for k_, (c, t, _) in kt.items()})
     del ws
     torch.cuda.empty_cache()
-    res["per_branch_dense"] = lmhead_dense(tt, tree, case, H, W, res["ms"], float(out_loss(rp, tid, tw, H, W, tt)))
+    if dense:
+        res["per_branch_dense"] = lmhead_dense(tt, tree, case, H, W, res["ms"],
+                                               float(out_loss(rp, tid, tw, H, W, tt)))
     del H, W
     torch.cuda.empty_cache()
     return res
@@ -486,7 +488,8 @@ def main():
 
     torch.cuda.set_device(0)
     if args.lmhead_only:
-        print(json.dumps({"lmhead_weighted_nll": lmhead_bench(tt, ts, args.steps)}), flush=True)
+        print(json.dumps({"lmhead_weighted_nll": lmhead_bench(tt, ts, args.steps, dense=not args.no_dense)}),
+              flush=True)
         return
     if args.study:
         print(json.dumps({"study": "compression_sweep", "workload": "8 branches x 8192 tokens, shared prefix p, "
