@@ -57,6 +57,19 @@ def test_path_bf16_vs_oracle_and_tree_mode(name, chunk, order):
         assert rel_err(g_, r) < 1e-2, (n, rel_err(g_, r))
 
 
+@pytest.mark.parametrize("hq,hkv", [(8, 1), (12, 1)])
+def test_path_bf16_wide_groups_vs_oracle(hq, hkv):
+    """Groups of 8 and 12 query heads: the shared backward launches split each
+    group over several four-head dQ workgroups (and 12 is not a power of
+    two)."""
+    _, o, _, (qn, kn, vn, don), (O, L, dq, dk, dv) = _run("beam_small", torch.bfloat16, 128, hq, hkv, 64, 0, 55)
+    Or, Lr, _ = OA.forward(o, qn, kn, vn, which="leaves")
+    dQr, dKr, dVr = OA.backward(o, qn, kn, vn, don, which="leaves")
+    for n, g_, r_ in (("o", O, Or), ("lse", L, Lr), ("dq", dq, dQr), ("dk", dk, dKr), ("dv", dv, dVr)):
+        print(f"  {n}: {rel_err(g_, r_):.2e}", flush=True)
+        assert rel_err(g_, r_) < 2e-2, (n, rel_err(g_, r_))
+
+
 @pytest.mark.parametrize("name", ["beam_small", "chain"])
 def test_path_bf16_gqa2_vs_oracle(name):
     """Groups of two query heads: each backward chunk is its own call (dQ and
