@@ -87,11 +87,19 @@ class Step:
                               accumulate=self.accumulate, workspace=self.ws, reuse_rotated=True)
 
 
-def _time(fn, steps, warmup):
+def _time(fn, steps, warmup, min_warm_s=0.1):
+    """Mean time of `steps` calls between two events.  The warm-up runs at
+    least `warmup` calls and at least min_warm_s of wall time, so that a
+    sub-millisecond call is timed at the clock the chip reaches under load,
+    not while it ramps up from idle."""
     import torch
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < min_warm_s:
+        fn()
+        torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record()
