@@ -110,6 +110,23 @@ def _time(fn, steps, warmup, min_warm_s=0.1):
     return e0.elapsed_time(e1) / steps
 
 
+def _graph(fn):
+    """fn captured into a HIP graph (after two warm-up calls on a side stream)."""
+    import torch
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for _ in range(2):
+            fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
 def secondary(tt, ts, steps):
     """Shorter measurements of the other configurations (not the headline)."""
     import numpy as np
@@ -131,8 +148,21 @@ def secondary(tt, ts, steps):
         tt.tree_weighted_nll(rp, tid, tw, logits=z)
 
     ms = _time(tiny, 20, 3)
-    out["tiny_tree_fp32"] = dict(N=tree.N, pairs=tree.info["pairs"], ms=round(ms, 4),
-                                 note="fwd + bwd + NLL (vocab 1000), outputs allocated per call; launch-bound")
+    # the same step with preallocated outputs, captured once and replayed as a HIP graph
+    o, lse = torch.empty_like(q), torch.empty(tree.N, 1, dtype=torch.float32, device="cuda")
+    dq, dk, dv, dz = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v), torch.empty_like(z)
+
+    def tiny_pre():
+        tt.tree_attn_fwd(tree, plan, q, k, v, o=o, lse=lse)
+        tt.tree_attn_bwd(tree, plan, q, k, v, o, lse, do, d_q=dq, d_k=dk, d_v=dv)
+        tt.tree_weighted_nll(rp, tid, tw, logits=z, d_logits=dz)
+
+    ms_pre = _time(tiny_pre, 20, 3)
+    ms_graph = _time(_graph(tiny_pre).replay, 20, 3)
+    out["tiny_tree_fp32"] = dict(N=tree.N, pairs=tree.info["pairs"], ms=round(ms, 4), ms_preallocated=round(ms_pre, 4),
+                                 ms_graph_replay=round(ms_graph, 4),
+                                 note="fwd + bwd + NLL (vocab 1000): outputs allocated per call, preallocated, "
+                                      "and the preallocated step replayed as a HIP graph; launch-bound")
     d = 128
     # 1.7B-class forward on the RL forest (16 q heads, 8 kv heads)
     case = ts.rl_forest_accepted(0)
@@ -218,6 +248,8 @@ def path_mode_bench(tt, tree, plan, q, k, v, do, steps, tree_ms):
 
         n = max(2, steps // 2)
         ms = _time(walk, n, 1)
+        # the whole walk (about 180 launches) captured once and replayed as a HIP graph
+        ms_graph = _time(_graph(walk).replay, n, 1) if (chunk, order) == (2048, 0) else None
         tt.timing_enable(True)
         walk()
         torch.cuda.synchronize()
@@ -232,6 +264,9 @@ def path_mode_bench(tt, tree, plan, q, k, v, do, steps, tree_ms):
             useful_tflops=round(useful / ms / 1e9, 1),
             pct_bf16_peak=round(useful / ms / 1e9 / PEAK_BF16_TFLOPS * 100, 2), workspace_bytes=nbytes,
             kernels={n_: {"launches": x[0], "total_ms": round(x[1], 3)} for n_, x in kt.items()})
+        if ms_graph is not None:
+            out[f"chunk{chunk}_dfs"].update(ms_graph_replay=round(ms_graph, 3),
+                                             graph_vs_tree_mode=round(ms_graph / tree_ms, 3))
         del ws, path
     return out
 
