@@ -273,6 +273,46 @@ __global__ __launch_bounds__(GTHREADS) __attribute__((amdgpu_waves_per_eu(2, 2))
     mma(a1, b1);
   }
 
+  if constexpr (OUT == 0) {
+    // bf16 output through LDS: the block's 256 x 256 tile is rounded once
+    // (nearest even) into the 128 KB the stages used, as rows of 512 bytes
+    // whose 16-byte chunk c sits at c ^ (4 ((row >> 2) & 1)) (the two halves
+    // of a wave write rows 4 apart: this puts them on disjoint banks), then
+    // every thread stores 16 contiguous bytes per row it covers.
+    __syncthreads();  // every wave has read its last stage
+#pragma unroll
+    for (int i = 0; i < WTM; ++i)
+#pragma unroll
+      for (int j = 0; j < WTN; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int row = wm * 128 + i * 32 + 8 * (e >> 2) + 4 * hh + (e & 3);
+          const int col = wn * 64 + j * 32 + r;
+          const int chunk = (col >> 3) ^ (((row >> 2) & 1) << 2);
+          smem[row * 256 + chunk * 8 + (col & 7)] = __builtin_bit_cast(uint16_t, __bf16(acc[i][j][e]));
+        }
+    __syncthreads();
+    const int c = tid & 31;  // 16-byte chunk of a row: columns 8c .. 8c + 7
+    const int64_t n = n0 + 8 * c;
+    const bool vec = (N & 7) == 0 && (reinterpret_cast<uintptr_t>(Cv) & 15) == 0;
+#pragma unroll
+    for (int it = 0; it < 16; ++it) {
+      const int row = it * 16 + (tid >> 5);
+      const int64_t m = m0 + row;
+      if (m >= M || n >= N) continue;
+      const uint4 w = *reinterpret_cast<const uint4*>(&smem[row * 256 + ((c ^ (((row >> 2) & 1) << 2)) * 8)]);
+      uint16_t* dst = static_cast<uint16_t*>(Cv) + m * N + n;
+      if (vec) {
+        *reinterpret_cast<uint4*>(dst) = w;
+      } else {
+        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (n + u < N) dst[u] = uint16_t(ws[u >> 1] >> (16 * (u & 1)));
+      }
+    }
+    return;
+  }
   // epilogue: lane holds C[m = 8*(e/4) + 4hh + e%4][n = r] of each 32 x 32 tile
 #pragma unroll
   for (int i = 0; i < WTM; ++i)
