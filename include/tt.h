@@ -201,10 +201,10 @@ typedef struct {
   const void* v;           /* device [n_k, h_kv, d] dtype */
   void* o;                 /* device [n_q, h_q, d] dtype: output of fwd, input of bwd */
   float* lse;              /* device [n_q, h_q] float32: output of fwd, input of bwd */
-  void* workspace;         /* device scratch, >= tree_attn_workspace_bytes: rotated q and k
-                              (with RoPE) first, at the same offsets for both calls; for the
-                              backward also D, fp32 dQ and a (cos, sin) table of the tree's
-                              depths.  The library keeps nothing there between calls; a
+  void* workspace;         /* device scratch, >= tree_attn_workspace_bytes: the query operand,
+                              rotated k and a (cos, sin) table of the tree's depths (with
+                              RoPE) first, at the same offsets for both calls; for the
+                              backward also D and fp32 dQ.  The library keeps nothing there between calls; a
                               caller that passes the forward's workspace, unmodified, to the
                               backward may set TT_BWD_REUSE_ROTATED */
   size_t workspace_bytes;

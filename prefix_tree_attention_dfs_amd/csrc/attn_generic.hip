@@ -54,14 +54,18 @@ __global__ __launch_bounds__(256) void rope_kernel(const Tin* __restrict__ x, To
 }
 
 // The bf16 -> bf16 rotation of rope_kernel with 16-byte accesses: one thread
-// per (row, 8 consecutive pairs, group of hpt heads), the same fp64 angles and
-// arithmetic (results are bit-identical), looping over its heads.  Few rows
-// (a path segment) split the heads over more threads so the grid still fills
-// the chip.  Needs half % 8 == 0, 16-byte aligned rows and hpt | heads.
+// per (row, 8 consecutive pairs, group of hpt heads), looping over its heads.
+// Few rows (a path segment) split the heads over more threads so the grid
+// still fills the chip.  Without a table: the same fp64 angles and arithmetic
+// as rope_kernel (bit-identical results).  With tab, the (cos, sin) table of
+// rope_table_kernel (fp64 angles rounded once to fp32, row = depth): the
+// rotation in fp32, rounded once to bf16 (what the matrix-core epilogues use
+// to rotate gradients back), and no fp64 trigonometry per thread.  Needs
+// half % 8 == 0, 16-byte aligned rows and hpt | heads.
 __global__ __launch_bounds__(256) void rope_bf16x8_kernel(const uint16_t* __restrict__ x, uint16_t* __restrict__ y,
                                                           PlanPtrs P, int32_t row0, int32_t n_rows, int32_t heads,
                                                           int32_t d, double base, double sign, double mul,
-                                                          int32_t hpt) {
+                                                          int32_t hpt, const float2* __restrict__ tab) {
   if (!plan_matches(P)) return;
   const int half = d >> 1, oct = half >> 3, hgroups = heads / hpt;
   const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
@@ -70,6 +74,41 @@ __global__ __launch_bounds__(256) void rope_bf16x8_kernel(const uint16_t* __rest
   const int k0 = int(idx - rh * oct) * 8;
   const int64_t r = rh / hgroups;
   const int h0 = int(rh - r * hgroups) * hpt;
+  if (tab) {
+    const float2* t = tab + int64_t(P.depth[row0 + r]) * half + k0;
+    const float mf = float(mul), sf = float(sign * mul);
+    float cf[8], sn[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float2 cs = t[e];
+      cf[e] = cs.x * mf;
+      sn[e] = cs.y * sf;
+    }
+#pragma unroll 2
+    for (int h = h0; h < h0 + hpt; ++h) {
+      const int64_t b = (r * heads + h) * d + k0;
+      const uint4 a1 = *reinterpret_cast<const uint4*>(x + b);
+      const uint4 a2 = *reinterpret_cast<const uint4*>(x + b + half);
+      const uint32_t w1[4] = {a1.x, a1.y, a1.z, a1.w}, w2[4] = {a2.x, a2.y, a2.z, a2.w};
+      uint32_t o1[4], o2[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        uint32_t lo1 = 0, lo2 = 0;
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          const int e = 2 * u + tt;
+          const float x1 = bf2f(uint16_t(w1[u] >> (16 * tt))), x2 = bf2f(uint16_t(w2[u] >> (16 * tt)));
+          lo1 |= uint32_t(f2bf(x1 * cf[e] - x2 * sn[e])) << (16 * tt);
+          lo2 |= uint32_t(f2bf(x2 * cf[e] + x1 * sn[e])) << (16 * tt);
+        }
+        o1[u] = lo1;
+        o2[u] = lo2;
+      }
+      *reinterpret_cast<uint4*>(y + b) = make_uint4(o1[0], o1[1], o1[2], o1[3]);
+      *reinterpret_cast<uint4*>(y + b + half) = make_uint4(o2[0], o2[1], o2[2], o2[3]);
+    }
+    return;
+  }
   double c[8], sn[8];
   const double pos = double(P.depth[row0 + r]);
 #pragma unroll
@@ -414,7 +453,8 @@ inline unsigned blocks_for(int64_t n, int per) { return unsigned((n + per - 1) /
 
 // ---------------------------------------------------------------- launchers
 int launch_rope(const void* x, void* y, tt_dtype tin, tt_dtype tout, bool acc, const PlanPtrs& P, int32_t row0,
-                int32_t n_rows, int32_t heads, int32_t d, float base, bool inverse, hipStream_t st, double mul) {
+                int32_t n_rows, int32_t heads, int32_t d, float base, bool inverse, hipStream_t st, double mul,
+                const float2* tab) {
   const int64_t n = int64_t(n_rows) * (d / 2);
   if (n == 0) return 0;
   const dim3 grid(blocks_for(n, 256)), block(256);
@@ -432,7 +472,7 @@ int launch_rope(const void* x, void* y, tt_dtype tin, tt_dtype tout, bool acc, c
     int hpt = heads;
     while (hpt % 2 == 0 && nv * (heads / hpt) < (int64_t(1) << 18)) hpt /= 2;
     rope_bf16x8_kernel<<<dim3(blocks_for(nv * (heads / hpt), 256)), block, 0, st>>>(
-        (const uint16_t*)x, (uint16_t*)y, P, row0, n_rows, heads, d, b, sg, mul, hpt);
+        (const uint16_t*)x, (uint16_t*)y, P, row0, n_rows, heads, d, b, sg, mul, hpt, base != 0.f ? tab : nullptr);
   } else if (tin == TT_BF16 && tout == TT_BF16 && !acc)
     rope_kernel<uint16_t, uint16_t, false><<<grid, block, 0, st>>>((const uint16_t*)x, (uint16_t*)y, P, row0, n_rows, heads, d, b, sg, mul);
   else if (tin == TT_F32 && tout == TT_BF16 && !acc)

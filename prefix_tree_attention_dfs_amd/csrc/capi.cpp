@@ -33,6 +33,13 @@ struct AttnWs {
   int32_t cs_pos = 0;  // rows of the (cos, sin) table: every depth of the tree
 };
 
+// bf16 RoPE rotates from the (cos, sin) table (fp32 per element instead of
+// fp64 angles per thread); forward and backward use the same table, so the
+// rotated copies the backward recomputes equal the forward's.
+const float2* rope_tab(const tt_attn_args* a, const AttnWs& w, char* ws) {
+  return w.rope && w.cs_pos > 0 && a->dtype == TT_BF16 ? reinterpret_cast<const float2*>(ws + w.cs) : nullptr;
+}
+
 // The matrix-core kernels take the query already multiplied by scale * log2(e)
 // (their scores come out in log2 units); that copy lives in the workspace even
 // without RoPE.
@@ -53,17 +60,15 @@ AttnWs attn_ws(const tt_attn_args* a, bool bwd) {
   if (w.rope) {
     w.k_rot = off;
     off = align_up(off + size_t(a->n_k) * a->h_kv * a->d * es);
+    w.cs_pos = a->tree->max_depth + 1;
+    w.cs = off;
+    off = align_up(off + size_t(w.cs_pos) * (a->d / 2) * 8);
   }
   if (bwd) {
     w.D = off;
     off = align_up(off + size_t(a->n_q) * a->h_q * 4);
     w.dq = off;
     off = align_up(off + size_t(a->n_q) * a->h_q * a->d * 4);
-    if (w.rope) {
-      w.cs_pos = a->tree->max_depth + 1;
-      w.cs = off;
-      off = align_up(off + size_t(w.cs_pos) * (a->d / 2) * 8);
-    }
   }
   w.total = off;
   return w;
@@ -301,17 +306,23 @@ extern "C" int tree_attn_fwd(const tt_attn_args* a, tt_stream stream) {
   char* ws = static_cast<char*>(a->workspace);
   const void* q = a->q;
   const void* k = a->k;
+  if (w.rope && w.cs_pos > 0) {
+    KTimer t("rope_table", st);
+    if (launch_rope_table(reinterpret_cast<float2*>(ws + w.cs), w.cs_pos, a->d / 2, a->rope_base, st))
+      return dev_fail(fn, "rope table");
+  }
+  const float2* tab = rope_tab(a, w, ws);
   if (w.qcopy) {
     KTimer t("rope_q", st);
     if (launch_rope(a->q, ws + w.q_rot, a->dtype, a->dtype, false, P, a->q_off, a->n_q, a->h_q, a->d,
-                    a->rope_base, false, st, ttc::q_operand_scale(a->dtype, g, P)))
+                    a->rope_base, false, st, ttc::q_operand_scale(a->dtype, g, P), tab))
       return dev_fail(fn, "rope(q)");
     q = ws + w.q_rot;
   }
   if (w.rope) {
     KTimer t("rope_k", st);
     if (launch_rope(a->k, ws + w.k_rot, a->dtype, a->dtype, false, P, 0, a->n_k, a->h_kv, a->d,
-                    a->rope_base, false, st))
+                    a->rope_base, false, st, 1.0, tab))
       return dev_fail(fn, "rope(k)");
     k = ws + w.k_rot;
   }
@@ -345,12 +356,22 @@ extern "C" int tree_attn_bwd(const tt_attn_bwd_args* b, tt_stream stream) {
   char* ws = static_cast<char*>(a->workspace);
   const void* q = a->q;
   const void* k = a->k;
-  // the forward wrote them at the same offsets (tree_attn_workspace_bytes layout)
+  // the forward wrote the rotated copies and the (cos, sin) table at the same
+  // offsets (tree_attn_workspace_bytes layout)
+  float2* cs_tab = nullptr;
+  if (w.rope && w.cs_pos > 0) {
+    cs_tab = reinterpret_cast<float2*>(ws + w.cs);
+    if (!reuse) {
+      KTimer t("rope_table", st);
+      if (launch_rope_table(cs_tab, w.cs_pos, a->d / 2, a->rope_base, st)) return dev_fail(fn, "rope table");
+    }
+  }
+  const float2* tab = rope_tab(a, w, ws);
   if (w.qcopy) {
     if (a->n_q > 0 && !reuse) {
       KTimer t("rope_q", st);
       if (launch_rope(a->q, ws + w.q_rot, a->dtype, a->dtype, false, P, a->q_off, a->n_q, a->h_q, a->d,
-                      a->rope_base, false, st, ttc::q_operand_scale(a->dtype, g, P)))
+                      a->rope_base, false, st, ttc::q_operand_scale(a->dtype, g, P), tab))
         return dev_fail(fn, "rope(q)");
     }
     q = ws + w.q_rot;
@@ -359,19 +380,13 @@ extern "C" int tree_attn_bwd(const tt_attn_bwd_args* b, tt_stream stream) {
     if (!reuse) {
       KTimer t("rope_k", st);
       if (launch_rope(a->k, ws + w.k_rot, a->dtype, a->dtype, false, P, 0, a->n_k, a->h_kv, a->d,
-                      a->rope_base, false, st))
+                      a->rope_base, false, st, 1.0, tab))
         return dev_fail(fn, "rope(k)");
     }
     k = ws + w.k_rot;
   }
   float* D = reinterpret_cast<float*>(ws + w.D);
   float* dq = reinterpret_cast<float*>(ws + w.dq);
-  float2* cs_tab = nullptr;
-  if (w.rope && w.cs_pos > 0) {
-    cs_tab = reinterpret_cast<float2*>(ws + w.cs);
-    KTimer t("rope_table", st);
-    if (launch_rope_table(cs_tab, w.cs_pos, a->d / 2, a->rope_base, st)) return dev_fail(fn, "rope table");
-  }
   const bool full_range = a->q_off == 0 && a->n_q == P.N;
   // the bf16 dQ kernel rotates back and converts in its epilogue (table
   // built above whenever RoPE is on); other paths finalize from fp32 below

@@ -9,9 +9,12 @@
 #include "tt.h"
 
 // RoPE (and its transpose) at the rows' depths; acc adds into an fp32 output.
+// tab: the (cos, sin) table of launch_rope_table for these depths, or null;
+// only the bf16 -> bf16 kernel uses it (fp32 rotation from the table instead
+// of fp64 angles per thread).
 int launch_rope(const void* x, void* y, tt_dtype tin, tt_dtype tout, bool acc, const PlanPtrs& P, int32_t row0,
                 int32_t n_rows, int32_t heads, int32_t d, float base, bool inverse, hipStream_t st,
-                double mul = 1.0);
+                double mul = 1.0, const float2* tab = nullptr);
 
 // Generic (any d <= 256) path, fp32 or bf16 storage.
 int launch_fwd_generic(tt_dtype dt, const void* q, const void* k, const void* v, void* o, float* lse,
