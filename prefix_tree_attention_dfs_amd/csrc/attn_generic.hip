@@ -56,12 +56,12 @@ __global__ __launch_bounds__(256) void rope_kernel(const Tin* __restrict__ x, To
 // The bf16 -> bf16 rotation of rope_kernel with 16-byte accesses: one thread
 // per (row, 8 consecutive pairs, group of hpt heads), looping over its heads.
 // Few rows (a path segment) split the heads over more threads so the grid
-// still fills the chip.  Without a table: the same fp64 angles and arithmetic
-// as rope_kernel (bit-identical results).  With tab, the (cos, sin) table of
-// rope_table_kernel (fp64 angles rounded once to fp32, row = depth): the
-// rotation in fp32, rounded once to bf16 (what the matrix-core epilogues use
-// to rotate gradients back), and no fp64 trigonometry per thread.  Needs
-// half % 8 == 0, 16-byte aligned rows and hpt | heads.
+// still fills the chip.  With tab, the (cos, sin) table of rope_table_kernel
+// (fp64 angles rounded once to fp32, row = depth), or with base 0 (no
+// rotation, only the factor mul): rot_pair_bf16 in fp32, the arithmetic the
+// matrix-core forward uses when it rotates its own query copy.  Otherwise
+// the same fp64 angles and arithmetic as rope_kernel (bit-identical results).
+// Needs half % 8 == 0, 16-byte aligned rows and hpt | heads.
 __global__ __launch_bounds__(256) void rope_bf16x8_kernel(const uint16_t* __restrict__ x, uint16_t* __restrict__ y,
                                                           PlanPtrs P, int32_t row0, int32_t n_rows, int32_t heads,
                                                           int32_t d, double base, double sign, double mul,
@@ -74,13 +74,13 @@ __global__ __launch_bounds__(256) void rope_bf16x8_kernel(const uint16_t* __rest
   const int k0 = int(idx - rh * oct) * 8;
   const int64_t r = rh / hgroups;
   const int h0 = int(rh - r * hgroups) * hpt;
-  if (tab) {
-    const float2* t = tab + int64_t(P.depth[row0 + r]) * half + k0;
+  if (tab || base == 0.0) {
+    const float2* t = tab ? tab + int64_t(P.depth[row0 + r]) * half + k0 : nullptr;
     const float mf = float(mul), sf = float(sign * mul);
     float cf[8], sn[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float2 cs = t[e];
+      const float2 cs = t ? t[e] : make_float2(1.f, 0.f);
       cf[e] = cs.x * mf;
       sn[e] = cs.y * sf;
     }
@@ -97,9 +97,10 @@ __global__ __launch_bounds__(256) void rope_bf16x8_kernel(const uint16_t* __rest
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
           const int e = 2 * u + tt;
-          const float x1 = bf2f(uint16_t(w1[u] >> (16 * tt))), x2 = bf2f(uint16_t(w2[u] >> (16 * tt)));
-          lo1 |= uint32_t(f2bf(x1 * cf[e] - x2 * sn[e])) << (16 * tt);
-          lo2 |= uint32_t(f2bf(x2 * cf[e] + x1 * sn[e])) << (16 * tt);
+          uint16_t y1, y2;
+          rot_pair_bf16(bf2f(uint16_t(w1[u] >> (16 * tt))), bf2f(uint16_t(w2[u] >> (16 * tt))), cf[e], sn[e], y1, y2);
+          lo1 |= uint32_t(y1) << (16 * tt);
+          lo2 |= uint32_t(y2) << (16 * tt);
         }
         o1[u] = lo1;
         o2[u] = lo2;

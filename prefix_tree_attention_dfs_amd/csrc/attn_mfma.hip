@@ -17,6 +17,11 @@
 //   online softmax over keys (columns are lanes: row statistics are per lane)
 //   O^T += V^T P^T      (A = V^T via ds_read_tr16_b64, B = P^T straight from
 //                        the S^T accumulator registers)
+// With PRO the kernel makes the query operand itself: it reads the caller's
+// Q, rotates each row at its depth from the (cos, sin) table, multiplies by
+// scale * log2(e), rounds to bf16 (rot_pair_bf16, the RoPE kernel's
+// arithmetic) and stores that copy for the backward, so no separate pass
+// over Q runs before the forward.
 #include "device.h"
 #include "kernels.h"
 #include "mfma_common.h"
@@ -45,11 +50,11 @@ struct __align__(16) FwdStage {
 
 // WIDE: K/V of 2 GiB or more; each tile's descriptors then start at the tile
 // (64-bit base) instead of one descriptor with a 32-bit tile offset.
-template <int G, bool WIDE>
+template <int G, bool WIDE, bool PRO>
 __global__ __launch_bounds__(FwdCfg<G>::THREADS, FwdCfg<G>::MINB) void fwd_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     uint16_t* __restrict__ o, float* __restrict__ lse, PlanPtrs P, AttnGeom g, int full_range, int qb_first,
-    int n_qb, int nsub) {
+    int n_qb, int nsub, uint16_t* __restrict__ q_out, const float2* __restrict__ qtab, float qmul) {
   using C = FwdCfg<G>;
   constexpr int NT = C::NT;
   __shared__ FwdStage st[2];
@@ -70,12 +75,14 @@ __global__ __launch_bounds__(FwdCfg<G>::THREADS, FwdCfg<G>::MINB) void fwd_mfma_
 
   // Q fragments (B operands): lane holds Q[row][dc*16 + 8hh .. +8]
   bf16x8 qf[NT][8];
+  int32_t qdep[NT];  // PRO: the rows' depths (table rows)
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const int row = qrow0 + pos0 + nt * 32 + r;
 #pragma unroll
     for (int dc = 0; dc < 8; ++dc)
       qf[nt][dc] = row < g.n_q ? ld16(q + (int64_t(row) * g.h_q + head) * D + dc * 16 + 8 * hh) : zero8();
+    if constexpr (PRO) qdep[nt] = row < g.n_q ? P.depth[g.q_off + row] : 0;
   }
 
   f32x16 oacc[NT][4];
@@ -138,10 +145,46 @@ __global__ __launch_bounds__(FwdCfg<G>::THREADS, FwdCfg<G>::MINB) void fwd_mfma_
   const int e0 = ld_uniform(P.qb_ptr, qb), e1 = ld_uniform(P.qb_ptr, qb + 1);
   int cur = e0 < e1 ? ld_uniform(P.qb_tiles, e0) : 0;
   int nxt = e0 + 1 < e1 ? ld_uniform(P.qb_tiles, e0 + 1) : 0;
-  if (e0 < e1) {
-    load_tile(cur & kKbMask, st[0]);
-    store_end(st[0]);
+  if (e0 < e1) load_tile(cur & kKbMask, st[0]);
+  if constexpr (PRO) {
+    // make the query operand while the first tile is in flight (stored to
+    // q_out in the epilogue): the pair (c, c + 64) of coordinate
+    // c = dc*16 + 8hh + e sits in this lane's qf[dc] and qf[dc + 4]; the
+    // table row holds pairs 0..63
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int row = qrow0 + pos0 + nt * 32 + r;
+      if (row >= g.n_q) continue;
+      // all table loads first, then the rotations, then the stores (a store
+      // between them would make the next load wait for it)
+      float4 cs[4][4];  // cs[dc][i]: (cos, sin) of pairs dc*16 + 8hh + 2i, + 2i + 1
+      if (qtab) {
+        const float4* t = reinterpret_cast<const float4*>(qtab + int64_t(qdep[nt]) * (D / 2) + 8 * hh);
+#pragma unroll
+        for (int dc = 0; dc < 4; ++dc)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) cs[dc][i] = t[dc * 8 + i];
+      } else {
+#pragma unroll
+        for (int dc = 0; dc < 4; ++dc)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) cs[dc][i] = make_float4(1.f, 0.f, 1.f, 0.f);
+      }
+#pragma unroll
+      for (int dc = 0; dc < 4; ++dc) {
+        uint16_t y1[8], y2[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float4 c4 = cs[dc][e >> 1];
+          const float c = (e & 1) ? c4.z : c4.x, sn = (e & 1) ? c4.w : c4.y;
+          ttd::rot_pair_bf16(float(qf[nt][dc][e]), float(qf[nt][dc + 4][e]), c * qmul, sn * qmul, y1[e], y2[e]);
+        }
+        qf[nt][dc] = __builtin_bit_cast(bf16x8, y1);
+        qf[nt][dc + 4] = __builtin_bit_cast(bf16x8, y2);
+      }
+    }
   }
+  if (e0 < e1) store_end(st[0]);
   wait_vmem();  // also the direct-to-LDS loads, which the compiler does not track
   __syncthreads();
 
@@ -279,12 +322,17 @@ __global__ __launch_bounds__(FwdCfg<G>::THREADS, FwdCfg<G>::MINB) void fwd_mfma_
       }
     // natural-log LSE from the log2-unit max: ln 2 (m + log2 sum 2^(s' - m))
     if (hh == 0) lse[int64_t(row) * g.h_q + head] = (m[nt] + __log2f(lt)) * 0.6931471805599453f;
+    if constexpr (PRO) {
+      uint16_t* dst = q_out + (int64_t(row) * g.h_q + head) * D + 8 * hh;
+#pragma unroll
+      for (int dc = 0; dc < 8; ++dc) *reinterpret_cast<bf16x8*>(dst + dc * 16) = qf[nt][dc];
+    }
   }
 }
 
 template <int G>
 int launch_fwd_g(const void* q, const void* k, const void* v, void* o, float* lse, const PlanPtrs& P,
-                 const AttnGeom& g, bool full_range, hipStream_t st) {
+                 const AttnGeom& g, bool full_range, hipStream_t st, const QRot* qr) {
   const int qb_first = g.q_off / BQ;
   const int qb_end = (g.q_off + g.n_q + BQ - 1) / BQ;
   const int n_qb = qb_end - qb_first;
@@ -292,14 +340,20 @@ int launch_fwd_g(const void* q, const void* k, const void* v, void* o, float* ls
   const int nsub = (g.h_q / g.h_kv) / G;
   const dim3 grid(unsigned(n_qb) * unsigned(g.h_kv) * unsigned(nsub)), block(FwdCfg<G>::THREADS);
   const bool wide = int64_t(g.n_k) * g.h_kv * D * 2 >= (int64_t(1) << 31);
-  if (wide)
-    fwd_mfma_kernel<G, true><<<grid, block, 0, st>>>((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
-                                                     (uint16_t*)o, lse, P, g, full_range ? 1 : 0, qb_first, n_qb,
-                                                     nsub);
-  else
-    fwd_mfma_kernel<G, false><<<grid, block, 0, st>>>((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
-                                                      (uint16_t*)o, lse, P, g, full_range ? 1 : 0, qb_first, n_qb,
-                                                      nsub);
+  uint16_t* q_out = qr ? static_cast<uint16_t*>(qr->out) : nullptr;
+  const float2* qtab = qr ? qr->tab : nullptr;
+  const float qmul = qr ? qr->mul : 1.f;
+#define TT_FWD(WIDE, PRO)                                                                                    \
+  fwd_mfma_kernel<G, WIDE, PRO><<<grid, block, 0, st>>>((const uint16_t*)q, (const uint16_t*)k,              \
+                                                        (const uint16_t*)v, (uint16_t*)o, lse, P, g,         \
+                                                        full_range ? 1 : 0, qb_first, n_qb, nsub, q_out, qtab, \
+                                                        qmul)
+  if (qr) {
+    if (wide) TT_FWD(true, true); else TT_FWD(false, true);
+  } else {
+    if (wide) TT_FWD(true, false); else TT_FWD(false, false);
+  }
+#undef TT_FWD
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
@@ -310,11 +364,11 @@ bool mfma_attn_supported(const AttnGeom& g, const PlanPtrs& P) {
 }
 
 int launch_fwd_mfma(const void* q, const void* k, const void* v, void* o, float* lse, const PlanPtrs& P,
-                    const AttnGeom& g, bool full_range, hipStream_t st) {
+                    const AttnGeom& g, bool full_range, hipStream_t st, const QRot* qr) {
   switch (group_split(g.h_q / g.h_kv)) {
-    case 1: return launch_fwd_g<1>(q, k, v, o, lse, P, g, full_range, st);
-    case 2: return launch_fwd_g<2>(q, k, v, o, lse, P, g, full_range, st);
-    case 4: return launch_fwd_g<4>(q, k, v, o, lse, P, g, full_range, st);
+    case 1: return launch_fwd_g<1>(q, k, v, o, lse, P, g, full_range, st, qr);
+    case 2: return launch_fwd_g<2>(q, k, v, o, lse, P, g, full_range, st, qr);
+    case 4: return launch_fwd_g<4>(q, k, v, o, lse, P, g, full_range, st, qr);
     default: return -1;
   }
 }

@@ -312,7 +312,10 @@ extern "C" int tree_attn_fwd(const tt_attn_args* a, tt_stream stream) {
       return dev_fail(fn, "rope table");
   }
   const float2* tab = rope_tab(a, w, ws);
-  if (w.qcopy) {
+  // the matrix-core kernel makes the query operand from the caller's Q itself
+  // and leaves it at q_rot for the backward (same arithmetic as rope_q)
+  const bool own_q = a->dtype == TT_BF16 && mfma_attn_supported(g, P);
+  if (w.qcopy && !own_q) {
     KTimer t("rope_q", st);
     if (launch_rope(a->q, ws + w.q_rot, a->dtype, a->dtype, false, P, a->q_off, a->n_q, a->h_q, a->d,
                     a->rope_base, false, st, ttc::q_operand_scale(a->dtype, g, P), tab))
@@ -327,6 +330,13 @@ extern "C" int tree_attn_fwd(const tt_attn_args* a, tt_stream stream) {
     k = ws + w.k_rot;
   }
   const bool full_range = a->q_off == 0 && a->n_q == P.N;
+  if (own_q) {
+    const QRot qr{ws + w.q_rot, tab, float(ttc::q_operand_scale(a->dtype, g, P))};
+    KTimer t("attn_fwd_mfma", st);
+    if (launch_fwd_mfma(a->q, k, a->v, a->o, a->lse, P, g, full_range, st, &qr))
+      return dev_fail(fn, "attention kernel");
+    return TT_OK;
+  }
   return ttc::attn_fwd_core(a->dtype, P, g, q, k, a->v, a->o, a->lse, full_range, st);
 }
 

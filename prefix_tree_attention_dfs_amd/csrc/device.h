@@ -19,6 +19,15 @@ __device__ __forceinline__ uint16_t f2bf(float f) {
   return uint16_t(u >> 16);
 }
 
+// One RoPE pair (x1, x2) = (x[c], x[c + d/2]) rotated by (c, s) in fp32, each
+// result rounded once to bf16: (x1 c - x2 s, x2 c + x1 s).  The products and
+// their fusing are written out, so every kernel that rotates through this
+// helper produces the same bits for the same inputs.
+__device__ __forceinline__ void rot_pair_bf16(float x1, float x2, float c, float s, uint16_t& y1, uint16_t& y2) {
+  y1 = f2bf(__builtin_fmaf(x1, c, -(x2 * s)));
+  y2 = f2bf(__builtin_fmaf(x2, c, x1 * s));
+}
+
 template <typename T> struct Elem;
 template <> struct Elem<float> {
   static __device__ __forceinline__ float load(const float* p, int64_t i) { return p[i]; }

@@ -29,8 +29,16 @@ int launch_dkdv_generic(tt_dtype dt, bool acc, const void* q, const void* k, con
 // bf16 MFMA path, head dim 128 (returns -2 if the geometry is not covered).
 bool mfma_attn_supported(const AttnGeom& g, const PlanPtrs& P);
 bool mfma_bwd_supported(const AttnGeom& g, const PlanPtrs& P);
+// The forward's own query operand: q is then the caller's Q; the kernel
+// rotates it at depth with tab (null: no rotation), multiplies by mul, rounds
+// to bf16, uses that and stores it to out ([n_q, h_q, 128] bf16).
+struct QRot {
+  void* out;
+  const float2* tab;
+  float mul;
+};
 int launch_fwd_mfma(const void* q, const void* k, const void* v, void* o, float* lse, const PlanPtrs& P,
-                    const AttnGeom& g, bool full_range, hipStream_t st);
+                    const AttnGeom& g, bool full_range, hipStream_t st, const QRot* qr = nullptr);
 // dQ into dq_acc (fp32, rotated frame), or, when dq_out is set, rotated back
 // with cs_tab (may be null: no rotation) and stored in bf16 to dq_out.
 int launch_dq_mfma(const void* q, const void* k, const void* v, const void* d_o, const float* lse, const float* D,

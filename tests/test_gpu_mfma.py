@@ -177,20 +177,25 @@ def test_mfma_backward_no_rope_custom_scale():
         assert rel_err(g_, r_) < TOL, (n, rel_err(g_, r_))
 
 
-def test_mfma_backward_reuses_forward_rotation():
+@pytest.mark.parametrize("rope_base", [10000.0, 0.0])
+def test_mfma_backward_reuses_forward_rotation(rope_base):
     """TT_BWD_REUSE_ROTATED with the forward's workspace gives the same bits
-    as a backward that rotates q and k itself; a q_off chunk too."""
+    as a backward that rotates q and k itself (the forward kernel makes its
+    own query operand, the backward's RoPE kernel the same one); a q_off
+    chunk too, and the scaled copy without rotation."""
     case = TREES["forest"]()
     tree = tt.Tree(case.seqs)
     plan = tree.upload_plan()
     (q, _), (k, _), (v, _), (do, _) = inputs(torch.bfloat16, 44, tree.N, tree.N, 8, 2, 128, 128 ** -0.5)
     for q_off in (0, 128):
         qc, doc = q[q_off:], do[q_off:]
-        nb = max(tt.attn_workspace_bytes(tree, plan, qc, k, v, fb, q_off=q_off) for fb in (True, False))
+        nb = max(tt.attn_workspace_bytes(tree, plan, qc, k, v, fb, q_off=q_off, rope_base=rope_base)
+                 for fb in (True, False))
         ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
-        O, L = tt.tree_attn_fwd(tree, plan, qc, k, v, q_off=q_off, workspace=ws)
-        got = tt.tree_attn_bwd(tree, plan, qc, k, v, O, L, doc, q_off=q_off, workspace=ws, reuse_rotated=True)
-        ref = tt.tree_attn_bwd(tree, plan, qc, k, v, O, L, doc, q_off=q_off)
+        O, L = tt.tree_attn_fwd(tree, plan, qc, k, v, q_off=q_off, rope_base=rope_base, workspace=ws)
+        got = tt.tree_attn_bwd(tree, plan, qc, k, v, O, L, doc, q_off=q_off, rope_base=rope_base, workspace=ws,
+                               reuse_rotated=True)
+        ref = tt.tree_attn_bwd(tree, plan, qc, k, v, O, L, doc, q_off=q_off, rope_base=rope_base)
         for n, g_, r_ in zip(("dq", "dk", "dv"), got, ref):
             assert torch.equal(g_, r_), (q_off, n)
 
