@@ -400,8 +400,9 @@ int tree_path_segments(const tt_path* path, int32_t* row0, int32_t* len, int32_t
  *   workspace     tree_path_workspace_bytes bytes, 256-byte aligned: the
  *                 stack (Q, K, V, O, LSE and, with d_o, float32 dK, dV: two
  *                 sets where chunk calls share a launch) of max_path
- *                 positions plus per-call buffers of chunk + 64 rows;
- *                 proportional to the longest path, not N
+ *                 positions (bf16 head dim 128: also each position's tree
+ *                 row and a (cos, sin) table) plus per-call buffers of
+ *                 chunk + 64 rows; proportional to the longest path, not N
  * Errors: TT_EINVAL, TT_EUNSUPPORTED, TT_EWORKSPACE, TT_EOVERFLOW, TT_EDEVICE.
  */
 typedef struct {

@@ -21,7 +21,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libtreeattn.so")
 
 HOST_SOURCES = ["tree_host.cpp", "path_host.cpp"]
-HIP_SOURCES = ["capi.cpp", "path.cpp", "attn_generic.hip", "attn_mfma.hip", "attn_mfma_bwd.hip", "nll.hip", "gemm.hip", "probe.hip"]
+HIP_SOURCES = ["capi.cpp", "path.cpp", "attn_generic.hip", "attn_mfma.hip", "attn_mfma_bwd.hip", "path_kernels.hip", "nll.hip", "gemm.hip", "probe.hip"]
 
 ARCH = "gfx950"
 

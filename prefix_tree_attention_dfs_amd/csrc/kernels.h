@@ -80,6 +80,23 @@ int launch_rope_table(float2* tab, int32_t n_pos, int32_t half, float base, hipS
 // bf16 out_k / out_v (n elements each, a multiple of 4) = the sum of nslot
 // fp32 accumulators (slot u at acc + u * slot_stride elements); the
 // accumulators' n elements are zeroed.
+// Path walk data movement (bf16, d % 16 == 0; 16-byte aligned rows).
+// push: tree rows [row0, row0 + n_rows) of q, k, v to stack positions
+// [pos0, ...): Q rotated at the position with tab (null: not rotated) and
+// multiplied by qmul, K rotated, V copied; srow[pos] = tree row.
+int launch_path_push(const void* q, const void* k, const void* v, void* Qp, void* Kp, void* Vp, int32_t* srow,
+                     const float2* tab, int32_t row0, int32_t pos0, int32_t n_rows, int32_t hq, int32_t hk,
+                     int32_t d, float qmul, hipStream_t st);
+// scatter: for positions p in [p0, p1), row srow[p] of a_out = row
+// a_src0 + (p - p0) of a (a_row_bytes, a multiple of 16), and b_n floats of
+// b_out = row p of b (b_n = 0: none).
+int launch_path_scatter(const void* a, void* a_out, int64_t a_row_bytes, int64_t a_src0, const float* b,
+                        float* b_out, int32_t b_n, const int32_t* srow, int32_t p0, int32_t p1, hipStream_t st);
+// dO block of a backward chunk: rows of positions [qo, c1) from d_o via srow
+// (zeros below c0) into dob, and D = rowsum(dob o O_stack) as launch_bwd_pre
+// computes it (d = 128).
+int launch_path_dout_pre(const void* Op, const void* d_o, void* dob, float* D, const int32_t* srow, int32_t qo,
+                         int32_t c0, int32_t c1, int32_t hq, int32_t d, hipStream_t st);
 int launch_acc_pop(float* acc_k, float* acc_v, int64_t slot_stride, int nslot, void* out_k, void* out_v, int64_t n,
                    hipStream_t st);
 

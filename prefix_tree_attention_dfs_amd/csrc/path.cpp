@@ -38,7 +38,9 @@ struct PathWs {
   size_t dka = 0, dva = 0;  // float32 dK, dV accumulators (backward), `slots` of max_path rows each
   size_t doc = 0, D = 0;    // per-call buffers, chunk + 64 rows, `slots` of each
   size_t dq = 0;            // float32 dQ of one call (vector kernels)
-  size_t dqs = 0, cs = 0;   // matrix-core path: per-call bf16 dQ (rotated back, `slots`) and the (cos, sin) table
+  size_t dqs = 0;           // matrix-core path: per-call bf16 dQ (rotated back, `slots`)
+  size_t srow = 0, cs = 0;  // matrix-core path: tree row at each stack position, (cos, sin) table
+  bool fused = false;       // matrix-core path: pushes, dO blocks and outputs by the walk's own kernels
   int slots = 1;            // chunk calls per backward launch
   size_t acc_slot = 0, doc_slot = 0, D_slot = 0, dqs_slot = 0;  // bytes per slot
   size_t total = 0;
@@ -69,16 +71,18 @@ PathWs path_ws(const tt_path_args* a, bool bwd) {
   w.vp = take(L * hk * d * es);
   w.op = take(L * hq * d * es);
   w.lsep = take(L * hq * 4);
+  w.fused = mfma;
+  if (mfma) {
+    w.srow = take(L * 4);
+    w.cs = take(L * (d / 2) * 8);
+  }
   if (bwd) {
     w.dka = take(S * w.acc_slot);
     w.dva = take(S * w.acc_slot);
     w.doc = take(S * w.doc_slot);
     w.D = take(S * w.D_slot);
     w.dq = take(C * hq * d * 4);
-    if (mfma) {
-      w.dqs = take(S * w.dqs_slot);
-      w.cs = take(L * (d / 2) * 8);
-    }
+    if (mfma) w.dqs = take(S * w.dqs_slot);
   }
   w.total = off;
   return w;
@@ -206,11 +210,13 @@ extern "C" int tree_attn_path(const tt_path_args* a, tt_stream stream) {
         launch_fill_zero(dVa, size_t(w.slots) * w.acc_slot, st))
       return dev_fail(fn, "clear");
   }
-  // matrix-core path: the dQ and dK/dV epilogues rotate back at the stack
-  // position (= depth) with this table (dQ stored as bf16 rows of the call)
+  // matrix-core path: pushes rotate with this table of stack positions
+  // (= depths), and the dQ and dK/dV epilogues rotate back with it (dQ stored
+  // as bf16 rows of the call)
   char* dqs = bwd && w.dqs ? ws + w.dqs : nullptr;
+  int32_t* srow = w.fused ? reinterpret_cast<int32_t*>(ws + w.srow) : nullptr;
   float2* cs_tab = nullptr;
-  if (dqs && rb != 0.f) {
+  if (w.fused && rb != 0.f) {
     cs_tab = reinterpret_cast<float2*>(ws + w.cs);
     KTimer t("rope_table", st);
     if (launch_rope_table(cs_tab, p->max_path, a->d / 2, rb, st)) return dev_fail(fn, "rope table");
@@ -227,6 +233,13 @@ extern "C" int tree_attn_path(const tt_path_args* a, tt_stream stream) {
         const tt_path::Seg& s = seg_of(rd, i);
         const size_t r0 = size_t(s.row0), n = size_t(s.len), d0 = size_t(s.depth0);
         KTimer t("path_push", st);
+        if (w.fused) {
+          // Q rotated and scaled, K rotated, V copied, srow set: one launch
+          if (launch_path_push(q, k, v, Qp, Kp, Vp, srow, cs_tab, s.row0, s.depth0, s.len, a->h_q, a->h_kv, a->d,
+                               float(qmul), st))
+            return dev_fail(fn, "push");
+          continue;
+        }
         if (launch_rope(q + r0 * qrow, Qp + d0 * qrow, dt, dt, false, P, s.depth0, s.len, a->h_q, a->d, rb, false,
                         st, qmul) ||
             launch_rope(k + r0 * krow, Kp + d0 * krow, dt, dt, false, P, s.depth0, s.len, a->h_kv, a->d, rb, false,
@@ -244,6 +257,13 @@ extern "C" int tree_attn_path(const tt_path_args* a, tt_stream stream) {
         if ((rc = ttc::attn_fwd_core(dt, P, g, Qp + size_t(qo) * qrow, Kp, Vp, Op + size_t(qo) * qrow,
                                      LSEp + size_t(qo) * hq, false, st)))
           return rc;
+      }
+      if (w.fused) {
+        // the round's segments are stacked one on the next: positions [p0, p1)
+        KTimer t("path_out", st);
+        if (launch_path_scatter(Op, o, int64_t(qrow), rd.p0, LSEp, a->lse, a->h_q, srow, rd.p0, rd.p1, st))
+          return dev_fail(fn, "forward outputs");
+        continue;
       }
       for (int32_t i = rd.ev0; i < rd.ev1; ++i) {
         const tt_path::Seg& s = seg_of(rd, i);
@@ -268,7 +288,14 @@ extern "C" int tree_attn_path(const tt_path_args* a, tt_stream stream) {
           const int32_t c0 = cs[nch - 1 - i0 - u].first, c1 = cs[nch - 1 - i0 - u].second, qo = c0 & ~63;
           const size_t pad = size_t(c0 - qo);
           char* dOu = dOc + u * w.doc_slot;
-          {
+          Ds[u] = reinterpret_cast<float*>(reinterpret_cast<char*>(D) + u * w.D_slot);
+          if (w.fused) {
+            // dO rows of the chunk gathered through srow (zeros on the pad
+            // rows) and D = rowsum(dO o O), one launch
+            KTimer t("path_dout", st);
+            if (launch_path_dout_pre(Op, d_o, dOu, Ds[u], srow, qo, c0, c1, a->h_q, a->d, st))
+              return dev_fail(fn, "upstream gradient");
+          } else {
             KTimer t("path_dout", st);
             if (launch_fill_zero(dOu, pad * qrow, st)) return dev_fail(fn, "upstream gradient");
             for (int32_t i = rd.ev0; i < rd.ev1; ++i) {
@@ -284,7 +311,6 @@ extern "C" int tree_attn_path(const tt_path_args* a, tt_stream stream) {
           g.q_off = qo;
           g.n_q = c1 - qo;
           g.n_k = c1;
-          Ds[u] = reinterpret_cast<float*>(reinterpret_cast<char*>(D) + u * w.D_slot);
           calls[u] = BwdCallPtrs{Qp + size_t(qo) * qrow, dOu, LSEp + size_t(qo) * hq, Ds[u], nullptr,
                                  dqs ? dqs + u * w.dqs_slot : nullptr,
                                  reinterpret_cast<char*>(dKa) + u * w.acc_slot,
@@ -292,7 +318,7 @@ extern "C" int tree_attn_path(const tt_path_args* a, tt_stream stream) {
         }
         bool dq_done = false;
         if (S > 1) {
-          for (size_t u = 0; u < nc; ++u) {
+          for (size_t u = 0; u < nc && !w.fused; ++u) {
             KTimer t("attn_bwd_pre", st);
             const AttnGeom& gu = calls[u].g;
             if (launch_bwd_pre(dt, Op + size_t(gu.q_off) * qrow, calls[u].d_o, Ds[u], int64_t(gu.n_q) * gu.h_q, gu.d,
@@ -315,6 +341,11 @@ extern "C" int tree_attn_path(const tt_path_args* a, tt_stream stream) {
           const int32_t c0 = cs[nch - 1 - i0 - u].first, c1 = cs[nch - 1 - i0 - u].second, qo = c0 & ~63;
           const char* dqu = dqs ? dqs + u * w.dqs_slot : nullptr;
           KTimer t("dq_finalize", st);
+          if (w.fused && dq_done) {
+            if (launch_path_scatter(dqu, d_q, int64_t(qrow), c0 - qo, nullptr, nullptr, 0, srow, c0, c1, st))
+              return dev_fail(fn, "dq finalize");
+            continue;
+          }
           for (int32_t i = rd.ev0; i < rd.ev1; ++i) {
             const tt_path::Seg& s = seg_of(rd, i);
             const int32_t lo = std::max(c0, s.depth0), hi = std::min(c1, s.depth0 + s.len);

@@ -193,18 +193,21 @@ def test_path_build_errors():
 
 def _path_ws_expected(L, chunk, hq, hk, d, es, bwd, slots, mfma):
     """The walk's workspace as tree_attn_path documents it: the stack of L
-    positions (Q, K, V, O in the data type, LSE fp32) and, with a backward,
-    `slots` sets of fp32 dK/dV accumulators, dO copies, D and bf16 dQ blocks of
-    chunk + 64 rows, one fp32 dQ block and the (cos, sin) table; every buffer
-    256-byte aligned."""
+    positions (Q, K, V, O in the data type, LSE fp32; on the matrix cores also
+    an int32 tree row and the (cos, sin) table entry per position) and, with a
+    backward, `slots` sets of fp32 dK/dV accumulators, dO copies, D and (matrix
+    cores) bf16 dQ blocks of chunk + 64 rows, and one fp32 dQ block; every
+    buffer 256-byte aligned."""
     al = lambda x: (x + 255) // 256 * 256  # noqa: E731
     C = chunk + 64
     n = al(L * hq * d * es) + 2 * al(L * hk * d * es) + al(L * hq * d * es) + al(L * hq * 4)
+    if mfma:
+        n += al(L * 4) + al(L * (d // 2) * 8)
     if bwd:
         n += 2 * slots * al(L * hk * d * 4) + slots * al(C * hq * d * es) + slots * al(C * hq * 4)
         n += al(C * hq * d * 4)
         if mfma:
-            n += slots * al(C * hq * d * 2) + al(L * (d // 2) * 8)
+            n += slots * al(C * hq * d * 2)
     return n
 
 
