@@ -306,7 +306,7 @@ extern "C" int tree_attn_fwd(const tt_attn_args* a, tt_stream stream) {
   char* ws = static_cast<char*>(a->workspace);
   const void* q = a->q;
   const void* k = a->k;
-  if (w.rope && w.cs_pos > 0) {
+  if (rope_tab(a, w, ws)) {  // only the bf16 kernels read the table
     KTimer t("rope_table", st);
     if (launch_rope_table(reinterpret_cast<float2*>(ws + w.cs), w.cs_pos, a->d / 2, a->rope_base, st))
       return dev_fail(fn, "rope table");
@@ -369,7 +369,7 @@ extern "C" int tree_attn_bwd(const tt_attn_bwd_args* b, tt_stream stream) {
   // the forward wrote the rotated copies and the (cos, sin) table at the same
   // offsets (tree_attn_workspace_bytes layout)
   float2* cs_tab = nullptr;
-  if (w.rope && w.cs_pos > 0) {
+  if (rope_tab(a, w, ws)) {
     cs_tab = reinterpret_cast<float2*>(ws + w.cs);
     if (!reuse) {
       KTimer t("rope_table", st);
