@@ -30,16 +30,19 @@ METRIC = "tree attn fwd+bwd unique tokens/s + useful TFLOP/s (% bf16 MFMA peak),
 
 # HBM traffic of the roofline kernel from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE
 # runs (scaled by the same counters' reading for a plain copy of known size),
-# valid only for the kernel source it was measured on.
-MEASURED_TRAFFIC = {"kernel": "attn_bwd_mfma", "source_sha1": "b5cfaa8f96aee42cdb8bcec641acc33f05f0aa74",
-                    "bytes_per_launch": 37796415022}
+# valid only for the kernel source and the host scheduler (which sets the
+# workgroups' launch order) it was measured on.
+MEASURED_TRAFFIC = {"kernel": "attn_bwd_mfma", "source_sha1": "d270e532cc3158c626a0b18cde0f85efc72196f4",
+                    "bytes_per_launch": 19839360756}
 
 
-def _source_sha(path):
-    """sha1 of a kernel source's code: // comments and blank lines removed, so
-    that a comment edit does not invalidate a traffic measurement."""
-    with open(path, encoding="utf-8") as f:
-        lines = [ln.split("//", 1)[0].rstrip() for ln in f]
+def _source_sha(*paths):
+    """sha1 of source code (the files in order): // comments and blank lines
+    removed, so that a comment edit does not invalidate a traffic measurement."""
+    lines = []
+    for path in paths:
+        with open(path, encoding="utf-8") as f:
+            lines += [ln.split("//", 1)[0].rstrip() for ln in f]
     return hashlib.sha1("\n".join(ln for ln in lines if ln).encode()).hexdigest()
 
 
@@ -600,11 +603,11 @@ def main():
     launches, tot, mx = kt[dom]
     avg_ms = tot / launches
     achieved = algo.get(dom, 0) / (avg_ms * 1e-3) / 1e12
-    src = os.path.join(ROOT, "prefix_tree_attention_dfs_amd", "csrc",
-                       "attn_mfma.hip" if dom == "attn_fwd_mfma" else "attn_mfma_bwd.hip")
+    csrc = os.path.join(ROOT, "prefix_tree_attention_dfs_amd", "csrc")
+    src = os.path.join(csrc, "attn_mfma.hip" if dom == "attn_fwd_mfma" else "attn_mfma_bwd.hip")
     traffic = None
     if MEASURED_TRAFFIC and MEASURED_TRAFFIC.get("kernel") == dom and \
-            MEASURED_TRAFFIC.get("source_sha1") == _source_sha(src):
+            MEASURED_TRAFFIC.get("source_sha1") == _source_sha(src, os.path.join(csrc, "tree_host.cpp")):
         traffic = MEASURED_TRAFFIC["bytes_per_launch"]
     roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,

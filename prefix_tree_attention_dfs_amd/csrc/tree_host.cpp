@@ -115,16 +115,15 @@ void build_schedule(tt_tree* t) {
   }
   t->n_tiles = ntiles;
   t->n_full = nfull;
-  // largest-first launch orders
+  // launch orders.  q-blocks from the last row up: the workgroups an XCD runs
+  // together are then DFS neighbours, which read nearly the same ancestor K/V
+  // tiles (one L2 fetch serves them all), and the root's blocks, whose tile
+  // lists are the shortest, come last.  Measured against largest-first on the
+  // 8B-shape tree: forward HBM reads 7.9 -> 3.3 GB, backward 37 -> 19 GB, both
+  // kernels ~1.8% faster.  k-blocks in key order, for the same sharing.
   std::vector<int32_t> qorder(t->nqb), korder(t->nkb);
-  for (int32_t i = 0; i < t->nqb; ++i) qorder[i] = i;
+  for (int32_t i = 0; i < t->nqb; ++i) qorder[i] = t->nqb - 1 - i;
   for (int32_t i = 0; i < t->nkb; ++i) korder[i] = i;
-  std::stable_sort(qorder.begin(), qorder.end(), [&](int32_t a, int32_t b) {
-    return cnt[a + 1] - cnt[a] > cnt[b + 1] - cnt[b];
-  });
-  std::stable_sort(korder.begin(), korder.end(), [&](int32_t a, int32_t b) {
-    return qhi[a] - qlo[a] > qhi[b] - qlo[b];
-  });
 
   // plan image
   int64_t w = ttp::H_WORDS;

@@ -94,11 +94,10 @@ def test_schedule_equals_bruteforce(case, blocks):
         seen = {i for j in keys for i in range(j, int(o["end"][j]))}
         assert seen == set(range(s["kb_qlo"][kb], s["kb_qhi"][kb]))
         assert s["kb_minend"][kb] == min(int(o["end"][j]) for j in keys)
-    # orders are permutations, largest first
-    cnt = np.diff(s["qb_ptr"])
-    assert sorted(s["qb_order"]) == list(range(len(cnt)))
-    assert all(cnt[s["qb_order"][i]] >= cnt[s["qb_order"][i + 1]] for i in range(len(cnt) - 1))
-    assert sorted(s["kb_order"]) == list(range(len(s["kb_qlo"])))
+    # launch orders: q-blocks from the last row up, k-blocks in key order
+    nqb = len(s["qb_ptr"]) - 1
+    assert list(s["qb_order"]) == list(range(nqb - 1, -1, -1))
+    assert list(s["kb_order"]) == list(range(len(s["kb_qlo"])))
 
 
 def test_schedule_workload_chain_and_tiny():
