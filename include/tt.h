@@ -159,7 +159,8 @@ int tree_target_weights(const tt_tree* tree, const float* seq_scale, const uint8
  * Device plan: depth[], end[] and the tile schedule (per q-block list of
  * non-empty k-blocks tagged FULL or PARTIAL; per k-block the contiguous range
  * of query rows that see it; launch orders: q-blocks from the last row up,
- * k-blocks in key order, so that workgroups running together share tiles).
+ * groups of 256 keys by the end of the rows that see them, latest first, so
+ * that workgroups running together share tiles).
  * tree_plan_bytes gives its size; tree_plan_upload copies it (hipMemcpyAsync on
  * `stream`) into the caller's device buffer of at least that many bytes.
  * Errors: TT_EINVAL, TT_EWORKSPACE (buffer too small), TT_EDEVICE.

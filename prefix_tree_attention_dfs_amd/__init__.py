@@ -297,7 +297,8 @@ class Tree:
         sec = lambda name, n: p[p[H[name]]:p[H[name]] + n].copy()  # noqa: E731
         return dict(tiles=tiles, qb_ptr=ptr.copy(), depth=sec("DEPTH", self.N), end=sec("END", self.N),
                     qb_order=sec("QB_ORDER", nqb), kb_qlo=sec("KB_QLO", nkb), kb_qhi=sec("KB_QHI", nkb),
-                    kb_minend=sec("KB_MINEND", nkb), kb_order=sec("KB_ORDER", nkb),
+                    kb_minend=sec("KB_MINEND", nkb),
+                    kb_order=sec("KB_ORDER", -(-nkb // max(1, 256 // int(p[H["BK"]])))),
                     bq=int(p[H["BQ"]]), bk=int(p[H["BK"]]))
 
     def upload_plan(self, device="cuda"):

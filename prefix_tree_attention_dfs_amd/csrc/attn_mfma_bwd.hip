@@ -269,7 +269,10 @@ __device__ __forceinline__ void dkdv_body(
   if (!plan_matches(P)) return;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r = lane & 31, hh = lane >> 5;
   const int kvh = bid % g.h_kv;
-  const int kb2 = bid / g.h_kv;
+  // a whole-tree call takes its key groups in the plan's launch order (latest
+  // query-range end first); a chunk call in key order
+  const bool whole = g.q_off == 0 && g.n_q == P.N && g.n_k == P.N;
+  const int kb2 = whole ? ld_uniform(P.kb_order, bid / g.h_kv) : bid / g.h_kv;
   const int kbase = kb2 * KV_KEYS;
   const int j = kbase + wave * 32 + r;  // this lane's key (lane column of S, dP, dK^T, dV^T)
   const bool jok = j < g.n_k;

@@ -76,6 +76,10 @@ bool pow2_in(int32_t b, int32_t lo, int32_t hi) { return b >= lo && b <= hi && (
 
 int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 
+// Keys per workgroup of the matrix-core dK/dV kernel: the unit of the key
+// launch order.
+constexpr int32_t kKeyGroup = 256;
+
 // Tile schedule (visibility j <= i < end[j]).  For a key block the rows that
 // see some key in it form the contiguous range [first key, max end): each
 // key j is seen by [j, end[j]) and consecutive keys' ranges touch.
@@ -120,10 +124,18 @@ void build_schedule(tt_tree* t) {
   // tiles (one L2 fetch serves them all), and the root's blocks, whose tile
   // lists are the shortest, come last.  Measured against largest-first on the
   // 8B-shape tree: forward HBM reads 7.9 -> 3.3 GB, backward 37 -> 19 GB, both
-  // kernels ~1.8% faster.  k-blocks in key order, for the same sharing.
-  std::vector<int32_t> qorder(t->nqb), korder(t->nkb);
+  // kernels ~1.8% faster.  Key groups (kKeyGroup keys, the backward's dK/dV
+  // workgroup) by the end of the rows that see them, latest first, ties in key
+  // order: groups that run together then walk the same query tiles from the
+  // same top row (a chain segment's keys share one end), and the shared
+  // root's groups, whose walks are the longest, start first.
+  std::vector<int32_t> qorder(t->nqb);
   for (int32_t i = 0; i < t->nqb; ++i) qorder[i] = t->nqb - 1 - i;
-  for (int32_t i = 0; i < t->nkb; ++i) korder[i] = i;
+  const int32_t gb = std::max(1, kKeyGroup / bk), ng = (t->nkb + gb - 1) / gb;
+  std::vector<int32_t> korder(ng), gend(ng, 0);
+  for (int32_t kb = 0; kb < t->nkb; ++kb) gend[kb / gb] = std::max(gend[kb / gb], qhi[kb]);
+  for (int32_t i = 0; i < ng; ++i) korder[i] = i;
+  std::stable_sort(korder.begin(), korder.end(), [&](int32_t a, int32_t b) { return gend[a] > gend[b]; });
 
   // plan image
   int64_t w = ttp::H_WORDS;
@@ -134,7 +146,7 @@ void build_schedule(tt_tree* t) {
   };
   const int64_t o_depth = place(N), o_end = place(N), o_qptr = place(t->nqb + 1),
                 o_qtiles = place(ntiles), o_qorder = place(t->nqb), o_qlo = place(t->nkb),
-                o_qhi = place(t->nkb), o_minend = place(t->nkb), o_korder = place(t->nkb);
+                o_qhi = place(t->nkb), o_minend = place(t->nkb), o_korder = place(ng);
   t->plan.assign(size_t(w), 0);
   int32_t* p = t->plan.data();
   p[ttp::H_MAGIC] = ttp::kMagic;

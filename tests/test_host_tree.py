@@ -94,10 +94,14 @@ def test_schedule_equals_bruteforce(case, blocks):
         seen = {i for j in keys for i in range(j, int(o["end"][j]))}
         assert seen == set(range(s["kb_qlo"][kb], s["kb_qhi"][kb]))
         assert s["kb_minend"][kb] == min(int(o["end"][j]) for j in keys)
-    # launch orders: q-blocks from the last row up, k-blocks in key order
+    # launch orders: q-blocks from the last row up; groups of 256 keys by the
+    # end of the rows that see them, latest first, ties in key order
     nqb = len(s["qb_ptr"]) - 1
     assert list(s["qb_order"]) == list(range(nqb - 1, -1, -1))
-    assert list(s["kb_order"]) == list(range(len(s["kb_qlo"])))
+    gb = max(1, 256 // bk)
+    ng = -(-len(s["kb_qlo"]) // gb)
+    gend = [max(int(o["end"][j]) for j in range(g * gb * bk, min(N, (g + 1) * gb * bk))) for g in range(ng)]
+    assert list(s["kb_order"]) == sorted(range(ng), key=lambda g: (-gend[g], g))
 
 
 def test_schedule_workload_chain_and_tiny():
