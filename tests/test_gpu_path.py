@@ -93,6 +93,21 @@ def test_path_f32_vs_oracle(name):
         assert rel_err(g_, r_) < 1e-5, (n, rel_err(g_, r_))
 
 
+def test_path_bf16_no_rope_custom_scale_vs_oracle():
+    """rope_base = 0 on the matrix-core walk: the push only scales the query
+    operand (no table), and no gradient is rotated back."""
+    case = TREES["beam_small"]()
+    tree = tt.Tree(case.seqs)
+    o = dfs_arrays(case.seqs)
+    path = tt.Path(tree, 128, 0)
+    (q, qn), (k, kn), (v, vn), (do, don) = inputs(torch.bfloat16, 57, tree.N, tree.N, 8, 2, 128, 128 ** -0.5)
+    O, L, dq, dk, dv = tt.tree_attn_path(path, q, k, v, d_o=do, scale=0.05, rope_base=0.0)
+    Or, Lr, _ = OA.forward(o, qn, kn, vn, scale=0.05, rope_base=0, which="leaves")
+    dQr, dKr, dVr = OA.backward(o, qn, kn, vn, don, scale=0.05, rope_base=0, which="leaves")
+    for n, g_, r_ in (("o", O, Or), ("lse", L, Lr), ("dq", dq, dQr), ("dk", dk, dKr), ("dv", dv, dVr)):
+        assert rel_err(g_, r_) < 2e-2, (n, rel_err(g_, r_))
+
+
 def test_path_forward_only_and_orders_agree():
     """Forward-only walk gives the combined walk's O and LSE; the child order
     changes no result (every call is deterministic per row)."""
