@@ -255,6 +255,10 @@ struct __align__(16) KvLds {
   KvStage st[2];
   int32_t red[KV_WAVES];
 };
+// After the tile loop of an accumulating call the whole KvLds is reused:
+// each wave's 32 x 128 fp32 dK (then dV) block, rows EST floats apart.
+constexpr int EST = 132;
+static_assert(KV_WAVES * 32 * EST * 4 <= int(sizeof(KvLds)), "the epilogue blocks fit in the LDS");
 
 // The body of the dK/dV kernel for workgroup `bid` (the kernel below, or the
 // dK/dV part of the combined backward launch).
@@ -476,54 +480,128 @@ __device__ __forceinline__ void dkdv_body(
     wait_vmem();  // this wave's direct-to-LDS loads of the next tile have landed
     __syncthreads();
   }
-  if (!jok) return;
-
-  // dK = R^T (scale * dK') at the key's depth, with (cos, sin) of depth *
-  // theta_c from the caller's table (none: no rotation); coordinates (c, c+64)
-  // are the same register of blocks dt and dt+2.  The Q operand carried
-  // scale * log2(e), so scale * dK' is the accumulator times ln 2.
-  const float2* __restrict__ cs_row = cs_tab ? cs_tab + int64_t(P.depth[j]) * (D / 2) : nullptr;
-  const int64_t base = (int64_t(j) * g.h_kv + kvh) * D;
+  if constexpr (ACC) {
+    // Accumulating (chunk) calls: each wave passes its 32 keys' dK (rotated
+    // back) and dV through its own part of the LDS, which is free after the
+    // loop's last barrier, so that the read-add-write of the fp32 accumulators
+    // goes by whole rows (32 lanes cover a key's 128 values in 16-byte pieces)
+    // instead of each lane reading and writing its own key's row 16 bytes at
+    // a time.
+    float* E = reinterpret_cast<float*>(&L) + wave * (32 * EST);
+    const auto put_rows = [&](TG* __restrict__ out) {
+      // two passes of 8 pieces per lane: all loads of a pass are in flight together
 #pragma unroll
-  for (int dt = 0; dt < 2; ++dt)
+      for (int h = 0; h < 2; ++h) {
+        float4 x[8];
+        int64_t o[8];
+        bool ok[8];
 #pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) {
-      float lo4[4], hi4[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int c = dt * 32 + 8 * i4 + 4 * hh + e;
-        const float x1 = dk[dt][4 * i4 + e] * kLn2, x2 = dk[dt + 2][4 * i4 + e] * kLn2;
-        float cs = 1.f, sn = 0.f;
-        if (cs_row) {
-          const float2 t = cs_row[c];
-          cs = t.x;
-          sn = t.y;
+        for (int u = 0; u < 8; ++u) {
+          const int f = (8 * h + u) * 64 + lane, jj = kbase + wave * 32 + (f >> 5);
+          x[u] = *reinterpret_cast<const float4*>(&E[(f >> 5) * EST + (f & 31) * 4]);
+          ok[u] = jj < g.n_k;
+          o[u] = (int64_t(ok[u] ? jj : 0) * g.h_kv + kvh) * D + (f & 31) * 4;
         }
-        lo4[e] = x1 * cs + x2 * sn;
-        hi4[e] = x2 * cs - x1 * sn;
-      }
-      const int c0 = dt * 32 + 8 * i4 + 4 * hh;
+        float4 y[8];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if (ACC) {
-          d_k[base + c0 + e] += lo4[e];
-          d_k[base + c0 + 64 + e] += hi4[e];
-        } else {
+        for (int u = 0; u < 8; ++u)
+          if (ok[u]) y[u] = *reinterpret_cast<const float4*>(out + o[u]);
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (ok[u])
+            *reinterpret_cast<float4*>(out + o[u]) =
+                make_float4(y[u].x + x[u].x, y[u].y + x[u].y, y[u].z + x[u].z, y[u].w + x[u].w);
+      }
+    };
+
+    // dK = R^T (scale * dK') at the key's depth, with (cos, sin) of depth *
+    // theta_c from the caller's table (none: no rotation); coordinates (c, c+64)
+    // are the same register of blocks dt and dt+2.  The Q operand carried
+    // scale * log2(e), so scale * dK' is the accumulator times ln 2.
+    const float2* __restrict__ cs_row = cs_tab && jok ? cs_tab + int64_t(P.depth[j]) * (D / 2) : nullptr;
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        float lo4[4], hi4[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int c = dt * 32 + 8 * i4 + 4 * hh + e;
+          const float x1 = dk[dt][4 * i4 + e] * kLn2, x2 = dk[dt + 2][4 * i4 + e] * kLn2;
+          float cs = 1.f, sn = 0.f;
+          if (cs_row) {
+            const float2 t = cs_row[c];
+            cs = t.x;
+            sn = t.y;
+          }
+          lo4[e] = x1 * cs + x2 * sn;
+          hi4[e] = x2 * cs - x1 * sn;
+        }
+        const int c0 = dt * 32 + 8 * i4 + 4 * hh;
+        *reinterpret_cast<float4*>(&E[r * EST + c0]) = make_float4(lo4[0], lo4[1], lo4[2], lo4[3]);
+        *reinterpret_cast<float4*>(&E[r * EST + c0 + 64]) = make_float4(hi4[0], hi4[1], hi4[2], hi4[3]);
+      }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    put_rows(d_k);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4)
+        *reinterpret_cast<float4*>(&E[r * EST + dt * 32 + 8 * i4 + 4 * hh]) =
+            make_float4(dv[dt][4 * i4], dv[dt][4 * i4 + 1], dv[dt][4 * i4 + 2], dv[dt][4 * i4 + 3]);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    put_rows(d_v);
+  } else {
+    // whole-tree calls: bf16 stores straight from the accumulators (staging
+    // them through LDS measured 0.6% slower here: the extra code spills)
+    if (!jok) return;
+
+    // dK = R^T (scale * dK') at the key's depth, with (cos, sin) of depth *
+    // theta_c from the caller's table (none: no rotation); coordinates (c, c+64)
+    // are the same register of blocks dt and dt+2.  The Q operand carried
+    // scale * log2(e), so scale * dK' is the accumulator times ln 2.
+    const float2* __restrict__ cs_row = cs_tab ? cs_tab + int64_t(P.depth[j]) * (D / 2) : nullptr;
+    const int64_t base = (int64_t(j) * g.h_kv + kvh) * D;
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        float lo4[4], hi4[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int c = dt * 32 + 8 * i4 + 4 * hh + e;
+          const float x1 = dk[dt][4 * i4 + e] * kLn2, x2 = dk[dt + 2][4 * i4 + e] * kLn2;
+          float cs = 1.f, sn = 0.f;
+          if (cs_row) {
+            const float2 t = cs_row[c];
+            cs = t.x;
+            sn = t.y;
+          }
+          lo4[e] = x1 * cs + x2 * sn;
+          hi4[e] = x2 * cs - x1 * sn;
+        }
+        const int c0 = dt * 32 + 8 * i4 + 4 * hh;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
           Elem<TG>::store(d_k, base + c0 + e, lo4[e]);
           Elem<TG>::store(d_k, base + c0 + 64 + e, hi4[e]);
         }
       }
-    }
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt)
+    for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int c = dt * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
-      if (ACC)
-        d_v[base + c] += dv[dt][i];
-      else
+      for (int i = 0; i < 16; ++i) {
+        const int c = dt * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
         Elem<TG>::store(d_v, base + c, dv[dt][i]);
-    }
+      }
+  }
 }
 
 // two waves per SIMD, except at G = 1, where the LDS stages of 2-wave
