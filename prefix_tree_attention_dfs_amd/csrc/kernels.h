@@ -92,11 +92,25 @@ int launch_path_push(const void* q, const void* k, const void* v, void* Qp, void
 // b_out = row p of b (b_n = 0: none).
 int launch_path_scatter(const void* a, void* a_out, int64_t a_row_bytes, int64_t a_src0, const float* b,
                         float* b_out, int32_t b_n, const int32_t* srow, int32_t p0, int32_t p1, hipStream_t st);
-// dO block of a backward chunk: rows of positions [qo, c1) from d_o via srow
-// (zeros below c0) into dob, and D = rowsum(dob o O_stack) as launch_bwd_pre
-// computes it (d = 128).
-int launch_path_dout_pre(const void* Op, const void* d_o, void* dob, float* D, const int32_t* srow, int32_t qo,
-                         int32_t c0, int32_t c1, int32_t hq, int32_t d, hipStream_t st);
+// The backward chunks of one launch: chunk u's dO block dob and D (rows
+// qo .. c1 - 1 of the stack; positions below c0 are the alignment pad) and
+// its bf16 dQ block dq_blk (same rows).
+struct PathChunk {
+  void* dob;
+  float* D;
+  const void* dq_blk;
+  int32_t qo, c0, c1;
+};
+struct PathChunks {
+  PathChunk c[kMaxBwdCalls];
+  int32_t n;
+};
+// dO blocks (rows of d_o via srow, zeros on the pad) and D = rowsum(dob o
+// O_stack) as launch_bwd_pre computes it, for every chunk of C (d = 128).
+int launch_path_dout_pre(const void* Op, const void* d_o, const int32_t* srow, const PathChunks& C, int32_t hq,
+                         int32_t d, hipStream_t st);
+// dQ rows [c0, c1) of every chunk of C from its block to tree rows srow[p].
+int launch_path_dq_scatter(void* d_q, int64_t row_bytes, const int32_t* srow, const PathChunks& C, hipStream_t st);
 int launch_acc_pop(float* acc_k, float* acc_v, int64_t slot_stride, int nslot, void* out_k, void* out_v, int64_t n,
                    hipStream_t st);
 

@@ -284,18 +284,15 @@ extern "C" int tree_attn_path(const tt_path_args* a, tt_stream stream) {
         const size_t nc = std::min(S, nch - i0);
         BwdCallPtrs calls[kMaxBwdCalls];
         float* Ds[kMaxBwdCalls];
+        PathChunks pc{};  // the launch's chunks, for the walk's own kernels
+        pc.n = int32_t(nc);
         for (size_t u = 0; u < nc; ++u) {
           const int32_t c0 = cs[nch - 1 - i0 - u].first, c1 = cs[nch - 1 - i0 - u].second, qo = c0 & ~63;
           const size_t pad = size_t(c0 - qo);
           char* dOu = dOc + u * w.doc_slot;
           Ds[u] = reinterpret_cast<float*>(reinterpret_cast<char*>(D) + u * w.D_slot);
-          if (w.fused) {
-            // dO rows of the chunk gathered through srow (zeros on the pad
-            // rows) and D = rowsum(dO o O), one launch
-            KTimer t("path_dout", st);
-            if (launch_path_dout_pre(Op, d_o, dOu, Ds[u], srow, qo, c0, c1, a->h_q, a->d, st))
-              return dev_fail(fn, "upstream gradient");
-          } else {
+          pc.c[u] = PathChunk{dOu, Ds[u], dqs ? dqs + u * w.dqs_slot : nullptr, qo, c0, c1};
+          if (!w.fused) {
             KTimer t("path_dout", st);
             if (launch_fill_zero(dOu, pad * qrow, st)) return dev_fail(fn, "upstream gradient");
             for (int32_t i = rd.ev0; i < rd.ev1; ++i) {
@@ -316,6 +313,12 @@ extern "C" int tree_attn_path(const tt_path_args* a, tt_stream stream) {
                                  reinterpret_cast<char*>(dKa) + u * w.acc_slot,
                                  reinterpret_cast<char*>(dVa) + u * w.acc_slot, g};
         }
+        if (w.fused) {
+          // every chunk's dO rows gathered through srow (zeros on the pad
+          // rows) and D = rowsum(dO o O): one launch
+          KTimer t("path_dout", st);
+          if (launch_path_dout_pre(Op, d_o, srow, pc, a->h_q, a->d, st)) return dev_fail(fn, "upstream gradient");
+        }
         bool dq_done = false;
         if (S > 1) {
           for (size_t u = 0; u < nc && !w.fused; ++u) {
@@ -334,18 +337,19 @@ extern "C" int tree_attn_path(const tt_path_args* a, tt_stream stream) {
                                             dq, dKa, dVa, true, false, cs_tab, st, dqs, &dq_done))) {
           return rc;
         }
-        // dQ rows of each chunk to their tree rows, segment by segment:
-        // copied from the bf16 block the kernel rotated back, or rotated back
-        // here from the fp32 block (vector kernels)
+        // dQ rows of each chunk to their tree rows: from the bf16 blocks the
+        // kernel rotated back, through srow in one launch; otherwise segment
+        // by segment, copied, or rotated back here from the fp32 block
+        // (vector kernels)
+        if (w.fused && dq_done) {
+          KTimer t("dq_finalize", st);
+          if (launch_path_dq_scatter(d_q, int64_t(qrow), srow, pc, st)) return dev_fail(fn, "dq finalize");
+          continue;
+        }
         for (size_t u = 0; u < nc; ++u) {
           const int32_t c0 = cs[nch - 1 - i0 - u].first, c1 = cs[nch - 1 - i0 - u].second, qo = c0 & ~63;
           const char* dqu = dqs ? dqs + u * w.dqs_slot : nullptr;
           KTimer t("dq_finalize", st);
-          if (w.fused && dq_done) {
-            if (launch_path_scatter(dqu, d_q, int64_t(qrow), c0 - qo, nullptr, nullptr, 0, srow, c0, c1, st))
-              return dev_fail(fn, "dq finalize");
-            continue;
-          }
           for (int32_t i = rd.ev0; i < rd.ev1; ++i) {
             const tt_path::Seg& s = seg_of(rd, i);
             const int32_t lo = std::max(c0, s.depth0), hi = std::min(c1, s.depth0 + s.len);

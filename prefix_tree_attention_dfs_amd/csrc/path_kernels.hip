@@ -7,6 +7,8 @@
 // srow[p] is the tree row held at stack position p.  A push writes it for the
 // segment's positions; positions above stay untouched until the segment is
 // popped, so the round's chunks and outputs look their rows up there.
+#include <algorithm>
+
 #include "device.h"
 #include "kernels.h"
 
@@ -88,21 +90,24 @@ __global__ __launch_bounds__(256) void path_scatter_kernel(const uint4* __restri
     b_out[row * b_n + (c - a_chunks)] = b[int64_t(p0 + r) * b_n + (c - a_chunks)];
 }
 
-// A backward chunk's dO block and D: for block row i (position qo + i),
-// dO_blk[i] = dO[srow[qo + i]] (zeros below c0, the 64-row alignment pad) and
-// D[i, h] = sum_c dO_blk[i, h, c] * O_stack[qo + i, h, c], summed as the
-// preprocess kernel sums (L = d/8 lanes of 8 products, then a butterfly), so
-// D has the same bits as from the copied block.
+// The dO blocks and D of the backward chunks of one launch (blockIdx.y =
+// chunk): for block row i (position qo + i), dO_blk[i] = dO[srow[qo + i]]
+// (zeros below c0, the 64-row alignment pad) and D[i, h] = sum_c dO_blk[i, h,
+// c] * O_stack[qo + i, h, c], summed as the preprocess kernel sums (L = d/8
+// lanes of 8 products, then a butterfly), so D has the same bits as from the
+// copied block.
 template <int L>
 __global__ __launch_bounds__(256) void path_dout_pre_kernel(const uint16_t* __restrict__ Op,
                                                             const uint16_t* __restrict__ d_o,
-                                                            uint16_t* __restrict__ dob, float* __restrict__ D,
-                                                            const int32_t* __restrict__ srow, int32_t qo, int32_t c0,
-                                                            int32_t n_rows, int32_t hq) {
+                                                            const int32_t* __restrict__ srow, PathChunks C,
+                                                            int32_t hq) {
+  const PathChunk& ch = C.c[blockIdx.y];
+  uint16_t* __restrict__ dob = static_cast<uint16_t*>(ch.dob);
+  const int32_t qo = ch.qo, c0 = ch.c0;
   const int64_t t = int64_t(blockIdx.x) * 256 + threadIdx.x;
   const int64_t rh = t / L;  // (block row, head)
   const int sub = int(t % L);
-  const int64_t rows = int64_t(n_rows) * hq;
+  const int64_t rows = int64_t(ch.c1 - qo) * hq;
   float a = 0.f;
   if (rh < rows) {
     const int i = int(rh / hq), h = int(rh - int64_t(i) * hq);
@@ -119,7 +124,20 @@ __global__ __launch_bounds__(256) void path_dout_pre_kernel(const uint16_t* __re
   }
 #pragma unroll
   for (int m = L / 2; m >= 1; m >>= 1) a += __shfl_xor(a, m, kWave);
-  if (rh < rows && sub == 0) D[rh] = a;
+  if (rh < rows && sub == 0) ch.D[rh] = a;
+}
+
+// The dQ rows of the backward chunks of one launch (blockIdx.y = chunk) to
+// their tree rows: position p in [c0, c1) is row p - qo of the chunk's block.
+__global__ __launch_bounds__(256) void path_dq_scatter_kernel(uint4* __restrict__ d_q,
+                                                              const int32_t* __restrict__ srow, PathChunks C,
+                                                              int32_t chunks_per_row) {
+  const PathChunk& ch = C.c[blockIdx.y];
+  const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx >= int64_t(ch.c1 - ch.c0) * chunks_per_row) return;
+  const int r = int(idx / chunks_per_row), c = int(idx - int64_t(r) * chunks_per_row);
+  d_q[int64_t(srow[ch.c0 + r]) * chunks_per_row + c] =
+      static_cast<const uint4*>(ch.dq_blk)[int64_t(ch.c0 - ch.qo + r) * chunks_per_row + c];
 }
 
 }  // namespace
@@ -149,15 +167,27 @@ int launch_path_scatter(const void* a, void* a_out, int64_t a_row_bytes, int64_t
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
-int launch_path_dout_pre(const void* Op, const void* d_o, void* dob, float* D, const int32_t* srow, int32_t qo,
-                         int32_t c0, int32_t c1, int32_t hq, int32_t d, hipStream_t st) {
-  const int32_t n_rows = c1 - qo;
-  if (n_rows <= 0) return 0;
-  if (d != 128) return -1;
+int launch_path_dout_pre(const void* Op, const void* d_o, const int32_t* srow, const PathChunks& C, int32_t hq,
+                         int32_t d, hipStream_t st) {
+  if (C.n <= 0) return 0;
+  if (d != 128 || C.n > kMaxBwdCalls) return -1;
   constexpr int L = 16;
-  const int64_t n = int64_t(n_rows) * hq * L;
-  path_dout_pre_kernel<L><<<dim3(blocks_for(n, 256)), dim3(256), 0, st>>>(
-      static_cast<const uint16_t*>(Op), static_cast<const uint16_t*>(d_o), static_cast<uint16_t*>(dob), D, srow, qo,
-      c0, n_rows, hq);
+  int64_t rows = 0;
+  for (int u = 0; u < C.n; ++u) rows = std::max<int64_t>(rows, C.c[u].c1 - C.c[u].qo);
+  if (rows <= 0) return 0;
+  path_dout_pre_kernel<L><<<dim3(blocks_for(rows * hq * L, 256), unsigned(C.n)), dim3(256), 0, st>>>(
+      static_cast<const uint16_t*>(Op), static_cast<const uint16_t*>(d_o), srow, C, hq);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int launch_path_dq_scatter(void* d_q, int64_t row_bytes, const int32_t* srow, const PathChunks& C, hipStream_t st) {
+  if (C.n <= 0) return 0;
+  if (row_bytes % 16 != 0 || C.n > kMaxBwdCalls) return -1;
+  const int32_t cpr = int32_t(row_bytes / 16);
+  int64_t rows = 0;
+  for (int u = 0; u < C.n; ++u) rows = std::max<int64_t>(rows, C.c[u].c1 - C.c[u].c0);
+  if (rows <= 0) return 0;
+  path_dq_scatter_kernel<<<dim3(blocks_for(rows * cpr, 256), unsigned(C.n)), dim3(256), 0, st>>>(
+      static_cast<uint4*>(d_q), srow, C, cpr);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
