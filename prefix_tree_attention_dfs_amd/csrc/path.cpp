@@ -28,9 +28,13 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 // Backward chunk calls per launch on the matrix-core path: the calls of a
 // launch run side by side (each with its own dO copy, D, dQ block and dK/dV
-// accumulators), so one launch's grid holds the workgroups of several chunks.
-constexpr int kPathCalls = 2;
-static_assert(kPathCalls <= kMaxBwdCalls, "one launch takes at most kMaxBwdCalls calls");
+// accumulators), so one launch's grid holds the workgroups of several chunks
+// and the launch's tail is shorter against its length.  Three for chunks of
+// up to 2048 rows, two above (measured on the 8B-shape walk: three chunks of
+// 2048 per launch 2% faster than two; three of 4096 3.5% slower than two).
+constexpr int kPathCallsSmall = 3, kPathCallsLarge = 2, kPathSmallChunk = 2048;
+static_assert(kPathCallsSmall <= kMaxBwdCalls && kPathCallsLarge <= kMaxBwdCalls,
+              "one launch takes at most kMaxBwdCalls calls");
 
 // Workspace carve-up, identical for the size query and the call.
 struct PathWs {
@@ -54,7 +58,9 @@ PathWs path_ws(const tt_path_args* a, bool bwd) {
   PathWs w;
   // several calls per launch where the combined matrix-core launch exists
   // (the dQ workgroups take four query heads: groups of a multiple of 4)
-  w.slots = mfma && (a->h_q / a->h_kv) % 4 == 0 ? kPathCalls : 1;
+  w.slots = !(mfma && (a->h_q / a->h_kv) % 4 == 0) ? 1
+            : p->chunk <= kPathSmallChunk          ? kPathCallsSmall
+                                                   : kPathCallsLarge;
   const size_t S = size_t(w.slots);
   w.acc_slot = align_up(L * hk * d * 4);
   w.doc_slot = align_up(C * hq * d * es);

@@ -211,17 +211,17 @@ def _path_ws_expected(L, chunk, hq, hk, d, es, bwd, slots, mfma):
     return n
 
 
-@pytest.mark.parametrize("hq,hk,d,dtype,slots", [(8, 2, 128, "bf16", 2), (32, 8, 128, "bf16", 2),
-                                                 (4, 2, 128, "bf16", 1), (8, 2, 64, "bf16", 1),
-                                                 (8, 2, 64, "f32", 1)])
-def test_path_workspace_slots(hq, hk, d, dtype, slots):
-    """Matrix-core walks with groups of a multiple of 4 heads hold two sets of
-    per-call buffers and accumulators (two chunks per backward launch); other
-    shapes one."""
+@pytest.mark.parametrize("hq,hk,d,dtype,chunk,slots", [(8, 2, 128, "bf16", 128, 3), (32, 8, 128, "bf16", 2048, 3),
+                                                       (32, 8, 128, "bf16", 4096, 2), (4, 2, 128, "bf16", 128, 1),
+                                                       (8, 2, 64, "bf16", 128, 1), (8, 2, 64, "f32", 128, 1)])
+def test_path_workspace_slots(hq, hk, d, dtype, chunk, slots):
+    """Matrix-core walks with groups of a multiple of 4 heads hold several sets
+    of per-call buffers and accumulators (three chunks per backward launch up
+    to chunks of 2048 rows, two above); other shapes one."""
     import ctypes
     case = ts.random_small_tree(3, n_seqs=6, max_len=300, vocab=3)
     t = tt.Tree(case.seqs)
-    p = tt.Path(t, 128, 0)
+    p = tt.Path(t, chunk, 0)
     L = p.info["max_path"]
     dt = tt.TT_BF16 if dtype == "bf16" else tt.TT_F32
     es = 2 if dtype == "bf16" else 4
@@ -230,4 +230,4 @@ def test_path_workspace_slots(hq, hk, d, dtype, slots):
         n = ctypes.c_size_t()
         assert tt.lib().tree_path_workspace_bytes(ctypes.byref(args), ctypes.byref(n)) == tt.TT_OK
         mfma = dtype == "bf16" and d == 128
-        assert n.value == _path_ws_expected(L, 128, hq, hk, d, es, bwd, slots, mfma), (bwd, n.value)
+        assert n.value == _path_ws_expected(L, chunk, hq, hk, d, es, bwd, slots, mfma), (bwd, n.value)
