@@ -442,28 +442,22 @@ __device__ __forceinline__ void dkdv_body(
       // usually issuing MFMAs, yields issue slots to it, which shortens the gap
       // before this wave's own dV/dK products
       __builtin_amdgcn_s_setprio(1);
+      // PARTIAL blocks: invisible pairs get S = -inf in place (exp2 gives 0),
+      // so both kinds of block share one exponential step and the branch
+      // leaves no values to merge
+      if (!full) {
 #pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const int ql = mt * 32 + 8 * i4 + 4 * hh;
-        if (full) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int i = 4 * i4 + e;
-            const float p = exp2_fast(s[i]);
-            s[i] = p;
-            ds[i] = p * dp[i];
-          }
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int i = 4 * i4 + e;
-            const int qq = qt * QT + ql + e;
-            const bool vis = (j <= qq) & (qq < endj) & (qq >= lo) & (qq < hi);
-            const float p = vis ? exp2_fast(s[i]) : 0.f;
-            s[i] = p;
-            ds[i] = p * dp[i];
-          }
+        for (int i = 0; i < 16; ++i) {
+          const int qq = qt * QT + mt * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
+          const bool vis = (j <= qq) & (qq < endj) & (qq >= lo) & (qq < hi);
+          s[i] = vis ? s[i] : -INFINITY;
         }
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float p = exp2_fast(s[i]);
+        s[i] = p;
+        ds[i] = p * dp[i];
       }
       const bf16x8 p0 = c_to_b(s, 0), p1 = c_to_b(s, 1);
       const bf16x8 s0 = c_to_b(ds, 0), s1 = c_to_b(ds, 1);
