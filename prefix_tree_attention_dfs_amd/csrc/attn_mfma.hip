@@ -155,8 +155,7 @@ __global__ __launch_bounds__(FwdCfg<G>::THREADS, FwdCfg<G>::MINB) void fwd_mfma_
     for (int nt = 0; nt < NT; ++nt) {
       const int row = qrow0 + pos0 + nt * 32 + r;
       if (row >= g.n_q) continue;
-      // all table loads first, then the rotations, then the stores (a store
-      // between them would make the next load wait for it)
+      // all table loads in flight together, then the rotations
       float4 cs[4][4];  // cs[dc][i]: (cos, sin) of pairs dc*16 + 8hh + 2i, + 2i + 1
       if (qtab) {
         const float4* t = reinterpret_cast<const float4*>(qtab + int64_t(qdep[nt]) * (D / 2) + 8 * hh);
