@@ -14,7 +14,8 @@
 //   S^T  = K Q^T        (A = K rows from LDS, B = Q; Q carries scale * log2(e),
 //                        so scores are in log2 units, and the accumulators
 //                        start at minus the running max: no per-score FMA)
-//   online softmax over keys (columns are lanes: row statistics are per lane)
+//   online softmax over keys (columns are lanes: row statistics are per lane;
+//                        no per-tile max unless a row's sum says it grew)
 //   O^T += V^T P^T      (A = V^T via ds_read_tr16_b64, B = P^T straight from
 //                        the S^T accumulator registers)
 // With PRO the kernel makes the query operand itself: it reads the caller's
@@ -68,10 +69,14 @@ __global__ __launch_bounds__(FwdCfg<G>::THREADS, FwdCfg<G>::MINB) void fwd_mfma_
   const int head = (kvh * nsub + sub) * G + wave / C::WPH;
   const int pos0 = (wave % C::WPH) * 32 * NT;
   const int qrow0 = qb * BQ - g.q_off;  // q-buffer row of the block's first position
-  // the running max (log2 units) moves only when a row's tile max exceeds it
-  // by more than tau (2^8 in probability); until then p may reach 2^8, which
-  // the fp32 sums and the bf16 P operand carry without loss of relative precision
-  constexpr float tau = 8.f;
+  // the exponentials run against the running max (log2 units) without a tile
+  // max: a lane's 16 values of a 32-key half are accepted while their sum is
+  // at most tsum (so every p <= 2^8, which the fp32 sums and the bf16 P
+  // operand carry without loss of relative precision); otherwise, and for a
+  // row with no max yet, the half is redone with the max moved to the exact
+  // running max.  Any max gives the same softmax: O and l share it, and the
+  // LSE adds it back.
+  constexpr float tsum = 256.f;
 
   // Q fragments (B operands): lane holds Q[row][dc*16 + 8hh .. +8]
   bf16x8 qf[NT][8];
@@ -198,8 +203,11 @@ __global__ __launch_bounds__(FwdCfg<G>::THREADS, FwdCfg<G>::MINB) void fwd_mfma_
     const FwdStage& S = st[sidx];
 
     // S^T = K Q^T - m for both 32-key halves (scores in log2 units relative to
-    // the running max), mask, one online-softmax update (rows = lanes) for the
-    // 64-key tile, then O^T += V^T P^T.
+    // the running max), mask, then per half: exponentials against the running
+    // max, redone in the rare case above (a row without a max yet, or a lane
+    // whose sum exceeds tsum), then O^T += V^T P^T for the half.  The first
+    // half's products and the second half's exponentials share a basic block,
+    // so the scheduler overlaps them.
     f32x16 sv[2][NT];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
@@ -216,78 +224,88 @@ __global__ __launch_bounds__(FwdCfg<G>::THREADS, FwdCfg<G>::MINB) void fwd_mfma_
         for (int nt = 0; nt < NT; ++nt) sv[kt][nt] = mfma(a, qf[nt][dc], sv[kt][nt]);
       }
     }
-    // mask (PARTIAL tiles)
-    if (!full) {
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          const int qpos = qb * BQ + pos0 + nt * 32 + r;
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int kl = kt * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
-            const bool vis = (kb * BK + kl <= qpos) & (qpos < S.end[kl]);
-            sv[kt][nt][i] = vis ? sv[kt][nt][i] : -INFINITY;
-          }
-        }
-    }
-    // tile max relative to the running max; a row shifts its max by dlt only
-    // when that exceeds tau (or on its first visible key)
-    float dlt[NT];
-    bool grow_any = false;
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sv[kt][nt][i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const bool grow = m[nt] == -INFINITY ? mx > -INFINITY : mx > tau;
-      dlt[nt] = grow ? mx : 0.f;
-      grow_any |= grow;
-    }
-    if (__any(grow_any)) {
-      // rare: move the max of the rows that grew (rescale O and l) and shift
-      // their scores to it
+    auto mask_half = [&](int kt) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-        if (dlt[nt] != 0.f && m[nt] != -INFINITY) {
-          const float alpha = exp2_fast(-dlt[nt]);
-          lpart[nt] *= alpha;
+        const int qpos = qb * BQ + pos0 + nt * 32 + r;
 #pragma unroll
-          for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) oacc[nt][dt][i] *= alpha;
+        for (int i = 0; i < 16; ++i) {
+          const int kl = kt * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
+          const bool vis = (kb * BK + kl <= qpos) & (qpos < S.end[kl]);
+          sv[kt][nt][i] = vis ? sv[kt][nt][i] : -INFINITY;
         }
-        m[nt] = m[nt] == -INFINITY ? dlt[nt] : m[nt] + dlt[nt];
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) sv[kt][nt][i] -= dlt[nt];
       }
+    };
+    if (!full) {
+      mask_half(0);
+      mask_half(1);
     }
-    // exponentials and P of both halves, then O^T += V^T P^T, in one straight
-    // block: the scheduler overlaps the first half's products with the second
-    // half's exponentials
     bf16x8 pf[2][2][NT];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+    for (int kt = 0; kt < 2; ++kt) {
+      float ls[NT];
+      bool redo = false;
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-        float ls = 0.f;
+        ls[nt] = 0.f;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const float p = exp2_fast(sv[kt][nt][i]);
           sv[kt][nt][i] = p;
-          ls += p;
+          ls[nt] += p;
         }
-        lpart[nt] += ls;
+        redo |= (m[nt] == -INFINITY) | !(ls[nt] <= tsum);
+      }
+      if (__any(redo)) {
+        // rare: raw scores of the half again, max moved to the exact running
+        // max (O and l rescaled), exponentials against it
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) sv[kt][nt] = zero16();
+#pragma unroll
+        for (int dc = 0; dc < 8; ++dc) {
+          const bf16x8 a = lds_read16(&S.K[soff(kt * 32 + r, dc * 16 + 8 * hh)]);
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) sv[kt][nt] = mfma(a, qf[nt][dc], sv[kt][nt]);
+        }
+        if (!full) mask_half(kt);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          float mx = -INFINITY;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sv[kt][nt][i]);
+          mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+          const float mn = m[nt] == -INFINITY ? mx : fmaxf(m[nt], mx);
+          if (m[nt] != -INFINITY && mn > m[nt]) {
+            const float alpha = exp2_fast(m[nt] - mn);
+            lpart[nt] *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+              for (int i = 0; i < 16; ++i) oacc[nt][dt][i] *= alpha;
+          }
+          // the other half's scores were taken against the old max: move them too
+          if (kt == 0) {
+            const float shift = mn == -INFINITY ? 0.f : (m[nt] == -INFINITY ? mn : mn - m[nt]);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) sv[1][nt][i] -= shift;
+          }
+          m[nt] = mn;
+          const float neg = mn == -INFINITY ? 0.f : -mn;
+          ls[nt] = 0.f;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const float p = exp2_fast(sv[kt][nt][i] + neg);
+            sv[kt][nt][i] = p;
+            ls[nt] += p;
+          }
+        }
+      }
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        lpart[nt] += ls[nt];
 #pragma unroll
         for (int c = 0; c < 2; ++c) pf[kt][c][nt] = c_to_b(sv[kt][nt], c);
       }
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
@@ -296,6 +314,7 @@ __global__ __launch_bounds__(FwdCfg<G>::THREADS, FwdCfg<G>::MINB) void fwd_mfma_
 #pragma unroll
           for (int nt = 0; nt < NT; ++nt) oacc[nt][dt] = mfma(a, pf[kt][c][nt], oacc[nt][dt]);
         }
+    }
 
     if (e + 1 < e1) store_end(st[sidx ^ 1]);
     wait_vmem();  // this wave's direct-to-LDS loads of the next tile have landed
