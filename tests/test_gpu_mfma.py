@@ -3,7 +3,8 @@
 Tolerance 2e-2 (max |gpu - oracle| / max |oracle| per tensor; where printed,
 also per row: each row judged against its own maximum).  Trees span several
 64-row tiles and end in a ragged tile; GQA groups 1, 2, 3, 4 and 8; scores
-both mild (std 1/sqrt(128)) and peaky (std 1); long query walks over a shared
+both mild (std 1/sqrt(128)) and peaky (std 1), and scores built to move the
+forward's running max along the walk; long query walks over a shared
 4096-token root; the full 8B tree against the same kernels run branch by
 branch; tensors past 4 GiB.
 """
@@ -53,6 +54,53 @@ def test_mfma_forward_peaky(name):
     O, L, Or, Lr = _fwd_case(name, 4, 1, 1.0, 32)
     assert rel_err(O, Or) < TOL, rel_err(O, Or)
     assert rel_err(L, Lr) < TOL, rel_err(L, Lr)
+
+
+def _moving_max_inputs(N, hq, hkv, prof, seed):
+    """bf16 q, k, v (device, and exact fp64 copies) whose score of query head
+    h against key row j is, in log2 units, about (1 + h/8) (s_j + noise_j):
+    q rows are one unit direction u, k row j is u times its target score."""
+    rng = np.random.default_rng(seed)
+    j = np.arange(N, dtype=np.float64)
+    if prof == "rising":        # every 32-key half climbs 16 log2 units
+        s = 0.5 * j
+    elif prof == "sawtooth":    # climbs and falls: some tiles move the max, some do not
+        s = 12.0 * np.sin(j / 37.0) + 0.02 * j
+    else:                       # flat, then +20 from a key in the second half of a tile
+        s = np.where(j >= (N // 128) * 64 + 45, 20.0, 0.0)
+    u = rng.normal(size=128)
+    u /= np.linalg.norm(u)
+    kn = (s[:, None] + rng.normal(0.0, 1.0, (N, hkv)))[..., None] * u * (128 ** 0.5 / np.log2(np.e))
+    qn = (1.0 + np.arange(hq) / 8.0)[None, :, None] * u + rng.normal(0.0, 1e-3, (N, hq, 128))
+    vn = rng.normal(size=(N, hkv, 128))
+    out = []
+    for x in (qn, kn, vn):
+        t = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).cuda()
+        out.append((t, t.float().cpu().double().numpy()))
+    return out
+
+
+@pytest.mark.parametrize("prof", ["rising", "sawtooth", "step"])
+@pytest.mark.parametrize("name,heads", [("beam_small", (8, 2)), ("chain", (4, 2)), ("forest", (8, 2))])
+def test_mfma_forward_moving_max(prof, name, heads):
+    """Scores that move the running max along the walk.  The forward takes its
+    exponentials against the running max and redoes a 32-key half when a
+    row's partial sum passes the bound or the row meets its first visible
+    key (then the other half's pending scores move with the max): here whole
+    walks of halves do that (rising), some tiles do and others not (sawtooth),
+    or one jump lands in a tile's second half after a quiet first half (step).
+    No RoPE, so each score is the one constructed."""
+    case = TREES[name]()
+    tree = tt.Tree(case.seqs)
+    o = dfs_arrays(case.seqs)
+    plan = tree.upload_plan()
+    (q, qn), (k, kn), (v, vn) = _moving_max_inputs(tree.N, heads[0], heads[1], prof, 41)
+    O, L = tt.tree_attn_fwd(tree, plan, q, k, v, rope_base=0.0)
+    Or, Lr, _ = OA.forward(o, qn, kn, vn, rope_base=0.0, which="leaves")
+    e_o, e_row, e_l = rel_err(O, Or), row_rel_err(O, Or), rel_err(L, Lr)
+    print(f"{name} {prof} N={tree.N}: O {e_o:.2e} (per row {e_row:.2e}), LSE {e_l:.2e}", flush=True)
+    assert np.isfinite(O.float().cpu().numpy()).all() and np.isfinite(L.cpu().numpy()).all()
+    assert e_o < TOL and e_row < TOL and e_l < TOL
 
 
 def test_mfma_forward_deterministic():
