@@ -340,7 +340,8 @@ int tree_weighted_nll_noalloc(const tt_nll_args* args, tt_stream stream);
  * (boundaries at multiples of the chunk length) from the right, adding dK, dV
  * into float32 stack accumulators, then writes each popped segment's dK, dV
  * rows out and clears their stack slots.  On the matrix cores with groups of
- * a multiple of 4 query heads, consecutive chunk calls share one launch
+ * a multiple of 4 query heads (or of 2 over an even number of kv heads),
+ * consecutive chunk calls share one launch
  * (three for chunks of up to 2048 rows, two above; each with its own dO
  * copy, dQ block and pair of accumulators, summed when the segment is
  * popped), so that one chunk's workgroups fill the CUs another leaves idle.  Each call starts at the 64-aligned

@@ -57,21 +57,28 @@ struct __align__(16) DqStage {
 // WIDE: K/V of 2 GiB or more (each tile's descriptors start at the tile).
 // The body of the dQ kernel for workgroup `bid` (the kernel below, or the
 // dQ part of the combined backward launch).
-template <int G, bool FIN, bool WIDE>
+// KVP: key/value heads per workgroup.  With KVP = 2 the workgroup runs the
+// same query block for two kv heads (2 G waves each, each set staging its own
+// head's K/V tiles: st[2 * buffer + set]); both sets walk the block's one tile
+// list, so they meet at every barrier.  That gives GQA-2 workgroups of 8
+// waves, the size the combined launch needs.
+template <int G, bool FIN, bool WIDE, int KVP = 1>
 __device__ __forceinline__ void dq_body(
-    DqStage (&st)[2], const int bid, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    DqStage* __restrict__ st, const int bid, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ d_o, const float* __restrict__ lse,
     const float* __restrict__ Dv, float* __restrict__ dq_acc, uint16_t* __restrict__ dq_out,
     const float2* __restrict__ cs_tab, const PlanPtrs& P, const AttnGeom& g, int full_range, int qb_first, int n_qb,
     int nsub) {
-  using C = DqCfg<G>;
+  static_assert(KVP == 1 || KVP == 2, "one or two kv heads per workgroup");
+  constexpr int KW = DqCfg<G>::WAVES;  // waves per kv head
   if (!plan_matches(P)) return;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r = lane & 31, hh = lane >> 5;
-  const int kvh = bid % g.h_kv;
-  const int rest = bid / g.h_kv;
+  const int kvs = KVP == 1 ? 0 : wave / KW, kw = KVP == 1 ? wave : wave % KW;  // kv set, wave within it
+  const int kvh = (bid % (g.h_kv / KVP)) * KVP + kvs;
+  const int rest = bid / (g.h_kv / KVP);
   const int sub = rest % nsub, idx = rest / nsub;
   const int qb = full_range ? ld_uniform(P.qb_order, idx) : (qb_first + n_qb - 1 - idx);
-  const int head = (kvh * nsub + sub) * G + (wave >> 1);
+  const int head = (kvh * nsub + sub) * G + (kw >> 1);
   const int pos0 = (wave & 1) * 32;
   const int row = qb * BQ - g.q_off + pos0 + r;  // q-buffer row of this lane's query
   const bool rok = row < g.n_q;
@@ -97,19 +104,20 @@ __device__ __forceinline__ void dq_body(
   const rsrc_t re = make_rsrc(P.end, uint32_t(g.n_k) * 4);
   const rsrc_t rk0 = make_rsrc(k, WIDE ? 0u : uint32_t(kv_elems * 2)), rv0 = make_rsrc(v, WIDE ? 0u : uint32_t(kv_elems * 2));
   // K and V tiles go from global memory straight into LDS in the swizzled
-  // layout, NL loads of 1 KB per wave each, as in the forward
-  constexpr int NL = (BK * D * 2 / 1024) / C::WAVES;
-  static_assert(NL * C::WAVES * 1024 == BK * D * 2, "the waves' 1 KB loads cover a tile");
+  // layout, NL loads of 1 KB per wave each, as in the forward (each kv set
+  // loads its own head's tiles)
+  constexpr int NL = (BK * D * 2 / 1024) / KW;
+  static_assert(NL * KW * 1024 == BK * D * 2, "the waves' 1 KB loads cover a tile");
   uint32_t dvoff[NL];
 #pragma unroll
   for (int i = 0; i < NL; ++i) {
-    const int p = (wave * NL + i) * 64 + lane;
+    const int p = (kw * NL + i) * 64 + lane;
     const int key = p >> 4, c = (p & 15) ^ swz(p >> 4);
     dvoff[i] = (uint32_t(key * g.h_kv + kvh) * D + c * 8) * 2;
   }
   int32_t ereg = 0;
   auto load_tile = [&](int kb, DqStage& s) {
-    const uint32_t kbase = lds_u32(s.K) + wave * NL * 1024, vbase = lds_u32(s.V) + wave * NL * 1024;
+    const uint32_t kbase = lds_u32(s.K) + kw * NL * 1024, vbase = lds_u32(s.V) + kw * NL * 1024;
     if constexpr (WIDE) {
       const int64_t t0 = int64_t(kb) * tile_elems;
       const uint32_t bytes = tile_rec_bytes(kv_elems - t0);
@@ -137,8 +145,9 @@ __device__ __forceinline__ void dq_body(
   const int e0 = ld_uniform(P.qb_ptr, qb), e1 = ld_uniform(P.qb_ptr, qb + 1);
   int cur = e0 < e1 ? ld_uniform(P.qb_tiles, e0) : 0;
   int nxt = e0 + 1 < e1 ? ld_uniform(P.qb_tiles, e0 + 1) : 0;
+  // the tile's end[] (the same for every kv head) goes to set 0's stage only
   if (e0 < e1) {
-    load_tile(cur & kKbMask, st[0]);
+    load_tile(cur & kKbMask, st[kvs]);
     store_end(st[0]);
   }
   wait_vmem();  // also the direct-to-LDS loads, which the compiler does not track
@@ -150,8 +159,10 @@ __device__ __forceinline__ void dq_body(
     const bool full = (ent & kFull) != 0;
     cur = nxt;
     if (e + 2 < e1) nxt = ld_uniform(P.qb_tiles, e + 2);
-    if (e + 1 < e1) load_tile(cur & kKbMask, st[sidx ^ 1]);  // that stage was last read in the previous tile
-    const DqStage& S = st[sidx];
+    // the other buffer was last read in the previous tile
+    if (e + 1 < e1) load_tile(cur & kKbMask, st[(sidx ^ 1) * KVP + kvs]);
+    const DqStage& S = st[sidx * KVP + kvs];
+    const int32_t* __restrict__ S_end = st[sidx * KVP].end;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
       f32x16 s = splat16_here(neg_lse2), dp = splat16_here(neg_D);
@@ -172,7 +183,7 @@ __device__ __forceinline__ void dq_body(
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int kl = kt * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
-          const bool vis = (kb * BK + kl <= qpos) & (qpos < S.end[kl]);
+          const bool vis = (kb * BK + kl <= qpos) & (qpos < S_end[kl]);
           s[i] = vis ? exp2_fast(s[i]) * dp[i] : 0.f;
         }
       }
@@ -184,7 +195,7 @@ __device__ __forceinline__ void dq_body(
         acc[dt] = mfma(tr_frag_swz(S.K, kt * 32 + 16, dt * 32, lane), d1, acc[dt]);
       }
     }
-    if (e + 1 < e1) store_end(st[sidx ^ 1]);
+    if (e + 1 < e1) store_end(st[(sidx ^ 1) * KVP]);
     wait_vmem();  // this wave's direct-to-LDS loads of the next tile have landed
     __syncthreads();
   }
@@ -627,10 +638,17 @@ __global__ __launch_bounds__(KV_THREADS, 2) void dkdv_mfma_kernel(
 // longest workgroups go first (dK/dV in tree mode, where a shared root's keys
 // walk every query; dQ for a short chunk of queries against a long prefix);
 // the rest fill the CUs the first leave idle.  Every workgroup has 8 waves
-// (four query heads per dQ workgroup); the two kinds share one LDS
-// allocation.
-static_assert(sizeof(KvLds) >= 2 * sizeof(DqStage), "the dK/dV workgroups' LDS holds the dQ stages");
-static_assert(DqCfg<4>::THREADS == KV_THREADS, "the combined launch needs equal workgroup sizes");
+// (four query heads per dQ workgroup: one kv head's group of 4, or two kv
+// heads' groups of 2); the two kinds share one LDS allocation.
+// GK: the dK/dV body's group size (0: a multiple of 4 read at run time).
+template <int GK>
+struct DqOf {
+  static constexpr int G = GK == 2 ? 2 : 4;    // query heads per kv head in a dQ workgroup
+  static constexpr int KVP = GK == 2 ? 2 : 1;  // kv heads per dQ workgroup
+};
+static_assert(sizeof(KvLds) >= 2 * 2 * sizeof(DqStage), "the dK/dV workgroups' LDS holds the dQ stages");
+static_assert(DqCfg<4>::THREADS == KV_THREADS && 2 * DqCfg<2>::THREADS == KV_THREADS,
+              "the combined launch needs equal workgroup sizes");
 
 struct BwdCall {
   const uint16_t* q;
@@ -666,8 +684,9 @@ __global__ __launch_bounds__(KV_THREADS, 2) void bwd_mfma_kernel(
     dkdv_body<GK, ACC, TG, WQ>(*reinterpret_cast<KvLds*>(smem), dq_first ? b - n_dq : b, q, k, v, d_o, lse, Dv,
                                d_k, d_v, cs_tab, P, g);
   else
-    dq_body<4, FIN, WKV>(*reinterpret_cast<DqStage(*)[2]>(smem), dq_first ? b : b - n_kv, q, k, v, d_o, lse, Dv,
-                         dq_acc, dq_out, cs_tab, P, g, full_range, qb_first, n_qb, nsub);
+    dq_body<DqOf<GK>::G, FIN, WKV, DqOf<GK>::KVP>(reinterpret_cast<DqStage*>(smem), dq_first ? b : b - n_kv, q, k,
+                                                  v, d_o, lse, Dv, dq_acc, dq_out, cs_tab, P, g, full_range,
+                                                  qb_first, n_qb, nsub);
 }
 
 // Several calls (a separate kernel: the per-call selection costs the
@@ -687,8 +706,9 @@ __global__ __launch_bounds__(KV_THREADS, 2) void bwd_multi_mfma_kernel(const uin
     dkdv_body<GK, ACC, TG, WQ>(*reinterpret_cast<KvLds*>(smem), lb, c.q, k, v, c.d_o, c.lse, c.Dv,
                                static_cast<TG*>(c.d_k), static_cast<TG*>(c.d_v), cs_tab, P, c.g);
   else
-    dq_body<4, FIN, WKV>(*reinterpret_cast<DqStage(*)[2]>(smem), lb, c.q, k, v, c.d_o, c.lse, c.Dv, c.dq_acc,
-                         c.dq_out, cs_tab, P, c.g, full_range, c.qb_first, c.n_qb, nsub);
+    dq_body<DqOf<GK>::G, FIN, WKV, DqOf<GK>::KVP>(reinterpret_cast<DqStage*>(smem), lb, c.q, k, v, c.d_o, c.lse,
+                                                  c.Dv, c.dq_acc, c.dq_out, cs_tab, P, c.g, full_range, c.qb_first,
+                                                  c.n_qb, nsub);
 }
 
 template <int G>
@@ -746,7 +766,10 @@ int launch_bwd_g(const BwdCallPtrs* calls, int n_calls, const void* k, const voi
     int32_t what, count;
   } seg[2 * kMaxBwdCalls];
   int ns = 0;
-  const int nsub = (calls[0].g.h_q / calls[0].g.h_kv) / 4;
+  // dQ workgroups: one per q-block and kv head (groups of a multiple of 4
+  // heads, nsub per kv head) or per q-block and pair of kv heads (groups of 2)
+  constexpr int KVP = DqOf<GK>::KVP;
+  const int nsub = (calls[0].g.h_q / calls[0].g.h_kv) / DqOf<GK>::G;
   for (int i = 0; i < n_calls; ++i) {
     const AttnGeom& g = calls[i].g;
     BwdCall& c = G.c[i];
@@ -762,7 +785,7 @@ int launch_bwd_g(const BwdCallPtrs* calls, int n_calls, const void* k, const voi
     c.qb_first = g.q_off / BQ;
     c.n_qb = (g.q_off + g.n_q + BQ - 1) / BQ - c.qb_first;
     const int n_kv = (g.n_k + KV_KEYS - 1) / KV_KEYS * g.h_kv;
-    const int n_dq = c.n_qb > 0 ? c.n_qb * g.h_kv * nsub : 0;
+    const int n_dq = c.n_qb > 0 ? c.n_qb * (g.h_kv / KVP) * nsub : 0;
     // a dK/dV workgroup walks up to n_q query rows x the group's heads (64
     // MFMAs per wave per 64 rows and head), a dQ one up to n_k keys (48 MFMAs
     // per wave per 64 keys); dK/dV is listed first, so it leads on a tie
@@ -815,7 +838,8 @@ int launch_bwd_mfma_multi(const BwdCallPtrs* calls, int n_calls, const void* k, 
   if (n_calls < 1 || n_calls > kMaxBwdCalls) return -1;
   const AttnGeom& g0 = calls[0].g;
   const int G = g0.h_q / g0.h_kv;
-  if (group_split(G) != 4) return -2;  // the dQ workgroups of smaller groups have fewer waves
+  // the dQ workgroups of other groups have fewer waves than the dK/dV ones
+  if (!bwd_combined_supported(g0.h_q, g0.h_kv)) return -2;
   const bool fin = calls[0].dq_out != nullptr;
   if (!acc && !fin) return -2;
   bool wide = false;
@@ -826,6 +850,10 @@ int launch_bwd_mfma_multi(const BwdCallPtrs* calls, int n_calls, const void* k, 
            int64_t(g.n_q) * g.h_q * D * 2 >= (int64_t(1) << 31);
   }
 #define TT_B(GK, ACC, TG, FIN) launch_bwd_g<GK, ACC, TG, FIN>(calls, n_calls, k, v, cs_tab, P, full_range, wide, st)
+  if (G == 2) {
+    if (!acc) return TT_B(2, false, uint16_t, true);
+    return fin ? TT_B(2, true, float, true) : TT_B(2, true, float, false);
+  }
   if (G == 4) {
     if (!acc) return TT_B(4, false, uint16_t, true);
     return fin ? TT_B(4, true, float, true) : TT_B(4, true, float, false);

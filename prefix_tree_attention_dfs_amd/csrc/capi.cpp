@@ -194,8 +194,9 @@ int attn_bwd_core(tt_dtype dt, const PlanPtrs& P, const AttnGeom& g, const void*
   }
   if (dt == TT_BF16 && mfma_bwd_supported(g, P)) {
     // one launch for dQ and dK/dV when the dQ workgroups have the dK/dV
-    // workgroups' size (four query heads each: groups of a multiple of 4)
-    if ((g.h_q / g.h_kv) % 4 == 0 && (acc || dq_final)) {
+    // workgroups' size (four query heads each: groups of a multiple of 4, or
+    // two kv heads' pairs)
+    if (bwd_combined_supported(g.h_q, g.h_kv) && (acc || dq_final)) {
       int rc = -2;
       {
         KTimer t("attn_bwd_mfma", st);

@@ -47,6 +47,15 @@ int launch_dq_mfma(const void* q, const void* k, const void* v, const void* d_o,
 int launch_dkdv_mfma(const void* q, const void* k, const void* v, const void* d_o, const float* lse, const float* D,
                      void* d_k, void* d_v, bool acc, const float2* cs_tab, const PlanPtrs& P, const AttnGeom& g,
                      hipStream_t st);
+// Group sizes the one-launch backward takes: a multiple of 4 query heads per
+// kv head (a dQ workgroup = one kv head's 4 heads), or 2 with an even number of
+// kv heads (a dQ workgroup = two kv heads' pairs); either way 8 waves, the
+// dK/dV workgroups' size.
+inline bool bwd_combined_supported(int32_t h_q, int32_t h_kv) {
+  if (h_kv <= 0 || h_q % h_kv != 0) return false;
+  const int32_t G = h_q / h_kv;
+  return G % 4 == 0 || (G == 2 && h_kv % 2 == 0);
+}
 // dQ (as launch_dq_mfma) and dK/dV (as launch_dkdv_mfma) in one launch;
 // returns -2 (nothing launched) when the group size or output form is not
 // covered (then the two launches above apply)

@@ -57,8 +57,9 @@ PathWs path_ws(const tt_path_args* a, bool bwd) {
   const bool mfma = a->dtype == TT_BF16 && ttc::mfma_shape(a->d, 64, 64);
   PathWs w;
   // several calls per launch where the combined matrix-core launch exists
-  // (the dQ workgroups take four query heads: groups of a multiple of 4)
-  w.slots = !(mfma && (a->h_q / a->h_kv) % 4 == 0) ? 1
+  // (8-wave dQ workgroups: groups of a multiple of 4 heads, or of 2 with an
+  // even number of kv heads)
+  w.slots = !(mfma && bwd_combined_supported(a->h_q, a->h_kv)) ? 1
             : p->chunk <= kPathSmallChunk          ? kPathCallsSmall
                                                    : kPathCallsLarge;
   const size_t S = size_t(w.slots);

@@ -194,8 +194,12 @@ def _bwd_case(name, hq, hkv, std, seed):
 
 
 @pytest.mark.parametrize("name", list(TREES))
-@pytest.mark.parametrize("heads", [(8, 2), (4, 2), (2, 2), (16, 2), (6, 2)])
+@pytest.mark.parametrize("heads", [(8, 2), (4, 2), (2, 2), (16, 2), (6, 2), (16, 8), (2, 1)])
 def test_mfma_backward(name, heads):
+    """Groups of 4 (and multiples) and groups of 2 over an even number of kv
+    heads run dQ and dK/dV in one launch (a GQA-2 dQ workgroup takes two kv
+    heads: (4, 2), (16, 8)); groups of 1, 3 and groups of 2 over one kv head
+    run them as two launches."""
     got, ref = _bwd_case(name, heads[0], heads[1], 128 ** -0.5, 41)
     for n, g_, r_ in zip(("dq", "dk", "dv"), got, ref):
         assert rel_err(g_, r_) < TOL, (n, rel_err(g_, r_))

@@ -71,11 +71,13 @@ def test_path_bf16_wide_groups_vs_oracle(hq, hkv):
 
 
 @pytest.mark.parametrize("name", ["beam_small", "chain"])
-def test_path_bf16_gqa2_vs_oracle(name):
-    """Groups of two query heads: each backward chunk is its own call (dQ and
-    dK/dV as separate launches, one accumulator); groups of four share a
-    launch between consecutive chunks (above)."""
-    _, o, _, (qn, kn, vn, don), (O, L, dq, dk, dv) = _run(name, torch.bfloat16, 128, 4, 2, 64, 0, 54)
+@pytest.mark.parametrize("hq,hkv", [(4, 2), (2, 1)])
+def test_path_bf16_gqa2_vs_oracle(name, hq, hkv):
+    """Groups of two query heads.  Over an even number of kv heads the dQ
+    workgroups take two kv heads' pairs, so consecutive chunks share a
+    backward launch as groups of four do; over one kv head each chunk is its
+    own call (dQ and dK/dV as separate launches, one accumulator)."""
+    _, o, _, (qn, kn, vn, don), (O, L, dq, dk, dv) = _run(name, torch.bfloat16, 128, hq, hkv, 64, 0, 54)
     Or, Lr, _ = OA.forward(o, qn, kn, vn, which="leaves")
     dQr, dKr, dVr = OA.backward(o, qn, kn, vn, don, which="leaves")
     for n, g_, r_ in (("o", O, Or), ("lse", L, Lr), ("dq", dq, dQr), ("dk", dk, dKr), ("dv", dv, dVr)):

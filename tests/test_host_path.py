@@ -212,12 +212,15 @@ def _path_ws_expected(L, chunk, hq, hk, d, es, bwd, slots, mfma):
 
 
 @pytest.mark.parametrize("hq,hk,d,dtype,chunk,slots", [(8, 2, 128, "bf16", 128, 3), (32, 8, 128, "bf16", 2048, 3),
-                                                       (32, 8, 128, "bf16", 4096, 2), (4, 2, 128, "bf16", 128, 1),
+                                                       (32, 8, 128, "bf16", 4096, 2), (4, 2, 128, "bf16", 128, 3),
+                                                       (16, 8, 128, "bf16", 4096, 2), (2, 1, 128, "bf16", 128, 1),
+                                                       (6, 2, 128, "bf16", 128, 1), (2, 2, 128, "bf16", 128, 1),
                                                        (8, 2, 64, "bf16", 128, 1), (8, 2, 64, "f32", 128, 1)])
 def test_path_workspace_slots(hq, hk, d, dtype, chunk, slots):
-    """Matrix-core walks with groups of a multiple of 4 heads hold several sets
-    of per-call buffers and accumulators (three chunks per backward launch up
-    to chunks of 2048 rows, two above); other shapes one."""
+    """Matrix-core walks whose backward runs as one launch (groups of a
+    multiple of 4 heads, or of 2 over an even number of kv heads) hold several
+    sets of per-call buffers and accumulators (three chunks per backward
+    launch up to chunks of 2048 rows, two above); other shapes one."""
     import ctypes
     case = ts.random_small_tree(3, n_seqs=6, max_len=300, vocab=3)
     t = tt.Tree(case.seqs)
