@@ -23,6 +23,11 @@
 //                    dV^T += dO^T P, dK^T += Q^T dS.
 // Recomputing S and dP in both kernels costs 14 d MFMA flops per visible pair
 // instead of 10 d, in exchange for no fp32 atomic traffic on dQ.
+// Where both kinds of workgroup have 8 waves (groups of a multiple of 4 query
+// heads; groups of 2 over an even number of kv heads, a dQ workgroup then
+// taking two kv heads) they run as one launch, bwd_mfma_kernel (or, for
+// several independent calls, bwd_multi_mfma_kernel), the kind with the
+// longest workgroups first.
 #include <algorithm>
 
 #include "device.h"
