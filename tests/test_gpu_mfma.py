@@ -316,6 +316,55 @@ def test_mfma_backward_agentic_8b_shape_sampled():
     assert tot < 2e-2 * np.abs(dkr).sum(0).max(), tot
 
 
+def test_mfma_backward_rl_forest_1p7b_sampled():
+    """The 1.7B-shape RL forest at full size (16 query heads, 8 kv heads: the
+    one-launch backward with dQ workgroups over kv-head pairs, 2,840 of them
+    beside 712 dK/dV workgroups): dQ on sampled rows, dK/dV on sampled keys
+    with subtrees of up to 40 rows and on one key whose subtree holds about 100
+    rows; over all keys, sum_j dV_j = sum over the group's two
+    query heads of sum_i dO_i, and sum_j R(depth_j) dK_j = 0."""
+    case = ts.rl_forest_accepted(0)
+    tree = tt.Tree(case.seqs)
+    o = dfs_arrays(case.seqs)
+    N = tree.N
+    rng = ts.rng_for(2100)
+    qb = ts.normal_bf16(rng, (N, 16, 128), 128 ** -0.5)
+    kb = ts.normal_bf16(rng, (N, 8, 128), 128 ** -0.5)
+    vb = ts.normal_bf16(rng, (N, 8, 128), 128 ** -0.5)
+    ob = ts.normal_bf16(rng, (N, 16, 128), 1.0)
+    dev = lambda b: torch.from_numpy(b.view(np.int16)).cuda().view(torch.bfloat16)  # noqa: E731
+    plan = tree.upload_plan()
+    q, k, v, do = dev(qb), dev(kb), dev(vb), dev(ob)
+    print(f"rl forest seed {case.seed}: N={N}", flush=True)
+    O, L = tt.tree_attn_fwd(tree, plan, q, k, v)
+    dq, dk, dv = tt.tree_attn_bwd(tree, plan, q, k, v, O, L, do)
+
+    def get(name, idx):
+        return ts.bf16_bits_to_f64({"q": qb, "k": kb, "v": vb, "do": ob}[name][idx])
+
+    rows = np.unique(np.concatenate([np.linspace(0, N - 1, 12).astype(int), [0, 63, 64, N - 1]]))
+    ref = OA.dq_rows(o, None, None, None, None, rows, get=get)
+    assert rel_err(dq[torch.as_tensor(rows, device="cuda")], ref) < TOL
+    sub = o["end"] - np.arange(N)
+    small = np.nonzero(sub <= 40)[0]
+    keys = small[np.linspace(0, len(small) - 1, 6).astype(int)]
+    # and the last key whose subtree holds 100-300 rows (the oracle's cost per
+    # key grows with subtree rows x depth: ~10 s here)
+    mid = np.nonzero((sub >= 100) & (sub <= 300))[0]
+    keys = np.concatenate([keys, mid[-1:]])
+    print(f"keys {keys.tolist()} subtree rows {sub[keys].tolist()}", flush=True)
+    rk, rv = OA.dkdv_keys(o, None, None, None, None, keys, get=get)
+    ki = torch.as_tensor(keys, device="cuda")
+    assert rel_err(dk[ki], rk) < TOL and rel_err(dv[ki], rv) < TOL
+    sdv = dv.float().sum(0).cpu().double().numpy()
+    sdo = do.float().reshape(N, 8, 2, 128).sum((0, 2)).cpu().double().numpy()
+    assert rel_err(torch.from_numpy(sdv), sdo) < TOL
+    from oracle.rope import rotate
+    dkr = rotate(dk.float().cpu().double().numpy(), o["depth"], 10000.0)
+    tot = np.abs(dkr.sum(0)).max()
+    assert tot < 2e-2 * np.abs(dkr).sum(0).max(), tot
+
+
 def test_mfma_chain_suffix_chunks_8b_full():
     """The 8B-shape path configuration at full size, launched as timed: a
     49,152-token chain whose last 16,384 queries run in 2048-row chunks right
