@@ -70,10 +70,10 @@ __global__ __launch_bounds__(FwdCfg<G>::THREADS, FwdCfg<G>::MINB) void fwd_mfma_
   const int pos0 = (wave % C::WPH) * 32 * NT;
   const int qrow0 = qb * BQ - g.q_off;  // q-buffer row of the block's first position
   // the exponentials run against the running max (log2 units) without a tile
-  // max: a lane's 16 values of a 32-key half are accepted while their sum is
-  // at most tsum (so every p <= 2^8, which the fp32 sums and the bf16 P
+  // max: a lane's 16 values of each 32-key half are accepted while their sum
+  // is at most tsum (so every p <= 2^8, which the fp32 sums and the bf16 P
   // operand carry without loss of relative precision); otherwise, and for a
-  // row with no max yet, the half is redone with the max moved to the exact
+  // row with no max yet, the tile is redone with the max moved to the exact
   // running max.  Any max gives the same softmax: O and l share it, and the
   // LSE adds it back.
   constexpr float tsum = 256.f;
@@ -203,11 +203,9 @@ __global__ __launch_bounds__(FwdCfg<G>::THREADS, FwdCfg<G>::MINB) void fwd_mfma_
     const FwdStage& S = st[sidx];
 
     // S^T = K Q^T - m for both 32-key halves (scores in log2 units relative to
-    // the running max), mask, then per half: exponentials against the running
-    // max, redone in the rare case above (a row without a max yet, or a lane
-    // whose sum exceeds tsum), then O^T += V^T P^T for the half.  The first
-    // half's products and the second half's exponentials share a basic block,
-    // so the scheduler overlaps them.
+    // the running max), mask, exponentials of both halves against the running
+    // max, one vote for the rare case above (a row without a max yet, or a
+    // lane's half whose sum exceeds tsum), then O^T += V^T P^T.
     f32x16 sv[2][NT];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
@@ -241,24 +239,27 @@ __global__ __launch_bounds__(FwdCfg<G>::THREADS, FwdCfg<G>::MINB) void fwd_mfma_
       mask_half(1);
     }
     bf16x8 pf[2][2][NT];
+    float ls[2][NT];
+    bool redo = false;
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      float ls[NT];
-      bool redo = false;
+    for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-        ls[nt] = 0.f;
+        ls[kt][nt] = 0.f;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const float p = exp2_fast(sv[kt][nt][i]);
           sv[kt][nt][i] = p;
-          ls[nt] += p;
+          ls[kt][nt] += p;
         }
-        redo |= (m[nt] == -INFINITY) | !(ls[nt] <= tsum);
+        redo |= (m[nt] == -INFINITY) | !(ls[kt][nt] <= tsum);
       }
-      if (__any(redo)) {
-        // rare: raw scores of the half again, max moved to the exact running
-        // max (O and l rescaled), exponentials against it
+    if (__any(redo)) {
+      // rare: raw scores of both halves again (the K tile is still staged),
+      // the max moved to the exact running max (O and l rescaled), the
+      // exponentials against it
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) sv[kt][nt] = zero16();
 #pragma unroll
@@ -268,44 +269,48 @@ __global__ __launch_bounds__(FwdCfg<G>::THREADS, FwdCfg<G>::MINB) void fwd_mfma_
           for (int nt = 0; nt < NT; ++nt) sv[kt][nt] = mfma(a, qf[nt][dc], sv[kt][nt]);
         }
         if (!full) mask_half(kt);
+      }
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          float mx = -INFINITY;
+      for (int nt = 0; nt < NT; ++nt) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
           for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sv[kt][nt][i]);
-          mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-          const float mn = m[nt] == -INFINITY ? mx : fmaxf(m[nt], mx);
-          if (m[nt] != -INFINITY && mn > m[nt]) {
-            const float alpha = exp2_fast(m[nt] - mn);
-            lpart[nt] *= alpha;
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        const float mn = m[nt] == -INFINITY ? mx : fmaxf(m[nt], mx);
+        if (m[nt] != -INFINITY && mn > m[nt]) {
+          const float alpha = exp2_fast(m[nt] - mn);
+          lpart[nt] *= alpha;
 #pragma unroll
-            for (int dt = 0; dt < 4; ++dt)
+          for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-              for (int i = 0; i < 16; ++i) oacc[nt][dt][i] *= alpha;
-          }
-          // the other half's scores were taken against the old max: move them too
-          if (kt == 0) {
-            const float shift = mn == -INFINITY ? 0.f : (m[nt] == -INFINITY ? mn : mn - m[nt]);
+            for (int i = 0; i < 16; ++i) oacc[nt][dt][i] *= alpha;
+        }
+        m[nt] = mn;
+        const float neg = mn == -INFINITY ? 0.f : -mn;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) sv[1][nt][i] -= shift;
-          }
-          m[nt] = mn;
-          const float neg = mn == -INFINITY ? 0.f : -mn;
-          ls[nt] = 0.f;
+        for (int kt = 0; kt < 2; ++kt) {
+          ls[kt][nt] = 0.f;
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const float p = exp2_fast(sv[kt][nt][i] + neg);
             sv[kt][nt][i] = p;
-            ls[nt] += p;
+            ls[kt][nt] += p;
           }
         }
       }
+    }
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-        lpart[nt] += ls[nt];
+        lpart[nt] += ls[kt][nt];
 #pragma unroll
         for (int c = 0; c < 2; ++c) pf[kt][c][nt] = c_to_b(sv[kt][nt], c);
       }
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
@@ -314,7 +319,6 @@ __global__ __launch_bounds__(FwdCfg<G>::THREADS, FwdCfg<G>::MINB) void fwd_mfma_
 #pragma unroll
           for (int nt = 0; nt < NT; ++nt) oacc[nt][dt] = mfma(a, pf[kt][c][nt], oacc[nt][dt]);
         }
-    }
 
     if (e + 1 < e1) store_end(st[sidx ^ 1]);
     wait_vmem();  // this wave's direct-to-LDS loads of the next tile have landed

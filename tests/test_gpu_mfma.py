@@ -84,12 +84,12 @@ def _moving_max_inputs(N, hq, hkv, prof, seed):
 @pytest.mark.parametrize("name,heads", [("beam_small", (8, 2)), ("chain", (4, 2)), ("forest", (8, 2))])
 def test_mfma_forward_moving_max(prof, name, heads):
     """Scores that move the running max along the walk.  The forward takes its
-    exponentials against the running max and redoes a 32-key half when a
-    row's partial sum passes the bound or the row meets its first visible
-    key (then the other half's pending scores move with the max): here whole
-    walks of halves do that (rising), some tiles do and others not (sawtooth),
-    or one jump lands in a tile's second half after a quiet first half (step).
-    No RoPE, so each score is the one constructed."""
+    exponentials against the running max and redoes a tile when a row's
+    partial sum over a 32-key half passes the bound or the row meets its
+    first visible key: here whole walks of tiles do that (rising), some tiles
+    do and others not (sawtooth), or one jump lands in a tile's second half
+    after a quiet first half (step).  No RoPE, so each score is the one
+    constructed."""
     case = TREES[name]()
     tree = tt.Tree(case.seqs)
     o = dfs_arrays(case.seqs)
