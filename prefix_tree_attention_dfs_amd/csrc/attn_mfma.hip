@@ -197,9 +197,14 @@ __global__ __launch_bounds__(FwdCfg<G>::THREADS, FwdCfg<G>::MINB) void fwd_mfma_
     const int ent = cur;
     const int kb = ent & kKbMask;
     const bool full = (ent & kFull) != 0;
+    // the next tile's loads, without a branch: on the block's last tile cur is
+    // that tile again (the list entry two ahead is clamped to the last one;
+    // tile 0 for a one-tile block), so the spare stage receives a copy nobody
+    // reads, and the wait before the barrier below still covers it (a uniform
+    // branch here cost 0.6%)
     cur = nxt;
-    if (e + 2 < e1) nxt = ld_uniform(P.qb_tiles, e + 2);
-    if (e + 1 < e1) load_tile(cur & kKbMask, st[sidx ^ 1]);  // that stage was last read in the previous tile
+    nxt = ld_uniform(P.qb_tiles, min(e + 2, e1 - 1));
+    load_tile(cur & kKbMask, st[sidx ^ 1]);  // that stage was last read in the previous tile
     const FwdStage& S = st[sidx];
 
     // S^T = K Q^T - m for both 32-key halves (scores in log2 units relative to
@@ -320,7 +325,7 @@ __global__ __launch_bounds__(FwdCfg<G>::THREADS, FwdCfg<G>::MINB) void fwd_mfma_
           for (int nt = 0; nt < NT; ++nt) oacc[nt][dt] = mfma(a, pf[kt][c][nt], oacc[nt][dt]);
         }
 
-    if (e + 1 < e1) store_end(st[sidx ^ 1]);
+    store_end(st[sidx ^ 1]);
     wait_vmem();  // this wave's direct-to-LDS loads of the next tile have landed
     __syncthreads();
   }
